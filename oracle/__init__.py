@@ -1,0 +1,191 @@
+"""Python access to the fp64 CPU oracle (oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the CPU
+baseline leg of the benchmark, never by the product path.  It shares no code
+with the HIP library; both only read the same generator-made input arrays.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SO = os.path.join(_HERE, "liboracle.so")
+
+F32, BF16, E4M3 = 0, 1, 2
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with gcc: OpenMP, no fp contraction, no fast-math."""
+    if force or not os.path.exists(_SO):
+        tmp = _SO + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared",
+                               os.path.join(_HERE, "oracle.c"), "-o", tmp, "-lm"])
+        os.replace(tmp, _SO)
+    return _SO
+
+
+class Cfg(ctypes.Structure):
+    _fields_ = [("H", ctypes.c_int32), ("E", ctypes.c_int32), ("G", ctypes.c_int32),
+                ("TG", ctypes.c_int32), ("K", ctypes.c_int32), ("I", ctypes.c_int32),
+                ("Is", ctypes.c_int32), ("rho", ctypes.c_double)]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO):
+            build()
+        L = ctypes.CDLL(_SO)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+        L.oracle_threads.restype = ctypes.c_int
+        L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+        L.oracle_e4m3_decode.restype = ctypes.c_double
+        L.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+        L.oracle_e4m3_encode.restype = ctypes.c_uint8
+        L.oracle_quant_rows.argtypes = [i64, i32, vp, vp, vp]
+        L.oracle_quant_rows.restype = None
+        L.oracle_logits.argtypes = [i64, i32, i32, vp, i32, vp, vp]
+        L.oracle_logits.restype = None
+        L.oracle_route_f64.argtypes = [ctypes.POINTER(Cfg), i64, vp, vp, vp, vp, vp]
+        L.oracle_route_f64.restype = ctypes.c_int
+        L.oracle_route_f32.argtypes = [ctypes.POINTER(Cfg), i64, vp, vp, vp, vp]
+        L.oracle_route_f32.restype = ctypes.c_int
+        L.oracle_permute.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp]
+        L.oracle_permute.restype = ctypes.c_int
+        L.oracle_layer.argtypes = [ctypes.POINTER(Cfg), i64, vp, vp, i32, vp, vp,
+                                   vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp]
+        L.oracle_layer.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _c(a, dtype=None):
+    a = np.ascontiguousarray(a if dtype is None else np.asarray(a, dtype=dtype))
+    return a
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data
+
+
+def cfg_of(c) -> Cfg:
+    """Oracle shape record from a synth.MoEConfig (or any object with the fields)."""
+    return Cfg(c.H, c.E, c.G, c.TG, c.K, c.I, c.Is, float(c.rho))
+
+
+def dtype_code(arr: np.ndarray, declared: str) -> int:
+    return {"f32": F32, "bf16": BF16, "fp8": E4M3}[declared]
+
+
+def threads() -> int:
+    return lib().oracle_threads()
+
+
+def e4m3_decode(code: int) -> float:
+    return lib().oracle_e4m3_decode(code)
+
+
+def e4m3_encode(v: float) -> int:
+    return lib().oracle_e4m3_encode(v)
+
+
+def quant_rows(v: np.ndarray):
+    """1x128 e4m3 quantisation of a float32 [rows, cols] array -> (codes u8, scales f32)."""
+    v = _c(v, np.float32)
+    rows, cols = v.shape
+    assert cols % 128 == 0
+    q = np.empty((rows, cols), np.uint8)
+    s = np.empty((rows, cols // 128), np.float32)
+    lib().oracle_quant_rows(rows, cols, _p(v), _p(q), _p(s))
+    return q, s
+
+
+def logits(x: np.ndarray, x_kind: str, gate_w: np.ndarray) -> np.ndarray:
+    """x [T,H] (float32, or bf16 bits as uint16) times gate_w [E,H]^T in fp64."""
+    x = _c(x)
+    gate_w = _c(gate_w, np.float32)
+    T, H = x.shape
+    E = gate_w.shape[0]
+    out = np.empty((T, E), np.float64)
+    lib().oracle_logits(T, H, E, _p(x), F32 if x_kind == "f32" else BF16, _p(gate_w), _p(out))
+    return out
+
+
+def route_f64(cfg, lg: np.ndarray, bias: np.ndarray):
+    """fp64 router -> (idx int32 [T,K], w float64 [T,K], margin float64 [T])."""
+    lg = _c(lg, np.float64)
+    bias = _c(bias, np.float32)
+    T = lg.shape[0]
+    idx = np.empty((T, cfg.K), np.int32)
+    w = np.empty((T, cfg.K), np.float64)
+    m = np.empty(T, np.float64)
+    rc = lib().oracle_route_f64(ctypes.byref(cfg_of(cfg)), T, _p(lg), _p(bias), _p(idx), _p(w), _p(m))
+    if rc:
+        raise ValueError(f"oracle_route_f64 rejected the configuration (rc={rc})")
+    return idx, w, m
+
+
+def route_f32(cfg, lg32: np.ndarray, bias: np.ndarray):
+    """Router under the fp32 selection contract -> (idx int32 [T,K], w float64 [T,K])."""
+    lg32 = _c(lg32, np.float32)
+    bias = _c(bias, np.float32)
+    T = lg32.shape[0]
+    idx = np.empty((T, cfg.K), np.int32)
+    w = np.empty((T, cfg.K), np.float64)
+    rc = lib().oracle_route_f32(ctypes.byref(cfg_of(cfg)), T, _p(lg32), _p(bias), _p(idx), _p(w))
+    if rc:
+        raise ValueError(f"oracle_route_f32 rejected the configuration (rc={rc})")
+    return idx, w
+
+
+def permute(idx: np.ndarray, E: int):
+    """-> (counts [E], offsets [E+1], perm [T*K], pos [T*K]), all int32."""
+    idx = _c(idx, np.int32)
+    T, K = idx.shape
+    counts = np.empty(E, np.int32)
+    offsets = np.empty(E + 1, np.int32)
+    perm = np.empty(T * K, np.int32)
+    pos = np.empty(T * K, np.int32)
+    rc = lib().oracle_permute(T, K, E, _p(idx), _p(counts), _p(offsets), _p(perm), _p(pos))
+    if rc:
+        raise ValueError("oracle_permute: expert index out of range")
+    return counts, offsets, perm, pos
+
+
+def layer(cfg, inp: dict, idx: np.ndarray, w: np.ndarray, tokens=None, quant_act=False):
+    """Layer output (fp64) for the listed tokens (default: all) -> [n_tok, H]."""
+    x = _c(inp["x"])
+    T = x.shape[0]
+    tokens = np.arange(T, dtype=np.int64) if tokens is None else _c(tokens, np.int64)
+    idx = _c(idx, np.int32)
+    w = _c(w, np.float64)
+    wd = {"f32": F32, "bf16": BF16, "fp8": E4M3}[cfg.wdtype]
+    xd = F32 if cfg.act == "f32" else BF16
+    g = lambda k: None if inp.get(k) is None else _c(inp[k])
+    arrs = [g(k) for k in ("w13", "w13_s", "w2", "w2_s", "ws13", "ws13_s", "ws2", "ws2_s")]
+    out = np.empty((len(tokens), cfg.H), np.float64)
+    rc = lib().oracle_layer(ctypes.byref(cfg_of(cfg)), len(tokens), _p(tokens), _p(x), xd,
+                            _p(idx), _p(w), *[_p(a) for a in arrs], wd, int(bool(quant_act)),
+                            _p(out))
+    if rc:
+        raise ValueError("oracle_layer failed (bad expert index or allocation)")
+    return out
+
+
+def forward(cfg, inp: dict, tokens=None, quant_act=False):
+    """Whole layer on the listed tokens with the oracle's own fp64 routing.
+    Returns dict(logits, idx, w, margin, out)."""
+    x = inp["x"] if tokens is None else inp["x"][np.asarray(tokens)]
+    lg = logits(x, cfg.act, inp["gate_w"])
+    idx, w, m = route_f64(cfg, lg, inp["bias"])
+    sub = dict(inp)
+    sub["x"] = x
+    out = layer(cfg, sub, idx, w, quant_act=quant_act)
+    return {"logits": lg, "idx": idx, "w": w, "margin": m, "out": out}

@@ -1,0 +1,428 @@
+"""Pins of the fp64 oracle to things other than itself: hand-worked cases,
+brute-force enumeration, closed forms, special cases that reduce to library
+routines, and invariants of the method.  CPU only."""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+class Shape:
+    def __init__(self, **kw):
+        self.__dict__.update(kw)
+
+
+def _logit(tok):
+    return {"0": 0.0, "ln3": math.log(3.0), "-ln3": -math.log(3.0)}[tok]
+
+
+# ---------------------------------------------------------------- hand cases
+
+def _hand_cases():
+    with open(os.path.join(GOLD, "routing_hand_cases.json")) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _hand_cases(), ids=lambda c: c["name"])
+def test_routing_hand_cases(case):
+    cfg = Shape(H=1, E=case["E"], G=case["G"], TG=case["TG"], K=case["K"], I=0, Is=0,
+                rho=case["rho"])
+    lg = np.array([[_logit(t) for t in case["logits"]]], np.float64)
+    bias = np.array(case["bias"], np.float32)
+    idx, w, _ = oracle.route_f64(cfg, lg, bias)
+    assert idx[0].tolist() == case["idx"]
+    np.testing.assert_allclose(w[0], case["w"], rtol=1e-12, atol=0)
+    # The fp32 contract router takes the same decisions on these exact inputs.
+    idx32, w32 = oracle.route_f32(cfg, lg.astype(np.float32), bias)
+    assert idx32[0].tolist() == case["idx"]
+    np.testing.assert_allclose(w32[0], case["w"], rtol=1e-6, atol=0)
+
+
+def test_ffn_closed_form_h1():
+    with open(os.path.join(GOLD, "ffn_closed_form.json")) as f:
+        c = json.load(f)
+    cfg = synth.MoEConfig("h1", T=1, H=1, E=2, G=1, TG=1, K=1, I=1, Is=1, rho=c["rho"],
+                          act="f32", wdtype="f32", bias_lo=0, bias_hi=0)
+    inp = {"x": np.array([c["x"]], np.float32),
+           "gate_w": np.array(c["gate_w"], np.float32),
+           "bias": np.array(c["bias"], np.float32),
+           "w13": np.array(c["w13"], np.float32), "w13_s": None,
+           "w2": np.array(c["w2"], np.float32), "w2_s": None,
+           "ws13": np.array(c["ws13"], np.float32), "ws13_s": None,
+           "ws2": np.array(c["ws2"], np.float32), "ws2_s": None}
+    r = oracle.forward(cfg, inp)
+    assert r["idx"].tolist() == [[1]]
+    np.testing.assert_allclose(r["w"], [[1.0]], rtol=1e-15)
+    np.testing.assert_allclose(r["out"][0], c["out"], rtol=1e-14)
+
+
+# ---------------------------------------------------------------- logits
+
+@pytest.mark.parametrize("kind", ["f32", "bf16"])
+def test_logits_match_numpy_matmul(kind):
+    T, H, E = 37, 256, 24
+    if kind == "f32":
+        x = synth.normal_f32(T * H, 3, synth.T_TEST, 0, 1.0).reshape(T, H)
+        xf = x.astype(np.float64)
+    else:
+        x = synth.normal_bf16(T * H, 3, synth.T_TEST, 0, 1.0).reshape(T, H)
+        xf = synth.bf16_to_f32(x).astype(np.float64)
+    wg = synth.normal_f32(E * H, 3, synth.T_TEST, 1, 1 / 16).reshape(E, H)
+    lg = oracle.logits(x, kind, wg)
+    ref = xf @ wg.astype(np.float64).T
+    np.testing.assert_allclose(lg, ref, rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------- routing: brute force
+
+def _brute_route(cfg, lg, bias, f32):
+    """Exhaustive reference: best group set = the TG-subset with the largest
+    sum of group scores, group score = best pair sum inside the group; best
+    expert set = the K-subset with the largest sum of masked scores."""
+    E, G, TG, K = cfg.E, cfg.G, cfg.TG, cfg.K
+    Eg = E // G
+    s64 = 1.0 / (1.0 + np.exp(-lg.astype(np.float64)))
+    if f32:
+        s = s64.astype(np.float32)
+        c = (s + bias.astype(np.float32)).astype(np.float32)
+    else:
+        s, c = s64, s64 + bias.astype(np.float64)
+    out = []
+    for t in range(lg.shape[0]):
+        g = []
+        for j in range(G):
+            best = None
+            for a, b in itertools.combinations(range(j * Eg, (j + 1) * Eg), 2):
+                v = c[t, a] + c[t, b]
+                best = v if best is None or v > best else best
+            g.append(float(best))
+        gset = max(itertools.combinations(range(G), TG), key=lambda S: sum(g[j] for j in S))
+        cm = np.array([float(c[t, e]) if (e // Eg) in gset else 0.0 for e in range(E)])
+        eset = max(itertools.combinations(range(E), K), key=lambda S: sum(cm[e] for e in S))
+        out.append((set(eset), cm))
+    return out, s64
+
+
+@pytest.mark.parametrize("G,TG,K", [(4, 2, 2), (2, 1, 1), (2, 1, 3), (4, 1, 2), (4, 3, 3),
+                                    (4, 4, 2), (1, 1, 2), (8, 3, 2)])
+@pytest.mark.parametrize("f32", [False, True])
+def test_route_bruteforce_tiny(G, TG, K, f32):
+    E, T = 16, 24
+    cfg = Shape(H=1, E=E, G=G, TG=TG, K=K, I=0, Is=0, rho=1.0)
+    lg = synth.normal_f32(T * E, 11 + G + 7 * K, synth.T_TEST, TG, 1.0).reshape(T, E).astype(np.float64)
+    bias = synth.uniform_f32(E, 5 + G, synth.T_TEST, 100 + K, -0.1, 0.1)
+    if f32:
+        idx, w = oracle.route_f32(cfg, lg.astype(np.float32), bias)
+        ref, s64 = _brute_route(cfg, lg.astype(np.float32), bias, True)
+        s64 = 1.0 / (1.0 + np.exp(-lg.astype(np.float32).astype(np.float64)))
+    else:
+        idx, w, margin = oracle.route_f64(cfg, lg, bias)
+        ref, s64 = _brute_route(cfg, lg, bias, False)
+    for t in range(T):
+        eset, cm = ref[t]
+        assert set(idx[t].tolist()) == eset, (t, idx[t], eset)
+        # slot order: descending masked score, then lower index
+        vals = [(-cm[e], e) for e in idx[t]]
+        assert vals == sorted(vals)
+        sw = s64[t, idx[t]]
+        expect = sw / (sw.sum() + 1e-20) if K > 1 else sw
+        np.testing.assert_allclose(w[t], expect * cfg.rho, rtol=1e-12)
+
+
+def test_route_special_case_single_group_is_plain_topk():
+    """G = 1 (or TG = G): the group limit is inert, idx = top-K of s + b;
+    with b = 0 as well, top-K of the logits (sigmoid is increasing)."""
+    T, E, K = 200, 64, 6
+    lg = synth.normal_f32(T * E, 1, synth.T_TEST, 2, 1.0).reshape(T, E).astype(np.float64)
+    bias = synth.uniform_f32(E, 1, synth.T_TEST, 3, -0.05, 0.05)
+    s = 1 / (1 + np.exp(-lg))
+    for G, TG in [(1, 1), (8, 8)]:
+        cfg = Shape(H=1, E=E, G=G, TG=TG, K=K, I=0, Is=0, rho=2.5)
+        idx, _, _ = oracle.route_f64(cfg, lg, bias)
+        ref = np.argsort(-(s + bias.astype(np.float64)), axis=1, kind="stable")[:, :K]
+        np.testing.assert_array_equal(idx, ref)
+        idx0, w0, _ = oracle.route_f64(cfg, lg, np.zeros(E, np.float32))
+        np.testing.assert_array_equal(idx0, np.argsort(-lg, axis=1, kind="stable")[:, :K])
+
+
+def test_route_k1_weight_is_scaled_sigmoid():
+    T, E = 64, 32
+    cfg = Shape(H=1, E=E, G=4, TG=2, K=1, I=0, Is=0, rho=2.5)
+    lg = synth.normal_f32(T * E, 2, synth.T_TEST, 4, 1.5).reshape(T, E).astype(np.float64)
+    bias = synth.uniform_f32(E, 2, synth.T_TEST, 5, -0.05, 0.05)
+    idx, w, _ = oracle.route_f64(cfg, lg, bias)
+    sel = np.take_along_axis(lg, idx.astype(np.int64), axis=1)
+    np.testing.assert_allclose(w, 2.5 / (1 + np.exp(-sel)), rtol=1e-15)
+
+
+# ---------------------------------------------------------------- routing: invariants at the V3 shape
+
+@pytest.fixture(scope="module")
+def v3_route():
+    cfg = synth.C2
+    T = 384
+    x = synth.gen_x(cfg, T)
+    wg, b = synth.gen_gate(cfg)
+    lg = oracle.logits(x, "bf16", wg)
+    idx, w, m = oracle.route_f64(cfg, lg, b)
+    return cfg, lg, b, idx, w, m
+
+
+def test_invariants_v3(v3_route):
+    cfg, lg, b, idx, w, m = v3_route
+    Eg = cfg.E // cfg.G
+    s = 1 / (1 + np.exp(-lg))
+    c = s + b.astype(np.float64)
+    for t in range(lg.shape[0]):
+        assert len(set(idx[t].tolist())) == cfg.K               # no duplicates
+        groups = set((idx[t] // Eg).tolist())
+        assert len(groups) <= cfg.TG                            # at most TG groups
+        g = np.sort(c[t].reshape(cfg.G, Eg), axis=1)[:, -2:].sum(1)
+        kept = set(np.argsort(-g, kind="stable")[:cfg.TG].tolist())
+        assert groups <= kept                                   # inside the kept groups
+    np.testing.assert_allclose(w.sum(1), cfg.rho, rtol=1e-12)   # sum w = rho (K > 1)
+    sel = np.take_along_axis(s, idx.astype(np.int64), 1)
+    np.testing.assert_allclose(w / w[:, :1], sel / sel[:, :1], rtol=1e-12)  # w_i/w_j = s_i/s_j
+    assert np.all(m > 0)
+
+
+def test_bias_changes_selection_only(v3_route):
+    cfg, lg, b, idx, w, _ = v3_route
+    # A constant shift of the bias keeps every choice (all kept scores stay
+    # positive here), so the weights must be bit-identical.
+    idx2, w2, _ = oracle.route_f64(cfg, lg, (b + np.float32(0.25)).astype(np.float32))
+    np.testing.assert_array_equal(idx2, idx)
+    assert np.array_equal(w2, w)
+    # A bias that changes the choice gives weights from the unbiased scores.
+    b3 = b.copy()
+    b3[idx[0, 0]] -= 3.0
+    idx3, w3, _ = oracle.route_f64(cfg, lg, b3)
+    assert idx[0, 0] not in idx3[0]
+    s = 1 / (1 + np.exp(-lg[0, idx3[0]]))
+    np.testing.assert_allclose(w3[0], cfg.rho * s / (s.sum() + 1e-20), rtol=1e-12)
+
+
+def test_contract_router_agrees_with_f64_router_away_from_ties(v3_route):
+    cfg, lg, b, idx, w, m = v3_route
+    idx32, w32 = oracle.route_f32(cfg, lg.astype(np.float32), b)
+    differ = np.any(idx32 != idx, axis=1)
+    # fp32 rounding of logits/scores moves choice scores by ~1e-7; a
+    # different decision is only possible inside that margin.
+    assert np.all(m[differ] < 1e-5)
+    assert differ.mean() < 0.01
+    np.testing.assert_allclose(w32[~differ], w[~differ], rtol=2e-6)
+
+
+# ---------------------------------------------------------------- permutation
+
+@pytest.mark.parametrize("T,K,E", [(1, 1, 4), (7, 2, 16), (513, 8, 256), (300, 1, 64)])
+def test_permute_is_stable_argsort(T, K, E):
+    r = synth.words(T * K, 9, synth.T_TEST, T)
+    # skewed ids: half the picks on expert 3 (distinct experts per token are
+    # not needed for the permutation itself)
+    idx = np.where(r % 2 == 0, 3 % E, (r >> 8) % E).astype(np.int32).reshape(T, K)
+    counts, offsets, perm, pos = oracle.permute(idx, E)
+    np.testing.assert_array_equal(counts, np.bincount(idx.ravel(), minlength=E))
+    assert offsets[0] == 0 and offsets[-1] == T * K
+    np.testing.assert_array_equal(np.diff(offsets), counts)
+    np.testing.assert_array_equal(perm, np.argsort(idx.ravel(), kind="stable"))
+    np.testing.assert_array_equal(pos[perm], np.arange(T * K))
+    np.testing.assert_array_equal(np.sort(perm), np.arange(T * K))
+
+
+def test_permute_rejects_bad_index():
+    with pytest.raises(ValueError):
+        oracle.permute(np.array([[0, 5]], np.int32), 4)
+
+
+# ---------------------------------------------------------------- FFN + combine
+
+def _np_ffn(x, w13, w2):
+    """Dense numpy SwiGLU: x [n,H], w13 [2I,H], w2 [H,I]."""
+    a = x @ w13.T
+    I = w2.shape[1]
+    g, u = a[:, :I], a[:, I:]
+    return (g / (1 + np.exp(-g)) * u) @ w2.T
+
+
+def _as64(a, kind):
+    if a is None:
+        return None
+    return synth.bf16_to_f32(a).astype(np.float64) if kind == "bf16" else a.astype(np.float64)
+
+
+@pytest.mark.parametrize("wdtype", ["f32", "bf16"])
+def test_dense_masked_equivalence(wdtype):
+    """out = shared(x) + sum over ALL experts of m[t,e] FFN_e(x), m = w at the
+    chosen experts and 0 elsewhere (numpy, no permutation) must equal the
+    oracle's routed sum."""
+    cfg = synth.C1.replace(T=40, H=128, E=8, G=4, TG=2, K=3, I=64, Is=96, rho=1.7,
+                           act="f32" if wdtype == "f32" else "bf16", wdtype=wdtype)
+    inp = synth.gen_inputs(cfg)
+    r = oracle.forward(cfg, inp)
+    x = _as64(inp["x"], cfg.act)
+    mask = np.zeros((cfg.T, cfg.E))
+    np.put_along_axis(mask, r["idx"].astype(np.int64), r["w"], axis=1)
+    ref = _np_ffn(x, _as64(inp["ws13"], wdtype), _as64(inp["ws2"], wdtype))
+    for e in range(cfg.E):
+        ref += mask[:, e:e + 1] * _np_ffn(x, _as64(inp["w13"][e], wdtype), _as64(inp["w2"][e], wdtype))
+    np.testing.assert_allclose(r["out"], ref, rtol=1e-11, atol=1e-12)
+
+
+def test_single_expert_reduces_to_dense_swiglu():
+    """Two identical experts, one group, top-1: out = rho sigmoid(l*) FFN(x) + shared(x)."""
+    cfg = synth.C1.replace(T=16, E=2, G=1, TG=1, K=1, rho=2.5)
+    inp = synth.gen_inputs(cfg)
+    inp["w13"][1] = inp["w13"][0]
+    inp["w2"][1] = inp["w2"][0]
+    r = oracle.forward(cfg, inp)
+    x = inp["x"].astype(np.float64)
+    sel = np.take_along_axis(r["logits"], r["idx"].astype(np.int64), 1)
+    ref = (2.5 / (1 + np.exp(-sel))) * _np_ffn(x, inp["w13"][0].astype(np.float64),
+                                              inp["w2"][0].astype(np.float64))
+    ref += _np_ffn(x, inp["ws13"].astype(np.float64), inp["ws2"].astype(np.float64))
+    np.testing.assert_allclose(r["out"], ref, rtol=1e-11, atol=1e-12)
+
+
+def test_zero_expert_weights_leave_shared_only():
+    cfg = synth.C1
+    inp = synth.gen_inputs(cfg)
+    inp["w13"][:] = 0
+    r = oracle.forward(cfg, inp)
+    ref = _np_ffn(inp["x"].astype(np.float64), inp["ws13"].astype(np.float64),
+                  inp["ws2"].astype(np.float64))
+    np.testing.assert_allclose(r["out"], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_no_shared_expert():
+    cfg = synth.C1.replace(Is=0)
+    inp = synth.gen_inputs(cfg)
+    r = oracle.forward(cfg, inp)
+    x = inp["x"].astype(np.float64)
+    ref = np.zeros((cfg.T, cfg.H))
+    for t in range(cfg.T):
+        for k in range(cfg.K):
+            e = r["idx"][t, k]
+            ref[t] += r["w"][t, k] * _np_ffn(x[t:t + 1], inp["w13"][e].astype(np.float64),
+                                             inp["w2"][e].astype(np.float64))[0]
+    np.testing.assert_allclose(r["out"], ref, rtol=1e-11, atol=1e-12)
+
+
+def test_token_subset_equals_full_rows():
+    cfg = synth.C1
+    inp = synth.gen_inputs(cfg)
+    r = oracle.forward(cfg, inp)
+    toks = np.array([5, 0, 63, 17])
+    out = oracle.layer(cfg, inp, r["idx"], r["w"], tokens=toks)
+    assert np.array_equal(out, r["out"][toks])
+
+
+# ---------------------------------------------------------------- e4m3 and the 1x128 quantiser
+
+def test_e4m3_decode_matches_torch_for_all_codes():
+    codes = torch.arange(256, dtype=torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    mine = np.array([oracle.e4m3_decode(c) for c in range(256)])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), nan) and nan.sum() == 2   # 0x7F, 0xFF
+    np.testing.assert_array_equal(mine[~nan], ref[~nan])
+    assert mine[0x7E] == 448.0 and mine[0x01] == 2.0 ** -9 and mine[0x08] == 2.0 ** -6
+
+
+def test_e4m3_encode_roundtrip_and_torch_rounding():
+    for c in range(256):
+        v = oracle.e4m3_decode(c)
+        if not np.isnan(v):
+            got = oracle.e4m3_encode(np.float32(v))
+            assert oracle.e4m3_decode(got) == v
+    # Midpoints between neighbouring codes (ties) and random values: the
+    # round-to-nearest-even encoder agrees with torch's float8 cast.
+    vals = [oracle.e4m3_decode(c) for c in range(0x7E)]
+    mids = [(a + b) / 2 for a, b in zip(vals[:-1], vals[1:])]
+    rnd = synth.normal_f32(20000, 4, synth.T_TEST, 9, 60.0)
+    tiny = synth.normal_f32(2000, 4, synth.T_TEST, 10, 0.01)
+    allv = np.concatenate([np.array(mids), -np.array(mids), rnd, tiny]).astype(np.float32)
+    allv = np.clip(allv, -448, 448)
+    ref = torch.from_numpy(allv).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    mine = np.array([oracle.e4m3_encode(v) for v in allv], np.uint8)
+    np.testing.assert_array_equal(mine, ref)
+    assert oracle.e4m3_encode(np.float32(1e6)) == 0x7E            # saturation
+    assert oracle.e4m3_encode(np.float32(-1e6)) == 0xFE
+
+
+def test_quant_rows_definition():
+    x = synth.normal_f32(5 * 384, 6, synth.T_TEST, 11, 3.0).reshape(5, 384)
+    x[2, 128:256] = 0.0                                             # an all-zero tile
+    q, s = oracle.quant_rows(x)
+    assert s[2, 1] == 1.0 and np.all(q[2, 128:256] == 0)
+    for r in range(5):
+        for t in range(3):
+            tile = x[r, t * 128:(t + 1) * 128]
+            a = float(np.abs(tile).max())
+            if a == 0:
+                continue
+            assert s[r, t] == np.float32(a / 448.0)
+            inv = np.float32(448.0 / a)
+            prod = np.clip((tile * inv).astype(np.float32), -448, 448)
+            ref = torch.from_numpy(prod).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            np.testing.assert_array_equal(q[r, t * 128:(t + 1) * 128], ref)
+            assert np.abs(prod).max() >= 447.0                       # the max maps to ~448
+    # dequantised error within half an e4m3 step (relative 2^-4) of each value
+    deq = np.vectorize(oracle.e4m3_decode)(q) * np.repeat(s, 128, axis=1)
+    err = np.abs(deq - x)
+    assert np.all(err <= np.abs(x) * 2 ** -4 + np.repeat(s, 128, axis=1) * 2 ** -9 + 1e-30)
+
+
+def test_generator_e4m3_weights_decode_close_to_draws():
+    """The generator's block-scaled weights dequantise to the normal draws
+    they were made from within an e4m3 rounding step."""
+    q, s = synth.normal_e4m3_blocks(256, 384, 0, synth.T_TEST, 12, 0.05)
+    v = synth.normal_f32(256 * 384, 0, synth.T_TEST, 12, 0.05).reshape(256, 384)
+    deq = np.vectorize(oracle.e4m3_decode)(q) * np.kron(s, np.ones((128, 128), np.float32))
+    np.testing.assert_allclose(deq, v, rtol=2 ** -4, atol=float(s.max()) * 2 ** -9)
+    # and the oracle's encoder gives the same codes on the same scaled values
+    for bi in range(2):
+        for bj in range(3):
+            blk = v[bi * 128:(bi + 1) * 128, bj * 128:(bj + 1) * 128]
+            inv = np.float32(448.0 / float(np.abs(blk).max()))
+            mine = np.array([oracle.e4m3_encode(t) for t in (blk * inv).astype(np.float32).ravel()])
+            np.testing.assert_array_equal(mine.reshape(128, 128),
+                                          q[bi * 128:(bi + 1) * 128, bj * 128:(bj + 1) * 128])
+
+
+def test_fp8_layer_uses_dequantised_weights():
+    """F1 mode: the layer on e4m3 weights equals the layer on their
+    dequantised fp32 values."""
+    cfg8 = synth.C1.replace(T=12, H=256, E=4, G=2, TG=1, K=2, I=128, Is=128, act="bf16",
+                            wdtype="fp8")
+    inp = synth.gen_inputs(cfg8)
+    r8 = oracle.forward(cfg8, inp)
+    deq = lambda q, s: (np.vectorize(oracle.e4m3_decode)(q) *
+                        np.kron(s, np.ones((128, 128)))).astype(np.float32)
+    inp32 = dict(inp)
+    inp32["w13"] = np.stack([deq(inp["w13"][e], inp["w13_s"][e]) for e in range(cfg8.E)])
+    inp32["w2"] = np.stack([deq(inp["w2"][e], inp["w2_s"][e]) for e in range(cfg8.E)])
+    inp32["ws13"] = deq(inp["ws13"], inp["ws13_s"])
+    inp32["ws2"] = deq(inp["ws2"], inp["ws2_s"])
+    for k in ("w13_s", "w2_s", "ws13_s", "ws2_s"):
+        inp32[k] = None
+    cfg32 = cfg8.replace(wdtype="f32")
+    r32 = oracle.forward(cfg32, inp32)
+    np.testing.assert_array_equal(r8["idx"], r32["idx"])
+    # e4m3 code x fp32 scale needs up to 28 significant bits, so the fp32
+    # copy above is rounded (relative 2^-24 per weight); a wrong block-scale
+    # index would be off by far more.
+    np.testing.assert_allclose(r8["out"], r32["out"], rtol=1e-5, atol=1e-6)
+    # F2 (activations quantised too) stays close to F1
+    r2 = oracle.forward(cfg8, inp, quant_act=True)
+    rel = np.linalg.norm(r2["out"] - r8["out"]) / np.linalg.norm(r8["out"])
+    assert 1e-4 < rel < 0.1
