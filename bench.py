@@ -1,0 +1,192 @@
+"""Benchmark: one MoE layer forward (gate, permute, expert FFNs, combine) per
+step on one MI355X, V3 shape (H=7168, 256 routed experts in 8 groups, top-4
+groups, top-8, expert and shared FFN width 2048, routed scaling 2.5), bf16,
+T=4096 tokens of synthetic seeded input resident in HBM.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--cpu-sample S]
+
+Prints one JSON line.  The per-phase times (HIP events on the stream the
+kernels run on) give the roofline of the dominant phase, the grouped expert
+GEMMs.  The CPU baseline is the fp64 oracle on a bounded sample of tokens.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5000.0       # dense fp8 MFMA
+
+
+def log(msg):
+    sys.stderr.write(msg + "\n")
+    sys.stderr.flush()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="v3-layer-bf16-T4096")
+    ap.add_argument("--cpu-sample", type=int, default=96,
+                    help="tokens of the workload run through the fp64 oracle (0 = skip)")
+    ap.add_argument("--profile-only", action="store_true",
+                    help="just run warmup + steps (for rocprofv3), print the JSON line")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import sparse_mixture_experts_30_amd as moe
+    from synth import device as sd
+
+    cfg = synth.CONFIGS[args.workload]
+    T, H, E, K, I, Is = cfg.T, cfg.H, cfg.E, cfg.K, cfg.I, cfg.Is
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t0 = time.time()
+    log(f"[bench] {cfg.name}: generating inputs")
+    inp = synth.gen_inputs(cfg)
+    log(f"[bench] generated in {time.time() - t0:.1f}s; uploading")
+    d = sd.to_device(inp)
+    W = sd.weights_struct(d)
+    C = sd.moe_config(cfg)
+    ws = sd.workspace(cfg, T)
+    act_dt = torch.bfloat16 if cfg.act == "bf16" else torch.float32
+    out = torch.empty((T, H), dtype=act_dt, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs resident in HBM ({time.time() - t0:.1f}s)")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        moe.moe_forward(C, T, d["x"], W, out, ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    log(f"[bench] {ms:.3f} ms/step")
+
+    # Per-phase timing with the separate entry points (same kernels, same
+    # stream), HIP events between phases.
+    lg = torch.empty((T, E), dtype=torch.float32, device=dev)
+    idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+    wt = torch.empty((T, K), dtype=torch.float32, device=dev)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offs = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(T * K, dtype=torch.int32, device=dev)
+    pos = torch.empty(T * K, dtype=torch.int32, device=dev)
+    y = torch.empty((T * K, H), dtype=act_dt, device=dev)
+    ys = torch.empty((T, H), dtype=act_dt, device=dev) if Is else None
+    phases = ["gate", "permute", "expert_ffn", "combine"]
+    acc = {p: 0.0 for p in phases}
+    nrep = max(3, min(args.steps, 10))
+    for rep in range(nrep + 1):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        evs[0].record(stream)
+        moe.moe_gate(C, T, d["x"], d["gate_w"], d["bias"], lg, idx, wt, ws, stream=stream)
+        evs[1].record(stream)
+        moe.moe_permute(C, T, idx, counts, offs, perm, pos, ws, stream=stream)
+        evs[2].record(stream)
+        moe.moe_expert_ffn(C, T, d["x"], perm, offs, W, y, ys, ws, stream=stream)
+        evs[3].record(stream)
+        moe.moe_combine(C, T, y, ys, pos, wt, out, stream=stream)
+        evs[4].record(stream)
+        torch.cuda.synchronize()
+        if rep:  # first repetition is a warmup
+            for i, p in enumerate(phases):
+                acc[p] += evs[i].elapsed_time(evs[i + 1]) / nrep
+    cnt = counts.cpu().numpy()
+    active = int((cnt > 0).sum())
+
+    # Algorithmic work (routed rows only; active experts' weights only).
+    wbytes = 1 if cfg.wdtype == "fp8" else (2 if cfg.wdtype == "bf16" else 4)
+    abytes = 2 if cfg.act == "bf16" else 4
+    expert_w = 3 * H * I * wbytes
+    shared_w = 3 * H * Is * wbytes
+    flop = T * (6.0 * H * (I * K + Is) + 2.0 * H * E)
+    layer_bytes = active * expert_w + shared_w + E * H * 4 + E * 4 + 2 * T * H * abytes
+    ffn_flop = T * 6.0 * H * (I * K + Is)
+    ffn_bytes = active * expert_w + shared_w + T * H * abytes + (T * K + T) * H * abytes
+    ffn_ms = acc["expert_ffn"]
+    ffn_gbs = ffn_bytes / (ffn_ms * 1e-3) / 1e9
+    ffn_tflops = ffn_flop / (ffn_ms * 1e-3) / 1e12
+    mfma_peak = FP8_PEAK_TFLOPS if cfg.wdtype == "fp8" else BF16_PEAK_TFLOPS
+    tok_s = T / (ms * 1e-3)
+
+    result = {
+        "metric": "MoE layer tokens/s + % bf16 MFMA peak (prefill), % HBM peak (decode)",
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"bf16": "bf16", "fp8": "fp8-e4m3", "f32": "f32"}[cfg.wdtype],
+        "data": "synthetic: seeded N(0,1) tokens, N(0,1/fan_in) weights, U(-0.05,0.05) bias",
+        "config": {"workload": cfg.name, "T": T, "hidden": H, "n_routed_experts": E,
+                   "n_group": cfg.G, "topk_group": cfg.TG, "top_k": K, "moe_inter": I,
+                   "shared_inter": Is, "routed_scaling_factor": cfg.rho,
+                   "act_dtype": cfg.act, "weight_dtype": cfg.wdtype},
+        "layer": {"tflops": round(flop / (ms * 1e-3) / 1e12, 2),
+                  "mfma_frac": round(flop / (ms * 1e-3) / 1e12 / mfma_peak, 4),
+                  "hbm_gbs": round(layer_bytes / (ms * 1e-3) / 1e9, 1),
+                  "hbm_frac": round(layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                  "algorithmic_bytes": layer_bytes, "algorithmic_flop": flop,
+                  "active_experts": active},
+        "phases_ms": {p: round(v, 4) for p, v in acc.items()},
+        "roofline": {
+            "kernel": "expert_ffn (grouped GEMM1 gate/up+SiLU and GEMM2, routed + shared)",
+            "bound": "hbm",
+            "achieved": round(ffn_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(ffn_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": ffn_bytes,
+            "mfma_tflops": round(ffn_tflops, 1),
+            "mfma_frac": round(ffn_tflops / mfma_peak, 4),
+        },
+    }
+
+    if args.cpu_sample > 0 and not args.profile_only:
+        import oracle
+        S = min(args.cpu_sample, T)
+        toks = np.arange(S)
+        log(f"[bench] cpu baseline: oracle forward on {S} tokens")
+        t1 = time.perf_counter()
+        oracle.forward(cfg, inp, tokens=toks)
+        dt = time.perf_counter() - t1
+        result["cpu_baseline"] = {"value": round(S / dt, 3), "unit": "tokens/s",
+                                  "cores": oracle.threads(), "kind": "oracle",
+                                  "sample": f"first {S} of the {T} tokens of {cfg.name}: fp64 "
+                                            f"gate logits, routing and the layer output "
+                                            f"({dt:.1f} s)"}
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,194 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) DeepSeek-V3-style MoE layer forward.
+ *
+ * The layer, as the pages state it:
+ *   - gate: sigmoid scores of a linear map of the token, a per-expert bias
+ *     that only takes part in choosing experts, a per-group sum of the two
+ *     largest choice scores, the topk_group best groups, the top_k best
+ *     experts inside them, weights from the unbiased scores normalised over
+ *     the chosen experts (top_k > 1) and multiplied by routed_scaling_factor
+ *     ("从 1024 块 GPU 到 558 万美元：拆解 DeepSeek-V3 的算法-系统协同设计",
+ *     section 2.2, the MoEGate module);
+ *   - dispatch: per-expert token counts and the tokens sorted by expert id
+ *     (same page, section 2.3, the dispatch skeleton);
+ *   - experts: 256 fine-grained routed experts of FFN width 2048 and one
+ *     always-active shared expert (same page, section 2.2; "深入理解
+ *     DeepSeek-V3：大规模缩放挑战与对 AI 架构硬件的反思（中文精读）", section 3.1:
+ *     8 routed + 1 shared per token); each a SwiGLU FFN (mqxn.cn/news/19449,
+ *     section 3.1);
+ *   - combine: the expert outputs collected back to their tokens (first page,
+ *     section 2.3), summed with the gate weights, plus the shared expert;
+ *   - FP8 variant: activations quantised per 1x128 tile and weights per
+ *     128x128 block, fp32 accumulation ("深入理解 DeepSeek-V3…", section 3.2).
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers, owned by the caller.  The
+ *     library allocates no device memory; scratch space comes from the
+ *     caller's workspace (ws, ws_bytes; see moe_workspace_bytes).
+ *   - All work is enqueued asynchronously on `stream` (a hipStream_t; NULL is
+ *     the default stream).  No entry point synchronises the host with the
+ *     device except moe_get_device_error.
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     failed validation returns an error code and enqueues nothing.  No C++
+ *     exception crosses the ABI.  moe_last_error() gives a thread-local text
+ *     for the last failing call on the calling thread.
+ *   - Layouts are row-major.  Weight matrices are stored "output rows x
+ *     input columns" with the input dimension contiguous.
+ *   - T == 0 is a no-op returning MOE_OK.
+ *   - The library holds no mutable global state; calls on different streams
+ *     with different workspaces may run concurrently.
+ *   - Results are deterministic: no floating-point atomics anywhere, so two
+ *     runs on the same inputs give bitwise-identical outputs.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,   /* null pointer, bad shape, inconsistent config   */
+    MOE_ERR_UNSUPPORTED = 2,   /* valid for the method, not handled by kernels   */
+    MOE_ERR_WORKSPACE = 3,     /* ws null or ws_bytes below the required size    */
+    MOE_ERR_HIP = 4,           /* a HIP runtime call or kernel launch failed     */
+    MOE_ERR_DEVICE_CHECK = 5   /* a kernel saw an out-of-range expert index      */
+} moe_status;
+
+typedef enum {
+    MOE_F32 = 0,       /* IEEE binary32                                        */
+    MOE_BF16 = 1,      /* bfloat16                                             */
+    MOE_FP8_E4M3 = 2   /* OCP e4m3fn + fp32 scale per 128x128 block (weights)  */
+} moe_dtype;
+
+/* Layer shape: the MoEGate constructor arguments of the first page's
+ * section 2.2 plus the expert FFN widths. */
+typedef struct {
+    int32_t hidden_size;              /* H                                         */
+    int32_t n_routed_experts;         /* E   (2 <= E <= 512)                        */
+    int32_t n_group;                  /* G   (E % G == 0, E / G >= 2, G <= 64)      */
+    int32_t topk_group;               /* TG  (1 <= TG <= G)                         */
+    int32_t num_experts_per_tok;      /* K   (1 <= K <= min(E, 64))                 */
+    int32_t moe_intermediate_size;    /* I   routed expert FFN width                */
+    int32_t shared_intermediate_size; /* Is  shared expert FFN width, 0 = none      */
+    float routed_scaling_factor;      /* rho (finite, > 0)                          */
+    moe_dtype act_dtype;              /* x, expert outputs and layer output:
+                                         MOE_F32 or MOE_BF16                        */
+    moe_dtype weight_dtype;           /* expert and shared weights: MOE_F32 (with
+                                         act F32), MOE_BF16 or MOE_FP8_E4M3 (with
+                                         act BF16)                                  */
+} moe_config;
+
+/* Layer weights.  The gate weight and the selection bias are always fp32.
+ * w13 stacks each expert's gate projection (rows 0..I-1) over its up
+ * projection (rows I..2I-1).  For MOE_FP8_E4M3 the *_scale arrays hold one
+ * fp32 per 128x128 block, row-major over (row block, column block); they are
+ * ignored (may be NULL) otherwise.  ws13/ws2 (+scales) may be NULL iff Is == 0. */
+typedef struct {
+    const float* gate_w;     /* [E, H]                                           */
+    const float* bias;       /* [E]  e_score_correction_bias                     */
+    const void* w13;         /* [E, 2I, H]                                       */
+    const float* w13_scale;  /* [E, 2I/128, H/128]                               */
+    const void* w2;          /* [E, H, I]                                        */
+    const float* w2_scale;   /* [E, H/128, I/128]                                */
+    const void* ws13;        /* [2Is, H]                                         */
+    const float* ws13_scale; /* [2Is/128, H/128]                                 */
+    const void* ws2;         /* [H, Is]                                          */
+    const float* ws2_scale;  /* [H/128, Is/128]                                  */
+} moe_weights;
+
+/* Bytes of workspace that every entry point below needs for T tokens (the
+ * maximum over them, so one buffer serves all).  Returns 0 if cfg is invalid
+ * or unsupported. */
+size_t moe_workspace_bytes(const moe_config* cfg, int64_t T);
+
+/* Gate and selection (first page, section 2.2).
+ *   x       [T, H] act_dtype
+ *   gate_w  [E, H] fp32,  bias [E] fp32
+ *   logits  [T, E] fp32 out, may be NULL (then kept in the workspace).  The
+ *           gate product is computed to fp32 accuracy: x is exact in bf16 and
+ *           the fp32 gate weight is split into three bf16 parts whose
+ *           products with x are exact, accumulated in fp32 on MFMA.
+ *   topk_idx [T, K] int32 out: chosen experts, in descending order of masked
+ *           choice score, ties to the lower expert id.
+ *   topk_w  [T, K] fp32 out: routed weights.
+ * Selection arithmetic (bit-reproducible from the fp32 logits): score =
+ * fp32 rounding of the double-precision sigmoid; choice = score + bias (fp32
+ * add); group score = fp32 sum of the group's two largest choices; groups and
+ * experts chosen by exact fp32 comparison, ties to the lower index; experts
+ * outside the kept groups compete with choice 0.0f. */
+moe_status moe_gate(const moe_config* cfg, int64_t T, const void* x, const float* gate_w,
+                    const float* bias, float* logits, int32_t* topk_idx, float* topk_w,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* Dispatch order (first page, section 2.3).
+ *   topk_idx [T, K] int32 in (values in [0, E); others set the device error
+ *           flag in ws, see moe_get_device_error, and are skipped)
+ *   counts  [E] int32 out: tokens per expert
+ *   offsets [E+1] int32 out: exclusive prefix sum, offsets[E] = T*K
+ *   perm    [T*K] int32 out: flat indices f = t*K + k sorted by expert id,
+ *           stable (ascending f inside an expert)
+ *   pos     [T*K] int32 out: inverse of perm (pos[perm[j]] = j) */
+moe_status moe_permute(const moe_config* cfg, int64_t T, const int32_t* topk_idx,
+                       int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* pos,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* Routed and shared expert FFNs (SwiGLU: W2 (silu(W_gate x) * (W_up x))).
+ *   x       [T, H] act_dtype
+ *   perm, offsets from moe_permute (device)
+ *   y       [T*K, H] act_dtype out: row j = expert e's output on token
+ *           perm[j] / K, where offsets[e] <= j < offsets[e+1]
+ *   y_shared [T, H] act_dtype out (NULL iff Is == 0)
+ * bf16 weights: bf16 MFMA, fp32 accumulation, SiLU*up fused, h kept in bf16.
+ * fp8 weights: x and h quantised per 1x128 tile to e4m3 (see
+ * moe_quantize_act), e4m3 MFMA, per-128-block scales applied to fp32 partial
+ * sums.  f32: fp32 arithmetic throughout. */
+moe_status moe_expert_ffn(const moe_config* cfg, int64_t T, const void* x, const int32_t* perm,
+                          const int32_t* offsets, const moe_weights* w, void* y, void* y_shared,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* Combine: out[t] = y_shared[t] + sum_k topk_w[t,k] * y[pos[t*K+k]], fp32
+ * accumulation in k order, rounded once to act_dtype.
+ *   y [T*K, H], y_shared [T, H] (NULL iff Is == 0), pos [T*K], topk_w [T, K],
+ *   out [T, H] act_dtype. */
+moe_status moe_combine(const moe_config* cfg, int64_t T, const void* y, const void* y_shared,
+                       const int32_t* pos, const float* topk_w, void* out, void* stream);
+
+/* The whole layer: gate, permute, expert FFNs, combine, enqueued in that
+ * order.  out [T, H] act_dtype.  logits [T,E], topk_idx/topk_w [T,K],
+ * counts [E] and perm [T*K] are optional copies of the intermediate results
+ * (NULL: kept in the workspace only). */
+moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const moe_weights* w,
+                       void* out, float* logits, int32_t* topk_idx, float* topk_w,
+                       int32_t* counts, int32_t* perm, void* ws, size_t ws_bytes, void* stream);
+
+/* FP8 activation quantiser ("深入理解 DeepSeek-V3…", section 3.2: 1x128
+ * activation tiles).  For each row of x [rows, H] (bf16, H % 128 == 0) and
+ * each tile of 128 columns: a = max |v|; scale = a / 448 and inv = 448 / a,
+ * each computed in double and rounded to fp32 (scale 1, inv 0 for a == 0);
+ * code = nearest e4m3fn value of the fp32 product v * inv, ties to even,
+ * saturated at +-448.
+ *   xq [rows, H] uint8 out, xs [rows, H/128] fp32 out. */
+moe_status moe_quantize_act(const moe_config* cfg, int64_t rows, const void* x, uint8_t* xq,
+                            float* xs, void* stream);
+
+/* Reads (and clears) the device error flag in ws: synchronises `stream`.
+ * Returns MOE_OK, MOE_ERR_DEVICE_CHECK if a kernel saw an invalid expert
+ * index since the last call, or MOE_ERR_HIP. */
+moe_status moe_get_device_error(void* ws, size_t ws_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* moe_strerror(moe_status s);
+
+/* Thread-local detail of the last failing call on this thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

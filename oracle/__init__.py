@@ -62,6 +62,11 @@ def lib():
         L.oracle_layer.argtypes = [ctypes.POINTER(Cfg), i64, vp, vp, i32, vp, vp,
                                    vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp]
         L.oracle_layer.restype = ctypes.c_int
+        L.oracle_ffn.argtypes = [ctypes.POINTER(Cfg), i64, vp, vp, vp, i32, vp, vp, vp, vp,
+                                 vp, vp, vp, vp, i32, i32, vp]
+        L.oracle_ffn.restype = ctypes.c_int
+        L.oracle_combine.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp]
+        L.oracle_combine.restype = None
         _lib = L
     return _lib
 
@@ -176,6 +181,36 @@ def layer(cfg, inp: dict, idx: np.ndarray, w: np.ndarray, tokens=None, quant_act
                             _p(out))
     if rc:
         raise ValueError("oracle_layer failed (bad expert index or allocation)")
+    return out
+
+
+def ffn(cfg, inp: dict, tokens, experts, quant_act=False):
+    """FFN_{experts[n]}(x_{tokens[n]}) in fp64 -> [n, H]; expert -1 = shared."""
+    x = _c(inp["x"])
+    tokens = _c(tokens, np.int64)
+    experts = _c(experts, np.int32)
+    wd = {"f32": F32, "bf16": BF16, "fp8": E4M3}[cfg.wdtype]
+    xd = F32 if cfg.act == "f32" else BF16
+    g = lambda k: None if inp.get(k) is None else _c(inp[k])
+    arrs = [g(k) for k in ("w13", "w13_s", "w2", "w2_s", "ws13", "ws13_s", "ws2", "ws2_s")]
+    out = np.empty((len(tokens), cfg.H), np.float64)
+    rc = lib().oracle_ffn(ctypes.byref(cfg_of(cfg)), len(tokens), _p(tokens), _p(experts), _p(x),
+                          xd, *[_p(a) for a in arrs], wd, int(bool(quant_act)), _p(out))
+    if rc:
+        raise ValueError("oracle_ffn failed (bad expert index or allocation)")
+    return out
+
+
+def combine(y: np.ndarray, ys, pos: np.ndarray, w: np.ndarray, K: int) -> np.ndarray:
+    """out[t] = ys[t] + sum_k w[t,k] y[pos[t*K+k]] in fp64 (y, ys as float64 arrays)."""
+    y = _c(y, np.float64)
+    ys = None if ys is None else _c(ys, np.float64)
+    pos = _c(pos, np.int32)
+    w = _c(w, np.float64)
+    T = w.shape[0]
+    H = y.shape[1]
+    out = np.empty((T, H), np.float64)
+    lib().oracle_combine(T, K, H, _p(y), _p(ys), _p(pos), _p(w), _p(out))
     return out
 
 

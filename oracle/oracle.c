@@ -510,3 +510,65 @@ int oracle_layer(const oracle_cfg *c, int64_t n_tok, const int64_t *tokens, cons
     }
     return bad;
 }
+
+/* Expert FFN on listed (token, expert) pairs: out[n] = FFN_{experts[n]}(x_t)
+ * with t = tokens[n]; experts[n] == -1 selects the shared expert (R5).  This
+ * is the row that the expert-sorted layout holds for that pair ([Co-design]
+ * 2.3: the sorted tokens are x[order // top_k]).  out is [n, H]. */
+int oracle_ffn(const oracle_cfg *c, int64_t n, const int64_t *tokens, const int32_t *experts,
+               const void *x, int32_t x_dtype, const void *w13, const float *w13_s,
+               const void *w2, const float *w2_s, const void *ws13, const float *ws13_s,
+               const void *ws2, const float *ws2_s, int32_t w_dtype, int32_t quant_act,
+               double *out)
+{
+    const int32_t H = c->H, I = c->I, Is = c->Is, E = c->E;
+    int bad = 0;
+    int32_t nmax = I > Is ? I : Is;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int64_t r = 0; r < n; ++r) {
+        int64_t t = tokens[r];
+        int32_t e = experts[r];
+        double *xr = malloc(sizeof(double) * H);
+        double *h = malloc(sizeof(double) * (nmax > 0 ? nmax : 1));
+        if (!xr || !h || e < -1 || e >= E || (e == -1 && Is == 0)) {
+            bad = 1;
+        } else {
+            for (int32_t k = 0; k < H; ++k)
+                xr[k] = mat_at(x, NULL, x_dtype, H, t, k);
+            if (quant_act)
+                quant_dequant_row(xr, H);
+            if (e < 0) {
+                ffn_row(H, Is, xr, ws13, ws13_s, ws2, ws2_s, w_dtype, quant_act, h, out + r * H);
+            } else {
+                int64_t n13 = 2LL * I * H, n2 = (int64_t)H * I;
+                const float *e13s = NULL, *e2s = NULL;
+                if (w_dtype == OR_E4M3) {
+                    e13s = w13_s + e * (n13 / (128 * 128));
+                    e2s = w2_s + e * (n2 / (128 * 128));
+                }
+                ffn_row(H, I, xr, expert_base(w13, w_dtype, e, n13), e13s,
+                        expert_base(w2, w_dtype, e, n2), e2s, w_dtype, quant_act, h, out + r * H);
+            }
+        }
+        free(xr); free(h);
+    }
+    return bad;
+}
+
+/* Step 13 from expert rows in the sorted order ([Co-design] 2.3, results
+ * collected back to their tokens; R6):
+ *   out[t] = ys[t] + sum_k w[t,k] * y[pos[t*K + k]]
+ * y is [T*K, H], ys [T, H] or NULL (no shared expert), out [T, H]. */
+void oracle_combine(int64_t T, int32_t K, int32_t H, const double *y, const double *ys,
+                    const int32_t *pos, const double *w, double *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t m = 0; m < H; ++m) {
+            double acc = ys ? ys[t * H + m] : 0.0;
+            for (int32_t k = 0; k < K; ++k)
+                acc += w[t * K + k] * y[(int64_t)pos[t * K + k] * H + m];
+            out[t * H + m] = acc;
+        }
+    }
+}

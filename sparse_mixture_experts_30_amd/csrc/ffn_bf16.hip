@@ -1,0 +1,269 @@
+// Grouped expert GEMMs on bf16 MFMA (gfx950), fp32 accumulation.
+//
+// Every routed expert and the shared expert is a SwiGLU FFN (mqxn.cn/news/19449,
+// section 3.1; one shared + fine-grained routed experts of width 2048 on the
+// page "从 1024 块 GPU 到 558 万美元：拆解 DeepSeek-V3 的算法-系统协同设计", section 2.2):
+//   GEMM1: [g u] = x_rows W13^T, h = silu(g) * u    (rows gathered via perm)
+//   GEMM2: y_rows = h_rows W2^T
+// The shared expert is group E of the same launch with all T tokens in order.
+//
+// Workgroup tile: up to 256 rows of one group x 256 weight rows, k in stages
+// of 64.  The rows of a tile are the group's actual rows (at most 256): only
+// the 32-row MFMA blocks that hold rows are computed, so an expert with 140
+// rows costs 5 row blocks, and its weight slice is read once.  4 waves; wave w
+// owns weight rows [64w, 64w+64) for all rows of the tile.  For GEMM1 those
+// are 32 gate rows and the 32 matching up rows, so SiLU(g)*u is formed in
+// registers.  LDS stages are XOR-swizzled by 16-byte chunk (conflict-free
+// operand reads) and double-buffered through registers.
+#include "moe_internal.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int BM = 256;    // max rows per tile
+constexpr int BNB = 256;   // weight rows per tile
+constexpr int BK = 64;     // k per stage
+constexpr int NT = 256;    // threads
+constexpr size_t kLds = (size_t)2 * (BM + BNB) * 8 * sizeof(uint4);   // 128 KiB
+
+struct GemmArgs {
+  const int32_t* tiles;
+  int ntn;                       // N-tiles per M-tile
+  int E, K;
+  const uint16_t* a_r;           // routed A rows base
+  const uint16_t* a_s;           // shared A rows base
+  int64_t lda_r, lda_s;
+  const int32_t* perm;           // GEMM1: routed A row = perm[j] / K (token)
+  int kdim_r, kdim_s;
+  const uint16_t* b_r;           // routed weights, expert stride b_es
+  int64_t b_es;
+  const uint16_t* b_s;           // shared weights
+  int ncol_r, ncol_s;            // output columns (GEMM1: I / Is; GEMM2: H)
+  uint16_t* c_r;
+  uint16_t* c_s;
+  int64_t ldc_r, ldc_s;
+};
+
+template <bool kGateUp>
+__global__ void __launch_bounds__(NT, 1) grouped_gemm_bf16(GemmArgs p) {
+  extern __shared__ uint4 smem[];
+  uint4* sA = smem;                   // [2][BM * 8]
+  uint4* sB = smem + 2 * BM * 8;      // [2][BNB * 8]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 31, lh = lane >> 5;
+
+  // Work item: XCD-contiguous over the real work count.
+  const int64_t work = (int64_t)p.tiles[0] * p.ntn;
+  const int64_t per = (work + kNumXcd - 1) / kNumXcd;
+  const int64_t q = blockIdx.x / kNumXcd;
+  const int64_t w = (int64_t)(blockIdx.x % kNumXcd) * per + q;
+  if (q >= per || w >= work) return;
+  int ntile;
+  const int32_t* ent = decode_work(p.tiles, w, p.ntn, ntile);
+  const int g = ent[0], row0 = ent[1], nrows = ent[2];
+  const bool sh = (g == p.E);
+  const int ncol = sh ? p.ncol_s : p.ncol_r;
+  const int n0 = ntile * (kGateUp ? BNB / 2 : BNB);
+  if (n0 >= ncol) return;
+  const int kdim = sh ? p.kdim_s : p.kdim_r;
+  const uint16_t* A = sh ? p.a_s : p.a_r;
+  const int64_t lda = sh ? p.lda_s : p.lda_r;
+  const uint16_t* B = sh ? p.b_s : p.b_r + (int64_t)g * p.b_es;
+  const int64_t ldb = kdim;
+
+  // Rows this thread stages: r = tid/8 + 32 j, 16-byte chunk tid % 8.
+  const int ch = tid & 7;
+  int arow[8], brow[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = (tid >> 3) + 32 * j;
+    arow[j] = -1;
+    if (r < nrows) arow[j] = (!sh && kGateUp) ? p.perm[row0 + r] / p.K : row0 + r;
+    int col, src;
+    if (kGateUp) {
+      const int wv = r >> 6, jj = r & 63;
+      col = n0 + wv * 32 + (jj & 31);
+      src = (jj < 32) ? col : ncol + col;
+    } else {
+      col = n0 + r;
+      src = col;
+    }
+    brow[j] = (col < ncol) ? src : -1;
+  }
+
+  uint4 ra[8], rb[8];
+  auto gload = [&](int step) {
+    const int k0 = step * BK + ch * 8;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      ra[j] = make_uint4(0, 0, 0, 0);
+      if (arow[j] >= 0) ra[j] = *reinterpret_cast<const uint4*>(A + (int64_t)arow[j] * lda + k0);
+      rb[j] = make_uint4(0, 0, 0, 0);
+      if (brow[j] >= 0) rb[j] = *reinterpret_cast<const uint4*>(B + (int64_t)brow[j] * ldb + k0);
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = (tid >> 3) + 32 * j;
+      const int o = r * 8 + (ch ^ (r & 7));
+      sA[buf * BM * 8 + o] = ra[j];
+      sB[buf * BNB * 8 + o] = rb[j];
+    }
+  };
+
+  f32x16 acc[8][2];
+#pragma unroll
+  for (int r = 0; r < 8; ++r)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[r][c][i] = 0.0f;
+
+  const int nrb = (nrows + 31) >> 5;
+  const int nsteps = kdim / BK;
+  gload(0);
+  sstore(0);
+  if (nsteps > 1) gload(1);
+  __syncthreads();
+
+  for (int step = 0; step < nsteps; ++step) {
+    const uint4* a_s = sA + (step & 1) * BM * 8;
+    const uint4* b_s = sB + (step & 1) * BNB * 8;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int c = 2 * kk + lh;
+      const int br0 = wave * 64 + lr, br1 = br0 + 32;
+      const bf16x8 b0 = as_bf16x8(b_s[br0 * 8 + (c ^ (br0 & 7))]);
+      const bf16x8 b1 = as_bf16x8(b_s[br1 * 8 + (c ^ (br1 & 7))]);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        if (r < nrb) {
+          const int ar = r * 32 + lr;
+          const bf16x8 a = as_bf16x8(a_s[ar * 8 + (c ^ (ar & 7))]);
+          acc[r][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc[r][0], 0, 0, 0);
+          acc[r][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc[r][1], 0, 0, 0);
+        }
+      }
+    }
+    if (step + 1 < nsteps) {
+      sstore((step + 1) & 1);
+      if (step + 2 < nsteps) gload(step + 2);
+    }
+    __syncthreads();
+  }
+
+  // Epilogue.  32x32 block layout: lane holds column lane%32, rows
+  // 8*(i/4) + 4*(lane/32) + i%4.
+  uint16_t* C = sh ? p.c_s : p.c_r;
+  const int64_t ldc = sh ? p.ldc_s : p.ldc_r;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    if (r >= nrb) break;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = r * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
+      if (row >= nrows) continue;
+      uint16_t* crow = C + (int64_t)(row0 + row) * ldc;
+      if (kGateUp) {
+        const int col = n0 + wave * 32 + lr;
+        if (col < ncol) {
+          const float gv = acc[r][0][i], uv = acc[r][1][i];
+          const float hv = gv / (1.0f + __expf(-gv)) * uv;
+          crow[col] = (uint16_t)f32_to_bf16_bits(hv);
+        }
+      } else {
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+          const int col = n0 + wave * 64 + cb * 32 + lr;
+          if (col < ncol) crow[col] = (uint16_t)f32_to_bf16_bits(acc[r][cb][i]);
+        }
+      }
+    }
+  }
+}
+
+bool g_attr_set = false;
+
+hipError_t set_attrs() {
+  if (g_attr_set) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute((const void*)grouped_gemm_bf16<true>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+  if (e != hipSuccess) return e;
+  e = hipFuncSetAttribute((const void*)grouped_gemm_bf16<false>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+  if (e == hipSuccess) g_attr_set = true;
+  return e;
+}
+
+unsigned grid_for(int64_t max_work) {
+  return (unsigned)(((max_work + kNumXcd - 1) / kNumXcd) * kNumXcd);
+}
+
+}  // namespace
+
+size_t ffn_tiles_bytes(const FfnDims& d) {
+  return (size_t)(8 + 8 * ffn_max_mtiles(d.N, d.T, d.E, BM)) * sizeof(int32_t);
+}
+
+// h holds routed rows [0, N) with width I, then shared rows [N, N+T) with width Is.
+hipError_t launch_ffn_bf16(const FfnDims& d, const uint16_t* x, const int32_t* perm,
+                           const int32_t* offsets, const uint16_t* w13, const uint16_t* w2,
+                           const uint16_t* ws13, const uint16_t* ws2, uint16_t* h,
+                           int32_t* tiles, uint16_t* y, uint16_t* ys, hipStream_t s) {
+  hipError_t e = set_attrs();
+  if (e != hipSuccess) return e;
+  const bool has_shared = d.Is > 0;
+  e = launch_build_tiles(offsets, d.E, d.T, has_shared, BM, tiles, s);
+  if (e != hipSuccess) return e;
+  const int64_t mt = ffn_max_mtiles(d.N, d.T, d.E, BM);
+  uint16_t* hs = h + d.N * d.I;
+
+  GemmArgs a1{};
+  a1.tiles = tiles;
+  a1.ntn = (int)((std::max(d.I, d.Is) + BNB / 2 - 1) / (BNB / 2));
+  a1.E = d.E;
+  a1.K = d.K;
+  a1.a_r = x;
+  a1.a_s = x;
+  a1.lda_r = a1.lda_s = d.H;
+  a1.perm = perm;
+  a1.kdim_r = a1.kdim_s = d.H;
+  a1.b_r = w13;
+  a1.b_es = (int64_t)2 * d.I * d.H;
+  a1.b_s = ws13;
+  a1.ncol_r = d.I;
+  a1.ncol_s = d.Is;
+  a1.c_r = h;
+  a1.c_s = hs;
+  a1.ldc_r = d.I;
+  a1.ldc_s = d.Is;
+  hipLaunchKernelGGL(grouped_gemm_bf16<true>, dim3(grid_for(mt * a1.ntn)), dim3(NT), kLds, s, a1);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  GemmArgs a2{};
+  a2.tiles = tiles;
+  a2.ntn = (d.H + BNB - 1) / BNB;
+  a2.E = d.E;
+  a2.K = d.K;
+  a2.a_r = h;
+  a2.a_s = hs;
+  a2.lda_r = d.I;
+  a2.lda_s = d.Is;
+  a2.perm = nullptr;
+  a2.kdim_r = d.I;
+  a2.kdim_s = d.Is;
+  a2.b_r = w2;
+  a2.b_es = (int64_t)d.H * d.I;
+  a2.b_s = ws2;
+  a2.ncol_r = a2.ncol_s = d.H;
+  a2.c_r = y;
+  a2.c_s = ys;
+  a2.ldc_r = a2.ldc_s = d.H;
+  hipLaunchKernelGGL(grouped_gemm_bf16<false>, dim3(grid_for(mt * a2.ntn)), dim3(NT), kLds, s, a2);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,62 @@
+// Device-side tile schedule for the grouped expert GEMMs.
+//
+// Group g < E is routed expert g with rows [offsets[g], offsets[g+1]) of the
+// expert-sorted order; group E is the shared expert with all T tokens.  Each
+// group is cut into M-tiles of at most BM rows.  Entry i of the list (8 int32):
+//   [0] group, [1] first row, [2] rows in the tile, [3] first entry of the
+//   group (L_g), [4] M-tiles of the group (mt_g).
+// tiles[0] holds the number of entries; entries start at tiles + 8.  The
+// host never reads the list: the GEMM grids are sized for the largest
+// possible count and surplus workgroups exit.
+#include "moe_internal.hpp"
+
+namespace moe {
+
+namespace {
+
+__global__ void __launch_bounds__(1024)
+build_tiles_kernel(const int32_t* __restrict__ offsets, int E, int64_t T, int has_shared,
+                   int BM, int32_t* __restrict__ tiles) {
+  __shared__ int32_t s[1024];
+  const int g = threadIdx.x;
+  int32_t n = 0, r0 = 0;
+  if (g < E) {
+    r0 = offsets[g];
+    n = offsets[g + 1] - r0;
+  } else if (g == E && has_shared) {
+    n = (int32_t)T;
+  }
+  const int32_t mt = (n + BM - 1) / BM;
+  s[g] = mt;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    int32_t v = (g >= off) ? s[g - off] : 0;
+    __syncthreads();
+    s[g] += v;
+    __syncthreads();
+  }
+  const int32_t L = s[g] - mt;
+  for (int32_t m = 0; m < mt; ++m) {
+    int32_t* ent = tiles + 8 + 8 * (int64_t)(L + m);
+    ent[0] = g;
+    ent[1] = r0 + m * BM;
+    ent[2] = min(BM, n - m * BM);
+    ent[3] = L;
+    ent[4] = mt;
+  }
+  if (g == 1023) tiles[0] = s[g];
+}
+
+}  // namespace
+
+int64_t ffn_max_mtiles(int64_t N, int64_t T, int E, int BM) {
+  return (N + BM - 1) / BM + E + (T + BM - 1) / BM;
+}
+
+hipError_t launch_build_tiles(const int32_t* offsets, int E, int64_t T, bool has_shared, int BM,
+                              int32_t* tiles, hipStream_t s) {
+  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, E, T,
+                     has_shared ? 1 : 0, BM, tiles);
+  return hipGetLastError();
+}
+}  // namespace moe

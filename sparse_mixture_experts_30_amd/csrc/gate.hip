@@ -1,0 +1,335 @@
+// Gate and selection kernels (gfx950).
+//
+// The gate of the layer (page "从 1024 块 GPU 到 558 万美元：拆解 DeepSeek-V3 的算法-系统协同设计",
+// section 2.2, MoEGate): logits = x W^T computed in fp32, sigmoid scores, a
+// per-expert bias added only to choose, the per-group sum of the two largest
+// choice scores, the topk_group best groups, the top_k best experts inside
+// them (0.0 for experts outside), weights from the unbiased scores normalised
+// over the chosen experts when top_k > 1, times routed_scaling_factor.
+//
+// Gate GEMM: x is exact in bf16, the fp32 gate weight w splits exactly into
+// three bf16 parts (hi = w truncated to bf16, mid = (w - hi) truncated,
+// lo = w - hi - mid, which has at most 8 significant bits).  Each product of a
+// bf16 x with a bf16 part is exact in fp32, so three bf16 MFMAs accumulated in
+// fp32 give an fp32-accurate x w^T at bf16-MFMA rate.  The split is done on
+// the fly from the fp32 weight tile in LDS.
+#include "moe_internal.hpp"
+
+#include <float.h>
+
+namespace moe {
+
+namespace {
+
+constexpr int GBM = 64;    // tokens per tile
+constexpr int GBN = 128;   // experts per tile
+constexpr int GBK = 64;    // k per stage
+constexpr int GTHREADS = 256;
+
+// Split 8 fp32 weights into hi/mid/lo bf16x8 operands (exact decomposition).
+__device__ __forceinline__ void split3(const float4& p, const float4& q, bf16x8& hi,
+                                       bf16x8& mid, bf16x8& lo) {
+  float v[8] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
+  uint32_t h[4], m[4], l[4];
+#pragma unroll
+  for (int j = 0; j < 8; j += 2) {
+    uint32_t hb[2], mb[2], lb[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      uint32_t b = __float_as_uint(v[j + u]);
+      float r1 = v[j + u] - __uint_as_float(b & 0xFFFF0000u);  // exact
+      uint32_t b1 = __float_as_uint(r1);
+      float r2 = r1 - __uint_as_float(b1 & 0xFFFF0000u);       // exact, <= 8 bits
+      hb[u] = b >> 16;
+      mb[u] = b1 >> 16;
+      lb[u] = __float_as_uint(r2) >> 16;
+    }
+    h[j / 2] = hb[0] | (hb[1] << 16);
+    m[j / 2] = mb[0] | (mb[1] << 16);
+    l[j / 2] = lb[0] | (lb[1] << 16);
+  }
+  hi = as_bf16x8(make_uint4(h[0], h[1], h[2], h[3]));
+  mid = as_bf16x8(make_uint4(m[0], m[1], m[2], m[3]));
+  lo = as_bf16x8(make_uint4(l[0], l[1], l[2], l[3]));
+}
+
+// partials[ks][t][e] = sum over the ks-th slice of H of x[t,h] w[e,h].
+// Tile 64 tokens x 128 experts; 4 waves, wave w owns experts [32w, 32w+32)
+// for all 64 tokens (two 32x32 MFMA blocks).  LDS tiles are XOR-swizzled by
+// 16-byte chunk so that MFMA operand reads are bank-conflict free.
+__global__ void __launch_bounds__(GTHREADS)
+gate_logits_bf16_kernel(const uint16_t* __restrict__ x, const float* __restrict__ wg,
+                        float* __restrict__ part, int64_t T, int H, int E, int hslice) {
+  __shared__ uint4 sA[2][GBM * 8];    // [row][8 chunks of 8 bf16]
+  __shared__ uint4 sB[2][GBN * 16];   // [row][16 chunks of 4 fp32]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t m0 = (int64_t)blockIdx.x * GBM;
+  const int n0 = blockIdx.y * GBN;
+  const int ks = blockIdx.z;
+  const int kbeg = ks * hslice;
+  const int nsteps = hslice / GBK;
+
+  // Global->register staging: A 2 chunks, B 8 chunks per thread.
+  uint4 ra[2], rb[8];
+  auto gload = [&](int step) {
+    const int k0 = kbeg + step * GBK;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      int c = tid + j * GTHREADS;       // 0..511
+      int row = c >> 3, ch = c & 7;
+      int64_t t = m0 + row;
+      if (t < T)
+        ra[j] = *reinterpret_cast<const uint4*>(x + t * H + k0 + ch * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      int c = tid + j * GTHREADS;       // 0..2047
+      int row = c >> 4, ch = c & 15;
+      int e = n0 + row;
+      if (e < E)
+        rb[j] = *reinterpret_cast<const uint4*>(wg + (int64_t)e * H + k0 + ch * 4);
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      int c = tid + j * GTHREADS;
+      int row = c >> 3, ch = c & 7;
+      sA[buf][row * 8 + (ch ^ (row & 7))] = ra[j];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      int c = tid + j * GTHREADS;
+      int row = c >> 4, ch = c & 15;
+      sB[buf][row * 16 + (ch ^ (row & 15))] = rb[j];
+    }
+  };
+
+  f32x16 acc[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[r][i] = 0.0f;
+
+  gload(0);
+  sstore(0);
+  if (nsteps > 1) gload(1);
+  __syncthreads();
+
+  const int lr = lane & 31, lh = lane >> 5;
+  for (int step = 0; step < nsteps; ++step) {
+    const int buf = step & 1;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {          // 4 x 16 k
+      bf16x8 a[2];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        int row = r * 32 + lr;
+        int ch = 2 * kk + lh;
+        a[r] = as_bf16x8(sA[buf][row * 8 + (ch ^ (row & 7))]);
+      }
+      int brow = wave * 32 + lr;
+      int c0 = 4 * kk + 2 * lh;
+      uint4 p = sB[buf][brow * 16 + (c0 ^ (brow & 15))];
+      uint4 q = sB[buf][brow * 16 + ((c0 + 1) ^ (brow & 15))];
+      bf16x8 bh, bm, bl;
+      split3(__builtin_bit_cast(float4, p), __builtin_bit_cast(float4, q), bh, bm, bl);
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[r], bh, acc[r], 0, 0, 0);
+        acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[r], bm, acc[r], 0, 0, 0);
+        acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[r], bl, acc[r], 0, 0, 0);
+      }
+    }
+    if (step + 1 < nsteps) {
+      sstore(buf ^ 1);
+      if (step + 2 < nsteps) gload(step + 2);
+    }
+    __syncthreads();
+  }
+
+  // C layout of a 32x32 MFMA block: lane holds column lane%32 and rows
+  // 8*(i/4) + 4*(lane/32) + i%4 for i = 0..15.
+  const int e = n0 + wave * 32 + lr;
+  if (e < E) {
+    float* base = part + (int64_t)ks * T * E;
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        int64_t t = m0 + r * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
+        if (t < T) base[t * E + e] = acc[r][i];
+      }
+  }
+}
+
+// fp32 activations: plain fp32 FMA dot products (used for fp32 layers).
+// 16x16 output tile per 256-thread block, k in LDS slices of 64.
+__global__ void __launch_bounds__(256)
+gate_logits_f32_kernel(const float* __restrict__ x, const float* __restrict__ wg,
+                       float* __restrict__ out, int64_t T, int H, int E) {
+  __shared__ float sx[16][65], sw[16][65];
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int64_t t = (int64_t)blockIdx.x * 16 + ty;
+  const int e = blockIdx.y * 16 + tx;
+  float acc = 0.0f;
+  for (int k0 = 0; k0 < H; k0 += 64) {
+    for (int j = threadIdx.x; j < 16 * 64; j += 256) {
+      int r = j >> 6, c = j & 63;
+      int64_t tt = (int64_t)blockIdx.x * 16 + r;
+      int ee = blockIdx.y * 16 + r;
+      sx[r][c] = (tt < T && k0 + c < H) ? x[tt * H + k0 + c] : 0.0f;
+      sw[r][c] = (ee < E && k0 + c < H) ? wg[(int64_t)ee * H + k0 + c] : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll 16
+    for (int c = 0; c < 64; ++c) acc = fmaf(sx[ty][c], sw[tx][c], acc);
+    __syncthreads();
+  }
+  if (t < T && e < E) out[t * E + e] = acc;
+}
+
+// Wave-level argmax of (v, i): larger v wins, equal v -> lower i.
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    float ov = __shfl_xor(v, off, 64);
+    int oi = __shfl_xor(i, off, 64);
+    if (ov > v || (ov == v && oi < i)) {
+      v = ov;
+      i = oi;
+    }
+  }
+}
+
+constexpr int SEL_WAVES = 4;
+constexpr int SEL_MAXV = 8;   // E <= 512 = 64 lanes x 8
+
+// One wavefront per token.  Lane l holds experts e = l + 64 v.
+__global__ void __launch_bounds__(SEL_WAVES * 64)
+select_kernel(const float* __restrict__ part, int ksplit, const float* __restrict__ bias,
+              float* __restrict__ logits_out, int32_t* __restrict__ idx_out,
+              float* __restrict__ w_out, int64_t T, int E, int G, int TG, int K, float rho) {
+  __shared__ float s_c[SEL_WAVES][512];
+  __shared__ float s_s[SEL_WAVES][512];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t t = (int64_t)blockIdx.x * SEL_WAVES + wave;
+  if (t >= T) return;
+  const int Eg = E / G;
+  const int V = (E + 63) / 64;
+
+  float c[SEL_MAXV], s32[SEL_MAXV];
+#pragma unroll
+  for (int v = 0; v < SEL_MAXV; ++v) {
+    int e = lane + 64 * v;
+    c[v] = -INFINITY;
+    s32[v] = 0.0f;
+    if (v < V && e < E) {
+      float lg = part[t * E + e];
+      for (int s = 1; s < ksplit; ++s) lg += part[(int64_t)s * T * E + t * E + e];
+      if (logits_out) logits_out[t * E + e] = lg;
+      double sd = 1.0 / (1.0 + exp(-(double)lg));
+      s32[v] = (float)sd;
+      c[v] = s32[v] + bias[e];
+      s_c[wave][e] = c[v];
+      s_s[wave][e] = s32[v];
+    }
+  }
+  __syncwarp();
+
+  // Group score: sum of the two largest choice scores of group `lane`.
+  float g = -INFINITY;
+  if (lane < G) {
+    float m1 = -INFINITY, m2 = -INFINITY;
+    for (int j = 0; j < Eg; ++j) {
+      float v = s_c[wave][lane * Eg + j];
+      if (v > m1) {
+        m2 = m1;
+        m1 = v;
+      } else if (v > m2) {
+        m2 = v;
+      }
+    }
+    g = m1 + m2;
+  }
+  // Keep the TG best groups.
+  uint64_t keep = 0;
+  for (int r = 0; r < TG; ++r) {
+    float v = g;
+    int i = (lane < G && !((keep >> lane) & 1ull)) ? lane : 0x7fffffff;
+    if (i == 0x7fffffff) v = -INFINITY;
+    wave_argmax(v, i);
+    keep |= 1ull << i;
+  }
+  // Masked choice scores: 0.0 outside the kept groups.
+#pragma unroll
+  for (int v = 0; v < SEL_MAXV; ++v) {
+    int e = lane + 64 * v;
+    if (v < V && e < E && !((keep >> (e / Eg)) & 1ull)) c[v] = 0.0f;
+  }
+  // Top K, descending, ties to the lower expert id.
+  float my_s = 0.0f;
+  int my_e = 0;
+  uint32_t taken = 0;
+  for (int k = 0; k < K; ++k) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int v = 0; v < SEL_MAXV; ++v) {
+      int e = lane + 64 * v;
+      if (v < V && e < E && !((taken >> v) & 1u) && c[v] > bv) {
+        bv = c[v];
+        bi = e;
+      }
+    }
+    wave_argmax(bv, bi);
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    if (lane == k) {
+      my_e = bi;
+      my_s = s_s[wave][bi];
+    }
+  }
+  // Weights: unbiased scores, normalised over the K slots (K > 1), times rho.
+  float sum = 0.0f;
+  for (int k = 0; k < K; ++k) sum += __shfl(my_s, k, 64);
+  if (lane < K) {
+    float wv = (K > 1) ? my_s / (sum + 1e-20f) : my_s;
+    idx_out[t * K + lane] = my_e;
+    w_out[t * K + lane] = wv * rho;
+  }
+}
+
+}  // namespace
+
+int gate_ksplit(int64_t T, int H, int E) {
+  if (H % GBK) return 1;
+  int64_t tiles = ((T + GBM - 1) / GBM) * ((E + GBN - 1) / GBN);
+  int ks = 1;
+  while (ks < 8 && tiles * ks < 512 && H % (GBK * ks * 2) == 0) ks *= 2;
+  return ks;
+}
+
+hipError_t launch_gate_logits(const void* x, bool x_bf16, const float* gate_w, float* partials,
+                              int64_t T, int H, int E, int ksplit, hipStream_t s) {
+  if (x_bf16) {
+    dim3 grid((unsigned)((T + GBM - 1) / GBM), (E + GBN - 1) / GBN, ksplit);
+    hipLaunchKernelGGL(gate_logits_bf16_kernel, grid, dim3(GTHREADS), 0, s,
+                       (const uint16_t*)x, gate_w, partials, T, H, E, H / ksplit);
+  } else {
+    dim3 grid((unsigned)((T + 15) / 16), (E + 15) / 16);
+    hipLaunchKernelGGL(gate_logits_f32_kernel, grid, dim3(256), 0, s, (const float*)x, gate_w,
+                       partials, T, H, E);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_select(const float* partials, int ksplit, const float* bias, float* logits_out,
+                         int32_t* idx, float* w, int64_t T, int E, int G, int TG, int K,
+                         float rho, hipStream_t s) {
+  dim3 grid((unsigned)((T + SEL_WAVES - 1) / SEL_WAVES));
+  hipLaunchKernelGGL(select_kernel, grid, dim3(SEL_WAVES * 64), 0, s, partials, ksplit, bias,
+                     logits_out, idx, w, T, E, G, TG, K, rho);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,390 @@
+// C ABI of libmoe: argument validation, workspace layout and launch order.
+// Every check happens on the host before anything is enqueued.
+#include "../../include/moe.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "moe_internal.hpp"
+
+namespace {
+
+thread_local char g_msg[512] = "";
+
+moe_status fail(moe_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+moe_status hip_fail(hipError_t e, const char* where) {
+  return fail(MOE_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+inline size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Shape checks shared by every entry point.
+moe_status check_cfg(const moe_config* c) {
+  if (!c) return fail(MOE_ERR_INVALID_ARG, "cfg is NULL");
+  const int H = c->hidden_size, E = c->n_routed_experts, G = c->n_group, TG = c->topk_group,
+            K = c->num_experts_per_tok, I = c->moe_intermediate_size,
+            Is = c->shared_intermediate_size;
+  if (H <= 0 || E <= 0 || G <= 0 || I <= 0 || Is < 0)
+    return fail(MOE_ERR_INVALID_ARG, "sizes must be positive (H=%d E=%d G=%d I=%d Is=%d)", H, E, G,
+                I, Is);
+  if (E % G != 0 || E / G < 2)
+    return fail(MOE_ERR_INVALID_ARG, "n_routed_experts %% n_group must be 0 with >= 2 experts per "
+                "group (E=%d G=%d)", E, G);
+  if (TG < 1 || TG > G)
+    return fail(MOE_ERR_INVALID_ARG, "topk_group must be in [1, n_group] (TG=%d G=%d)", TG, G);
+  if (K < 1 || K > E)
+    return fail(MOE_ERR_INVALID_ARG, "num_experts_per_tok must be in [1, E] (K=%d E=%d)", K, E);
+  if (!(isfinite(c->routed_scaling_factor) && c->routed_scaling_factor > 0.0f))
+    return fail(MOE_ERR_INVALID_ARG, "routed_scaling_factor must be finite and > 0");
+  const moe_dtype a = c->act_dtype, w = c->weight_dtype;
+  if (a != MOE_F32 && a != MOE_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "act_dtype must be MOE_F32 or MOE_BF16");
+  if (w != MOE_F32 && w != MOE_BF16 && w != MOE_FP8_E4M3)
+    return fail(MOE_ERR_INVALID_ARG, "unknown weight_dtype");
+  // Valid for the method, not handled by these kernels:
+  if (E > 512) return fail(MOE_ERR_UNSUPPORTED, "n_routed_experts > 512");
+  if (G > 64) return fail(MOE_ERR_UNSUPPORTED, "n_group > 64");
+  if (K > 64) return fail(MOE_ERR_UNSUPPORTED, "num_experts_per_tok > 64");
+  if ((a == MOE_F32) != (w == MOE_F32))
+    return fail(MOE_ERR_UNSUPPORTED, "fp32 activations need fp32 weights and vice versa");
+  const int mult = (w == MOE_FP8_E4M3) ? 128 : 64;
+  if (H % mult || I % mult || Is % mult)
+    return fail(MOE_ERR_UNSUPPORTED, "hidden and FFN sizes must be multiples of %d", mult);
+  return MOE_OK;
+}
+
+moe_status check_T(int64_t T, const moe_config* c) {
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T < 0");
+  if (T * (int64_t)c->num_experts_per_tok > 0x7fffffffLL || T > 0x7fffffffLL)
+    return fail(MOE_ERR_UNSUPPORTED, "T * top_k exceeds int32 indexing");
+  return MOE_OK;
+}
+
+size_t act_bytes(const moe_config* c) { return c->act_dtype == MOE_BF16 ? 2 : 4; }
+
+// Workspace segments (byte offsets, 256-aligned).
+struct Layout {
+  size_t err, part, idx, w, counts, offsets, perm, pos, hist, tiles, h, hs, xq, xs, y, ys, total;
+  int ksplit;
+};
+
+Layout layout(const moe_config* c, int64_t T) {
+  Layout L{};
+  const int64_t H = c->hidden_size, E = c->n_routed_experts, K = c->num_experts_per_tok,
+                I = c->moe_intermediate_size, Is = c->shared_intermediate_size;
+  const int64_t N = T * K;
+  const bool fp8 = c->weight_dtype == MOE_FP8_E4M3;
+  L.ksplit = c->act_dtype == MOE_BF16 ? moe::gate_ksplit(T, (int)H, (int)E) : 1;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o += up(bytes);
+    return at;
+  };
+  L.err = take(sizeof(int32_t));
+  L.part = take((size_t)L.ksplit * T * E * 4);
+  L.idx = take((size_t)N * 4);
+  L.w = take((size_t)N * 4);
+  L.counts = take((size_t)E * 4);
+  L.offsets = take((size_t)(E + 1) * 4);
+  L.perm = take((size_t)N * 4);
+  L.pos = take((size_t)N * 4);
+  L.hist = take((size_t)moe::permute_nblk(N) * (E + 1) * 4);
+  moe::FfnDims d{T, N, (int)H, (int)I, (int)Is, (int)E, (int)K};
+  L.tiles = take(moe::ffn_tiles_bytes(d));
+  const size_t hel = (size_t)(N * I + T * Is);
+  if (fp8) {
+    L.h = take(hel);
+    L.hs = take(hel / 128 * 4);
+    L.xq = take((size_t)T * H);
+    L.xs = take((size_t)T * H / 128 * 4);
+  } else {
+    L.h = take(hel * act_bytes(c));
+    L.hs = L.xq = L.xs = o;
+  }
+  L.y = take((size_t)N * H * act_bytes(c));
+  L.ys = take((size_t)T * H * act_bytes(c));
+  L.total = o;
+  return L;
+}
+
+template <typename P>
+P* at(void* ws, size_t off) {
+  return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
+}
+
+moe_status check_ws(void* ws, size_t ws_bytes, const Layout& L) {
+  if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign)
+    return fail(MOE_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
+  if (ws_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, L.total);
+  return MOE_OK;
+}
+
+#define CHECK(expr)                  \
+  do {                               \
+    moe_status _s = (expr);          \
+    if (_s != MOE_OK) return _s;     \
+  } while (0)
+#define NONNULL(p)                                                     \
+  do {                                                                 \
+    if (!(p)) return fail(MOE_ERR_INVALID_ARG, "%s is NULL", #p);      \
+  } while (0)
+#define HIPCALL(expr, where)                              \
+  do {                                                    \
+    hipError_t _e = (expr);                               \
+    if (_e != hipSuccess) return hip_fail(_e, where);     \
+  } while (0)
+
+// ---- the pieces, after validation -------------------------------------------
+
+moe_status run_gate(const moe_config* c, int64_t T, const void* x, const float* gate_w,
+                    const float* bias, float* logits, int32_t* idx, float* w, void* ws,
+                    const Layout& L, hipStream_t s) {
+  float* part = at<float>(ws, L.part);
+  const bool bf16 = c->act_dtype == MOE_BF16;
+  HIPCALL(moe::launch_gate_logits(x, bf16, gate_w, part, T, c->hidden_size, c->n_routed_experts,
+                                  L.ksplit, s),
+          "gate logits");
+  HIPCALL(moe::launch_select(part, L.ksplit, bias, logits, idx, w, T, c->n_routed_experts,
+                             c->n_group, c->topk_group, c->num_experts_per_tok,
+                             c->routed_scaling_factor, s),
+          "select");
+  return MOE_OK;
+}
+
+moe_status run_permute(const moe_config* c, int64_t T, const int32_t* idx, int32_t* counts,
+                       int32_t* offsets, int32_t* perm, int32_t* pos, void* ws, const Layout& L,
+                       hipStream_t s) {
+  HIPCALL(moe::launch_permute(idx, T * c->num_experts_per_tok, c->n_routed_experts,
+                              at<int32_t>(ws, L.hist), counts, offsets, perm, pos,
+                              at<int32_t>(ws, L.err), s),
+          "permute");
+  return MOE_OK;
+}
+
+moe_status run_ffn(const moe_config* c, int64_t T, const void* x, const int32_t* perm,
+                   const int32_t* offsets, const moe_weights* wt, void* y, void* ys, void* ws,
+                   const Layout& L, hipStream_t s) {
+  moe::FfnDims d{T, T * c->num_experts_per_tok, c->hidden_size, c->moe_intermediate_size,
+                 c->shared_intermediate_size, c->n_routed_experts, c->num_experts_per_tok};
+  switch (c->weight_dtype) {
+    case MOE_F32:
+      HIPCALL(moe::launch_ffn_f32(d, (const float*)x, perm, offsets, (const float*)wt->w13,
+                                  (const float*)wt->w2, (const float*)wt->ws13,
+                                  (const float*)wt->ws2, at<float>(ws, L.h), (float*)y,
+                                  (float*)ys, s),
+              "ffn f32");
+      break;
+    case MOE_BF16:
+      HIPCALL(moe::launch_ffn_bf16(d, (const uint16_t*)x, perm, offsets, (const uint16_t*)wt->w13,
+                                   (const uint16_t*)wt->w2, (const uint16_t*)wt->ws13,
+                                   (const uint16_t*)wt->ws2, at<uint16_t>(ws, L.h),
+                                   at<int32_t>(ws, L.tiles), (uint16_t*)y, (uint16_t*)ys, s),
+              "ffn bf16");
+      break;
+    case MOE_FP8_E4M3: {
+      uint8_t* xq = at<uint8_t>(ws, L.xq);
+      float* xs = at<float>(ws, L.xs);
+      HIPCALL(moe::launch_quant_rows((const uint16_t*)x, T, c->hidden_size, xq, xs, s),
+              "quantise x");
+      HIPCALL(moe::launch_ffn_fp8(d, xq, xs, perm, offsets, (const uint8_t*)wt->w13, wt->w13_scale,
+                                  (const uint8_t*)wt->w2, wt->w2_scale, (const uint8_t*)wt->ws13,
+                                  wt->ws13_scale, (const uint8_t*)wt->ws2, wt->ws2_scale,
+                                  at<uint8_t>(ws, L.h), at<float>(ws, L.hs),
+                                  at<int32_t>(ws, L.tiles), (uint16_t*)y, (uint16_t*)ys, s),
+              "ffn fp8");
+      break;
+    }
+  }
+  return MOE_OK;
+}
+
+moe_status check_weights(const moe_config* c, const moe_weights* w, bool need_gate) {
+  NONNULL(w);
+  if (need_gate) {
+    NONNULL(w->gate_w);
+    NONNULL(w->bias);
+  }
+  NONNULL(w->w13);
+  NONNULL(w->w2);
+  const bool fp8 = c->weight_dtype == MOE_FP8_E4M3;
+  if (fp8) {
+    NONNULL(w->w13_scale);
+    NONNULL(w->w2_scale);
+  }
+  if (c->shared_intermediate_size > 0) {
+    NONNULL(w->ws13);
+    NONNULL(w->ws2);
+    if (fp8) {
+      NONNULL(w->ws13_scale);
+      NONNULL(w->ws2_scale);
+    }
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_bytes(const moe_config* cfg, int64_t T) {
+  if (check_cfg(cfg) != MOE_OK || T < 0 || check_T(T, cfg) != MOE_OK) return 0;
+  return layout(cfg, T).total;
+}
+
+moe_status moe_gate(const moe_config* cfg, int64_t T, const void* x, const float* gate_w,
+                    const float* bias, float* logits, int32_t* topk_idx, float* topk_w, void* ws,
+                    size_t ws_bytes, void* stream) {
+  CHECK(check_cfg(cfg));
+  CHECK(check_T(T, cfg));
+  if (T == 0) return MOE_OK;
+  NONNULL(x);
+  NONNULL(gate_w);
+  NONNULL(bias);
+  NONNULL(topk_idx);
+  NONNULL(topk_w);
+  const Layout L = layout(cfg, T);
+  CHECK(check_ws(ws, ws_bytes, L));
+  return run_gate(cfg, T, x, gate_w, bias, logits, topk_idx, topk_w, ws, L, (hipStream_t)stream);
+}
+
+moe_status moe_permute(const moe_config* cfg, int64_t T, const int32_t* topk_idx, int32_t* counts,
+                       int32_t* offsets, int32_t* perm, int32_t* pos, void* ws, size_t ws_bytes,
+                       void* stream) {
+  CHECK(check_cfg(cfg));
+  CHECK(check_T(T, cfg));
+  if (T == 0) return MOE_OK;
+  NONNULL(topk_idx);
+  NONNULL(counts);
+  NONNULL(offsets);
+  NONNULL(perm);
+  NONNULL(pos);
+  const Layout L = layout(cfg, T);
+  CHECK(check_ws(ws, ws_bytes, L));
+  return run_permute(cfg, T, topk_idx, counts, offsets, perm, pos, ws, L, (hipStream_t)stream);
+}
+
+moe_status moe_expert_ffn(const moe_config* cfg, int64_t T, const void* x, const int32_t* perm,
+                          const int32_t* offsets, const moe_weights* w, void* y, void* y_shared,
+                          void* ws, size_t ws_bytes, void* stream) {
+  CHECK(check_cfg(cfg));
+  CHECK(check_T(T, cfg));
+  if (T == 0) return MOE_OK;
+  NONNULL(x);
+  NONNULL(perm);
+  NONNULL(offsets);
+  NONNULL(y);
+  CHECK(check_weights(cfg, w, false));
+  if (cfg->shared_intermediate_size > 0) NONNULL(y_shared);
+  const Layout L = layout(cfg, T);
+  CHECK(check_ws(ws, ws_bytes, L));
+  return run_ffn(cfg, T, x, perm, offsets, w, y,
+                 cfg->shared_intermediate_size > 0 ? y_shared : nullptr, ws, L,
+                 (hipStream_t)stream);
+}
+
+moe_status moe_combine(const moe_config* cfg, int64_t T, const void* y, const void* y_shared,
+                       const int32_t* pos, const float* topk_w, void* out, void* stream) {
+  CHECK(check_cfg(cfg));
+  CHECK(check_T(T, cfg));
+  if (T == 0) return MOE_OK;
+  NONNULL(y);
+  NONNULL(pos);
+  NONNULL(topk_w);
+  NONNULL(out);
+  if (cfg->shared_intermediate_size > 0) NONNULL(y_shared);
+  if (cfg->hidden_size % 8)
+    return fail(MOE_ERR_UNSUPPORTED, "hidden_size must be a multiple of 8");
+  HIPCALL(moe::launch_combine(y, cfg->shared_intermediate_size > 0 ? y_shared : nullptr, pos,
+                              topk_w, out, T, cfg->hidden_size, cfg->num_experts_per_tok,
+                              cfg->act_dtype == MOE_BF16, (hipStream_t)stream),
+          "combine");
+  return MOE_OK;
+}
+
+moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const moe_weights* w,
+                       void* out, float* logits, int32_t* topk_idx, float* topk_w,
+                       int32_t* counts, int32_t* perm, void* ws, size_t ws_bytes, void* stream) {
+  CHECK(check_cfg(cfg));
+  CHECK(check_T(T, cfg));
+  if (T == 0) return MOE_OK;
+  NONNULL(x);
+  NONNULL(out);
+  CHECK(check_weights(cfg, w, true));
+  const Layout L = layout(cfg, T);
+  CHECK(check_ws(ws, ws_bytes, L));
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* idx = topk_idx ? topk_idx : at<int32_t>(ws, L.idx);
+  float* wt = topk_w ? topk_w : at<float>(ws, L.w);
+  int32_t* cnt = counts ? counts : at<int32_t>(ws, L.counts);
+  int32_t* pm = perm ? perm : at<int32_t>(ws, L.perm);
+  int32_t* offs = at<int32_t>(ws, L.offsets);
+  int32_t* pos = at<int32_t>(ws, L.pos);
+  void* y = at<void>(ws, L.y);
+  void* ys = cfg->shared_intermediate_size > 0 ? at<void>(ws, L.ys) : nullptr;
+  CHECK(run_gate(cfg, T, x, w->gate_w, w->bias, logits, idx, wt, ws, L, s));
+  CHECK(run_permute(cfg, T, idx, cnt, offs, pm, pos, ws, L, s));
+  CHECK(run_ffn(cfg, T, x, pm, offs, w, y, ys, ws, L, s));
+  HIPCALL(moe::launch_combine(y, ys, pos, wt, out, T, cfg->hidden_size, cfg->num_experts_per_tok,
+                              cfg->act_dtype == MOE_BF16, s),
+          "combine");
+  return MOE_OK;
+}
+
+moe_status moe_quantize_act(const moe_config* cfg, int64_t rows, const void* x, uint8_t* xq,
+                            float* xs, void* stream) {
+  CHECK(check_cfg(cfg));
+  if (rows < 0) return fail(MOE_ERR_INVALID_ARG, "rows < 0");
+  if (rows == 0) return MOE_OK;
+  if (cfg->act_dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "the fp8 quantiser takes bf16 activations");
+  if (cfg->hidden_size % 128) return fail(MOE_ERR_UNSUPPORTED, "hidden_size %% 128 != 0");
+  NONNULL(x);
+  NONNULL(xq);
+  NONNULL(xs);
+  HIPCALL(moe::launch_quant_rows((const uint16_t*)x, rows, cfg->hidden_size, xq, xs,
+                                 (hipStream_t)stream),
+          "quantise");
+  return MOE_OK;
+}
+
+moe_status moe_get_device_error(void* ws, size_t ws_bytes, void* stream) {
+  if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
+  if (ws_bytes < sizeof(int32_t)) return fail(MOE_ERR_WORKSPACE, "workspace too small");
+  int32_t flag = 0;
+  hipStream_t s = (hipStream_t)stream;
+  HIPCALL(hipMemcpyAsync(&flag, ws, sizeof(flag), hipMemcpyDeviceToHost, s), "read error flag");
+  HIPCALL(hipStreamSynchronize(s), "synchronise");
+  if (flag) return fail(MOE_ERR_DEVICE_CHECK, "an expert index was outside [0, E)");
+  return MOE_OK;
+}
+
+const char* moe_strerror(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    case MOE_ERR_DEVICE_CHECK: return "device check failed (expert index out of range)";
+  }
+  return "unknown status";
+}
+
+const char* moe_last_error(void) { return g_msg; }
+
+}  // extern "C"

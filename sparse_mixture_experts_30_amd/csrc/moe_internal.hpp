@@ -1,0 +1,109 @@
+// Internal declarations shared by the HIP sources of libmoe (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---------------------------------------------------------------- vector types
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kNumXcd = 8;  // MI355X: 8 XCDs, workgroups dispatched round-robin
+
+// ---------------------------------------------------------------- scalar helpers
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (u >> 16) | 0x40u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Map a linear workgroup id onto a work index so that each XCD receives one
+// contiguous range of the work list (consecutive ids go to different XCDs).
+// `nb` is the grid size (a multiple of kNumXcd).
+__device__ __forceinline__ int xcd_contiguous(int b, int nb) {
+  int per = nb / kNumXcd;
+  return (b % kNumXcd) * per + b / kNumXcd;
+}
+
+// ---------------------------------------------------------------- host launchers
+struct GroupedGemmArgs;
+
+hipError_t launch_gate_logits(const void* x, bool x_bf16, const float* gate_w, float* partials,
+                              int64_t T, int H, int E, int ksplit, hipStream_t s);
+int gate_ksplit(int64_t T, int H, int E);
+hipError_t launch_select(const float* partials, int ksplit, const float* bias, float* logits_out,
+                         int32_t* idx, float* w, int64_t T, int E, int G, int TG, int K,
+                         float rho, hipStream_t s);
+
+int permute_nblk(int64_t N);
+hipError_t launch_permute(const int32_t* idx, int64_t N, int E, int32_t* hist, int32_t* counts,
+                          int32_t* offsets, int32_t* perm, int32_t* pos, int32_t* err,
+                          hipStream_t s);
+
+// Expert FFN tile schedule (see ffn_sched.hip for the entry format).
+int64_t ffn_max_mtiles(int64_t N, int64_t T, int E, int BM);
+hipError_t launch_build_tiles(const int32_t* offsets, int E, int64_t T, bool has_shared, int BM,
+                              int32_t* tiles, hipStream_t s);
+
+// Work item w (0 <= w < tiles[0] * ntn) of a grouped GEMM with ntn N-tiles:
+// returns the M-tile entry and the N-tile.  Inside a group the N-tile index
+// is the slow one, so workgroups that run together on one XCD share one
+// weight slice across the group's M-tiles.
+__device__ __forceinline__ const int32_t* decode_work(const int32_t* tiles, int64_t w, int ntn,
+                                                      int& ntile) {
+  const int64_t i0 = w / ntn;
+  const int32_t* e0 = tiles + 8 + 8 * i0;
+  const int32_t L = e0[3], mt = e0[4];
+  const int64_t local = w - (int64_t)L * ntn;
+  ntile = (int)(local / mt);
+  return tiles + 8 + 8 * (int64_t)(L + local % mt);
+}
+
+// Expert FFN plans: the GEMMs.
+struct FfnDims {
+  int64_t T;       // tokens
+  int64_t N;       // routed rows T*K
+  int H, I, Is, E, K;
+};
+size_t ffn_tiles_bytes(const FfnDims& d);
+hipError_t launch_ffn_bf16(const FfnDims& d, const uint16_t* x, const int32_t* perm,
+                           const int32_t* offsets, const uint16_t* w13, const uint16_t* w2,
+                           const uint16_t* ws13, const uint16_t* ws2, uint16_t* h,
+                           int32_t* tiles, uint16_t* y, uint16_t* ys, hipStream_t s);
+hipError_t launch_ffn_f32(const FfnDims& d, const float* x, const int32_t* perm,
+                          const int32_t* offsets, const float* w13, const float* w2,
+                          const float* ws13, const float* ws2, float* h, float* y, float* ys,
+                          hipStream_t s);
+hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int cols, uint8_t* q, float* sc,
+                             hipStream_t s);
+hipError_t launch_ffn_fp8(const FfnDims& d, const uint8_t* xq, const float* xs,
+                          const int32_t* perm, const int32_t* offsets, const uint8_t* w13,
+                          const float* w13s, const uint8_t* w2, const float* w2s,
+                          const uint8_t* ws13, const float* ws13s, const uint8_t* ws2,
+                          const float* ws2s, uint8_t* hq, float* hs, int32_t* tiles,
+                          uint16_t* y, uint16_t* ys, hipStream_t s);
+
+hipError_t launch_combine(const void* y, const void* ys, const int32_t* pos, const float* w,
+                          void* out, int64_t T, int H, int K, bool bf16, hipStream_t s);
+
+}  // namespace moe

@@ -22,4 +22,8 @@ def _host_libs():
         synth.build()
     if not os.path.exists(oracle._SO):
         oracle.build()
+    import sparse_mixture_experts_30_amd._lib as L
+    if not os.path.exists(L.SO_PATH):
+        from sparse_mixture_experts_30_amd import build
+        build.build()
     yield

@@ -1,0 +1,118 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and rejects invalid arguments on the host before any HIP
+call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_mixture_experts_30_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def _header_functions():
+    with open(os.path.join(ROOT, "include", "moe.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    names = _header_functions()
+    assert names == sorted(moe.EXPORTS)
+    L = moe.lib()
+    for n in names:
+        assert getattr(L, n) is not None
+
+
+def _cfg(**kw):
+    base = dict(H=7168, E=256, G=8, TG=4, K=8, I=2048, Is=2048, rho=2.5, act="bf16", wdtype="bf16")
+    base.update(kw)
+    return moe.config(base["H"], base["E"], base["G"], base["TG"], base["K"], base["I"],
+                      base["Is"], base["rho"], base["act"], base["wdtype"])
+
+
+def _gate(cfg, T=4, ws_bytes=1 << 40, x=FAKE, gw=FAKE, b=FAKE, idx=FAKE, w=FAKE, ws=FAKE * 256):
+    return moe.lib().moe_gate(ctypes.byref(cfg), T, x, gw, b, None, idx, w, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(E=250, G=8), moe.MOE_ERR_INVALID_ARG),          # E % G != 0
+    (dict(E=8, G=8), moe.MOE_ERR_INVALID_ARG),            # one expert per group
+    (dict(TG=9), moe.MOE_ERR_INVALID_ARG),                # topk_group > n_group
+    (dict(TG=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(K=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(K=257), moe.MOE_ERR_INVALID_ARG),               # K > E
+    (dict(rho=0.0), moe.MOE_ERR_INVALID_ARG),
+    (dict(rho=float("inf")), moe.MOE_ERR_INVALID_ARG),
+    (dict(rho=float("nan")), moe.MOE_ERR_INVALID_ARG),
+    (dict(H=-1), moe.MOE_ERR_INVALID_ARG),
+    (dict(E=1024, G=8), moe.MOE_ERR_UNSUPPORTED),         # E > 512
+    (dict(E=256, G=128), moe.MOE_ERR_UNSUPPORTED),        # G > 64
+    (dict(K=65), moe.MOE_ERR_UNSUPPORTED),
+    (dict(H=7000), moe.MOE_ERR_UNSUPPORTED),              # H % 64
+    (dict(wdtype="fp8", I=2048 + 64), moe.MOE_ERR_UNSUPPORTED),  # fp8 needs % 128
+    (dict(act="f32", wdtype="bf16"), moe.MOE_ERR_UNSUPPORTED),
+])
+def test_config_validation(kw, status):
+    cfg = _cfg(**kw)
+    assert _gate(cfg) == status
+    assert moe.moe_workspace_bytes(cfg, 16) == 0
+    assert moe.moe_last_error() != ""
+
+
+def test_argument_validation():
+    cfg = _cfg()
+    assert _gate(cfg, T=-1) == moe.MOE_ERR_INVALID_ARG
+    assert _gate(cfg, x=None) == moe.MOE_ERR_INVALID_ARG
+    assert _gate(cfg, gw=None) == moe.MOE_ERR_INVALID_ARG
+    assert _gate(cfg, idx=None) == moe.MOE_ERR_INVALID_ARG
+    assert _gate(cfg, ws=None) == moe.MOE_ERR_WORKSPACE
+    assert _gate(cfg, ws_bytes=100) == moe.MOE_ERR_WORKSPACE
+    assert _gate(cfg, ws=FAKE * 256 + 4) == moe.MOE_ERR_WORKSPACE       # misaligned
+    assert "workspace" in moe.moe_last_error()
+    # T == 0 is a no-op that succeeds without touching any pointer
+    assert _gate(cfg, T=0, x=None, ws=None) == moe.MOE_OK
+    L = moe.lib()
+    assert L.moe_permute(ctypes.byref(cfg), 4, None, FAKE, FAKE, FAKE, FAKE, FAKE * 256, 1 << 40,
+                         None) == moe.MOE_ERR_INVALID_ARG
+    w = moe.weights(gate_w=FAKE, bias=FAKE, w13=FAKE, w2=FAKE)           # no shared weights
+    assert L.moe_expert_ffn(ctypes.byref(cfg), 4, FAKE, FAKE, FAKE, ctypes.byref(w), FAKE, FAKE,
+                            FAKE * 256, 1 << 40, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_forward(ctypes.byref(cfg), 4, FAKE, ctypes.byref(w), FAKE, None, None, None,
+                         None, None, FAKE * 256, 1 << 40, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_combine(ctypes.byref(cfg), 4, FAKE, None, FAKE, FAKE, FAKE, None) == \
+        moe.MOE_ERR_INVALID_ARG                                          # y_shared NULL, Is > 0
+    cfg8 = _cfg(wdtype="fp8")
+    w8 = moe.weights(gate_w=FAKE, bias=FAKE, w13=FAKE, w2=FAKE, ws13=FAKE, ws2=FAKE)
+    assert L.moe_forward(ctypes.byref(cfg8), 4, FAKE, ctypes.byref(w8), FAKE, None, None, None,
+                         None, None, FAKE * 256, 1 << 40, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_quantize_act(ctypes.byref(_cfg(act="f32", wdtype="f32")), 4, FAKE, FAKE, FAKE,
+                              None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_get_device_error(None, 0, None) == moe.MOE_ERR_WORKSPACE
+
+
+def test_workspace_bytes_grows_with_tokens():
+    cfg = _cfg()
+    a, b = moe.moe_workspace_bytes(cfg, 32), moe.moe_workspace_bytes(cfg, 4096)
+    assert 0 < a < b
+    assert b % 256 == 0
+    # y [T*K, H] bf16 alone is part of it
+    assert b > 4096 * 8 * 7168 * 2
+
+
+def test_strerror():
+    for s in range(6):
+        assert moe.moe_strerror(s)
+    assert moe.moe_strerror(99) == "unknown status"
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    import sparse_mixture_experts_30_amd._lib as L
+    monkeypatch.setattr(L, "_lib", None)
+    monkeypatch.setattr(L, "SO_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        L.lib()

@@ -426,3 +426,37 @@ def test_fp8_layer_uses_dequantised_weights():
     r2 = oracle.forward(cfg8, inp, quant_act=True)
     rel = np.linalg.norm(r2["out"] - r8["out"]) / np.linalg.norm(r8["out"])
     assert 1e-4 < rel < 0.1
+
+
+# ---------------------------------------------------------------- per-row FFN and the combine step
+
+def test_ffn_rows_match_numpy_and_compose_to_layer():
+    cfg = synth.C1.replace(T=30, H=128, E=8, G=4, TG=2, K=3, I=64, Is=96, rho=1.3)
+    inp = synth.gen_inputs(cfg)
+    r = oracle.forward(cfg, inp)
+    counts, offsets, perm, pos = oracle.permute(r["idx"], cfg.E)
+    experts = np.repeat(np.arange(cfg.E), counts)
+    y = oracle.ffn(cfg, inp, perm // cfg.K, experts)              # sorted-order rows
+    ys = oracle.ffn(cfg, inp, np.arange(cfg.T), -np.ones(cfg.T, np.int32))
+    x = inp["x"].astype(np.float64)
+    for j in (0, 7, len(perm) - 1):
+        e, t = experts[j], perm[j] // cfg.K
+        ref = _np_ffn(x[t:t + 1], inp["w13"][e].astype(np.float64), inp["w2"][e].astype(np.float64))
+        np.testing.assert_allclose(y[j], ref[0], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(ys, _np_ffn(x, inp["ws13"].astype(np.float64),
+                                           inp["ws2"].astype(np.float64)), rtol=1e-12, atol=1e-13)
+    # combine of the sorted rows = the layer computed token by token
+    out = oracle.combine(y, ys, pos, r["w"], cfg.K)
+    np.testing.assert_allclose(out, r["out"], rtol=1e-12, atol=1e-13)
+
+
+def test_combine_formula_on_random_rows():
+    T, K, H = 9, 3, 16
+    y = synth.normal_f32(T * K * H, 7, synth.T_TEST, 20, 1.0).reshape(T * K, H).astype(np.float64)
+    ys = synth.normal_f32(T * H, 7, synth.T_TEST, 21, 1.0).reshape(T, H).astype(np.float64)
+    w = synth.uniform_f32(T * K, 7, synth.T_TEST, 22, 0, 2).reshape(T, K).astype(np.float64)
+    pos = np.argsort(synth.words(T * K, 7, synth.T_TEST, 23), kind="stable").astype(np.int32)
+    out = oracle.combine(y, ys, pos, w, K)
+    ref = ys + np.einsum("tk,tkh->th", w, y[pos.reshape(T, K)])
+    np.testing.assert_allclose(out, ref, rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(oracle.combine(y, None, pos, w, K), ref - ys, rtol=1e-13, atol=1e-14)
