@@ -87,7 +87,9 @@ typedef struct {
  * w13 stacks each expert's gate projection (rows 0..I-1) over its up
  * projection (rows I..2I-1).  For MOE_FP8_E4M3 the *_scale arrays hold one
  * fp32 per 128x128 block, row-major over (row block, column block); they are
- * ignored (may be NULL) otherwise.  ws13/ws2 (+scales) may be NULL iff Is == 0. */
+ * ignored (may be NULL) otherwise.  ws13/ws2 (+scales) may be NULL iff Is == 0.
+ * packed = 0: w13, w2, ws13, ws2 are row-major as shown; packed = 1: all four
+ * were rearranged by moe_pack_weight (bf16 weights only; scales unchanged). */
 typedef struct {
     const float* gate_w;     /* [E, H]                                           */
     const float* bias;       /* [E]  e_score_correction_bias                     */
@@ -99,7 +101,11 @@ typedef struct {
     const float* ws13_scale; /* [2Is/128, H/128]                                 */
     const void* ws2;         /* [H, Is]                                          */
     const float* ws2_scale;  /* [H/128, Is/128]                                  */
+    int32_t packed;          /* 0 = row-major, 1 = moe_pack_weight layout         */
 } moe_weights;
+
+/* Which expert weight matrix a pack call converts. */
+typedef enum { MOE_W13 = 0, MOE_W2 = 1, MOE_WS13 = 2, MOE_WS2 = 3 } moe_weight_id;
 
 /* Bytes of workspace that every entry point below needs for T tokens (the
  * maximum over them, so one buffer serves all).  Returns 0 if cfg is invalid
@@ -176,9 +182,27 @@ moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const mo
 moe_status moe_quantize_act(const moe_config* cfg, int64_t rows, const void* x, uint8_t* xq,
                             float* xs, void* stream);
 
-/* Reads (and clears) the device error flag in ws: synchronises `stream`.
- * Returns MOE_OK, MOE_ERR_DEVICE_CHECK if a kernel saw an invalid expert
- * index since the last call, or MOE_ERR_HIP. */
+/* Weight streaming layout for the bf16 expert GEMMs.  The grouped GEMM reads
+ * each weight matrix once per call; in row-major order that is one 128-byte
+ * piece per weight row per k step, rows 2*H bytes apart.  The packed layout
+ * stores, for every (expert, output tile, k step), the MFMA operand
+ * fragments of the tile's 256 weight rows x 64 k as one contiguous 32 KiB
+ * block in the order the kernel consumes them (per wave, per 32-row block,
+ * per 16-k slice: 64 lanes x 16 bytes), so the weights stream sequentially
+ * from HBM into registers.  Pack once when the weights are loaded.
+ *   moe_packed_bytes: size of the packed copy of matrix `which` (0 for an
+ *     invalid or non-bf16 config, or for MOE_WS13/MOE_WS2 when Is == 0).
+ *   moe_pack_weight: src is the row-major matrix (w13 [E,2I,H], w2 [E,H,I],
+ *     ws13 [2Is,H] or ws2 [H,Is], bf16), dst a device buffer of
+ *     moe_packed_bytes(cfg, which) bytes (tile padding is zero-filled). */
+size_t moe_packed_bytes(const moe_config* cfg, moe_weight_id which);
+moe_status moe_pack_weight(const moe_config* cfg, moe_weight_id which, const void* src,
+                           void* dst, void* stream);
+
+/* Reads the device error flag in ws, which each moe_permute / moe_forward
+ * call rewrites; synchronises `stream`.  Returns MOE_OK, MOE_ERR_DEVICE_CHECK
+ * if the last permutation on this workspace saw an expert index outside
+ * [0, E), or MOE_ERR_HIP. */
 moe_status moe_get_device_error(void* ws, size_t ws_bytes, void* stream);
 
 /* Static text for a status code. */

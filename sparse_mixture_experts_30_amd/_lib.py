@@ -16,8 +16,9 @@ MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 
 # Every function declared in include/moe.h.
 EXPORTS = ("moe_workspace_bytes", "moe_gate", "moe_permute", "moe_expert_ffn", "moe_combine",
-           "moe_forward", "moe_quantize_act", "moe_get_device_error", "moe_strerror",
-           "moe_last_error")
+           "moe_forward", "moe_quantize_act", "moe_packed_bytes", "moe_pack_weight",
+           "moe_get_device_error", "moe_strerror", "moe_last_error")
+MOE_W13, MOE_W2, MOE_WS13, MOE_WS2 = 0, 1, 2, 3
 
 
 class MoeError(RuntimeError):
@@ -38,7 +39,7 @@ class MoeConfig(ctypes.Structure):
 class MoeWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("gate_w", "bias", "w13", "w13_scale", "w2",
                                                "w2_scale", "ws13", "ws13_scale", "ws2",
-                                               "ws2_scale")]
+                                               "ws2_scale")] + [("packed", ctypes.c_int32)]
 
 
 _lib = None
@@ -63,6 +64,8 @@ def lib():
             "moe_combine": (ctypes.c_int, [cfgp, i64, vp, vp, vp, vp, vp, vp]),
             "moe_forward": (ctypes.c_int, [cfgp, i64, vp, wp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
             "moe_quantize_act": (ctypes.c_int, [cfgp, i64, vp, vp, vp, vp]),
+            "moe_packed_bytes": (sz, [cfgp, ctypes.c_int]),
+            "moe_pack_weight": (ctypes.c_int, [cfgp, ctypes.c_int, vp, vp, vp]),
             "moe_get_device_error": (ctypes.c_int, [vp, sz, vp]),
             "moe_strerror": (ctypes.c_char_p, [ctypes.c_int]),
             "moe_last_error": (ctypes.c_char_p, []),
@@ -108,9 +111,9 @@ def config(H, E, G, TG, K, I, Is, rho, act="bf16", wdtype="bf16") -> MoeConfig:
 
 
 def weights(gate_w=None, bias=None, w13=None, w13_scale=None, w2=None, w2_scale=None, ws13=None,
-            ws13_scale=None, ws2=None, ws2_scale=None) -> MoeWeights:
+            ws13_scale=None, ws2=None, ws2_scale=None, packed=False) -> MoeWeights:
     return MoeWeights(*[_ptr(t) for t in (gate_w, bias, w13, w13_scale, w2, w2_scale, ws13,
-                                          ws13_scale, ws2, ws2_scale)])
+                                          ws13_scale, ws2, ws2_scale)], int(bool(packed)))
 
 
 def moe_workspace_bytes(cfg: MoeConfig, T: int) -> int:
@@ -150,6 +153,14 @@ def moe_forward(cfg, T, x, w: MoeWeights, out, ws, logits=None, topk_idx=None, t
 def moe_quantize_act(cfg, rows, x, xq, xs, stream=None):
     _check(lib().moe_quantize_act(ctypes.byref(cfg), rows, _ptr(x), _ptr(xq), _ptr(xs),
                                   _stream(stream)))
+
+
+def moe_packed_bytes(cfg: MoeConfig, which: int) -> int:
+    return lib().moe_packed_bytes(ctypes.byref(cfg), which)
+
+
+def moe_pack_weight(cfg, which, src, dst, stream=None):
+    _check(lib().moe_pack_weight(ctypes.byref(cfg), which, _ptr(src), _ptr(dst), _stream(stream)))
 
 
 def moe_get_device_error(ws, stream=None) -> int:

@@ -15,7 +15,8 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libmoe.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["gate.hip", "permute.hip", "ffn_sched.hip", "ffn_bf16.hip", "ffn_fp8.hip",
+SOURCES = ["gate.hip", "permute.hip", "ffn_sched.hip", "ffn_bf16.hip", "ffn_bf16_packed.hip",
+           "ffn_fp8.hip",
            "ffn_f32.hip", "combine.hip", "moe_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -25,11 +26,12 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, src + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, build_dir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(build_dir, src + ".o")
+    flags = FLAGS + list(extra)
+    cmd = [HIPCC] + flags + ["-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
-        cmd = [HIPCC] + FLAGS + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC] + flags + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in (r.stderr or "").splitlines()
                     if "packed-fp32-ops" not in l)
@@ -40,14 +42,15 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build() -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(out: str = OUT, build_dir: str = BUILD, extra=()) -> str:
+    """Compile every source and link `out`; `extra` adds compiler flags."""
+    os.makedirs(build_dir, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = OUT + ".tmp"
+        objs = list(ex.map(lambda f: _compile(f, build_dir, extra), SOURCES))
+    tmp = out + ".tmp"
     subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs)
-    os.replace(tmp, OUT)
-    return OUT
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

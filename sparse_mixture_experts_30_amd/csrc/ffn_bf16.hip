@@ -7,15 +7,23 @@
 //   GEMM2: y_rows = h_rows W2^T
 // The shared expert is group E of the same launch with all T tokens in order.
 //
-// Workgroup tile: up to 256 rows of one group x 256 weight rows, k in stages
+// Workgroup tile: up to 256 rows of one group x 256 weight rows, k in steps
 // of 64.  The rows of a tile are the group's actual rows (at most 256): only
 // the 32-row MFMA blocks that hold rows are computed, so an expert with 140
-// rows costs 5 row blocks, and its weight slice is read once.  4 waves; wave w
-// owns weight rows [64w, 64w+64) for all rows of the tile.  For GEMM1 those
-// are 32 gate rows and the 32 matching up rows, so SiLU(g)*u is formed in
-// registers.  LDS stages are XOR-swizzled by 16-byte chunk (conflict-free
-// operand reads) and double-buffered through registers.
+// rows costs 5 row blocks and its weight slice is read once.  4 waves; wave w
+// owns weight rows [64w, 64w+64) for all rows of the tile (for GEMM1, 32 gate
+// rows and the 32 matching up rows, so SiLU(g)*u is formed in registers).
+//
+// Both operands are staged through LDS (XOR-swizzled by 16-byte chunk, so
+// MFMA operand reads are conflict free).  Global loads read whole 128-byte
+// lines (8 lanes per row) and go through two register stages, so every load
+// has two compute steps to arrive: at step s the LDS holds step s, the
+// registers hold steps s+1 and s+2.  The loads are unconditional (rows past
+// the tile's end re-read its first row, loads past the last step re-read the
+// last step), which keeps the compiler's memory-counter waits partial.
 #include "moe_internal.hpp"
+
+#include <algorithm>
 
 namespace moe {
 
@@ -23,9 +31,12 @@ namespace {
 
 constexpr int BM = 256;    // max rows per tile
 constexpr int BNB = 256;   // weight rows per tile
-constexpr int BK = 64;     // k per stage
+constexpr int BK = 64;     // k per step
 constexpr int NT = 256;    // threads
-constexpr size_t kLds = (size_t)2 * (BM + BNB) * 8 * sizeof(uint4);   // 128 KiB
+#ifndef MOE_WEIGHT_NT
+#define MOE_WEIGHT_NT 1
+#endif
+constexpr size_t kLds = (size_t)2 * (BM + BNB) * 8 * sizeof(u32x4);   // 128 KiB
 
 struct GemmArgs {
   const int32_t* tiles;
@@ -45,11 +56,21 @@ struct GemmArgs {
   int64_t ldc_r, ldc_s;
 };
 
+struct Stage {
+  u32x4 a[8], b[8];
+};
+
+// Physical 16-byte chunk of logical chunk c in LDS row r (rows of 128 bytes).
+// Rows r and r+8 differ in the XOR term, so 8 consecutive rows (a 32-bank
+// LDS cycle) and 16 consecutive rows (a 64-bank cycle) of one logical chunk
+// fall in distinct banks.
+__device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ ((r ^ (r >> 3)) & 7)); }
+
 template <bool kGateUp>
 __global__ void __launch_bounds__(NT, 1) grouped_gemm_bf16(GemmArgs p) {
-  extern __shared__ uint4 smem[];
-  uint4* sA = smem;                   // [2][BM * 8]
-  uint4* sB = smem + 2 * BM * 8;      // [2][BNB * 8]
+  extern __shared__ u32x4 smem[];
+  u32x4* sA = smem;                   // [2][BM * 8]
+  u32x4* sB = smem + 2 * BM * 8;      // [2][BNB * 8]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 31, lh = lane >> 5;
 
@@ -72,16 +93,18 @@ __global__ void __launch_bounds__(NT, 1) grouped_gemm_bf16(GemmArgs p) {
   const uint16_t* B = sh ? p.b_s : p.b_r + (int64_t)g * p.b_es;
   const int64_t ldb = kdim;
 
-  // Rows this thread stages: r = tid/8 + 32 j, 16-byte chunk tid % 8.
+  // Rows this thread stages: r = tid/8 + 32 j (j < 8), 16-byte chunk tid % 8.
   const int ch = tid & 7;
+  const int first = (!sh && kGateUp) ? p.perm[row0] / p.K : row0;
   int arow[8], brow[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int r = (tid >> 3) + 32 * j;
-    arow[j] = -1;
-    if (r < nrows) arow[j] = (!sh && kGateUp) ? p.perm[row0 + r] / p.K : row0 + r;
+    int a = first;
+    if (r < nrows) a = (!sh && kGateUp) ? p.perm[row0 + r] / p.K : row0 + r;
+    arow[j] = a;
     int col, src;
-    if (kGateUp) {
+    if (kGateUp) {   // tile row r: wave r/64, gate (r%64 < 32) or up column
       const int wv = r >> 6, jj = r & 63;
       col = n0 + wv * 32 + (jj & 31);
       src = (jj < 32) ? col : ncol + col;
@@ -89,28 +112,29 @@ __global__ void __launch_bounds__(NT, 1) grouped_gemm_bf16(GemmArgs p) {
       col = n0 + r;
       src = col;
     }
-    brow[j] = (col < ncol) ? src : -1;
+    brow[j] = col < ncol ? src : 0;   // a column past ncol is never stored
   }
+  const uint16_t* abase = A + ch * 8;
+  const uint16_t* bbase = B + ch * 8;
+  const int nsteps = kdim / BK;
+  const int last = nsteps - 1;
 
-  uint4 ra[8], rb[8];
-  auto gload = [&](int step) {
-    const int k0 = step * BK + ch * 8;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      ra[j] = make_uint4(0, 0, 0, 0);
-      if (arow[j] >= 0) ra[j] = *reinterpret_cast<const uint4*>(A + (int64_t)arow[j] * lda + k0);
-      rb[j] = make_uint4(0, 0, 0, 0);
-      if (brow[j] >= 0) rb[j] = *reinterpret_cast<const uint4*>(B + (int64_t)brow[j] * ldb + k0);
-    }
+  // Load / store one staged row pair (A row and weight row j) of a step.
+  auto gload1 = [&](Stage& st, int j, int step) {
+    const int k0 = min(step, last) * BK;
+    st.a[j] = *reinterpret_cast<const u32x4*>(abase + (int64_t)arow[j] * lda + k0);
+    const u32x4* pb = reinterpret_cast<const u32x4*>(bbase + (int64_t)brow[j] * ldb + k0);
+#if MOE_WEIGHT_NT
+    st.b[j] = __builtin_nontemporal_load(pb);
+#else
+    st.b[j] = *pb;
+#endif
   };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int r = (tid >> 3) + 32 * j;
-      const int o = r * 8 + (ch ^ (r & 7));
-      sA[buf * BM * 8 + o] = ra[j];
-      sB[buf * BNB * 8 + o] = rb[j];
-    }
+  auto sstore1 = [&](const Stage& st, int j, int buf) {
+    const int r = (tid >> 3) + 32 * j;
+    const int o = buf * BM * 8 + swz(r, ch);
+    sA[o] = st.a[j];
+    sB[o] = st.b[j];
   };
 
   f32x16 acc[8][2];
@@ -120,38 +144,55 @@ __global__ void __launch_bounds__(NT, 1) grouped_gemm_bf16(GemmArgs p) {
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[r][c][i] = 0.0f;
-
   const int nrb = (nrows + 31) >> 5;
-  const int nsteps = kdim / BK;
-  gload(0);
-  sstore(0);
-  if (nsteps > 1) gload(1);
-  __syncthreads();
 
-  for (int step = 0; step < nsteps; ++step) {
-    const uint4* a_s = sA + (step & 1) * BM * 8;
-    const uint4* b_s = sB + (step & 1) * BNB * 8;
+  // One step: MFMAs on LDS buffer `buf`; between its four 16-wide k slices,
+  // the next step's rows move from registers `st` to LDS buffer `nbuf`, and
+  // `st` is refilled with step `ld` from memory.
+  auto step_body = [&](int buf, Stage& st, int nbuf, int ld) {
+    const u32x4* as = sA + buf * BM * 8;
+    const u32x4* bs = sB + buf * BNB * 8;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int c = 2 * kk + lh;
       const int br0 = wave * 64 + lr, br1 = br0 + 32;
-      const bf16x8 b0 = as_bf16x8(b_s[br0 * 8 + (c ^ (br0 & 7))]);
-      const bf16x8 b1 = as_bf16x8(b_s[br1 * 8 + (c ^ (br1 & 7))]);
+      const bf16x8 b0 = as_bf16x8(bs[swz(br0, c)]);
+      const bf16x8 b1 = as_bf16x8(bs[swz(br1, c)]);
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         if (r < nrb) {
           const int ar = r * 32 + lr;
-          const bf16x8 a = as_bf16x8(a_s[ar * 8 + (c ^ (ar & 7))]);
+          const bf16x8 a = as_bf16x8(as[swz(ar, c)]);
           acc[r][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc[r][0], 0, 0, 0);
           acc[r][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc[r][1], 0, 0, 0);
         }
       }
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        sstore1(st, 2 * kk + jj, nbuf);
+        gload1(st, 2 * kk + jj, ld);
+      }
     }
-    if (step + 1 < nsteps) {
-      sstore((step + 1) & 1);
-      if (step + 2 < nsteps) gload(step + 2);
-    }
+  };
+
+  // Register stage R[t % 2] holds step t; LDS buffer t % 2 holds step t.
+  Stage R0, R1;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) gload1(R0, j, 0);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) sstore1(R0, j, 0);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) gload1(R1, j, 1);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) gload1(R0, j, 2);
+  __syncthreads();
+  for (int s = 0; s < nsteps; s += 2) {
+    step_body(0, R1, 1, s + 3);     // step s; stage s+1 to LDS; load s+3
     __syncthreads();
+    if (s + 1 < nsteps) {
+      step_body(1, R0, 0, s + 4);   // step s+1; stage s+2 to LDS; load s+4
+      __syncthreads();
+    }
   }
 
   // Epilogue.  32x32 block layout: lane holds column lane%32, rows

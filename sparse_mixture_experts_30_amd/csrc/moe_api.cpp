@@ -190,11 +190,20 @@ moe_status run_ffn(const moe_config* c, int64_t T, const void* x, const int32_t*
               "ffn f32");
       break;
     case MOE_BF16:
-      HIPCALL(moe::launch_ffn_bf16(d, (const uint16_t*)x, perm, offsets, (const uint16_t*)wt->w13,
-                                   (const uint16_t*)wt->w2, (const uint16_t*)wt->ws13,
-                                   (const uint16_t*)wt->ws2, at<uint16_t>(ws, L.h),
-                                   at<int32_t>(ws, L.tiles), (uint16_t*)y, (uint16_t*)ys, s),
-              "ffn bf16");
+      if (wt->packed) {
+        HIPCALL(moe::launch_ffn_bf16_packed(d, (const uint16_t*)x, perm, offsets, wt->w13, wt->w2,
+                                            wt->ws13, wt->ws2, at<uint16_t>(ws, L.h),
+                                            at<int32_t>(ws, L.tiles), (uint16_t*)y,
+                                            (uint16_t*)ys, s),
+                "ffn bf16 packed");
+      } else {
+        HIPCALL(moe::launch_ffn_bf16(d, (const uint16_t*)x, perm, offsets,
+                                     (const uint16_t*)wt->w13, (const uint16_t*)wt->w2,
+                                     (const uint16_t*)wt->ws13, (const uint16_t*)wt->ws2,
+                                     at<uint16_t>(ws, L.h), at<int32_t>(ws, L.tiles),
+                                     (uint16_t*)y, (uint16_t*)ys, s),
+                "ffn bf16");
+      }
       break;
     case MOE_FP8_E4M3: {
       uint8_t* xq = at<uint8_t>(ws, L.xq);
@@ -215,6 +224,10 @@ moe_status run_ffn(const moe_config* c, int64_t T, const void* x, const int32_t*
 
 moe_status check_weights(const moe_config* c, const moe_weights* w, bool need_gate) {
   NONNULL(w);
+  if (w->packed != 0 && w->packed != 1)
+    return fail(MOE_ERR_INVALID_ARG, "moe_weights.packed must be 0 or 1");
+  if (w->packed && c->weight_dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "the packed weight layout is for bf16 weights");
   if (need_gate) {
     NONNULL(w->gate_w);
     NONNULL(w->bias);
@@ -359,6 +372,41 @@ moe_status moe_quantize_act(const moe_config* cfg, int64_t rows, const void* x, 
   HIPCALL(moe::launch_quant_rows((const uint16_t*)x, rows, cfg->hidden_size, xq, xs,
                                  (hipStream_t)stream),
           "quantise");
+  return MOE_OK;
+}
+
+size_t moe_packed_bytes(const moe_config* cfg, moe_weight_id which) {
+  if (check_cfg(cfg) != MOE_OK || cfg->weight_dtype != MOE_BF16) return 0;
+  const int H = cfg->hidden_size, I = cfg->moe_intermediate_size,
+            Is = cfg->shared_intermediate_size, E = cfg->n_routed_experts;
+  switch (which) {
+    case MOE_W13: return moe::packed_bytes(true, E, I, H);
+    case MOE_W2: return moe::packed_bytes(false, E, H, I);
+    case MOE_WS13: return Is ? moe::packed_bytes(true, 1, Is, H) : 0;
+    case MOE_WS2: return Is ? moe::packed_bytes(false, 1, H, Is) : 0;
+  }
+  return 0;
+}
+
+moe_status moe_pack_weight(const moe_config* cfg, moe_weight_id which, const void* src,
+                           void* dst, void* stream) {
+  CHECK(check_cfg(cfg));
+  if (cfg->weight_dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "the packed weight layout is for bf16 weights");
+  if (which < MOE_W13 || which > MOE_WS2) return fail(MOE_ERR_INVALID_ARG, "unknown weight id");
+  const int H = cfg->hidden_size, I = cfg->moe_intermediate_size,
+            Is = cfg->shared_intermediate_size, E = cfg->n_routed_experts;
+  if ((which == MOE_WS13 || which == MOE_WS2) && Is == 0)
+    return fail(MOE_ERR_INVALID_ARG, "no shared expert (shared_intermediate_size == 0)");
+  NONNULL(src);
+  NONNULL(dst);
+  const bool gate_up = which == MOE_W13 || which == MOE_WS13;
+  const int64_t experts = (which == MOE_W13 || which == MOE_W2) ? E : 1;
+  const int inter = (which == MOE_W13 || which == MOE_W2) ? I : Is;
+  const int n = gate_up ? inter : H, kd = gate_up ? H : inter;
+  HIPCALL(moe::launch_pack(gate_up, (const uint16_t*)src, dst, experts, n, kd,
+                           (hipStream_t)stream),
+          "pack weight");
   return MOE_OK;
 }
 

@@ -12,6 +12,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kNumXcd = 8;  // MI355X: 8 XCDs, workgroups dispatched round-robin
@@ -35,6 +36,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
   return __builtin_bit_cast(bf16x8, v);
+}
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// 16-byte streaming load (non-temporal: data read once, not kept in cache).
+__device__ __forceinline__ u32x4 load_stream16(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
 // Map a linear workgroup id onto a work index so that each XCD receives one
@@ -90,6 +99,14 @@ hipError_t launch_ffn_bf16(const FfnDims& d, const uint16_t* x, const int32_t* p
                            const int32_t* offsets, const uint16_t* w13, const uint16_t* w2,
                            const uint16_t* ws13, const uint16_t* ws2, uint16_t* h,
                            int32_t* tiles, uint16_t* y, uint16_t* ys, hipStream_t s);
+// Packed weight layout (ffn_bf16_packed.hip).
+size_t packed_bytes(bool gate_up, int64_t experts, int n, int kd);
+hipError_t launch_pack(bool gate_up, const uint16_t* src, void* dst, int64_t experts, int n,
+                       int kd, hipStream_t s);
+hipError_t launch_ffn_bf16_packed(const FfnDims& d, const uint16_t* x, const int32_t* perm,
+                                  const int32_t* offsets, const void* w13p, const void* w2p,
+                                  const void* ws13p, const void* ws2p, uint16_t* h,
+                                  int32_t* tiles, uint16_t* y, uint16_t* ys, hipStream_t s);
 hipError_t launch_ffn_f32(const FfnDims& d, const float* x, const int32_t* perm,
                           const int32_t* offsets, const float* w13, const float* w2,
                           const float* ws13, const float* ws2, float* h, float* y, float* ys,

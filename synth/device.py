@@ -30,7 +30,26 @@ def weights_struct(dev: dict):
     return moe.weights(gate_w=dev.get("gate_w"), bias=dev.get("bias"), w13=dev.get("w13"),
                        w13_scale=dev.get("w13_s"), w2=dev.get("w2"), w2_scale=dev.get("w2_s"),
                        ws13=dev.get("ws13"), ws13_scale=dev.get("ws13_s"), ws2=dev.get("ws2"),
-                       ws2_scale=dev.get("ws2_s"))
+                       ws2_scale=dev.get("ws2_s"), packed=dev.get("packed", False))
+
+
+def packed_copy(dev: dict, device="cuda") -> dict:
+    """Same inputs with the bf16 expert weights in the library's packed
+    streaming layout (moe_pack_weight)."""
+    import torch
+    import sparse_mixture_experts_30_amd as moe
+    cfg = dev["cfg"]
+    C = moe_config(cfg)
+    out = dict(dev)
+    for key, which in (("w13", moe.MOE_W13), ("w2", moe.MOE_W2), ("ws13", moe.MOE_WS13),
+                       ("ws2", moe.MOE_WS2)):
+        if dev.get(key) is None:
+            continue
+        buf = torch.empty(moe.moe_packed_bytes(C, which), dtype=torch.uint8, device=device)
+        moe.moe_pack_weight(C, which, dev[key], buf)
+        out[key] = buf
+    out["packed"] = True
+    return out
 
 
 def moe_config(cfg):

@@ -70,10 +70,13 @@ def check_routing(cfg, x_host, gate_w, bias, lg_gpu, idx_gpu, w_gpu, label=""):
     exact = np.array_equal(idx_c, idx_gpu)
     werr = float(np.abs(w_gpu - w_c).max())
     idx_o, _, margin = oracle.route_f64(cfg, lg_ref, bias)
-    differ = np.any(idx_o != idx_gpu, axis=1)
+    # The chosen set is what the layer uses; slot order between two chosen
+    # experts with near-equal scores may differ between fp32 and fp64.
+    differ = np.any(np.sort(idx_o, 1) != np.sort(idx_gpu, 1), axis=1)
+    order_only = int(np.sum(np.any(idx_o != idx_gpu, axis=1) & ~differ))
     log(f"[routing {label}] logits relL2={r:.3e} idx exact={exact} w maxerr={werr:.3e} "
-        f"independent differ={int(differ.sum())}/{len(differ)} "
-        f"max margin of differing={float(margin[differ].max()) if differ.any() else 0:.2e}")
+        f"independent set differs={int(differ.sum())}/{len(differ)} (slot order only: "
+        f"{order_only}) max margin of differing={float(margin[differ].max()) if differ.any() else 0:.2e}")
     assert r <= 1e-5, r
     assert exact, np.argwhere(idx_c != idx_gpu)[:5]
     assert werr <= 1e-6 * cfg.rho, werr
@@ -90,7 +93,7 @@ def layer_reference(cfg, inp, idx_gpu_tok, tokens, quant_act=False):
     x_sub = inp["x"][tokens]
     lg = oracle.logits(x_sub, cfg.act, inp["gate_w"])
     idx_o, w_o, margin = oracle.route_f64(cfg, lg, inp["bias"])
-    differ = np.any(idx_o != idx_gpu_tok, axis=1)
+    differ = np.any(np.sort(idx_o, 1) != np.sort(idx_gpu_tok, 1), axis=1)
     assert np.all(margin[differ] < 1e-5), margin[differ]
     idx_ref = np.where(differ[:, None], idx_gpu_tok, idx_o).astype(np.int32)
     s = 1.0 / (1.0 + np.exp(-lg))

@@ -30,8 +30,11 @@ K1_NOSHARED = synth.C3.replace(name="bf16-T7-K1-noshared", T=7, H=512, E=16, G=4
 SMALL_FP8 = synth.C5.replace(name="fp8-T200-H1024-E32", T=200, H=1024, E=32, G=4, TG=2, K=4,
                              I=256, Is=384, rho=2.5)
 TINY_T1 = SMALL_BF16.replace(name="bf16-T1", T=1)
+# 32 < T <= 64: decode path with two 32-row blocks per group
+DECODE48 = synth.C3.replace(name="bf16-T48-H512-E16", T=48, H=512, E=16, G=4, TG=2, K=4, I=256,
+                            Is=128, rho=2.5)
 
-LAYER_CASES = [C1, SMALL_BF16, RAGGED_BF16, TALL_BF16, K1_NOSHARED, TINY_T1, SMALL_FP8]
+LAYER_CASES = [C1, SMALL_BF16, RAGGED_BF16, TALL_BF16, K1_NOSHARED, TINY_T1, DECODE48, SMALL_FP8]
 
 
 def _tol(cfg):
@@ -100,13 +103,24 @@ def test_permute_flags_out_of_range_index():
     assert status == moe.MOE_OK
 
 
-@pytest.mark.parametrize("cfg", [C1, SMALL_BF16, RAGGED_BF16, TALL_BF16, K1_NOSHARED, SMALL_FP8],
-                         ids=lambda c: c.name)
-def test_expert_ffn(cfg):
+FFN_CASES = [(C1, False), (SMALL_BF16, False), (RAGGED_BF16, False), (TALL_BF16, False),
+             (K1_NOSHARED, False), (SMALL_FP8, False), (SMALL_BF16, True), (RAGGED_BF16, True),
+             (TALL_BF16, True), (K1_NOSHARED, True), (DECODE48, True), (DECODE48, False)]
+
+
+def _case_id(c):
+    return c[0].name + ("-packed" if c[1] else "")
+
+
+@pytest.mark.parametrize("case", FFN_CASES, ids=_case_id)
+def test_expert_ffn(case):
     """y (expert-sorted rows) and y_shared against the oracle's per-row FFN,
     on an oracle-made routing and permutation."""
-    log(f"ffn {cfg.name}")
+    cfg, packed = case
+    log(f"ffn {cfg.name} packed={packed}")
     inp, dev = inputs(cfg)
+    if packed:
+        dev = sd.packed_copy(dev)
     T, K, H = cfg.T, cfg.K, cfg.H
     lg = oracle.logits(inp["x"], cfg.act, inp["gate_w"])
     idx, _, _ = oracle.route_f64(cfg, lg, inp["bias"])
@@ -162,10 +176,17 @@ def test_combine(act):
         assert r <= (4e-3 if act == "bf16" else 1e-6)
 
 
-@pytest.mark.parametrize("cfg", LAYER_CASES, ids=lambda c: c.name)
-def test_forward(cfg):
-    log(f"forward {cfg.name}")
+FORWARD_CASES = [(c, False) for c in LAYER_CASES] + [(c, True) for c in LAYER_CASES
+                                                     if c.wdtype == "bf16"]
+
+
+@pytest.mark.parametrize("case", FORWARD_CASES, ids=_case_id)
+def test_forward(case):
+    cfg, packed = case
+    log(f"forward {cfg.name} packed={packed}")
     inp, dev = inputs(cfg)
+    if packed:
+        dev = sd.packed_copy(dev)
     r = run_forward(cfg, dev, cfg.T)
     check_routing(cfg, inp["x"], inp["gate_w"], inp["bias"], r["logits"], r["idx"], r["w"],
                   cfg.name)
@@ -213,3 +234,39 @@ def test_forward_zero_tokens_is_noop():
     moe.moe_forward(sd.moe_config(cfg), 0, dev["x"], sd.weights_struct(dev), out, None)
     sync()
     assert torch.count_nonzero(out).item() == 0
+
+
+def test_pack_layout():
+    """moe_pack_weight against the layout stated in include/moe.h, written
+    out here with numpy: per (expert, tile, 64-k step) a block of
+    [wave 4][col block 2][k slice 4][lane 64][8 values]."""
+    cfg = RAGGED_BF16          # I = 192: a partial GEMM1 tile (zero padding)
+    inp, dev = inputs(cfg)
+    C = sd.moe_config(cfg)
+    E, H, I = cfg.E, cfg.H, cfg.I
+    w13 = synth.bf16_to_f32(inp["w13"]).view(np.uint32) >> 16
+    w2 = synth.bf16_to_f32(inp["w2"]).view(np.uint32) >> 16
+    for key, which, src, gate_up, n, kd in (("w13", moe.MOE_W13, w13, True, I, H),
+                                            ("w2", moe.MOE_W2, w2, False, H, I)):
+        buf = torch.empty(moe.moe_packed_bytes(C, which), dtype=torch.uint8, device=DEV)
+        moe.moe_pack_weight(C, which, dev[key], buf)
+        got = host(buf).view(np.uint16).reshape(-1, 8)
+        nt = -(-n // (128 if gate_up else 256))
+        steps = kd // 64
+        c = np.arange(got.shape[0])
+        l, kk, cb, w = c & 63, (c >> 6) & 3, (c >> 8) & 1, (c >> 9) & 3
+        rest = c >> 11
+        ks, tile, e = rest % steps, (rest // steps) % nt, rest // (steps * nt)
+        if gate_up:
+            col = tile * 128 + 32 * w + (l & 31)
+            ok = col < n
+            row = np.where(cb == 1, n + col, col)
+        else:
+            row = tile * 256 + 64 * w + 32 * cb + (l & 31)
+            ok = row < n
+        k0 = ks * 64 + 32 * (l >> 5) + 8 * kk
+        ref = np.zeros_like(got)
+        idx = np.nonzero(ok)[0]
+        for j in range(8):
+            ref[idx, j] = src[e[idx], row[idx], k0[idx] + j]
+        np.testing.assert_array_equal(got, ref)
