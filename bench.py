@@ -1,9 +1,12 @@
 """Benchmark: one MoE layer forward (gate, permute, expert FFNs, combine) per
 step on one MI355X, V3 shape (H=7168, 256 routed experts in 8 groups, top-4
 groups, top-8, expert and shared FFN width 2048, routed scaling 2.5), bf16,
-T=4096 tokens of synthetic seeded input resident in HBM.
+T=4096 tokens of synthetic seeded input resident in HBM.  bf16 expert weights
+are packed once into the streaming layout (moe_pack_weight) before timing,
+as a model load would.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--cpu-sample S]
+    python bench.py --copy-calibration     (a 1 GiB device copy, for counters)
 
 Prints one JSON line.  The per-phase times (HIP events on the stream the
 kernels run on) give the roofline of the dominant phase, the grouped expert
@@ -30,17 +33,100 @@ def log(msg):
     sys.stderr.flush()
 
 
+KERNEL_SOURCES = {
+    # kernel name (as the library's timer and rocprofv3 name it) -> sources it is built from
+    "grouped_gemm_bf16_packed": ("ffn_bf16_packed.hip", "moe_internal.hpp"),
+    "grouped_gemm_bf16": ("ffn_bf16.hip", "moe_internal.hpp"),
+    "grouped_gemm_fp8": ("ffn_fp8.hip", "moe_internal.hpp"),
+    "gate_logits_bf16_kernel": ("gate.hip", "moe_internal.hpp"),
+}
+
+
+def kernel_source_digest(kernel):
+    """sha256 over the sources a kernel is compiled from (None if unknown)."""
+    import hashlib
+    base = kernel.split("<")[0]
+    files = KERNEL_SOURCES.get(base)
+    if not files:
+        return None
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(HERE, "sparse_mixture_experts_30_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def _traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` on `workload`, from the committed
+    counter record (FETCH_SIZE + WRITE_SIZE, calibrated), or None when there is
+    no record or the kernel source changed since it was taken."""
+    path = os.path.join(HERE, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except OSError:
+        return None
+    entry = rec.get(f"{workload}:{kernel}")
+    if not entry or entry.get("kernel_source_sha256") != kernel_source_digest(kernel):
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def kernel_work(kernel, cfg, active):
+    """Algorithmic (bytes, flop) of one launch of `kernel` on cfg, counting the
+    active experts' weights once, each activation row once and each result
+    once; None for kernels without a model here."""
+    T, H, E, K, I, Is = cfg.T, cfg.H, cfg.E, cfg.K, cfg.I, cfg.Is
+    N = T * K
+    wb = {"fp8": 1, "bf16": 2, "f32": 4}[cfg.wdtype]
+    ab = 2 if cfg.act == "bf16" else 4
+    hb = 1 if cfg.wdtype == "fp8" else ab       # h is kept in e4m3 on the fp8 path
+    scale = (lambda r, c: (r // 128) * (c // 128) * 4) if cfg.wdtype == "fp8" else (lambda r, c: 0)
+    hsc = ((N * I + T * Is) // 128) * 4 if cfg.wdtype == "fp8" else 0
+    base = kernel.split("<")[0]
+    gate_up = "<true" in kernel
+    if base.startswith("grouped_gemm"):
+        if gate_up:
+            w = active * (2 * I * H * wb + scale(2 * I, H)) + (2 * Is * H * wb + scale(2 * Is, H))
+            a_in = T * H * (1 if cfg.wdtype == "fp8" else ab) + (T * (H // 128) * 4 if cfg.wdtype == "fp8" else 0)
+            out = (N * I + T * Is) * hb + hsc
+            flop = 2.0 * (N * 2 * I + T * 2 * Is) * H
+        else:
+            w = active * (H * I * wb + scale(H, I)) + (H * Is * wb + scale(H, Is))
+            a_in = (N * I + T * Is) * hb + hsc
+            out = (N + T) * H * ab
+            flop = 2.0 * (N * I + T * Is) * H
+        return w + a_in + out, flop
+    if base == "gate_logits_bf16_kernel":
+        return T * H * ab + E * H * 4 + T * E * 4, 2.0 * T * E * H
+    return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="v3-layer-bf16-T4096")
-    ap.add_argument("--cpu-sample", type=int, default=96,
+    ap.add_argument("--cpu-sample", type=int, default=384,
                     help="tokens of the workload run through the fp64 oracle (0 = skip)")
     ap.add_argument("--profile-only", action="store_true",
                     help="just run warmup + steps (for rocprofv3), print the JSON line")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="copy 1 GiB device-to-device 5 times (HBM counter calibration)")
+    ap.add_argument("--row-major", action="store_true",
+                    help="use the row-major weight layout instead of the packed one")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        a.fill_(1)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": 1 << 30, "copies": 5}))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
@@ -62,6 +148,8 @@ def main():
     inp = synth.gen_inputs(cfg)
     log(f"[bench] generated in {time.time() - t0:.1f}s; uploading")
     d = sd.to_device(inp)
+    if cfg.wdtype == "bf16" and not args.row_major:
+        d = sd.packed_copy(d)   # the row-major device copies are released here
     W = sd.weights_struct(d)
     C = sd.moe_config(cfg)
     ws = sd.workspace(cfg, T)
@@ -77,6 +165,23 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+
+    # Per-kernel breakdown (every launch bracketed by HIP events on its
+    # stream), to find the dominant kernel; not part of the timed region.
+    moe.moe_kernel_timer_read()
+    moe.moe_kernel_timer_enable(True)
+    nbreak = max(3, min(args.steps, 10))
+    for _ in range(nbreak):
+        step()
+    torch.cuda.synchronize()
+    moe.moe_kernel_timer_enable(False)
+    kt = moe.moe_kernel_timer_read()
+    kernels_ms = {k: v[0] / v[1] for k, v in kt.items()}
+    dominant = max(kt, key=lambda k: kt[k][0])
+
+    # Timed region: K steps between a synchronisation on both sides.  Only
+    # the dominant kernel is bracketed by events here.
+    moe.moe_kernel_timer_enable(True, dominant)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     ev0.record(stream)
@@ -84,8 +189,11 @@ def main():
         step()
     ev1.record(stream)
     torch.cuda.synchronize()
+    moe.moe_kernel_timer_enable(False)
+    dom_ms, dom_launches = moe.moe_kernel_timer_read()[dominant]
+    dom_ms /= dom_launches
     ms = ev0.elapsed_time(ev1) / args.steps
-    log(f"[bench] {ms:.3f} ms/step")
+    log(f"[bench] {ms:.3f} ms/step; dominant kernel {dominant}: {dom_ms:.3f} ms/launch")
 
     # Per-phase timing with the separate entry points (same kernels, same
     # stream), HIP events between phases.
@@ -134,6 +242,25 @@ def main():
     mfma_peak = FP8_PEAK_TFLOPS if cfg.wdtype == "fp8" else BF16_PEAK_TFLOPS
     tok_s = T / (ms * 1e-3)
 
+    work = kernel_work(dominant, cfg, active)
+    if work is None:
+        roof = {"kernel": dominant, "bound": None, "achieved": None, "peak": None, "unit": None,
+                "frac": None, "traffic": None, "avg_launch_ms": round(dom_ms, 4)}
+    else:
+        kbytes, kflop = work
+        ridge = mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)
+        if kflop / kbytes > ridge:
+            ach, peak, unit, bound = kflop / (dom_ms * 1e-3) / 1e12, mfma_peak, "TFLOP/s", "mfma"
+        else:
+            ach, peak, unit, bound = kbytes / (dom_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s", "hbm"
+        roof = {"kernel": dominant, "bound": bound, "achieved": round(ach, 1), "peak": peak,
+                "unit": unit, "frac": round(ach / peak, 4),
+                "traffic": _traffic(cfg.name, dominant),
+                "avg_launch_ms": round(dom_ms, 4), "launches_timed": dom_launches,
+                "algorithmic_bytes_per_launch": kbytes, "algorithmic_flop_per_launch": kflop,
+                "hbm_gbs": round(kbytes / (dom_ms * 1e-3) / 1e9, 1),
+                "mfma_tflops": round(kflop / (dom_ms * 1e-3) / 1e12, 1)}
+
     result = {
         "metric": "MoE layer tokens/s + % bf16 MFMA peak (prefill), % HBM peak (decode)",
         "value": round(tok_s, 1),
@@ -146,7 +273,9 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": {"bf16": "bf16", "fp8": "fp8-e4m3", "f32": "f32"}[cfg.wdtype],
-        "data": "synthetic: seeded N(0,1) tokens, N(0,1/fan_in) weights, U(-0.05,0.05) bias",
+        "data": "synthetic: seeded N(0,1) tokens, N(0,1/fan_in) weights, gate N(0,1/H), bias "
+                + (f"from {cfg.bias_file} (Zipf(1.2) expert loads)" if cfg.bias_file
+                   else f"U({cfg.bias_lo},{cfg.bias_hi})"),
         "config": {"workload": cfg.name, "T": T, "hidden": H, "n_routed_experts": E,
                    "n_group": cfg.G, "topk_group": cfg.TG, "top_k": K, "moe_inter": I,
                    "shared_inter": Is, "routed_scaling_factor": cfg.rho,
@@ -158,18 +287,12 @@ def main():
                   "algorithmic_bytes": layer_bytes, "algorithmic_flop": flop,
                   "active_experts": active},
         "phases_ms": {p: round(v, 4) for p, v in acc.items()},
-        "roofline": {
-            "kernel": "expert_ffn (grouped GEMM1 gate/up+SiLU and GEMM2, routed + shared)",
-            "bound": "hbm",
-            "achieved": round(ffn_gbs, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(ffn_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "algorithmic_bytes_per_launch": ffn_bytes,
-            "mfma_tflops": round(ffn_tflops, 1),
-            "mfma_frac": round(ffn_tflops / mfma_peak, 4),
-        },
+        "kernels_ms": {k: round(v, 4) for k, v in sorted(kernels_ms.items())},
+        "expert_ffn": {"ms": round(ffn_ms, 4), "hbm_gbs": round(ffn_gbs, 1),
+                       "tflops": round(ffn_tflops, 1),
+                       "hbm_frac": round(ffn_gbs / HBM_PEAK_GBS, 4),
+                       "mfma_frac": round(ffn_tflops / mfma_peak, 4)},
+        "roofline": roof,
     }
 
     if args.cpu_sample > 0 and not args.profile_only:

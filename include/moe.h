@@ -35,8 +35,9 @@
  *   - Layouts are row-major.  Weight matrices are stored "output rows x
  *     input columns" with the input dimension contiguous.
  *   - T == 0 is a no-op returning MOE_OK.
- *   - The library holds no mutable global state; calls on different streams
- *     with different workspaces may run concurrently.
+ *   - Apart from the kernel timer below (off by default) the library holds no
+ *     mutable global state; calls on different streams with different
+ *     workspaces may run concurrently.
  *   - Results are deterministic: no floating-point atomics anywhere, so two
  *     runs on the same inputs give bitwise-identical outputs.
  */
@@ -204,6 +205,21 @@ moe_status moe_pack_weight(const moe_config* cfg, moe_weight_id which, const voi
  * if the last permutation on this workspace saw an expert index outside
  * [0, E), or MOE_ERR_HIP. */
 moe_status moe_get_device_error(void* ws, size_t ws_bytes, void* stream);
+
+/* Kernel timer, for measurement.  While enabled, every kernel launch of the
+ * library is bracketed by two HIP events recorded on the stream the kernel
+ * runs on; `only` (NULL = all) restricts this to the kernels of that name
+ * (names are those listed by moe_kernel_timer_read, e.g.
+ * "grouped_gemm_bf16_packed<true>").  Enabling or disabling keeps what was
+ * recorded so far.  The timer is process-wide and its calls are serialised
+ * by a lock. */
+moe_status moe_kernel_timer_enable(int on, const char* only);
+
+/* Waits for every recorded event pair, sums durations per kernel name and
+ * clears the record.  Returns the number n of distinct names; fills
+ * names[i] (valid until the next read), total_ms[i] (summed event time) and
+ * launches[i] for i < min(n, cap).  Any output pointer may be NULL. */
+int moe_kernel_timer_read(int cap, const char** names, double* total_ms, int64_t* launches);
 
 /* Static text for a status code. */
 const char* moe_strerror(moe_status s);

@@ -7,7 +7,8 @@ from ._lib import (EXPORTS, MOE_BF16, MOE_ERR_DEVICE_CHECK, MOE_ERR_HIP, MOE_ERR
                    MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_F32, MOE_FP8_E4M3, MOE_OK,
                    MOE_W13, MOE_W2, MOE_WS13, MOE_WS2, moe_pack_weight, moe_packed_bytes,
                    MoeConfig, MoeError, MoeWeights, SO_PATH, config, lib, moe_combine,
-                   moe_expert_ffn, moe_forward, moe_gate, moe_get_device_error, moe_last_error,
+                   moe_expert_ffn, moe_forward, moe_gate, moe_get_device_error,
+                   moe_kernel_timer_enable, moe_kernel_timer_read, moe_last_error,
                    moe_permute, moe_quantize_act, moe_strerror, moe_workspace_bytes, weights)
 
 __all__ = [n for n in dir() if not n.startswith("_")]

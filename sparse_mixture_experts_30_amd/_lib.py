@@ -17,7 +17,8 @@ MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 # Every function declared in include/moe.h.
 EXPORTS = ("moe_workspace_bytes", "moe_gate", "moe_permute", "moe_expert_ffn", "moe_combine",
            "moe_forward", "moe_quantize_act", "moe_packed_bytes", "moe_pack_weight",
-           "moe_get_device_error", "moe_strerror", "moe_last_error")
+           "moe_get_device_error", "moe_strerror", "moe_last_error", "moe_kernel_timer_enable",
+           "moe_kernel_timer_read")
 MOE_W13, MOE_W2, MOE_WS13, MOE_WS2 = 0, 1, 2, 3
 
 
@@ -69,6 +70,11 @@ def lib():
             "moe_get_device_error": (ctypes.c_int, [vp, sz, vp]),
             "moe_strerror": (ctypes.c_char_p, [ctypes.c_int]),
             "moe_last_error": (ctypes.c_char_p, []),
+            "moe_kernel_timer_enable": (ctypes.c_int, [ctypes.c_int, ctypes.c_char_p]),
+            "moe_kernel_timer_read": (ctypes.c_int, [ctypes.c_int,
+                                                     ctypes.POINTER(ctypes.c_char_p),
+                                                     ctypes.POINTER(ctypes.c_double),
+                                                     ctypes.POINTER(ctypes.c_int64)]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -166,6 +172,21 @@ def moe_pack_weight(cfg, which, src, dst, stream=None):
 def moe_get_device_error(ws, stream=None) -> int:
     """Returns the status (MOE_OK or MOE_ERR_DEVICE_CHECK) instead of raising."""
     return lib().moe_get_device_error(_ptr(ws), _nbytes(ws), _stream(stream))
+
+
+def moe_kernel_timer_enable(on: bool, only: Optional[str] = None) -> None:
+    _check(lib().moe_kernel_timer_enable(1 if on else 0, only.encode() if only else None))
+
+
+def moe_kernel_timer_read() -> dict:
+    """{kernel name: (summed ms, launches)} since the last read."""
+    L = lib()
+    cap = 64
+    names = (ctypes.c_char_p * cap)()
+    ms = (ctypes.c_double * cap)()
+    cnt = (ctypes.c_int64 * cap)()
+    n = L.moe_kernel_timer_read(cap, names, ms, cnt)
+    return {names[i].decode(): (ms[i], int(cnt[i])) for i in range(min(n, cap))}
 
 
 def moe_strerror(status: int) -> str:

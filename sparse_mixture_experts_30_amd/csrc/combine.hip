@@ -77,11 +77,13 @@ combine_f32_kernel(const float* __restrict__ y, const float* __restrict__ ys,
 hipError_t launch_combine(const void* y, const void* ys, const int32_t* pos, const float* w,
                           void* out, int64_t T, int H, int K, bool bf16, hipStream_t s) {
   if (bf16)
-    hipLaunchKernelGGL(combine_bf16_kernel, dim3((unsigned)T), dim3(CT), 0, s,
-                       (const uint16_t*)y, (const uint16_t*)ys, pos, w, (uint16_t*)out, H, K);
+    MOE_TIMED_LAUNCH(s, "combine_bf16_kernel",
+      hipLaunchKernelGGL(combine_bf16_kernel, dim3((unsigned)T), dim3(CT), 0, s,
+                         (const uint16_t*)y, (const uint16_t*)ys, pos, w, (uint16_t*)out, H, K));
   else
-    hipLaunchKernelGGL(combine_f32_kernel, dim3((unsigned)T), dim3(CT), 0, s, (const float*)y,
-                       (const float*)ys, pos, w, (float*)out, H, K);
+    MOE_TIMED_LAUNCH(s, "combine_f32_kernel",
+      hipLaunchKernelGGL(combine_f32_kernel, dim3((unsigned)T), dim3(CT), 0, s, (const float*)y,
+                         (const float*)ys, pos, w, (float*)out, H, K));
   return hipGetLastError();
 }
 

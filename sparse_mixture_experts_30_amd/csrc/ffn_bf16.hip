@@ -280,7 +280,8 @@ hipError_t launch_ffn_bf16(const FfnDims& d, const uint16_t* x, const int32_t* p
   a1.c_s = hs;
   a1.ldc_r = d.I;
   a1.ldc_s = d.Is;
-  hipLaunchKernelGGL(grouped_gemm_bf16<true>, dim3(grid_for(mt * a1.ntn)), dim3(NT), kLds, s, a1);
+  MOE_TIMED_LAUNCH(s, "grouped_gemm_bf16<true>",
+    hipLaunchKernelGGL(grouped_gemm_bf16<true>, dim3(grid_for(mt * a1.ntn)), dim3(NT), kLds, s, a1));
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -303,7 +304,8 @@ hipError_t launch_ffn_bf16(const FfnDims& d, const uint16_t* x, const int32_t* p
   a2.c_r = y;
   a2.c_s = ys;
   a2.ldc_r = a2.ldc_s = d.H;
-  hipLaunchKernelGGL(grouped_gemm_bf16<false>, dim3(grid_for(mt * a2.ntn)), dim3(NT), kLds, s, a2);
+  MOE_TIMED_LAUNCH(s, "grouped_gemm_bf16<false>",
+    hipLaunchKernelGGL(grouped_gemm_bf16<false>, dim3(grid_for(mt * a2.ntn)), dim3(NT), kLds, s, a2));
   return hipGetLastError();
 }
 

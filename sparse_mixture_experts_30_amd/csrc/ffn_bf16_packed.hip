@@ -383,11 +383,13 @@ hipError_t launch_pack(bool gate_up, const uint16_t* src, void* dst, int64_t exp
   const int64_t nfrag = experts * nt * steps * FRAG;
   const unsigned blocks = (unsigned)((nfrag + 255) / 256);
   if (gate_up)
-    hipLaunchKernelGGL(pack_kernel<true>, dim3(blocks), dim3(256), 0, s, src, (u32x4*)dst, nfrag,
-                       n, kd, 2 * n, nt, steps);
+    MOE_TIMED_LAUNCH(s, "pack_kernel<true>",
+      hipLaunchKernelGGL(pack_kernel<true>, dim3(blocks), dim3(256), 0, s, src, (u32x4*)dst, nfrag,
+                         n, kd, 2 * n, nt, steps));
   else
-    hipLaunchKernelGGL(pack_kernel<false>, dim3(blocks), dim3(256), 0, s, src, (u32x4*)dst,
-                       nfrag, n, kd, n, nt, steps);
+    MOE_TIMED_LAUNCH(s, "pack_kernel<false>",
+      hipLaunchKernelGGL(pack_kernel<false>, dim3(blocks), dim3(256), 0, s, src, (u32x4*)dst,
+                         nfrag, n, kd, n, nt, steps));
   return hipGetLastError();
 }
 
@@ -427,14 +429,17 @@ hipError_t launch_ffn_bf16_packed(const FfnDims& d, const uint16_t* x, const int
   // Every group has at most T rows (a token picks an expert at most once).
   const int few = d.T <= 32 ? 1 : d.T <= 64 ? 2 : 0;
   if (few == 1)
-    hipLaunchKernelGGL((grouped_gemm_bf16_packed_few<true, 1>), dim3(grid(mt * a1.ntn)), dim3(NT),
-                       0, s, a1);
+    MOE_TIMED_LAUNCH(s, "grouped_gemm_bf16_packed_few<true, 1>",
+      hipLaunchKernelGGL((grouped_gemm_bf16_packed_few<true, 1>), dim3(grid(mt * a1.ntn)), dim3(NT),
+                         0, s, a1));
   else if (few == 2)
-    hipLaunchKernelGGL((grouped_gemm_bf16_packed_few<true, 2>), dim3(grid(mt * a1.ntn)), dim3(NT),
-                       0, s, a1);
+    MOE_TIMED_LAUNCH(s, "grouped_gemm_bf16_packed_few<true, 2>",
+      hipLaunchKernelGGL((grouped_gemm_bf16_packed_few<true, 2>), dim3(grid(mt * a1.ntn)), dim3(NT),
+                         0, s, a1));
   else
-    hipLaunchKernelGGL(grouped_gemm_bf16_packed<true>, dim3(grid(mt * a1.ntn)), dim3(NT), kLdsP, s,
-                       a1);
+    MOE_TIMED_LAUNCH(s, "grouped_gemm_bf16_packed<true>",
+      hipLaunchKernelGGL(grouped_gemm_bf16_packed<true>, dim3(grid(mt * a1.ntn)), dim3(NT), kLdsP, s,
+                         a1));
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -458,14 +463,17 @@ hipError_t launch_ffn_bf16_packed(const FfnDims& d, const uint16_t* x, const int
   a2.c_s = ys;
   a2.ldc_r = a2.ldc_s = d.H;
   if (few == 1)
-    hipLaunchKernelGGL((grouped_gemm_bf16_packed_few<false, 1>), dim3(grid(mt * a2.ntn)),
-                       dim3(NT), 0, s, a2);
+    MOE_TIMED_LAUNCH(s, "grouped_gemm_bf16_packed_few<false, 1>",
+      hipLaunchKernelGGL((grouped_gemm_bf16_packed_few<false, 1>), dim3(grid(mt * a2.ntn)),
+                         dim3(NT), 0, s, a2));
   else if (few == 2)
-    hipLaunchKernelGGL((grouped_gemm_bf16_packed_few<false, 2>), dim3(grid(mt * a2.ntn)),
-                       dim3(NT), 0, s, a2);
+    MOE_TIMED_LAUNCH(s, "grouped_gemm_bf16_packed_few<false, 2>",
+      hipLaunchKernelGGL((grouped_gemm_bf16_packed_few<false, 2>), dim3(grid(mt * a2.ntn)),
+                         dim3(NT), 0, s, a2));
   else
-    hipLaunchKernelGGL(grouped_gemm_bf16_packed<false>, dim3(grid(mt * a2.ntn)), dim3(NT), kLdsP,
-                       s, a2);
+    MOE_TIMED_LAUNCH(s, "grouped_gemm_bf16_packed<false>",
+      hipLaunchKernelGGL(grouped_gemm_bf16_packed<false>, dim3(grid(mt * a2.ntn)), dim3(NT), kLdsP,
+                         s, a2));
   return hipGetLastError();
 }
 

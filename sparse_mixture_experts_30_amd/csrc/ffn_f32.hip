@@ -92,12 +92,14 @@ hipError_t launch_ffn_f32(const FfnDims& d, const float* x, const int32_t* perm,
   const int64_t rows = d.N + (d.Is > 0 ? d.T : 0);
   if (rows > 0x7fffffff) return hipErrorInvalidValue;
   const int imax = d.I > d.Is ? d.I : d.Is;
-  hipLaunchKernelGGL(ffn1_f32_kernel, dim3((unsigned)rows, (imax + 127) / 128), dim3(128), 0, s,
-                     x, perm, offsets, w13, ws13, h, d.T, d.N, d.H, d.I, d.Is, d.E, d.K);
+  MOE_TIMED_LAUNCH(s, "ffn1_f32_kernel",
+    hipLaunchKernelGGL(ffn1_f32_kernel, dim3((unsigned)rows, (imax + 127) / 128), dim3(128), 0, s,
+                       x, perm, offsets, w13, ws13, h, d.T, d.N, d.H, d.I, d.Is, d.E, d.K));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(ffn2_f32_kernel, dim3((unsigned)rows, (d.H + 127) / 128), dim3(128), 0, s,
-                     h, offsets, w2, ws2, y, ys, d.T, d.N, d.H, d.I, d.Is, d.E);
+  MOE_TIMED_LAUNCH(s, "ffn2_f32_kernel",
+    hipLaunchKernelGGL(ffn2_f32_kernel, dim3((unsigned)rows, (d.H + 127) / 128), dim3(128), 0, s,
+                       h, offsets, w2, ws2, y, ys, d.T, d.N, d.H, d.I, d.Is, d.E));
   return hipGetLastError();
 }
 

@@ -349,8 +349,9 @@ unsigned grid8(int64_t max_work) {
 hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int cols, uint8_t* q, float* sc,
                              hipStream_t s) {
   const int64_t tiles = rows * (cols / 128);
-  hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)((tiles + 15) / 16)), dim3(256), 0, s, x,
-                     rows, cols, q, sc);
+  MOE_TIMED_LAUNCH(s, "quant_rows_kernel",
+    hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)((tiles + 15) / 16)), dim3(256), 0, s, x,
+                       rows, cols, q, sc));
   return hipGetLastError();
 }
 
@@ -391,7 +392,8 @@ hipError_t launch_ffn_fp8(const FfnDims& d, const uint8_t* xq, const float* xs,
   a1.hq_s = hq_s;
   a1.hs_r = hs;
   a1.hs_s = hs_s;
-  hipLaunchKernelGGL(grouped_gemm_fp8<true>, dim3(grid8(mt * a1.ntn)), dim3(NT), kLds8, s, a1);
+  MOE_TIMED_LAUNCH(s, "grouped_gemm_fp8<true>",
+    hipLaunchKernelGGL(grouped_gemm_fp8<true>, dim3(grid8(mt * a1.ntn)), dim3(NT), kLds8, s, a1));
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -416,7 +418,8 @@ hipError_t launch_ffn_fp8(const FfnDims& d, const uint8_t* xq, const float* xs,
   a2.ncol_r = a2.ncol_s = d.H;
   a2.c_r = y;
   a2.c_s = ys;
-  hipLaunchKernelGGL(grouped_gemm_fp8<false>, dim3(grid8(mt * a2.ntn)), dim3(NT), kLds8, s, a2);
+  MOE_TIMED_LAUNCH(s, "grouped_gemm_fp8<false>",
+    hipLaunchKernelGGL(grouped_gemm_fp8<false>, dim3(grid8(mt * a2.ntn)), dim3(NT), kLds8, s, a2));
   return hipGetLastError();
 }
 

@@ -55,8 +55,9 @@ int64_t ffn_max_mtiles(int64_t N, int64_t T, int E, int BM) {
 
 hipError_t launch_build_tiles(const int32_t* offsets, int E, int64_t T, bool has_shared, int BM,
                               int32_t* tiles, hipStream_t s) {
-  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, E, T,
-                     has_shared ? 1 : 0, BM, tiles);
+  MOE_TIMED_LAUNCH(s, "build_tiles_kernel",
+    hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, E, T,
+                       has_shared ? 1 : 0, BM, tiles));
   return hipGetLastError();
 }
 }  // namespace moe

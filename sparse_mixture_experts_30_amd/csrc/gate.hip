@@ -313,12 +313,14 @@ hipError_t launch_gate_logits(const void* x, bool x_bf16, const float* gate_w, f
                               int64_t T, int H, int E, int ksplit, hipStream_t s) {
   if (x_bf16) {
     dim3 grid((unsigned)((T + GBM - 1) / GBM), (E + GBN - 1) / GBN, ksplit);
-    hipLaunchKernelGGL(gate_logits_bf16_kernel, grid, dim3(GTHREADS), 0, s,
-                       (const uint16_t*)x, gate_w, partials, T, H, E, H / ksplit);
+    MOE_TIMED_LAUNCH(s, "gate_logits_bf16_kernel",
+      hipLaunchKernelGGL(gate_logits_bf16_kernel, grid, dim3(GTHREADS), 0, s,
+                         (const uint16_t*)x, gate_w, partials, T, H, E, H / ksplit));
   } else {
     dim3 grid((unsigned)((T + 15) / 16), (E + 15) / 16);
-    hipLaunchKernelGGL(gate_logits_f32_kernel, grid, dim3(256), 0, s, (const float*)x, gate_w,
-                       partials, T, H, E);
+    MOE_TIMED_LAUNCH(s, "gate_logits_f32_kernel",
+      hipLaunchKernelGGL(gate_logits_f32_kernel, grid, dim3(256), 0, s, (const float*)x, gate_w,
+                         partials, T, H, E));
   }
   return hipGetLastError();
 }
@@ -327,8 +329,9 @@ hipError_t launch_select(const float* partials, int ksplit, const float* bias, f
                          int32_t* idx, float* w, int64_t T, int E, int G, int TG, int K,
                          float rho, hipStream_t s) {
   dim3 grid((unsigned)((T + SEL_WAVES - 1) / SEL_WAVES));
-  hipLaunchKernelGGL(select_kernel, grid, dim3(SEL_WAVES * 64), 0, s, partials, ksplit, bias,
-                     logits_out, idx, w, T, E, G, TG, K, rho);
+  MOE_TIMED_LAUNCH(s, "select_kernel",
+    hipLaunchKernelGGL(select_kernel, grid, dim3(SEL_WAVES * 64), 0, s, partials, ksplit, bias,
+                       logits_out, idx, w, T, E, G, TG, K, rho));
   return hipGetLastError();
 }
 

@@ -54,8 +54,29 @@ __device__ __forceinline__ int xcd_contiguous(int b, int nb) {
   return (b % kNumXcd) * per + b / kNumXcd;
 }
 
+// ---------------------------------------------------------------- kernel timer
+// Brackets one kernel launch with HIP events on its stream while the timer
+// (moe_kernel_timer_enable) is on; `name` must be a string literal.
+class KernelTimerScope {
+ public:
+  KernelTimerScope(hipStream_t s, const char* name);
+  ~KernelTimerScope();
+  KernelTimerScope(const KernelTimerScope&) = delete;
+  KernelTimerScope& operator=(const KernelTimerScope&) = delete;
+
+ private:
+  hipStream_t s_;
+  const char* name_;
+  void* begin_ = nullptr;
+};
+
+#define MOE_TIMED_LAUNCH(stream, name, ...)             \
+  do {                                                  \
+    ::moe::KernelTimerScope moe_timer_scope_((stream), (name)); \
+    __VA_ARGS__;                                        \
+  } while (0)
+
 // ---------------------------------------------------------------- host launchers
-struct GroupedGemmArgs;
 
 hipError_t launch_gate_logits(const void* x, bool x_bf16, const float* gate_w, float* partials,
                               int64_t T, int H, int E, int ksplit, hipStream_t s);

@@ -137,10 +137,13 @@ hipError_t launch_permute(const int32_t* idx, int64_t N, int E, int32_t* hist, i
                           int32_t* offsets, int32_t* perm, int32_t* pos, int32_t* err,
                           hipStream_t s) {
   const int nblk = permute_nblk(N);
-  hipLaunchKernelGGL(hist_kernel, dim3(nblk), dim3(PTHREADS), 0, s, idx, N, E, hist);
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(PMAXE), 0, s, hist, nblk, E, counts, offsets, err);
-  hipLaunchKernelGGL(scatter_kernel, dim3(nblk), dim3(PTHREADS), 0, s, idx, N, E,
-                     (const int32_t*)hist, perm, pos);
+  MOE_TIMED_LAUNCH(s, "hist_kernel",
+    hipLaunchKernelGGL(hist_kernel, dim3(nblk), dim3(PTHREADS), 0, s, idx, N, E, hist));
+  MOE_TIMED_LAUNCH(s, "scan_kernel",
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(PMAXE), 0, s, hist, nblk, E, counts, offsets, err));
+  MOE_TIMED_LAUNCH(s, "scatter_kernel",
+    hipLaunchKernelGGL(scatter_kernel, dim3(nblk), dim3(PTHREADS), 0, s, idx, N, E,
+                       (const int32_t*)hist, perm, pos));
   return hipGetLastError();
 }
 

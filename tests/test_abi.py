@@ -116,3 +116,10 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(L, "SO_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(RuntimeError, match="missing"):
         L.lib()
+
+
+def test_kernel_timer_without_launches():
+    # enabling, disabling and reading touch no device when nothing was launched
+    moe.moe_kernel_timer_enable(True, "grouped_gemm_bf16_packed<true>")
+    moe.moe_kernel_timer_enable(False)
+    assert moe.moe_kernel_timer_read() == {}

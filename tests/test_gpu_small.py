@@ -236,6 +236,31 @@ def test_forward_zero_tokens_is_noop():
     assert torch.count_nonzero(out).item() == 0
 
 
+def test_kernel_timer_names_every_launch():
+    cfg = SMALL_BF16
+    inp, dev = inputs(cfg)
+    dev = sd.packed_copy(dev)
+    moe.moe_kernel_timer_read()
+    moe.moe_kernel_timer_enable(True)
+    for _ in range(3):
+        run_forward(cfg, dev, cfg.T)
+    moe.moe_kernel_timer_enable(False)
+    kt = moe.moe_kernel_timer_read()
+    log(f"  {kt}")
+    for name in ("gate_logits_bf16_kernel", "select_kernel", "hist_kernel", "scan_kernel",
+                 "scatter_kernel", "build_tiles_kernel", "grouped_gemm_bf16_packed<true>",
+                 "grouped_gemm_bf16_packed<false>", "combine_bf16_kernel"):
+        assert name in kt, name
+        ms, n = kt[name]
+        assert n == 3 and ms > 0, (name, ms, n)
+    # restricted to one kernel
+    moe.moe_kernel_timer_enable(True, "combine_bf16_kernel")
+    run_forward(cfg, dev, cfg.T)
+    moe.moe_kernel_timer_enable(False)
+    kt = moe.moe_kernel_timer_read()
+    assert list(kt) == ["combine_bf16_kernel"] and kt["combine_bf16_kernel"][1] == 1
+
+
 def test_pack_layout():
     """moe_pack_weight against the layout stated in include/moe.h, written
     out here with numpy: per (expert, tile, 64-k step) a block of
