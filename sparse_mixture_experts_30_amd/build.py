@@ -6,6 +6,7 @@ from __future__ import annotations
 
 import concurrent.futures
 import os
+import re
 import subprocess
 import sys
 
@@ -27,15 +28,47 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
 
 
+RESOURCE_REMARKS = "-Rpass-analysis=kernel-resource-usage"
+
+
+def _scratch_kernels(stderr: str):
+    """(kernel, bytes/lane) for every kernel the compiler gave private
+    scratch memory (register spills or arrays it could not keep in VGPRs)."""
+    out, name = [], None
+    for line in stderr.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and int(m.group(1)) and name:
+            out.append((name, int(m.group(1))))
+    return out
+
+
 def _compile(src: str, build_dir: str = BUILD, extra=()) -> str:
     obj = os.path.join(build_dir, src + ".o")
-    flags = FLAGS + list(extra)
+    flags = FLAGS + list(extra) + ([RESOURCE_REMARKS] if src.endswith(".hip") else [])
     cmd = [HIPCC] + flags + ["-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd = [HIPCC] + flags + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
-    err = "\n".join(l for l in (r.stderr or "").splitlines()
-                    if "packed-fp32-ops" not in l)
+    if r.returncode == 0:
+        # Device kernels must not use scratch: it turns register traffic into
+        # memory traffic on every access.
+        bad = _scratch_kernels(r.stderr or "")
+        if bad:
+            raise RuntimeError(f"{src}: kernels with scratch memory: {bad}")
+    lines, skip = [], False
+    for l in (r.stderr or "").splitlines():
+        if "remark:" in l:          # a remark and the source excerpt under it
+            skip = True
+            continue
+        if skip and re.match(r"^\s*(\d+\s*)?\|", l):
+            continue
+        skip = False
+        if "packed-fp32-ops" not in l:
+            lines.append(l)
+    err = "\n".join(lines)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{err}")
     if err.strip():

@@ -13,7 +13,7 @@
 //     GEMM2: row n0 + 64w + 32cb + l%32
 //   at k = 64 step + 32 (l / 32) + 8 kk .. +8 (rows past the matrix: zeros).
 // Each wave loads its fragments with fully coalesced 1 KiB loads straight
-// into registers, PF steps ahead, with no LDS traffic; the activation rows
+// into registers, a step ahead, with no LDS traffic; the activation rows
 // (shared by the 4 waves) use the double-buffered LDS tile of the row-major
 // kernel, with the same k assignment (lane half lh holds k in
 // [32 lh, 32 lh + 32)).
@@ -28,7 +28,12 @@ namespace {
 constexpr int BM = 256;    // max rows per tile
 constexpr int BK = 64;     // k per step
 constexpr int NT = 256;    // threads
-constexpr int PF = 2;      // weight prefetch depth (steps)
+// Pipeline depth D in steps: the weights of steps t .. t+D-1 and the
+// activation rows of steps t+1 .. t+D sit in registers (or are in flight)
+// while step t computes, so loads get D-1 steps to arrive.  On gfx950 one
+// step of lead already covers the load latency for every tile height (a
+// deeper pipeline only costs registers), so D = 2 throughout.
+constexpr int depth_for(int) { return 2; }
 constexpr int FRAG = 2048; // 16-byte fragments per packed block (32 KiB)
 constexpr size_t kLdsP = (size_t)2 * BM * 8 * sizeof(u32x4);   // 64 KiB
 
@@ -91,7 +96,7 @@ __device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ ((r ^ (r 
 // The work of one tile with NRB 32-row blocks (compile time, so the MFMA
 // loop has no branches and the fragment reads of a k slice can all be in
 // flight together).
-template <bool kGateUp, int NRB>
+template <bool kGateUp, int NRB, int D, bool kStream>
 __device__ __forceinline__ void packed_tile(const PackedArgs& p, u32x4* sA, int g, int row0,
                                             int nrows, int ntile) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -120,7 +125,7 @@ __device__ __forceinline__ void packed_tile(const PackedArgs& p, u32x4* sA, int 
     arow[j] = a;
   }
   const uint16_t* abase = A + ch * 8;
-  u32x4 ra[2][NRB];   // two register stages of activation rows
+  u32x4 ra[D][NRB];   // register stages of activation rows
   auto aload = [&](u32x4 (&st)[NRB], int j, int step) {
     st[j] = *reinterpret_cast<const u32x4*>(abase + (int64_t)arow[j] * lda +
                                             min(step, last) * BK);
@@ -128,11 +133,12 @@ __device__ __forceinline__ void packed_tile(const PackedArgs& p, u32x4* sA, int 
   auto astore = [&](const u32x4 (&st)[NRB], int j, int buf) {
     sA[buf * BM * 8 + swz((tid >> 3) + 32 * j, ch)] = st[j];
   };
-  u32x4 rb[PF][8];    // weight fragments [slot][cb * 4 + kk]
+  u32x4 rb[D][8];     // weight fragments [slot][cb * 4 + kk]
   auto bload = [&](u32x4 (&dst)[8], int step) {
     const u32x4* src = bw + (int64_t)min(step, last) * FRAG;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dst[i] = __builtin_nontemporal_load(src + i * 64);
+    for (int i = 0; i < 8; ++i)
+      dst[i] = kStream ? __builtin_nontemporal_load(src + i * 64) : src[i * 64];
   };
 
   f32x16 acc[NRB][2];
@@ -143,60 +149,94 @@ __device__ __forceinline__ void packed_tile(const PackedArgs& p, u32x4* sA, int 
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[r][c][i] = 0.0f;
 
-  // One step on LDS buffer `buf` with weight slot `b`; the next step's
-  // activation rows move from registers `st` to LDS buffer `nbuf` and `st`
-  // is refilled with step `ld`, spread over the four k slices.
-  auto step_body = [&](bool active, int buf, const u32x4 (&b)[8], u32x4 (&st)[NRB], int nbuf,
-                       int ld) {
+  // One step on LDS buffer `buf` with weight slot `b`.  The instruction
+  // order is fixed by hand (scheduling barriers): each pair of MFMAs of row
+  // block r is followed by the LDS read of row block r's fragment for the
+  // next k slice and by at most one memory operation, so loads, LDS traffic
+  // and matrix work stay interleaved instead of queueing up in bursts.
+  // Memory operations of slice kk: the activation chunks j = kk, kk + 4 of
+  // the next step move from registers `st` to LDS buffer `nbuf` and `st` is
+  // refilled with step `ld`; after the slice's last MFMA its two weight
+  // fragments, no longer needed, are refilled with step `bld`.
+  auto step_body = [&](int buf, u32x4 (&b)[8], u32x4 (&st)[NRB], int nbuf, int ld, int bld) {
     const u32x4* as = sA + buf * BM * 8;
+    const u32x4* bsrc = bw + (int64_t)min(bld, last) * FRAG;
+    bf16x8 a[2][NRB];
+#pragma unroll
+    for (int r = 0; r < NRB; ++r) a[0][r] = as_bf16x8(as[swz(r * 32 + lr, 4 * lh)]);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      if (active) {
-        const int c = 4 * lh + kk;
-        bf16x8 a[NRB];
+      const bf16x8 b0 = as_bf16x8(b[kk]);
+      const bf16x8 b1 = as_bf16x8(b[4 + kk]);
+      // activation chunk operations of this slice, in order
+      constexpr int kOps = 2 * ((NRB + 3) / 4);
+      int nop = 0;
 #pragma unroll
-        for (int r = 0; r < NRB; ++r) a[r] = as_bf16x8(as[swz(r * 32 + lr, c)]);
-        const bf16x8 b0 = as_bf16x8(b[kk]);
-        const bf16x8 b1 = as_bf16x8(b[4 + kk]);
+      for (int r = 0; r < NRB; ++r) {
+        acc[r][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk & 1][r], b0, acc[r][0], 0, 0, 0);
+        if (kk < 3) a[(kk + 1) & 1][r] = as_bf16x8(as[swz(r * 32 + lr, 4 * lh + kk + 1)]);
+        acc[r][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk & 1][r], b1, acc[r][1], 0, 0, 0);
+        // one activation operation per pair (all of them by the last pair)
+        const int upto = (r == NRB - 1) ? kOps : r + 1;
 #pragma unroll
-        for (int r = 0; r < NRB; ++r) {
-          acc[r][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[r], b0, acc[r][0], 0, 0, 0);
-          acc[r][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[r], b1, acc[r][1], 0, 0, 0);
+        for (; nop < upto && nop < kOps; ++nop) {
+          const int j = kk + 4 * (nop >> 1);
+          if (j < NRB) {
+            if ((nop & 1) == 0) astore(st, j, nbuf);
+            else aload(st, j, ld);
+          }
         }
-      }
-#pragma unroll
-      for (int j = kk; j < NRB; j += 4) {
-        astore(st, j, nbuf);
-        aload(st, j, ld);
+        if (r == NRB - 1) {
+          b[kk] = kStream ? __builtin_nontemporal_load(bsrc + kk * 64) : bsrc[kk * 64];
+          b[4 + kk] = kStream ? __builtin_nontemporal_load(bsrc + (4 + kk) * 64)
+                              : bsrc[(4 + kk) * 64];
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
 
-  // Prologue: weights for steps 0..PF-1, activations of step 0 in LDS, of
-  // steps 1 and 2 in the two register stages.
+  // Prologue: activations of step 0 into LDS buffer 0, of steps 1..D into
+  // ra[1 % D] .. ra[D % D], weights of steps 0..D-1 into rb.  The loads are
+  // issued in the order the loop issues them (activations of step j + 1, then
+  // weights of step j), so that at the loop head every register has as many
+  // younger loads on entry as on the back edge: the compiler's wait counts,
+  // merged over both paths, then wait only for the step about to be used.
+  auto aload_all = [&](u32x4 (&st)[NRB], int step) {
 #pragma unroll
-  for (int s = 0; s < PF; ++s) bload(rb[s], s);
+    for (int j = 0; j < NRB; ++j) aload(st, j, step);
+  };
+  aload_all(ra[0], 0);
 #pragma unroll
-  for (int j = 0; j < NRB; ++j) aload(ra[0], j, 0);
+  for (int j = 0; j < D; ++j) {
+    if ((j + 1) % D == 0) {
 #pragma unroll
-  for (int j = 0; j < NRB; ++j) astore(ra[0], j, 0);
-#pragma unroll
-  for (int j = 0; j < NRB; ++j) aload(ra[1], j, 1);
-#pragma unroll
-  for (int j = 0; j < NRB; ++j) aload(ra[0], j, 2);
+      for (int i = 0; i < NRB; ++i) astore(ra[0], i, 0);
+    }
+    aload_all(ra[(j + 1) % D], j + 1);
+    bload(rb[j], j);
+  }
   __syncthreads();
 
-  // Step t: LDS buffer t % 2; ra[(t+1) % 2] holds step t+1; weight slot
-  // t % PF.  Unrolled by PF (even) so every index is static.
-  for (int s = 0; s < nsteps; s += PF) {
+  // Step t: LDS buffer t % 2 holds its activations, rb[t % D] its weights,
+  // ra[(t + 1) % D] those of step t + 1 (moved to the other LDS buffer during
+  // the step and refilled with step t + 1 + D).  Unrolled by U = lcm(D, 2)
+  // so every index is static.
+  constexpr int U = (D % 2) ? 2 * D : D;
+  auto step = [&](int t, int u) {
+    step_body(u & 1, rb[u % D], ra[(u + 1) % D], (u + 1) & 1, t + 1 + D, t + D);
+    __syncthreads();
+  };
+  int s = 0;
+  for (; s + U <= nsteps; s += U) {
 #pragma unroll
-    for (int u = 0; u < PF; ++u) {
-      const int t = s + u;
-      step_body(t < nsteps, u & 1, rb[u], ra[(u + 1) & 1], (u + 1) & 1, t + 3);
-      bload(rb[u], t + PF);
-      __syncthreads();
-    }
+    for (int u = 0; u < U; ++u) step(s + u, u);
   }
+  // Tail of fewer than U steps (k dimensions that are not a multiple of
+  // U * 64); the guard is uniform across the workgroup.
+#pragma unroll
+  for (int u = 0; u < U - 1; ++u)
+    if (s + u < nsteps) step(s + u, u);
 
   // Epilogue: lane holds column lane%32, rows 8*(i/4) + 4*(lane/32) + i%4.
   uint16_t* C = sh ? p.c_s : p.c_r;
@@ -237,15 +277,28 @@ __global__ void __launch_bounds__(NT, 1) grouped_gemm_bf16_packed(PackedArgs p) 
   const int32_t* ent = decode_work(p.tiles, w, p.ntn, ntile);
   const int g = ent[0], row0 = ent[1], nrows = ent[2];
   if (ntile >= ((g == p.E) ? p.nt_s : p.nt_r)) return;
-  switch ((nrows + 31) >> 5) {
-    case 1: packed_tile<kGateUp, 1>(p, smem, g, row0, nrows, ntile); break;
-    case 2: packed_tile<kGateUp, 2>(p, smem, g, row0, nrows, ntile); break;
-    case 3: packed_tile<kGateUp, 3>(p, smem, g, row0, nrows, ntile); break;
-    case 4: packed_tile<kGateUp, 4>(p, smem, g, row0, nrows, ntile); break;
-    case 5: packed_tile<kGateUp, 5>(p, smem, g, row0, nrows, ntile); break;
-    case 6: packed_tile<kGateUp, 6>(p, smem, g, row0, nrows, ntile); break;
-    case 7: packed_tile<kGateUp, 7>(p, smem, g, row0, nrows, ntile); break;
-    default: packed_tile<kGateUp, 8>(p, smem, g, row0, nrows, ntile); break;
+  // A weight tile read by one M-tile only streams past the caches
+  // (non-temporal loads); one shared by several M-tiles of a group (their
+  // workgroups run side by side on one XCD) is kept in L2 for the others.
+  const bool stream = ent[4] == 1;
+  switch (((nrows + 31) >> 5) * 2 + (stream ? 1 : 0)) {
+#define MOE_TILE_CASE(n)                                                                      \
+    case 2 * n: packed_tile<kGateUp, n, depth_for(n), false>(p, smem, g, row0, nrows, ntile); \
+      break;                                                                                  \
+    case 2 * n + 1: packed_tile<kGateUp, n, depth_for(n), true>(p, smem, g, row0, nrows, ntile); \
+      break;
+    MOE_TILE_CASE(1)
+    MOE_TILE_CASE(2)
+    MOE_TILE_CASE(3)
+    MOE_TILE_CASE(4)
+    MOE_TILE_CASE(5)
+    MOE_TILE_CASE(6)
+    MOE_TILE_CASE(7)
+#undef MOE_TILE_CASE
+    default:
+      if (stream) packed_tile<kGateUp, 8, depth_for(8), true>(p, smem, g, row0, nrows, ntile);
+      else packed_tile<kGateUp, 8, depth_for(8), false>(p, smem, g, row0, nrows, ntile);
+      break;
   }
 }
 
@@ -359,9 +412,10 @@ hipError_t set_attrs_packed() {
   static hipError_t once = []() {
     hipError_t e = hipFuncSetAttribute((const void*)grouped_gemm_bf16_packed<true>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsP);
-    if (e != hipSuccess) return e;
-    return hipFuncSetAttribute((const void*)grouped_gemm_bf16_packed<false>,
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsP);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)grouped_gemm_bf16_packed<false>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsP);
+    return e;
   }();
   return once;
 }

@@ -27,30 +27,29 @@ constexpr int GBK = 64;    // k per stage
 constexpr int GTHREADS = 256;
 
 // Split 8 fp32 weights into hi/mid/lo bf16x8 operands (exact decomposition).
-__device__ __forceinline__ void split3(const float4& p, const float4& q, bf16x8& hi,
-                                       bf16x8& mid, bf16x8& lo) {
-  float v[8] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
-  uint32_t h[4], m[4], l[4];
+__device__ __forceinline__ void split3(u32x4 p, u32x4 q, bf16x8& hi, bf16x8& mid, bf16x8& lo) {
+  const uint32_t v[8] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
+  u32x4 h, m, l;
 #pragma unroll
-  for (int j = 0; j < 8; j += 2) {
+  for (int j = 0; j < 4; ++j) {
     uint32_t hb[2], mb[2], lb[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      uint32_t b = __float_as_uint(v[j + u]);
-      float r1 = v[j + u] - __uint_as_float(b & 0xFFFF0000u);  // exact
-      uint32_t b1 = __float_as_uint(r1);
-      float r2 = r1 - __uint_as_float(b1 & 0xFFFF0000u);       // exact, <= 8 bits
+      const uint32_t b = v[2 * j + u];
+      const float r1 = __uint_as_float(b) - __uint_as_float(b & 0xFFFF0000u);  // exact
+      const uint32_t b1 = __float_as_uint(r1);
+      const float r2 = r1 - __uint_as_float(b1 & 0xFFFF0000u);  // exact, <= 8 bits
       hb[u] = b >> 16;
       mb[u] = b1 >> 16;
       lb[u] = __float_as_uint(r2) >> 16;
     }
-    h[j / 2] = hb[0] | (hb[1] << 16);
-    m[j / 2] = mb[0] | (mb[1] << 16);
-    l[j / 2] = lb[0] | (lb[1] << 16);
+    h[j] = hb[0] | (hb[1] << 16);
+    m[j] = mb[0] | (mb[1] << 16);
+    l[j] = lb[0] | (lb[1] << 16);
   }
-  hi = as_bf16x8(make_uint4(h[0], h[1], h[2], h[3]));
-  mid = as_bf16x8(make_uint4(m[0], m[1], m[2], m[3]));
-  lo = as_bf16x8(make_uint4(l[0], l[1], l[2], l[3]));
+  hi = as_bf16x8(h);
+  mid = as_bf16x8(m);
+  lo = as_bf16x8(l);
 }
 
 // partials[ks][t][e] = sum over the ks-th slice of H of x[t,h] w[e,h].
@@ -60,8 +59,8 @@ __device__ __forceinline__ void split3(const float4& p, const float4& q, bf16x8&
 __global__ void __launch_bounds__(GTHREADS)
 gate_logits_bf16_kernel(const uint16_t* __restrict__ x, const float* __restrict__ wg,
                         float* __restrict__ part, int64_t T, int H, int E, int hslice) {
-  __shared__ uint4 sA[2][GBM * 8];    // [row][8 chunks of 8 bf16]
-  __shared__ uint4 sB[2][GBN * 16];   // [row][16 chunks of 4 fp32]
+  __shared__ u32x4 sA[2][GBM * 8];    // [row][8 chunks of 8 bf16]
+  __shared__ u32x4 sB[2][GBN * 16];   // [row][16 chunks of 4 fp32]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t m0 = (int64_t)blockIdx.x * GBM;
   const int n0 = blockIdx.y * GBN;
@@ -69,25 +68,25 @@ gate_logits_bf16_kernel(const uint16_t* __restrict__ x, const float* __restrict_
   const int kbeg = ks * hslice;
   const int nsteps = hslice / GBK;
 
-  // Global->register staging: A 2 chunks, B 8 chunks per thread.
-  uint4 ra[2], rb[8];
+  // Global->register staging: A 2 chunks, B 8 chunks per thread.  Rows past
+  // the end of x or of the experts re-read the last row (results dropped), so
+  // every load is unconditional.
+  u32x4 ra[2], rb[8];
   auto gload = [&](int step) {
     const int k0 = kbeg + step * GBK;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       int c = tid + j * GTHREADS;       // 0..511
       int row = c >> 3, ch = c & 7;
-      int64_t t = m0 + row;
-      if (t < T)
-        ra[j] = *reinterpret_cast<const uint4*>(x + t * H + k0 + ch * 8);
+      const int64_t t = min(m0 + row, T - 1);
+      ra[j] = *reinterpret_cast<const u32x4*>(x + t * H + k0 + ch * 8);
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       int c = tid + j * GTHREADS;       // 0..2047
       int row = c >> 4, ch = c & 15;
-      int e = n0 + row;
-      if (e < E)
-        rb[j] = *reinterpret_cast<const uint4*>(wg + (int64_t)e * H + k0 + ch * 4);
+      const int e = min(n0 + row, E - 1);
+      rb[j] = *reinterpret_cast<const u32x4*>(wg + (int64_t)e * H + k0 + ch * 4);
     }
   };
   auto sstore = [&](int buf) {
@@ -130,10 +129,10 @@ gate_logits_bf16_kernel(const uint16_t* __restrict__ x, const float* __restrict_
       }
       int brow = wave * 32 + lr;
       int c0 = 4 * kk + 2 * lh;
-      uint4 p = sB[buf][brow * 16 + (c0 ^ (brow & 15))];
-      uint4 q = sB[buf][brow * 16 + ((c0 + 1) ^ (brow & 15))];
+      const u32x4 p = sB[buf][brow * 16 + (c0 ^ (brow & 15))];
+      const u32x4 q = sB[buf][brow * 16 + ((c0 + 1) ^ (brow & 15))];
       bf16x8 bh, bm, bl;
-      split3(__builtin_bit_cast(float4, p), __builtin_bit_cast(float4, q), bh, bm, bl);
+      split3(p, q, bh, bm, bl);
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
         acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[r], bh, acc[r], 0, 0, 0);

@@ -1,6 +1,6 @@
 // C ABI of libmoe: argument validation, workspace layout and launch order.
 // Every check happens on the host before anything is enqueued.
-#include "../../include/moe.h"
+#include "moe.h"
 
 #include <math.h>
 #include <stdarg.h>
