@@ -143,14 +143,21 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
+    # The gate + permute workload times those two entry points only; every
+    # other workload times the whole layer.
+    gate_only = cfg.name == synth.C2.name
     t0 = time.time()
     log(f"[bench] {cfg.name}: generating inputs")
-    inp = synth.gen_inputs(cfg)
+    if gate_only:
+        inp = {"cfg": cfg, "x": synth.gen_x(cfg)}
+        inp["gate_w"], inp["bias"] = synth.gen_gate(cfg)
+    else:
+        inp = synth.gen_inputs(cfg)
     log(f"[bench] generated in {time.time() - t0:.1f}s; uploading")
     d = sd.to_device(inp)
-    if cfg.wdtype == "bf16" and not args.row_major:
+    if cfg.wdtype == "bf16" and not args.row_major and not gate_only:
         d = sd.packed_copy(d)   # the row-major device copies are released here
-    W = sd.weights_struct(d)
+    W = None if gate_only else sd.weights_struct(d)
     C = sd.moe_config(cfg)
     ws = sd.workspace(cfg, T)
     act_dt = torch.bfloat16 if cfg.act == "bf16" else torch.float32
@@ -159,8 +166,20 @@ def main():
     log(f"[bench] inputs resident in HBM ({time.time() - t0:.1f}s)")
     stream = torch.cuda.current_stream()
 
+    lg = torch.empty((T, E), dtype=torch.float32, device=dev)
+    idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+    wt = torch.empty((T, K), dtype=torch.float32, device=dev)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offs = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(T * K, dtype=torch.int32, device=dev)
+    pos = torch.empty(T * K, dtype=torch.int32, device=dev)
+
     def step():
-        moe.moe_forward(C, T, d["x"], W, out, ws, stream=stream)
+        if gate_only:
+            moe.moe_gate(C, T, d["x"], d["gate_w"], d["bias"], lg, idx, wt, ws, stream=stream)
+            moe.moe_permute(C, T, idx, counts, offs, perm, pos, ws, stream=stream)
+        else:
+            moe.moe_forward(C, T, d["x"], W, out, ws, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -197,29 +216,23 @@ def main():
 
     # Per-phase timing with the separate entry points (same kernels, same
     # stream), HIP events between phases.
-    lg = torch.empty((T, E), dtype=torch.float32, device=dev)
-    idx = torch.empty((T, K), dtype=torch.int32, device=dev)
-    wt = torch.empty((T, K), dtype=torch.float32, device=dev)
-    counts = torch.empty(E, dtype=torch.int32, device=dev)
-    offs = torch.empty(E + 1, dtype=torch.int32, device=dev)
-    perm = torch.empty(T * K, dtype=torch.int32, device=dev)
-    pos = torch.empty(T * K, dtype=torch.int32, device=dev)
-    y = torch.empty((T * K, H), dtype=act_dt, device=dev)
-    ys = torch.empty((T, H), dtype=act_dt, device=dev) if Is else None
-    phases = ["gate", "permute", "expert_ffn", "combine"]
+    y = torch.empty((T * K, H), dtype=act_dt, device=dev) if not gate_only else None
+    ys = torch.empty((T, H), dtype=act_dt, device=dev) if Is and not gate_only else None
+    phases = ["gate", "permute"] + ([] if gate_only else ["expert_ffn", "combine"])
     acc = {p: 0.0 for p in phases}
     nrep = max(3, min(args.steps, 10))
     for rep in range(nrep + 1):
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)]
         evs[0].record(stream)
         moe.moe_gate(C, T, d["x"], d["gate_w"], d["bias"], lg, idx, wt, ws, stream=stream)
         evs[1].record(stream)
         moe.moe_permute(C, T, idx, counts, offs, perm, pos, ws, stream=stream)
         evs[2].record(stream)
-        moe.moe_expert_ffn(C, T, d["x"], perm, offs, W, y, ys, ws, stream=stream)
-        evs[3].record(stream)
-        moe.moe_combine(C, T, y, ys, pos, wt, out, stream=stream)
-        evs[4].record(stream)
+        if not gate_only:
+            moe.moe_expert_ffn(C, T, d["x"], perm, offs, W, y, ys, ws, stream=stream)
+            evs[3].record(stream)
+            moe.moe_combine(C, T, y, ys, pos, wt, out, stream=stream)
+            evs[4].record(stream)
         torch.cuda.synchronize()
         if rep:  # first repetition is a warmup
             for i, p in enumerate(phases):
@@ -232,15 +245,24 @@ def main():
     abytes = 2 if cfg.act == "bf16" else 4
     expert_w = 3 * H * I * wbytes
     shared_w = 3 * H * Is * wbytes
-    flop = T * (6.0 * H * (I * K + Is) + 2.0 * H * E)
-    layer_bytes = active * expert_w + shared_w + E * H * 4 + E * 4 + 2 * T * H * abytes
-    ffn_flop = T * 6.0 * H * (I * K + Is)
-    ffn_bytes = active * expert_w + shared_w + T * H * abytes + (T * K + T) * H * abytes
-    ffn_ms = acc["expert_ffn"]
-    ffn_gbs = ffn_bytes / (ffn_ms * 1e-3) / 1e9
-    ffn_tflops = ffn_flop / (ffn_ms * 1e-3) / 1e12
     mfma_peak = FP8_PEAK_TFLOPS if cfg.wdtype == "fp8" else BF16_PEAK_TFLOPS
     tok_s = T / (ms * 1e-3)
+    if gate_only:
+        # x and the gate weight in; routing (idx, w), counts, perm and pos out
+        flop = 2.0 * T * H * E
+        layer_bytes = T * H * abytes + E * H * 4 + E * 4 + T * K * 8 + E * 8 + T * K * 8
+        ffn = None
+    else:
+        flop = T * (6.0 * H * (I * K + Is) + 2.0 * H * E)
+        layer_bytes = active * expert_w + shared_w + E * H * 4 + E * 4 + 2 * T * H * abytes
+        ffn_flop = T * 6.0 * H * (I * K + Is)
+        ffn_bytes = active * expert_w + shared_w + T * H * abytes + (T * K + T) * H * abytes
+        ffn_ms = acc["expert_ffn"]
+        ffn_gbs = ffn_bytes / (ffn_ms * 1e-3) / 1e9
+        ffn_tflops = ffn_flop / (ffn_ms * 1e-3) / 1e12
+        ffn = {"ms": round(ffn_ms, 4), "hbm_gbs": round(ffn_gbs, 1), "tflops": round(ffn_tflops, 1),
+               "hbm_frac": round(ffn_gbs / HBM_PEAK_GBS, 4),
+               "mfma_frac": round(ffn_tflops / mfma_peak, 4)}
 
     work = kernel_work(dominant, cfg, active)
     if work is None:
@@ -274,7 +296,8 @@ def main():
         "vs_baseline": None,
         "dtype": {"bf16": "bf16", "fp8": "fp8-e4m3", "f32": "f32"}[cfg.wdtype],
         "data": "synthetic: seeded N(0,1) tokens, N(0,1/fan_in) weights, gate N(0,1/H), bias "
-                + (f"from {cfg.bias_file} (Zipf(1.2) expert loads)" if cfg.bias_file
+                + (f"from {os.path.basename(cfg.bias_file)} (Zipf(1.2) expert loads)"
+                   if cfg.bias_file
                    else f"U({cfg.bias_lo},{cfg.bias_hi})"),
         "config": {"workload": cfg.name, "T": T, "hidden": H, "n_routed_experts": E,
                    "n_group": cfg.G, "topk_group": cfg.TG, "top_k": K, "moe_inter": I,
@@ -288,25 +311,28 @@ def main():
                   "active_experts": active},
         "phases_ms": {p: round(v, 4) for p, v in acc.items()},
         "kernels_ms": {k: round(v, 4) for k, v in sorted(kernels_ms.items())},
-        "expert_ffn": {"ms": round(ffn_ms, 4), "hbm_gbs": round(ffn_gbs, 1),
-                       "tflops": round(ffn_tflops, 1),
-                       "hbm_frac": round(ffn_gbs / HBM_PEAK_GBS, 4),
-                       "mfma_frac": round(ffn_tflops / mfma_peak, 4)},
+        "expert_ffn": ffn,
         "roofline": roof,
     }
 
     if args.cpu_sample > 0 and not args.profile_only:
         import oracle
-        S = min(args.cpu_sample, T)
+        S = min(args.cpu_sample * (64 if gate_only else 1), T)
         toks = np.arange(S)
-        log(f"[bench] cpu baseline: oracle forward on {S} tokens")
+        log(f"[bench] cpu baseline: oracle on {S} tokens")
         t1 = time.perf_counter()
-        oracle.forward(cfg, inp, tokens=toks)
+        if gate_only:
+            lg_ref = oracle.logits(inp["x"][:S], "bf16", inp["gate_w"])
+            idx_ref, _, _ = oracle.route_f64(cfg, lg_ref, inp["bias"])
+            oracle.permute(idx_ref, E)
+            what = "fp64 gate logits, group-limited routing and the stable permutation"
+        else:
+            oracle.forward(cfg, inp, tokens=toks)
+            what = "fp64 gate logits, routing and the layer output"
         dt = time.perf_counter() - t1
         result["cpu_baseline"] = {"value": round(S / dt, 3), "unit": "tokens/s",
                                   "cores": oracle.threads(), "kind": "oracle",
-                                  "sample": f"first {S} of the {T} tokens of {cfg.name}: fp64 "
-                                            f"gate logits, routing and the layer output "
+                                  "sample": f"first {S} of the {T} tokens of {cfg.name}: {what} "
                                             f"({dt:.1f} s)"}
     print(json.dumps(result))
 
