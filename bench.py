@@ -155,7 +155,7 @@ def main():
         inp = synth.gen_inputs(cfg)
     log(f"[bench] generated in {time.time() - t0:.1f}s; uploading")
     d = sd.to_device(inp)
-    if cfg.wdtype == "bf16" and not args.row_major and not gate_only:
+    if cfg.wdtype != "f32" and not args.row_major and not gate_only:
         d = sd.packed_copy(d)   # the row-major device copies are released here
     W = None if gate_only else sd.weights_struct(d)
     C = sd.moe_config(cfg)

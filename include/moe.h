@@ -90,7 +90,7 @@ typedef struct {
  * fp32 per 128x128 block, row-major over (row block, column block); they are
  * ignored (may be NULL) otherwise.  ws13/ws2 (+scales) may be NULL iff Is == 0.
  * packed = 0: w13, w2, ws13, ws2 are row-major as shown; packed = 1: all four
- * were rearranged by moe_pack_weight (bf16 weights only; scales unchanged). */
+ * were rearranged by moe_pack_weight (bf16 or e4m3 weights; scales unchanged). */
 typedef struct {
     const float* gate_w;     /* [E, H]                                           */
     const float* bias;       /* [E]  e_score_correction_bias                     */
@@ -183,18 +183,29 @@ moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const mo
 moe_status moe_quantize_act(const moe_config* cfg, int64_t rows, const void* x, uint8_t* xq,
                             float* xs, void* stream);
 
-/* Weight streaming layout for the bf16 expert GEMMs.  The grouped GEMM reads
- * each weight matrix once per call; in row-major order that is one 128-byte
- * piece per weight row per k step, rows 2*H bytes apart.  The packed layout
- * stores, for every (expert, output tile, k step), the MFMA operand
- * fragments of the tile's 256 weight rows x 64 k as one contiguous 32 KiB
- * block in the order the kernel consumes them (per wave, per 32-row block,
- * per 16-k slice: 64 lanes x 16 bytes), so the weights stream sequentially
- * from HBM into registers.  Pack once when the weights are loaded.
+/* Weight streaming layout for the expert GEMMs.  The grouped GEMM reads
+ * each weight matrix once per call; in row-major order that is one short
+ * piece per weight row per k step, rows a whole row length apart.  The packed
+ * layout stores, for every (expert, output tile, k step), the MFMA operand
+ * fragments of the tile's 256 weight rows as one contiguous 32 KiB block in
+ * the order the kernel consumes them, so the weights stream sequentially
+ * from HBM into registers.  Output tiles are 128 h columns (gate and up rows
+ * together) for w13/ws13 and 256 output rows for w2/ws2.
+ *   bf16: k steps of 64; block = [wave 4][col block 2][k slice 4][lane 64]
+ *         x 16 bytes, lane l holding 8 values at k = 64 step + 32 (l / 32)
+ *         + 8 slice.
+ *   e4m3: k steps of 128 (one scale block); block = [wave 4][col block 2]
+ *         [k half 2][16-byte half 2][lane 64] x 16 bytes, lane l holding 16
+ *         codes at k = 128 step + 64 half_k + 32 (l / 32) + 16 half_16.
+ *   Row of (wave w, col block cb, lane l) in tile t: w13/ws13 gate row
+ *   128 t + 32 w + l % 32 (cb = 0) or the up row I + 128 t + 32 w + l % 32
+ *   (cb = 1); w2/ws2 row 256 t + 64 w + 32 cb + l % 32.  Rows past the
+ *   matrix are zero.  The fp8 block scales keep their row-major layout.
+ * Pack once when the weights are loaded.
  *   moe_packed_bytes: size of the packed copy of matrix `which` (0 for an
- *     invalid or non-bf16 config, or for MOE_WS13/MOE_WS2 when Is == 0).
+ *     invalid or fp32 config, or for MOE_WS13/MOE_WS2 when Is == 0).
  *   moe_pack_weight: src is the row-major matrix (w13 [E,2I,H], w2 [E,H,I],
- *     ws13 [2Is,H] or ws2 [H,Is], bf16), dst a device buffer of
+ *     ws13 [2Is,H] or ws2 [H,Is], bf16 or e4m3), dst a device buffer of
  *     moe_packed_bytes(cfg, which) bytes (tile padding is zero-filled). */
 size_t moe_packed_bytes(const moe_config* cfg, moe_weight_id which);
 moe_status moe_pack_weight(const moe_config* cfg, moe_weight_id which, const void* src,

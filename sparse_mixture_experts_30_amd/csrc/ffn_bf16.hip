@@ -245,7 +245,7 @@ unsigned grid_for(int64_t max_work) {
 }  // namespace
 
 size_t ffn_tiles_bytes(const FfnDims& d) {
-  return (size_t)(8 + 8 * ffn_max_mtiles(d.N, d.T, d.E, BM)) * sizeof(int32_t);
+  return (size_t)(8 + 8 * ffn_max_mtiles(d.N, d.T, d.E, kMinTileRows)) * sizeof(int32_t);
 }
 
 // h holds routed rows [0, N) with width I, then shared rows [N, N+T) with width Is.

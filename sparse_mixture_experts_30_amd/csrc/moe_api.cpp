@@ -210,6 +210,15 @@ moe_status run_ffn(const moe_config* c, int64_t T, const void* x, const int32_t*
       float* xs = at<float>(ws, L.xs);
       HIPCALL(moe::launch_quant_rows((const uint16_t*)x, T, c->hidden_size, xq, xs, s),
               "quantise x");
+      if (wt->packed) {
+        HIPCALL(moe::launch_ffn_fp8_packed(d, xq, xs, perm, offsets, wt->w13, wt->w13_scale,
+                                           wt->w2, wt->w2_scale, wt->ws13, wt->ws13_scale, wt->ws2,
+                                           wt->ws2_scale, at<uint8_t>(ws, L.h), at<float>(ws, L.hs),
+                                           at<int32_t>(ws, L.tiles), (uint16_t*)y, (uint16_t*)ys,
+                                           s),
+                "ffn fp8 packed");
+        break;
+      }
       HIPCALL(moe::launch_ffn_fp8(d, xq, xs, perm, offsets, (const uint8_t*)wt->w13, wt->w13_scale,
                                   (const uint8_t*)wt->w2, wt->w2_scale, (const uint8_t*)wt->ws13,
                                   wt->ws13_scale, (const uint8_t*)wt->ws2, wt->ws2_scale,
@@ -226,8 +235,8 @@ moe_status check_weights(const moe_config* c, const moe_weights* w, bool need_ga
   NONNULL(w);
   if (w->packed != 0 && w->packed != 1)
     return fail(MOE_ERR_INVALID_ARG, "moe_weights.packed must be 0 or 1");
-  if (w->packed && c->weight_dtype != MOE_BF16)
-    return fail(MOE_ERR_UNSUPPORTED, "the packed weight layout is for bf16 weights");
+  if (w->packed && c->weight_dtype == MOE_F32)
+    return fail(MOE_ERR_UNSUPPORTED, "the packed weight layout is for bf16 and fp8 weights");
   if (need_gate) {
     NONNULL(w->gate_w);
     NONNULL(w->bias);
@@ -376,14 +385,15 @@ moe_status moe_quantize_act(const moe_config* cfg, int64_t rows, const void* x, 
 }
 
 size_t moe_packed_bytes(const moe_config* cfg, moe_weight_id which) {
-  if (check_cfg(cfg) != MOE_OK || cfg->weight_dtype != MOE_BF16) return 0;
+  if (check_cfg(cfg) != MOE_OK || cfg->weight_dtype == MOE_F32) return 0;
   const int H = cfg->hidden_size, I = cfg->moe_intermediate_size,
             Is = cfg->shared_intermediate_size, E = cfg->n_routed_experts;
+  auto bytes = cfg->weight_dtype == MOE_FP8_E4M3 ? moe::packed8_bytes : moe::packed_bytes;
   switch (which) {
-    case MOE_W13: return moe::packed_bytes(true, E, I, H);
-    case MOE_W2: return moe::packed_bytes(false, E, H, I);
-    case MOE_WS13: return Is ? moe::packed_bytes(true, 1, Is, H) : 0;
-    case MOE_WS2: return Is ? moe::packed_bytes(false, 1, H, Is) : 0;
+    case MOE_W13: return bytes(true, E, I, H);
+    case MOE_W2: return bytes(false, E, H, I);
+    case MOE_WS13: return Is ? bytes(true, 1, Is, H) : 0;
+    case MOE_WS2: return Is ? bytes(false, 1, H, Is) : 0;
   }
   return 0;
 }
@@ -391,8 +401,8 @@ size_t moe_packed_bytes(const moe_config* cfg, moe_weight_id which) {
 moe_status moe_pack_weight(const moe_config* cfg, moe_weight_id which, const void* src,
                            void* dst, void* stream) {
   CHECK(check_cfg(cfg));
-  if (cfg->weight_dtype != MOE_BF16)
-    return fail(MOE_ERR_UNSUPPORTED, "the packed weight layout is for bf16 weights");
+  if (cfg->weight_dtype == MOE_F32)
+    return fail(MOE_ERR_UNSUPPORTED, "the packed weight layout is for bf16 and fp8 weights");
   if (which < MOE_W13 || which > MOE_WS2) return fail(MOE_ERR_INVALID_ARG, "unknown weight id");
   const int H = cfg->hidden_size, I = cfg->moe_intermediate_size,
             Is = cfg->shared_intermediate_size, E = cfg->n_routed_experts;
@@ -404,9 +414,14 @@ moe_status moe_pack_weight(const moe_config* cfg, moe_weight_id which, const voi
   const int64_t experts = (which == MOE_W13 || which == MOE_W2) ? E : 1;
   const int inter = (which == MOE_W13 || which == MOE_W2) ? I : Is;
   const int n = gate_up ? inter : H, kd = gate_up ? H : inter;
-  HIPCALL(moe::launch_pack(gate_up, (const uint16_t*)src, dst, experts, n, kd,
-                           (hipStream_t)stream),
-          "pack weight");
+  if (cfg->weight_dtype == MOE_FP8_E4M3)
+    HIPCALL(moe::launch_pack8(gate_up, (const uint8_t*)src, dst, experts, n, kd,
+                              (hipStream_t)stream),
+            "pack weight");
+  else
+    HIPCALL(moe::launch_pack(gate_up, (const uint16_t*)src, dst, experts, n, kd,
+                             (hipStream_t)stream),
+            "pack weight");
   return MOE_OK;
 }
 

@@ -90,7 +90,9 @@ hipError_t launch_permute(const int32_t* idx, int64_t N, int E, int32_t* hist, i
                           int32_t* offsets, int32_t* perm, int32_t* pos, int32_t* err,
                           hipStream_t s);
 
-// Expert FFN tile schedule (see ffn_sched.hip for the entry format).
+// Expert FFN tile schedule (see ffn_sched.hip for the entry format).  The
+// smallest M-tile height any GEMM uses sizes the list in the workspace.
+constexpr int kMinTileRows = 128;
 int64_t ffn_max_mtiles(int64_t N, int64_t T, int E, int BM);
 hipError_t launch_build_tiles(const int32_t* offsets, int E, int64_t T, bool has_shared, int BM,
                               int32_t* tiles, hipStream_t s);
@@ -132,6 +134,16 @@ hipError_t launch_ffn_f32(const FfnDims& d, const float* x, const int32_t* perm,
                           const int32_t* offsets, const float* w13, const float* w2,
                           const float* ws13, const float* ws2, float* h, float* y, float* ys,
                           hipStream_t s);
+// Packed fp8 weight layout (ffn_fp8_packed.hip).
+size_t packed8_bytes(bool gate_up, int64_t experts, int n, int kd);
+hipError_t launch_pack8(bool gate_up, const uint8_t* src, void* dst, int64_t experts, int n,
+                        int kd, hipStream_t s);
+hipError_t launch_ffn_fp8_packed(const FfnDims& d, const uint8_t* xq, const float* xs,
+                                 const int32_t* perm, const int32_t* offsets, const void* w13p,
+                                 const float* w13s, const void* w2p, const float* w2s,
+                                 const void* ws13p, const float* ws13s, const void* ws2p,
+                                 const float* ws2s, uint8_t* hq, float* hs, int32_t* tiles,
+                                 uint16_t* y, uint16_t* ys, hipStream_t s);
 hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int cols, uint8_t* q, float* sc,
                              hipStream_t s);
 hipError_t launch_ffn_fp8(const FfnDims& d, const uint8_t* xq, const float* xs,

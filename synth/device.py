@@ -34,8 +34,8 @@ def weights_struct(dev: dict):
 
 
 def packed_copy(dev: dict, device="cuda") -> dict:
-    """Same inputs with the bf16 expert weights in the library's packed
-    streaming layout (moe_pack_weight)."""
+    """Same inputs with the bf16 or e4m3 expert weights in the library's
+    packed streaming layout (moe_pack_weight); block scales are unchanged."""
     import torch
     import sparse_mixture_experts_30_amd as moe
     cfg = dev["cfg"]

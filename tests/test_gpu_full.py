@@ -37,9 +37,9 @@ class _Weights:
                 synth.gen_shared_weights(cfg)
             log(f"  generated in {time.time() - t0:.1f}s; uploading")
             dev_w = {k: sd.tensor(v) for k, v in host_w.items()}
-            if wdtype == "bf16":   # the benchmark's configuration: packed weights
-                dev_w = sd.packed_copy(dict(dev_w, cfg=cfg))
-                dev_w.pop("cfg")
+            # the benchmark's configuration: packed weights
+            dev_w = sd.packed_copy(dict(dev_w, cfg=cfg))
+            dev_w.pop("cfg")
             sync()
             log(f"  uploaded ({time.time() - t0:.1f}s)")
             cls.cache[wdtype] = (host_w, dev_w)

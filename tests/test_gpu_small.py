@@ -30,11 +30,15 @@ K1_NOSHARED = synth.C3.replace(name="bf16-T7-K1-noshared", T=7, H=512, E=16, G=4
 SMALL_FP8 = synth.C5.replace(name="fp8-T200-H1024-E32", T=200, H=1024, E=32, G=4, TG=2, K=4,
                              I=256, Is=384, rho=2.5)
 TINY_T1 = SMALL_BF16.replace(name="bf16-T1", T=1)
+# fp8 with 256 rows per expert: two 128-row M-tiles share each weight tile
+TALL_FP8 = synth.C5.replace(name="fp8-T1024-H512-E8-K2", T=1024, H=512, E=8, G=2, TG=1, K=2,
+                            I=256, Is=256, rho=1.0)
 # 32 < T <= 64: decode path with two 32-row blocks per group
 DECODE48 = synth.C3.replace(name="bf16-T48-H512-E16", T=48, H=512, E=16, G=4, TG=2, K=4, I=256,
                             Is=128, rho=2.5)
 
-LAYER_CASES = [C1, SMALL_BF16, RAGGED_BF16, TALL_BF16, K1_NOSHARED, TINY_T1, DECODE48, SMALL_FP8]
+LAYER_CASES = [C1, SMALL_BF16, RAGGED_BF16, TALL_BF16, K1_NOSHARED, TINY_T1, DECODE48, SMALL_FP8,
+               TALL_FP8]
 
 
 def _tol(cfg):
@@ -105,7 +109,8 @@ def test_permute_flags_out_of_range_index():
 
 FFN_CASES = [(C1, False), (SMALL_BF16, False), (RAGGED_BF16, False), (TALL_BF16, False),
              (K1_NOSHARED, False), (SMALL_FP8, False), (SMALL_BF16, True), (RAGGED_BF16, True),
-             (TALL_BF16, True), (K1_NOSHARED, True), (DECODE48, True), (DECODE48, False)]
+             (TALL_BF16, True), (K1_NOSHARED, True), (DECODE48, True), (DECODE48, False),
+             (SMALL_FP8, True), (TALL_FP8, True), (TALL_FP8, False)]
 
 
 def _case_id(c):
@@ -177,7 +182,7 @@ def test_combine(act):
 
 
 FORWARD_CASES = [(c, False) for c in LAYER_CASES] + [(c, True) for c in LAYER_CASES
-                                                     if c.wdtype == "bf16"]
+                                                     if c.wdtype != "f32"]
 
 
 @pytest.mark.parametrize("case", FORWARD_CASES, ids=_case_id)
@@ -298,3 +303,41 @@ def test_pack_layout():
         for j in range(8):
             ref[idx, j] = src[e[idx], row[idx], k0[idx] + j]
         np.testing.assert_array_equal(got, ref)
+
+
+def test_pack_layout_fp8():
+    """moe_pack_weight for e4m3 weights against the layout stated in
+    include/moe.h, written out with numpy: per (expert, tile, 128-k step) a
+    block of [wave 4][col block 2][k half 2][16-byte half 2][lane 64][16 codes]."""
+    cfg = SMALL_FP8            # Is = 384: three GEMM1 tiles for the shared expert
+    inp, dev = inputs(cfg)
+    C = sd.moe_config(cfg)
+    E, H, I, Is = cfg.E, cfg.H, cfg.I, cfg.Is
+    for key, which, experts, gate_up, n, kd in (("w13", moe.MOE_W13, E, True, I, H),
+                                                ("w2", moe.MOE_W2, E, False, H, I),
+                                                ("ws13", moe.MOE_WS13, 1, True, Is, H),
+                                                ("ws2", moe.MOE_WS2, 1, False, H, Is)):
+        src = inp[key].reshape(experts, -1, kd)
+        buf = torch.empty(moe.moe_packed_bytes(C, which), dtype=torch.uint8, device=DEV)
+        moe.moe_pack_weight(C, which, dev[key], buf)
+        got = host(buf).reshape(-1, 16)
+        nt = -(-n // (128 if gate_up else 256))
+        steps = kd // 128
+        assert got.shape[0] == experts * nt * steps * 2048
+        c = np.arange(got.shape[0])
+        l, hf, kk, cb, w = c & 63, (c >> 6) & 1, (c >> 7) & 1, (c >> 8) & 1, (c >> 9) & 3
+        rest = c >> 11
+        ks, tile, e = rest % steps, (rest // steps) % nt, rest // (steps * nt)
+        if gate_up:
+            col = tile * 128 + 32 * w + (l & 31)
+            ok = col < n
+            row = np.where(cb == 1, n + col, col)
+        else:
+            row = tile * 256 + 64 * w + 32 * cb + (l & 31)
+            ok = row < n
+        k0 = ks * 128 + 64 * kk + 32 * (l >> 5) + 16 * hf
+        ref = np.zeros_like(got)
+        idx = np.nonzero(ok)[0]
+        for j in range(16):
+            ref[idx, j] = src[e[idx], row[idx], k0[idx] + j]
+        np.testing.assert_array_equal(got, ref, err_msg=key)
