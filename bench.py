@@ -36,6 +36,9 @@ def log(msg):
 KERNEL_SOURCES = {
     # kernel name (as the library's timer and rocprofv3 name it) -> sources it is built from
     "grouped_gemm_bf16_packed": ("ffn_bf16_packed.hip", "moe_internal.hpp"),
+    "grouped_gemm_bf16_packed_x2": ("ffn_bf16_packed.hip", "moe_internal.hpp"),
+    "grouped_gemm_bf16_packed_few": ("ffn_bf16_packed.hip", "moe_internal.hpp"),
+    "grouped_gemm_fp8_packed": ("ffn_fp8_packed.hip", "moe_internal.hpp"),
     "grouped_gemm_bf16": ("ffn_bf16.hip", "moe_internal.hpp"),
     "grouped_gemm_fp8": ("ffn_fp8.hip", "moe_internal.hpp"),
     "gate_logits_bf16_kernel": ("gate.hip", "moe_internal.hpp"),

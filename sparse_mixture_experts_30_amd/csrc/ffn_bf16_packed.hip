@@ -96,7 +96,7 @@ __device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ ((r ^ (r 
 // The work of one tile with NRB 32-row blocks (compile time, so the MFMA
 // loop has no branches and the fragment reads of a k slice can all be in
 // flight together).
-template <bool kGateUp, int NRB, int D, bool kStream>
+template <bool kGateUp, int NRB, int D, bool kStream, int kBM>
 __device__ __forceinline__ void packed_tile(const PackedArgs& p, u32x4* sA, int g, int row0,
                                             int nrows, int ntile) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -131,7 +131,7 @@ __device__ __forceinline__ void packed_tile(const PackedArgs& p, u32x4* sA, int 
                                             min(step, last) * BK);
   };
   auto astore = [&](const u32x4 (&st)[NRB], int j, int buf) {
-    sA[buf * BM * 8 + swz((tid >> 3) + 32 * j, ch)] = st[j];
+    sA[buf * kBM * 8 + swz((tid >> 3) + 32 * j, ch)] = st[j];
   };
   u32x4 rb[D][8];     // weight fragments [slot][cb * 4 + kk]
   auto bload = [&](u32x4 (&dst)[8], int step) {
@@ -159,7 +159,7 @@ __device__ __forceinline__ void packed_tile(const PackedArgs& p, u32x4* sA, int 
   // refilled with step `ld`; after the slice's last MFMA its two weight
   // fragments, no longer needed, are refilled with step `bld`.
   auto step_body = [&](int buf, u32x4 (&b)[8], u32x4 (&st)[NRB], int nbuf, int ld, int bld) {
-    const u32x4* as = sA + buf * BM * 8;
+    const u32x4* as = sA + buf * kBM * 8;
     const u32x4* bsrc = bw + (int64_t)min(bld, last) * FRAG;
     bf16x8 a[2][NRB];
 #pragma unroll
@@ -283,9 +283,11 @@ __global__ void __launch_bounds__(NT, 1) grouped_gemm_bf16_packed(PackedArgs p) 
   const bool stream = ent[4] == 1;
   switch (((nrows + 31) >> 5) * 2 + (stream ? 1 : 0)) {
 #define MOE_TILE_CASE(n)                                                                      \
-    case 2 * n: packed_tile<kGateUp, n, depth_for(n), false>(p, smem, g, row0, nrows, ntile); \
+    case 2 * n:                                                                               \
+      packed_tile<kGateUp, n, depth_for(n), false, BM>(p, smem, g, row0, nrows, ntile);       \
       break;                                                                                  \
-    case 2 * n + 1: packed_tile<kGateUp, n, depth_for(n), true>(p, smem, g, row0, nrows, ntile); \
+    case 2 * n + 1:                                                                           \
+      packed_tile<kGateUp, n, depth_for(n), true, BM>(p, smem, g, row0, nrows, ntile);        \
       break;
     MOE_TILE_CASE(1)
     MOE_TILE_CASE(2)
@@ -296,8 +298,47 @@ __global__ void __launch_bounds__(NT, 1) grouped_gemm_bf16_packed(PackedArgs p) 
     MOE_TILE_CASE(7)
 #undef MOE_TILE_CASE
     default:
-      if (stream) packed_tile<kGateUp, 8, depth_for(8), true>(p, smem, g, row0, nrows, ntile);
-      else packed_tile<kGateUp, 8, depth_for(8), false>(p, smem, g, row0, nrows, ntile);
+      if (stream) packed_tile<kGateUp, 8, depth_for(8), true, BM>(p, smem, g, row0, nrows, ntile);
+      else packed_tile<kGateUp, 8, depth_for(8), false, BM>(p, smem, g, row0, nrows, ntile);
+      break;
+  }
+}
+
+// Two workgroups per CU: tiles of at most BM2 = 128 rows, a single register
+// stage for weights and activations (each weight fragment is refilled for
+// the next step right after its last use), so that a wave fits in 256
+// registers and two waves share each SIMD, one computing while the other
+// waits.  Used for the down projection, whose k dimension (the FFN width) is
+// short: with 8 waves per CU the pipeline start of one tile overlaps the
+// steady state of the other.
+constexpr int BM2 = kMinTileRows;
+constexpr size_t kLdsP2 = (size_t)2 * BM2 * 8 * sizeof(u32x4);   // 32 KiB
+
+template <bool kGateUp>
+__global__ void __launch_bounds__(NT, 2) grouped_gemm_bf16_packed_x2(PackedArgs p) {
+  extern __shared__ u32x4 smem[];
+  const int64_t work = (int64_t)p.tiles[0] * p.ntn;
+  const int64_t per = (work + kNumXcd - 1) / kNumXcd;
+  const int64_t q = blockIdx.x / kNumXcd;
+  const int64_t w = (int64_t)(blockIdx.x % kNumXcd) * per + q;
+  if (q >= per || w >= work) return;
+  int ntile;
+  const int32_t* ent = decode_work(p.tiles, w, p.ntn, ntile);
+  const int g = ent[0], row0 = ent[1], nrows = ent[2];
+  if (ntile >= ((g == p.E) ? p.nt_s : p.nt_r)) return;
+  const bool stream = ent[4] == 1;
+  switch (((nrows + 31) >> 5) * 2 + (stream ? 1 : 0)) {
+#define MOE_TILE_CASE(n)                                                            \
+    case 2 * n: packed_tile<kGateUp, n, 1, false, BM2>(p, smem, g, row0, nrows, ntile); \
+      break;                                                                        \
+    case 2 * n + 1: packed_tile<kGateUp, n, 1, true, BM2>(p, smem, g, row0, nrows, ntile); \
+      break;
+    MOE_TILE_CASE(1)
+    MOE_TILE_CASE(2)
+    MOE_TILE_CASE(3)
+    MOE_TILE_CASE(4)
+#undef MOE_TILE_CASE
+    default:
       break;
   }
 }
@@ -413,8 +454,8 @@ hipError_t set_attrs_packed() {
     hipError_t e = hipFuncSetAttribute((const void*)grouped_gemm_bf16_packed<true>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsP);
     if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void*)grouped_gemm_bf16_packed<false>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsP);
+      e = hipFuncSetAttribute((const void*)grouped_gemm_bf16_packed_x2<false>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsP2);
     return e;
   }();
   return once;
@@ -524,10 +565,15 @@ hipError_t launch_ffn_bf16_packed(const FfnDims& d, const uint16_t* x, const int
     MOE_TIMED_LAUNCH(s, "grouped_gemm_bf16_packed_few<false, 2>",
       hipLaunchKernelGGL((grouped_gemm_bf16_packed_few<false, 2>), dim3(grid(mt * a2.ntn)),
                          dim3(NT), 0, s, a2));
-  else
-    MOE_TIMED_LAUNCH(s, "grouped_gemm_bf16_packed<false>",
-      hipLaunchKernelGGL(grouped_gemm_bf16_packed<false>, dim3(grid(mt * a2.ntn)), dim3(NT), kLdsP,
-                         s, a2));
+  else {
+    // The down projection uses 128-row tiles, two workgroups per CU.
+    e = launch_build_tiles(offsets, d.E, d.T, d.Is > 0, BM2, tiles, s);
+    if (e != hipSuccess) return e;
+    const int64_t mt2 = ffn_max_mtiles(d.N, d.T, d.E, BM2);
+    MOE_TIMED_LAUNCH(s, "grouped_gemm_bf16_packed_x2<false>",
+      hipLaunchKernelGGL(grouped_gemm_bf16_packed_x2<false>, dim3(grid(mt2 * a2.ntn)), dim3(NT),
+                         kLdsP2, s, a2));
+  }
   return hipGetLastError();
 }
 

@@ -260,7 +260,9 @@ def test_kernel_timer_names_every_launch():
                  "combine_bf16_kernel"):
         assert name in kt, name
         ms, n = kt[name]
-        assert n == 3 and ms > 0, (name, ms, n)
+        # one launch per forward (the tile list may be built once per GEMM)
+        assert n % 3 == 0 and 3 <= n <= (6 if name == "build_tiles_kernel" else 3), (name, n)
+        assert ms > 0, (name, ms)
     # restricted to one kernel
     moe.moe_kernel_timer_enable(True, "combine_bf16_kernel")
     run_forward(cfg, dev, cfg.T)
