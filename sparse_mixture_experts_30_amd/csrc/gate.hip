@@ -11,8 +11,9 @@
 // three bf16 parts (hi = w truncated to bf16, mid = (w - hi) truncated,
 // lo = w - hi - mid, which has at most 8 significant bits).  Each product of a
 // bf16 x with a bf16 part is exact in fp32, so three bf16 MFMAs accumulated in
-// fp32 give an fp32-accurate x w^T at bf16-MFMA rate.  The split is done on
-// the fly from the fp32 weight tile in LDS.
+// fp32 give an fp32-accurate x w^T at bf16-MFMA rate.  The split is done once
+// per call by a small kernel that also lays the three parts out in MFMA
+// fragment order; the GEMM then streams them straight into registers.
 #include "moe_internal.hpp"
 
 #include <float.h>
@@ -21,15 +22,15 @@ namespace moe {
 
 namespace {
 
-constexpr int GBM = 64;    // tokens per tile
-constexpr int GBN = 128;   // experts per tile
-constexpr int GBK = 64;    // k per stage
+constexpr int GBM = 128;   // tokens per tile
+constexpr int GEB = 4;     // 32-expert blocks per tile (one per wave)
+constexpr int GBK = 64;    // k per step
 constexpr int GTHREADS = 256;
+constexpr int GFRAG = 3 * 4 * 64;   // 16-byte fragments per (expert block, step)
 
 // Split 8 fp32 weights into hi/mid/lo bf16x8 operands (exact decomposition).
-__device__ __forceinline__ void split3(u32x4 p, u32x4 q, bf16x8& hi, bf16x8& mid, bf16x8& lo) {
+__device__ __forceinline__ void split3(u32x4 p, u32x4 q, u32x4& h, u32x4& m, u32x4& l) {
   const uint32_t v[8] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
-  u32x4 h, m, l;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     uint32_t hb[2], mb[2], lb[2];
@@ -47,116 +48,141 @@ __device__ __forceinline__ void split3(u32x4 p, u32x4 q, bf16x8& hi, bf16x8& mid
     m[j] = mb[0] | (mb[1] << 16);
     l[j] = lb[0] | (lb[1] << 16);
   }
-  hi = as_bf16x8(h);
-  mid = as_bf16x8(m);
-  lo = as_bf16x8(l);
 }
 
-// partials[ks][t][e] = sum over the ks-th slice of H of x[t,h] w[e,h].
-// Tile 64 tokens x 128 experts; 4 waves, wave w owns experts [32w, 32w+32)
-// for all 64 tokens (two 32x32 MFMA blocks).  LDS tiles are XOR-swizzled by
-// 16-byte chunk so that MFMA operand reads are bank-conflict free.
-__global__ void __launch_bounds__(GTHREADS)
-gate_logits_bf16_kernel(const uint16_t* __restrict__ x, const float* __restrict__ wg,
-                        float* __restrict__ part, int64_t T, int H, int E, int hslice) {
-  __shared__ u32x4 sA[2][GBM * 8];    // [row][8 chunks of 8 bf16]
-  __shared__ u32x4 sB[2][GBN * 16];   // [row][16 chunks of 4 fp32]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// wp block (eb, step) = [part 3][k slice 4][lane 64] x 16 bytes: lane l of
+// slice kk holds expert 32 eb + l%32 (zero past E) at k = 64 step +
+// 32 (l / 32) + 8 kk .. +8, as bf16 part hi, mid or lo.
+__global__ void __launch_bounds__(256)
+gate_split_kernel(const float* __restrict__ wg, u32x4* __restrict__ wp, int E, int H,
+                  int64_t nslot) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;   // (eb, step, kk, lane)
+  if (c >= nslot) return;
+  const int nsteps = H / GBK;
+  const int lane = (int)(c & 63), kk = (int)((c >> 6) & 3);
+  const int64_t rest = c >> 8;
+  const int step = (int)(rest % nsteps);
+  const int64_t eb = rest / nsteps;
+  const int e = (int)(eb * 32 + (lane & 31));
+  const int k = step * GBK + 32 * (lane >> 5) + 8 * kk;
+  u32x4 p = {0, 0, 0, 0}, q = {0, 0, 0, 0};
+  if (e < E) {
+    p = *reinterpret_cast<const u32x4*>(wg + (int64_t)e * H + k);
+    q = *reinterpret_cast<const u32x4*>(wg + (int64_t)e * H + k + 4);
+  }
+  u32x4 h, m, l;
+  split3(p, q, h, m, l);
+  u32x4* dst = wp + (eb * nsteps + step) * GFRAG + kk * 64 + lane;
+  dst[0] = h;
+  dst[256] = m;
+  dst[512] = l;
+}
+
+__device__ __forceinline__ int gswz(int r, int c) { return r * 8 + (c ^ ((r ^ (r >> 3)) & 7)); }
+
+// partials[ks][t][e] = sum over the ks-th k range of x[t,h] w[e,h].
+// Tile: 128 tokens x 128 experts; wave w owns expert block 4 blockIdx.y + w
+// (32 experts) for all 128 tokens (four 32x32 MFMA blocks, each fed by the
+// three weight parts).  The token tile is shared through double-buffered,
+// XOR-swizzled LDS; the weight parts go straight from the split copy into
+// registers, one step ahead.  Two workgroups share a CU.
+__global__ void __launch_bounds__(GTHREADS, 2)
+gate_logits_bf16_kernel(const uint16_t* __restrict__ x, const u32x4* __restrict__ wp,
+                        float* __restrict__ part, int64_t T, int H, int E, int neb,
+                        int steps_per_split) {
+  __shared__ u32x4 sA[2][GBM * 8];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 31, lh = lane >> 5;
   const int64_t m0 = (int64_t)blockIdx.x * GBM;
-  const int n0 = blockIdx.y * GBN;
+  const int eb = blockIdx.y * GEB + wave;
+  const bool active = eb < neb;
+  const int ebc = active ? eb : neb - 1;        // idle waves re-read a valid block
   const int ks = blockIdx.z;
-  const int kbeg = ks * hslice;
-  const int nsteps = hslice / GBK;
+  const int nsteps_all = H / GBK;
+  const int s0 = ks * steps_per_split;
+  const int nsteps = min(nsteps_all, s0 + steps_per_split) - s0;
+  const int last = nsteps - 1;
+  if (nsteps <= 0) return;                      // uniform over the workgroup
 
-  // Global->register staging: A 2 chunks, B 8 chunks per thread.  Rows past
-  // the end of x or of the experts re-read the last row (results dropped), so
-  // every load is unconditional.
-  u32x4 ra[2], rb[8];
-  auto gload = [&](int step) {
-    const int k0 = kbeg + step * GBK;
+  // Token rows staged by this thread: (tid / 8) + 32 j, chunk tid % 8; rows
+  // past T re-read row T - 1 (results dropped).
+  const int ch = tid & 7;
+  const uint16_t* arow[4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      int c = tid + j * GTHREADS;       // 0..511
-      int row = c >> 3, ch = c & 7;
-      const int64_t t = min(m0 + row, T - 1);
-      ra[j] = *reinterpret_cast<const u32x4*>(x + t * H + k0 + ch * 8);
-    }
+  for (int j = 0; j < 4; ++j) {
+    const int64_t t = min(m0 + (tid >> 3) + 32 * j, T - 1);
+    arow[j] = x + t * H + s0 * GBK + ch * 8;
+  }
+  const u32x4* bsrc = wp + ((int64_t)ebc * nsteps_all + s0) * GFRAG + lane;
+  u32x4 ra[4], rb[2][12];
+  auto aload = [&](int step) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      int c = tid + j * GTHREADS;       // 0..2047
-      int row = c >> 4, ch = c & 15;
-      const int e = min(n0 + row, E - 1);
-      rb[j] = *reinterpret_cast<const u32x4*>(wg + (int64_t)e * H + k0 + ch * 4);
-    }
+    for (int j = 0; j < 4; ++j)
+      ra[j] = *reinterpret_cast<const u32x4*>(arow[j] + min(step, last) * GBK);
   };
-  auto sstore = [&](int buf) {
+  auto astore = [&](int buf) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      int c = tid + j * GTHREADS;
-      int row = c >> 3, ch = c & 7;
-      sA[buf][row * 8 + (ch ^ (row & 7))] = ra[j];
-    }
+    for (int j = 0; j < 4; ++j) sA[buf][gswz((tid >> 3) + 32 * j, ch)] = ra[j];
+  };
+  auto bload = [&](int slot, int step) {
+    const u32x4* src = bsrc + (int64_t)min(step, last) * GFRAG;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      int c = tid + j * GTHREADS;
-      int row = c >> 4, ch = c & 15;
-      sB[buf][row * 16 + (ch ^ (row & 15))] = rb[j];
-    }
+    for (int i = 0; i < 12; ++i) rb[slot][i] = src[i * 64];   // [part][kk]
   };
 
-  f32x16 acc[2];
+  f32x16 acc[4];
 #pragma unroll
-  for (int r = 0; r < 2; ++r)
+  for (int r = 0; r < 4; ++r)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[r][i] = 0.0f;
 
-  gload(0);
-  sstore(0);
-  if (nsteps > 1) gload(1);
+  aload(0);
+  bload(0, 0);
+  astore(0);
+  aload(1);
+  bload(1, 1);
   __syncthreads();
 
-  const int lr = lane & 31, lh = lane >> 5;
-  for (int step = 0; step < nsteps; ++step) {
-    const int buf = step & 1;
+  auto step_body = [&](int buf, int u, int step) {
+    const u32x4* as = sA[buf];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {          // 4 x 16 k
-      bf16x8 a[2];
+    for (int kk = 0; kk < 4; ++kk) {
+      bf16x8 a[4];
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        int row = r * 32 + lr;
-        int ch = 2 * kk + lh;
-        a[r] = as_bf16x8(sA[buf][row * 8 + (ch ^ (row & 7))]);
-      }
-      int brow = wave * 32 + lr;
-      int c0 = 4 * kk + 2 * lh;
-      const u32x4 p = sB[buf][brow * 16 + (c0 ^ (brow & 15))];
-      const u32x4 q = sB[buf][brow * 16 + ((c0 + 1) ^ (brow & 15))];
-      bf16x8 bh, bm, bl;
-      split3(p, q, bh, bm, bl);
+      for (int r = 0; r < 4; ++r) a[r] = as_bf16x8(as[gswz(r * 32 + lr, 4 * lh + kk)]);
+      if (active) {
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[r], bh, acc[r], 0, 0, 0);
-        acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[r], bm, acc[r], 0, 0, 0);
-        acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[r], bl, acc[r], 0, 0, 0);
+        for (int pt = 0; pt < 3; ++pt) {
+          const bf16x8 b = as_bf16x8(rb[u][pt * 4 + kk]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[r], b, acc[r], 0, 0, 0);
+        }
       }
     }
-    if (step + 1 < nsteps) {
-      sstore(buf ^ 1);
-      if (step + 2 < nsteps) gload(step + 2);
-    }
+    astore(buf ^ 1);
+    aload(step + 2);
+    bload(u, step + 2);
     __syncthreads();
+  };
+  int s = 0;
+  for (; s + 2 <= nsteps; s += 2) {
+    step_body(0, 0, s);
+    step_body(1, 1, s + 1);
   }
+  if (s < nsteps) step_body(0, 0, s);
 
   // C layout of a 32x32 MFMA block: lane holds column lane%32 and rows
   // 8*(i/4) + 4*(lane/32) + i%4 for i = 0..15.
-  const int e = n0 + wave * 32 + lr;
-  if (e < E) {
+  const int e = eb * 32 + lr;
+  if (active && e < E) {
     float* base = part + (int64_t)ks * T * E;
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
+    for (int r = 0; r < 4; ++r)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        int64_t t = m0 + r * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
+        const int64_t t = m0 + r * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
         if (t < T) base[t * E + e] = acc[r][i];
       }
   }
@@ -301,20 +327,35 @@ select_kernel(const float* __restrict__ part, int ksplit, const float* __restric
 }  // namespace
 
 int gate_ksplit(int64_t T, int H, int E) {
-  if (H % GBK) return 1;
-  int64_t tiles = ((T + GBM - 1) / GBM) * ((E + GBN - 1) / GBN);
+  const int nsteps = H / GBK;
+  if (H % GBK || nsteps < 1) return 1;
+  const int64_t tiles = ((T + GBM - 1) / GBM) * ((gate_expert_blocks(E) + GEB - 1) / GEB);
   int ks = 1;
-  while (ks < 8 && tiles * ks < 512 && H % (GBK * ks * 2) == 0) ks *= 2;
+  while (ks < 8 && tiles * ks < 512 && nsteps / (ks * 2) >= 4) ks *= 2;
   return ks;
 }
 
-hipError_t launch_gate_logits(const void* x, bool x_bf16, const float* gate_w, float* partials,
-                              int64_t T, int H, int E, int ksplit, hipStream_t s) {
+int gate_expert_blocks(int E) { return (E + 31) / 32; }
+
+size_t gate_split_bytes(int H, int E) {
+  return (size_t)gate_expert_blocks(E) * (H / GBK) * GFRAG * sizeof(u32x4);
+}
+
+hipError_t launch_gate_logits(const void* x, bool x_bf16, const float* gate_w, void* wsplit,
+                              float* partials, int64_t T, int H, int E, int ksplit,
+                              hipStream_t s) {
   if (x_bf16) {
-    dim3 grid((unsigned)((T + GBM - 1) / GBM), (E + GBN - 1) / GBN, ksplit);
+    const int neb = gate_expert_blocks(E);
+    const int64_t nslot = (int64_t)neb * (H / GBK) * 256;
+    MOE_TIMED_LAUNCH(s, "gate_split_kernel",
+      hipLaunchKernelGGL(gate_split_kernel, dim3((unsigned)((nslot + 255) / 256)), dim3(256), 0,
+                         s, gate_w, (u32x4*)wsplit, E, H, nslot));
+    const int nsteps = H / GBK;
+    const int spk = (nsteps + ksplit - 1) / ksplit;
+    dim3 grid((unsigned)((T + GBM - 1) / GBM), (neb + GEB - 1) / GEB, ksplit);
     MOE_TIMED_LAUNCH(s, "gate_logits_bf16_kernel",
       hipLaunchKernelGGL(gate_logits_bf16_kernel, grid, dim3(GTHREADS), 0, s,
-                         (const uint16_t*)x, gate_w, partials, T, H, E, H / ksplit));
+                         (const uint16_t*)x, (const u32x4*)wsplit, partials, T, H, E, neb, spk));
   } else {
     dim3 grid((unsigned)((T + 15) / 16), (E + 15) / 16);
     MOE_TIMED_LAUNCH(s, "gate_logits_f32_kernel",

@@ -76,7 +76,8 @@ size_t act_bytes(const moe_config* c) { return c->act_dtype == MOE_BF16 ? 2 : 4;
 
 // Workspace segments (byte offsets, 256-aligned).
 struct Layout {
-  size_t err, part, idx, w, counts, offsets, perm, pos, hist, tiles, h, hs, xq, xs, y, ys, total;
+  size_t err, part, gsplit, idx, w, counts, offsets, perm, pos, hist, tiles, h, hs, xq, xs, y, ys,
+      total;
   int ksplit;
 };
 
@@ -95,6 +96,7 @@ Layout layout(const moe_config* c, int64_t T) {
   };
   L.err = take(sizeof(int32_t));
   L.part = take((size_t)L.ksplit * T * E * 4);
+  L.gsplit = c->act_dtype == MOE_BF16 ? take(moe::gate_split_bytes((int)H, (int)E)) : o;
   L.idx = take((size_t)N * 4);
   L.w = take((size_t)N * 4);
   L.counts = take((size_t)E * 4);
@@ -156,8 +158,8 @@ moe_status run_gate(const moe_config* c, int64_t T, const void* x, const float* 
                     const Layout& L, hipStream_t s) {
   float* part = at<float>(ws, L.part);
   const bool bf16 = c->act_dtype == MOE_BF16;
-  HIPCALL(moe::launch_gate_logits(x, bf16, gate_w, part, T, c->hidden_size, c->n_routed_experts,
-                                  L.ksplit, s),
+  HIPCALL(moe::launch_gate_logits(x, bf16, gate_w, at<void>(ws, L.gsplit), part, T,
+                                  c->hidden_size, c->n_routed_experts, L.ksplit, s),
           "gate logits");
   HIPCALL(moe::launch_select(part, L.ksplit, bias, logits, idx, w, T, c->n_routed_experts,
                              c->n_group, c->topk_group, c->num_experts_per_tok,

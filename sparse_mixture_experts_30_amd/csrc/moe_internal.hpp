@@ -78,8 +78,13 @@ class KernelTimerScope {
 
 // ---------------------------------------------------------------- host launchers
 
-hipError_t launch_gate_logits(const void* x, bool x_bf16, const float* gate_w, float* partials,
-                              int64_t T, int H, int E, int ksplit, hipStream_t s);
+// Gate: the fp32 weight is split into three bf16 parts in `wsplit`
+// (gate_split_bytes) and multiplied on bf16 MFMA; partials [ksplit, T, E].
+hipError_t launch_gate_logits(const void* x, bool x_bf16, const float* gate_w, void* wsplit,
+                              float* partials, int64_t T, int H, int E, int ksplit,
+                              hipStream_t s);
+int gate_expert_blocks(int E);
+size_t gate_split_bytes(int H, int E);
 int gate_ksplit(int64_t T, int H, int E);
 hipError_t launch_select(const float* partials, int ksplit, const float* bias, float* logits_out,
                          int32_t* idx, float* w, int64_t T, int E, int G, int TG, int K,
