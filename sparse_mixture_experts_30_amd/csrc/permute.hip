@@ -46,24 +46,25 @@ hist_kernel(const int32_t* __restrict__ idx, int64_t N, int E, int32_t* __restri
 __global__ void __launch_bounds__(PMAXE)
 scan_kernel(int32_t* __restrict__ hist, int nblk, int E, int32_t* __restrict__ counts,
             int32_t* __restrict__ offsets, int32_t* __restrict__ err) {
+  constexpr int B = 16;   // histogram rows read per batch (independent loads)
   __shared__ int32_t s[PMAXE];
   const int e = threadIdx.x;
   const int64_t ld = E + 1;
+  // Per-expert total over the blocks (thread E also totals the invalid ids).
   int32_t total = 0;
-  if (e < E) {
-    for (int b = 0; b < nblk; ++b) {
-      int32_t v = hist[b * ld + e];
-      hist[b * ld + e] = total;
-      total += v;
+  if (e <= E) {
+    for (int b0 = 0; b0 < nblk; b0 += B) {
+      int32_t v[B];
+#pragma unroll
+      for (int j = 0; j < B; ++j) v[j] = (b0 + j < nblk) ? hist[(b0 + j) * ld + e] : 0;
+#pragma unroll
+      for (int j = 0; j < B; ++j) total += v[j];
     }
-    counts[e] = total;
   }
-  if (e == 0) {
-    int32_t bad = 0;
-    for (int b = 0; b < nblk; ++b) bad += hist[b * ld + E];
-    *err = bad ? 1 : 0;
-  }
-  s[e] = (e < E) ? total : 0;
+  if (e == E) *err = total ? 1 : 0;
+  const int32_t mine = (e < E) ? total : 0;
+  if (e < E) counts[e] = mine;
+  s[e] = mine;
   __syncthreads();
   // Hillis-Steele inclusive scan over experts.
   for (int off = 1; off < PMAXE; off <<= 1) {
@@ -72,10 +73,21 @@ scan_kernel(int32_t* __restrict__ hist, int nblk, int E, int32_t* __restrict__ c
     s[e] += v;
     __syncthreads();
   }
-  int32_t excl = s[e] - ((e < E) ? total : 0);
+  const int32_t excl = s[e] - mine;
   if (e < E) {
     offsets[e] = excl;
-    for (int b = 0; b < nblk; ++b) hist[b * ld + e] += excl;
+    // hist[b][e] becomes the first position of block b's elements of e.
+    int32_t run = excl;
+    for (int b0 = 0; b0 < nblk; b0 += B) {
+      int32_t v[B];
+#pragma unroll
+      for (int j = 0; j < B; ++j) v[j] = (b0 + j < nblk) ? hist[(b0 + j) * ld + e] : 0;
+#pragma unroll
+      for (int j = 0; j < B; ++j) {
+        if (b0 + j < nblk) hist[(b0 + j) * ld + e] = run;
+        run += v[j];
+      }
+    }
   }
   if (e == E - 1) offsets[E] = s[e];
 }
