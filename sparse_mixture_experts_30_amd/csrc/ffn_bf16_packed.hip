@@ -348,20 +348,29 @@ __global__ void __launch_bounds__(NT, 2) grouped_gemm_bf16_packed_x2(PackedArgs 
 // loads its own MFMA operands for them straight from global memory: waves
 // are independent (no LDS, no barrier), use few registers, and two waves
 // share each SIMD, which keeps more weight loads in flight.
+//
+// Workgroups are single waves: a tile's four waves are independent, and
+// with one wave per workgroup the few active tiles of a small batch spread
+// over all CUs instead of queueing behind each other.
+constexpr int kFewSlots = 4;   // waves (packed wave slots) per tile
+
 template <bool kGateUp, int NRB>
-__global__ void __launch_bounds__(NT, 2) grouped_gemm_bf16_packed_few(PackedArgs p) {
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+grouped_gemm_bf16_packed_few(PackedArgs p) {
   constexpr int D = NRB == 1 ? 3 : 2;   // steps of weights + activations in flight
-  const int64_t work = (int64_t)p.tiles[0] * p.ntn;
+  const int64_t work = (int64_t)p.tiles[0] * p.ntn * kFewSlots;
   const int64_t per = (work + kNumXcd - 1) / kNumXcd;
   const int64_t q = blockIdx.x / kNumXcd;
-  const int64_t w = (int64_t)(blockIdx.x % kNumXcd) * per + q;
-  if (q >= per || w >= work) return;
+  const int64_t wi = (int64_t)(blockIdx.x % kNumXcd) * per + q;
+  if (q >= per || wi >= work) return;
+  const int64_t w = wi / kFewSlots;
+  const int wave = (int)(wi % kFewSlots);
   int ntile;
   const int32_t* ent = decode_work(p.tiles, w, p.ntn, ntile);
   const int g = ent[0], row0 = ent[1], nrows = ent[2];
   const bool sh = (g == p.E);
   if (ntile >= (sh ? p.nt_s : p.nt_r)) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
   const int lr = lane & 31, lh = lane >> 5;
   const int ncol = sh ? p.ncol_s : p.ncol_r;
   const int n0 = ntile * (kGateUp ? 128 : 256);
@@ -525,12 +534,12 @@ hipError_t launch_ffn_bf16_packed(const FfnDims& d, const uint16_t* x, const int
   const int few = d.T <= 32 ? 1 : d.T <= 64 ? 2 : 0;
   if (few == 1)
     MOE_TIMED_LAUNCH(s, "grouped_gemm_bf16_packed_few<true, 1>",
-      hipLaunchKernelGGL((grouped_gemm_bf16_packed_few<true, 1>), dim3(grid(mt * a1.ntn)), dim3(NT),
-                         0, s, a1));
+      hipLaunchKernelGGL((grouped_gemm_bf16_packed_few<true, 1>),
+                         dim3(grid(mt * a1.ntn * kFewSlots)), dim3(64), 0, s, a1));
   else if (few == 2)
     MOE_TIMED_LAUNCH(s, "grouped_gemm_bf16_packed_few<true, 2>",
-      hipLaunchKernelGGL((grouped_gemm_bf16_packed_few<true, 2>), dim3(grid(mt * a1.ntn)), dim3(NT),
-                         0, s, a1));
+      hipLaunchKernelGGL((grouped_gemm_bf16_packed_few<true, 2>),
+                         dim3(grid(mt * a1.ntn * kFewSlots)), dim3(64), 0, s, a1));
   else
     MOE_TIMED_LAUNCH(s, "grouped_gemm_bf16_packed<true>",
       hipLaunchKernelGGL(grouped_gemm_bf16_packed<true>, dim3(grid(mt * a1.ntn)), dim3(NT), kLdsP, s,
@@ -559,12 +568,12 @@ hipError_t launch_ffn_bf16_packed(const FfnDims& d, const uint16_t* x, const int
   a2.ldc_r = a2.ldc_s = d.H;
   if (few == 1)
     MOE_TIMED_LAUNCH(s, "grouped_gemm_bf16_packed_few<false, 1>",
-      hipLaunchKernelGGL((grouped_gemm_bf16_packed_few<false, 1>), dim3(grid(mt * a2.ntn)),
-                         dim3(NT), 0, s, a2));
+      hipLaunchKernelGGL((grouped_gemm_bf16_packed_few<false, 1>),
+                         dim3(grid(mt * a2.ntn * kFewSlots)), dim3(64), 0, s, a2));
   else if (few == 2)
     MOE_TIMED_LAUNCH(s, "grouped_gemm_bf16_packed_few<false, 2>",
-      hipLaunchKernelGGL((grouped_gemm_bf16_packed_few<false, 2>), dim3(grid(mt * a2.ntn)),
-                         dim3(NT), 0, s, a2));
+      hipLaunchKernelGGL((grouped_gemm_bf16_packed_few<false, 2>),
+                         dim3(grid(mt * a2.ntn * kFewSlots)), dim3(64), 0, s, a2));
   else {
     // The down projection uses 128-row tiles, two workgroups per CU.
     e = launch_build_tiles(offsets, d.E, d.T, d.Is > 0, BM2, tiles, s);
