@@ -103,7 +103,15 @@ gate_logits_bf16_kernel(const uint16_t* __restrict__ x, const u32x4* __restrict_
   const int s0 = ks * steps_per_split;
   const int nsteps = min(nsteps_all, s0 + steps_per_split) - s0;
   const int last = nsteps - 1;
-  if (nsteps <= 0) return;                      // uniform over the workgroup
+  if (nsteps <= 0) {                            // an empty split contributes zero
+    const int e = eb * 32 + lr;
+    if (active && e < E)
+      for (int r = 0; r < GBM / 2; ++r) {
+        const int64_t t = m0 + 2 * r + lh;
+        if (t < T) part[((int64_t)ks * T + t) * E + e] = 0.0f;
+      }
+    return;                                     // uniform over the workgroup
+  }
 
   // Token rows staged by this thread: (tid / 8) + 32 j, chunk tid % 8; rows
   // past T re-read row T - 1 (results dropped).
@@ -330,8 +338,11 @@ int gate_ksplit(int64_t T, int H, int E) {
   const int nsteps = H / GBK;
   if (H % GBK || nsteps < 1) return 1;
   const int64_t tiles = ((T + GBM - 1) / GBM) * ((gate_expert_blocks(E) + GEB - 1) / GEB);
+  // Enough k splits for ~512 workgroups; small batches split k finely so
+  // that the weight stream is spread over many CUs.
+  // Splits divide the k steps evenly, so that every split has work.
   int ks = 1;
-  while (ks < 8 && tiles * ks < 512 && nsteps / (ks * 2) >= 4) ks *= 2;
+  while (ks < 32 && tiles * ks < 512 && nsteps % (ks * 2) == 0 && nsteps / (ks * 2) >= 2) ks *= 2;
   return ks;
 }
 

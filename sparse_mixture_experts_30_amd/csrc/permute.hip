@@ -6,7 +6,7 @@
 // indices f = t*K + k grouped by expert, ascending f inside an expert (a
 // stable sort); pos = inverse of perm.
 //
-// Three launches, no global atomics, deterministic:
+// Three launches (one for a single chunk), no global atomics, deterministic:
 //   1. per-block histograms in LDS over chunks of the flat index range;
 //   2. one block: per-expert totals, exclusive scan over experts, and the
 //      base position of every (block, expert) pair;
@@ -141,6 +141,80 @@ scatter_kernel(const int32_t* __restrict__ idx, int64_t N, int E,
   }
 }
 
+// All three steps in one block of PMAXE threads, for N <= PCHUNK (decode
+// batches), where the launches of the three-kernel path would dominate.
+__global__ void __launch_bounds__(PMAXE)
+permute_small_kernel(const int32_t* __restrict__ idx, int N, int E, int32_t* __restrict__ counts,
+                     int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+                     int32_t* __restrict__ pos, int32_t* __restrict__ err) {
+  constexpr int W = PMAXE / 64;
+  __shared__ int32_t h[PMAXE + 1];   // h[E] counts ids outside [0, E)
+  __shared__ int32_t s[PMAXE];
+  __shared__ int32_t running[PMAXE];
+  __shared__ int32_t wcnt[W][PMAXE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e <= E; e += PMAXE) h[e] = 0;
+  for (int e = tid; e < PMAXE; e += PMAXE)
+#pragma unroll
+    for (int w = 0; w < W; ++w) wcnt[w][e] = 0;
+  __syncthreads();
+  for (int f = tid; f < N; f += PMAXE) {
+    const int e = idx[f];
+    atomicAdd(&h[(e >= 0 && e < E) ? e : E], 1);
+  }
+  __syncthreads();
+  const int32_t mine = (tid < E) ? h[tid] : 0;
+  if (tid < E) counts[tid] = mine;
+  if (tid == 0) *err = h[E] ? 1 : 0;
+  s[tid] = mine;
+  __syncthreads();
+  for (int off = 1; off < PMAXE; off <<= 1) {
+    const int32_t v = (tid >= off) ? s[tid - off] : 0;
+    __syncthreads();
+    s[tid] += v;
+    __syncthreads();
+  }
+  const int32_t excl = s[tid] - mine;
+  if (tid < E) {
+    offsets[tid] = excl;
+    running[tid] = excl;
+  }
+  if (tid == E - 1) offsets[E] = s[tid];
+  __syncthreads();
+  // Stable scatter, PMAXE elements at a time in index order (as scatter_kernel).
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int sub = 0; sub < N; sub += PMAXE) {
+    const int f = sub + tid;
+    int e = (f < N) ? idx[f] : -1;
+    const bool valid = (e >= 0 && e < E);
+    if (!valid) e = -1;
+    uint64_t peers = ~0ull;
+#pragma unroll
+    for (int bit = 0; bit < 10; ++bit) {
+      const bool b = (e >> bit) & 1;
+      const uint64_t m = __ballot(b);
+      peers &= b ? m : ~m;
+    }
+    const int rank = __popcll(peers & lt);
+    const bool leader = (peers & lt) == 0;
+    const int cnt = __popcll(peers);
+    if (valid && leader) wcnt[wave][e] = cnt;
+    __syncthreads();
+    if (valid) {
+      int p = running[e] + rank;
+      for (int w = 0; w < wave; ++w) p += wcnt[w][e];
+      perm[p] = f;
+      pos[f] = p;
+    }
+    __syncthreads();
+    if (valid && leader) {
+      atomicAdd(&running[e], cnt);
+      wcnt[wave][e] = 0;
+    }
+    __syncthreads();
+  }
+}
+
 }  // namespace
 
 int permute_nblk(int64_t N) { return (int)((N + PCHUNK - 1) / PCHUNK); }
@@ -149,6 +223,12 @@ hipError_t launch_permute(const int32_t* idx, int64_t N, int E, int32_t* hist, i
                           int32_t* offsets, int32_t* perm, int32_t* pos, int32_t* err,
                           hipStream_t s) {
   const int nblk = permute_nblk(N);
+  if (nblk == 1) {
+    MOE_TIMED_LAUNCH(s, "permute_small_kernel",
+      hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(PMAXE), 0, s, idx, (int)N, E, counts,
+                         offsets, perm, pos, err));
+    return hipGetLastError();
+  }
   MOE_TIMED_LAUNCH(s, "hist_kernel",
     hipLaunchKernelGGL(hist_kernel, dim3(nblk), dim3(PTHREADS), 0, s, idx, N, E, hist));
   MOE_TIMED_LAUNCH(s, "scan_kernel",
