@@ -67,6 +67,8 @@ def lib():
         L.oracle_ffn.restype = ctypes.c_int
         L.oracle_combine.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp]
         L.oracle_combine.restype = None
+        L.oracle_bias_update.argtypes = [i32, vp, ctypes.c_float, vp, vp]
+        L.oracle_bias_update.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -224,3 +226,21 @@ def forward(cfg, inp: dict, tokens=None, quant_act=False):
     sub["x"] = x
     out = layer(cfg, sub, idx, w, quant_act=quant_act)
     return {"logits": lg, "idx": idx, "w": w, "margin": m, "out": out}
+
+
+def bias_update(counts: np.ndarray, gamma: float, bias: np.ndarray) -> np.ndarray:
+    """One load-balancing step of the fp32 selection bias -> new bias [E] float32.
+
+    Each expert's bias moves by gamma toward the mean load sum(counts)/E (up
+    when below it, down when above, unchanged at it), rounded once to fp32;
+    gamma is taken as an fp32 value.
+    """
+    counts = _c(counts, np.int32)
+    bias = _c(bias, np.float32)
+    E = counts.shape[0]
+    assert bias.shape == (E,)
+    out = np.empty(E, np.float32)
+    rc = lib().oracle_bias_update(E, _p(counts), float(np.float32(gamma)), _p(bias), _p(out))
+    if rc:
+        raise ValueError("oracle_bias_update rejected its arguments")
+    return out

@@ -34,6 +34,12 @@
  *   R7  FP8 scale of a tile with max |v| = a: scale = a / 448, codes are the
  *       e4m3 values nearest v * (448 / a) (ties to even, saturating);
  *       an all-zero tile has scale 1 and zero codes.
+ *   R8  the selection bias follows the experts' observed load ([Co-design]
+ *       2.2 keeps it as a buffer updated from load statistics, not from a
+ *       gradient, and prints no rule): each expert's bias moves one fixed
+ *       step gamma toward balance -- up when the expert received fewer rows
+ *       than the mean over experts, down when more, unchanged at exactly the
+ *       mean.  The bias is an fp32 buffer; the step is rounded once to fp32.
  *
  * Every floating-point step here is in double unless it is marked as the
  * fp32 selection contract.  Compile without floating-point contraction.
@@ -571,4 +577,40 @@ void oracle_combine(int64_t T, int32_t K, int32_t H, const double *y, const doub
             out[t * H + m] = acc;
         }
     }
+}
+
+/* ---- selection-bias update ---------------------------------------------- */
+
+/* One load-balancing update of the selection bias (R8).  counts[e] is the
+ * number of rows routed to expert e over the batch (or batches) being
+ * balanced; the mean load is sum(counts) / E.  For every expert:
+ *   counts[e] < mean:  bias += gamma
+ *   counts[e] > mean:  bias -= gamma
+ *   otherwise:         bias unchanged (bit for bit)
+ * gamma is an fp32 value; the new value is computed in double (exact for
+ * the sum of two fp32 values) and rounded once to fp32.  bias_in and
+ * bias_out may alias.  Returns 1 for a negative or non-finite gamma, E < 1 or
+ * a negative count. */
+int oracle_bias_update(int32_t E, const int32_t *counts, float gamma, const float *bias_in,
+                       float *bias_out)
+{
+    if (E < 1 || !(gamma >= 0.0f) || isinf(gamma))
+        return 1;
+    double total = 0.0;
+    for (int32_t e = 0; e < E; ++e) {
+        if (counts[e] < 0)
+            return 1;
+        total += counts[e];
+    }
+    double mean = total / E;
+    for (int32_t e = 0; e < E; ++e) {
+        double b = bias_in[e];
+        if (counts[e] < mean)
+            bias_out[e] = (float)(b + (double)gamma);
+        else if (counts[e] > mean)
+            bias_out[e] = (float)(b - (double)gamma);
+        else
+            bias_out[e] = bias_in[e];
+    }
+    return 0;
 }

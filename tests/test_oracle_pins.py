@@ -460,3 +460,82 @@ def test_combine_formula_on_random_rows():
     ref = ys + np.einsum("tk,tkh->th", w, y[pos.reshape(T, K)])
     np.testing.assert_allclose(out, ref, rtol=1e-14, atol=1e-14)
     np.testing.assert_allclose(oracle.combine(y, None, pos, w, K), ref - ys, rtol=1e-13, atol=1e-14)
+
+
+# ---------------------------------------------------------------- bias update
+
+def _bias_cases():
+    with open(os.path.join(GOLD, "bias_update_hand_cases.json")) as f:
+        return json.load(f)["cases"]
+
+
+def _f32(vals):
+    return np.array([float(v) for v in vals], np.float32)
+
+
+@pytest.mark.parametrize("case", _bias_cases(), ids=lambda c: c["name"])
+def test_bias_update_hand_cases(case):
+    out = oracle.bias_update(np.array(case["counts"]), case["gamma"], _f32(case["bias"]))
+    if "expected_bits" in case:
+        want = np.array(case["expected_bits"], np.uint32)
+    else:
+        want = _f32(case["expected"]).view(np.uint32)
+    assert out.view(np.uint32).tolist() == want.tolist()
+
+
+def test_bias_update_rejects_bad_arguments():
+    b = np.zeros(3, np.float32)
+    for gamma in (-0.1, float("nan"), float("inf")):
+        with pytest.raises(ValueError):
+            oracle.bias_update(np.array([1, 2, 3]), gamma, b)
+    with pytest.raises(ValueError):
+        oracle.bias_update(np.array([1, -2, 3]), 0.1, b)
+
+
+def test_bias_update_moves_depend_on_counts_only():
+    # With dyadic biases and step every sum is exact, so adding a constant to
+    # every bias adds it to every result: the moves are the same.
+    rng = np.random.default_rng(5)
+    counts = rng.integers(0, 40, 64)
+    b = (rng.integers(-1024, 1024, 64) / 1024.0).astype(np.float32)
+    gamma = 2.0 ** -8
+    d0 = oracle.bias_update(counts, gamma, b).astype(np.float64) - b
+    d1 = oracle.bias_update(counts, gamma, b + np.float32(0.5)).astype(np.float64) - (b + 0.5)
+    assert np.array_equal(d0, d1)
+    mean = counts.sum() / 64
+    assert np.array_equal(np.sign(d0), np.sign(mean - counts) * (gamma > 0))
+
+
+def test_bias_update_is_permutation_equivariant():
+    rng = np.random.default_rng(6)
+    counts = rng.integers(0, 9, 33)
+    b = rng.standard_normal(33).astype(np.float32)
+    p = rng.permutation(33)
+    out = oracle.bias_update(counts, 0.01, b)
+    outp = oracle.bias_update(counts[p], 0.01, b[p])
+    assert np.array_equal(out[p].view(np.uint32), outp.view(np.uint32))
+
+
+def test_bias_update_balances_a_skewed_router():
+    # Closed loop on a small group-limited router: route, count, update.  A
+    # bias that favours three experts is driven back toward the mean load;
+    # a sign slip in the update would make the imbalance grow instead.
+    cfg = Shape(H=1, E=16, G=4, TG=2, K=2, I=0, Is=0, rho=1.0)
+    rng = np.random.default_rng(7)
+    lg = rng.standard_normal((512, 16))
+    bias = np.zeros(16, np.float32)
+    bias[:3] = 0.5
+
+    def imbalance(b):
+        idx, _, _ = oracle.route_f64(cfg, lg, b)
+        counts, _, _, _ = oracle.permute(idx, 16)
+        return counts, counts.max() / counts.mean()
+
+    _, start = imbalance(bias)
+    history = []
+    for _ in range(400):
+        counts, r = imbalance(bias)
+        history.append(r)
+        bias = oracle.bias_update(counts, 0.005, bias)
+    assert start > 2.0
+    assert np.mean(history[-50:]) < 1.25
