@@ -243,6 +243,28 @@ def main():
     cnt = counts.cpu().numpy()
     active = int((cnt > 0).sum())
 
+    # Load-balancing update of the selection bias from this batch's counts:
+    # the training-step follow-up to the forward, not part of the layer step.
+    # One launch reads E counts and reads and writes E biases (12 E bytes),
+    # a single workgroup: launch latency bound.  Timed on a copy of the bias.
+    bias_copy = d["bias"].clone()
+    nbu = 200
+    moe.moe_bias_update(C, counts, 1e-3, bias_copy, stream=stream)
+    torch.cuda.synchronize()
+    moe.moe_kernel_timer_read()
+    moe.moe_kernel_timer_enable(True, "bias_update_kernel")
+    eb0, eb1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    eb0.record(stream)
+    for _ in range(nbu):
+        moe.moe_bias_update(C, counts, 1e-3, bias_copy, stream=stream)
+    eb1.record(stream)
+    torch.cuda.synchronize()
+    moe.moe_kernel_timer_enable(False)
+    bu_ms, bu_launches = moe.moe_kernel_timer_read()["bias_update_kernel"]
+    bias_update = {"kernel_us": round(bu_ms / bu_launches * 1e3, 2),
+                   "calls_per_s": round(nbu / (eb0.elapsed_time(eb1) * 1e-3), 1),
+                   "bytes_per_launch": 12 * E, "bound": "launch latency (one workgroup)"}
+
     # Algorithmic work (routed rows only; active experts' weights only).
     wbytes = 1 if cfg.wdtype == "fp8" else (2 if cfg.wdtype == "bf16" else 4)
     abytes = 2 if cfg.act == "bf16" else 4
@@ -315,6 +337,7 @@ def main():
         "phases_ms": {p: round(v, 4) for p, v in acc.items()},
         "kernels_ms": {k: round(v, 4) for k, v in sorted(kernels_ms.items())},
         "expert_ffn": ffn,
+        "bias_update": bias_update,
         "roofline": roof,
     }
 

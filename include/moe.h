@@ -183,6 +183,24 @@ moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const mo
 moe_status moe_quantize_act(const moe_config* cfg, int64_t rows, const void* x, uint8_t* xq,
                             float* xs, void* stream);
 
+/* Load-balancing update of the selection bias.  The bias takes part only in
+ * choosing experts and is steered by the experts' observed load instead of
+ * a gradient ("从 1024 块 GPU 到 558 万美元：拆解 DeepSeek-V3 的算法-系统协同设计",
+ * section 2.2, where the bias is a buffer updated from load statistics; the
+ * page gives no formula).  Rule: with mean = sum(counts) / E, each expert's
+ * bias becomes bias + gamma if counts[e] < mean, bias - gamma if
+ * counts[e] > mean, and stays bit-identical otherwise; one fp32 add,
+ * round-to-nearest-even.  The comparison with the mean is exact.
+ *   counts [E] int32 in (device): rows per expert, e.g. the counts written
+ *          by moe_permute or moe_forward, or their sum over several batches;
+ *          a negative entry leaves the whole bias unchanged.
+ *   bias   [E] fp32 in/out (device): updated in place; stream-ordered with
+ *          the gate calls that read it.
+ *   gamma  step, finite and >= 0 (MOE_ERR_INVALID_ARG otherwise).
+ * Enqueues one small kernel; no workspace. */
+moe_status moe_bias_update(const moe_config* cfg, const int32_t* counts, float gamma,
+                           float* bias, void* stream);
+
 /* Weight streaming layout for the expert GEMMs.  The grouped GEMM reads
  * each weight matrix once per call; in row-major order that is one short
  * piece per weight row per k step, rows a whole row length apart.  The packed

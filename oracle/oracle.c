@@ -18,7 +18,7 @@
  *   [mqxn]       mqxn.cn/news/19449, section 3.1: the FFN is SwiGLU.
  *
  * Readings where the pages are silent or ambiguous (each is repeated at the
- * step it affects):
+ * step it affects; R8-R10 concern only the GPU path and are not listed):
  *   R1  ties in every top-k go to the lower index; the top_k slots are in
  *       descending order of the masked choice score (the printed code uses
  *       topk(..., sorted=False), which fixes neither).
@@ -34,7 +34,7 @@
  *   R7  FP8 scale of a tile with max |v| = a: scale = a / 448, codes are the
  *       e4m3 values nearest v * (448 / a) (ties to even, saturating);
  *       an all-zero tile has scale 1 and zero codes.
- *   R8  the selection bias follows the experts' observed load ([Co-design]
+ *   R11 the selection bias follows the experts' observed load ([Co-design]
  *       2.2 keeps it as a buffer updated from load statistics, not from a
  *       gradient, and prints no rule): each expert's bias moves one fixed
  *       step gamma toward balance -- up when the expert received fewer rows
@@ -581,7 +581,7 @@ void oracle_combine(int64_t T, int32_t K, int32_t H, const double *y, const doub
 
 /* ---- selection-bias update ---------------------------------------------- */
 
-/* One load-balancing update of the selection bias (R8).  counts[e] is the
+/* One load-balancing update of the selection bias (R11).  counts[e] is the
  * number of rows routed to expert e over the batch (or batches) being
  * balanced; the mean load is sum(counts) / E.  For every expert:
  *   counts[e] < mean:  bias += gamma

@@ -18,7 +18,7 @@ MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 EXPORTS = ("moe_workspace_bytes", "moe_gate", "moe_permute", "moe_expert_ffn", "moe_combine",
            "moe_forward", "moe_quantize_act", "moe_packed_bytes", "moe_pack_weight",
            "moe_get_device_error", "moe_strerror", "moe_last_error", "moe_kernel_timer_enable",
-           "moe_kernel_timer_read")
+           "moe_kernel_timer_read", "moe_bias_update")
 MOE_W13, MOE_W2, MOE_WS13, MOE_WS2 = 0, 1, 2, 3
 
 
@@ -65,6 +65,7 @@ def lib():
             "moe_combine": (ctypes.c_int, [cfgp, i64, vp, vp, vp, vp, vp, vp]),
             "moe_forward": (ctypes.c_int, [cfgp, i64, vp, wp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
             "moe_quantize_act": (ctypes.c_int, [cfgp, i64, vp, vp, vp, vp]),
+            "moe_bias_update": (ctypes.c_int, [cfgp, vp, ctypes.c_float, vp, vp]),
             "moe_packed_bytes": (sz, [cfgp, ctypes.c_int]),
             "moe_pack_weight": (ctypes.c_int, [cfgp, ctypes.c_int, vp, vp, vp]),
             "moe_get_device_error": (ctypes.c_int, [vp, sz, vp]),
@@ -159,6 +160,11 @@ def moe_forward(cfg, T, x, w: MoeWeights, out, ws, logits=None, topk_idx=None, t
 def moe_quantize_act(cfg, rows, x, xq, xs, stream=None):
     _check(lib().moe_quantize_act(ctypes.byref(cfg), rows, _ptr(x), _ptr(xq), _ptr(xs),
                                   _stream(stream)))
+
+
+def moe_bias_update(cfg, counts, gamma, bias, stream=None):
+    _check(lib().moe_bias_update(ctypes.byref(cfg), _ptr(counts), float(gamma), _ptr(bias),
+                                 _stream(stream)))
 
 
 def moe_packed_bytes(cfg: MoeConfig, which: int) -> int:

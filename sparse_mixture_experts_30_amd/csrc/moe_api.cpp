@@ -369,6 +369,19 @@ moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const mo
   return MOE_OK;
 }
 
+moe_status moe_bias_update(const moe_config* cfg, const int32_t* counts, float gamma,
+                           float* bias, void* stream) {
+  CHECK(check_cfg(cfg));
+  if (!(gamma >= 0.0f) || isinf(gamma))
+    return fail(MOE_ERR_INVALID_ARG, "gamma must be finite and >= 0");
+  NONNULL(counts);
+  NONNULL(bias);
+  HIPCALL(moe::launch_bias_update(counts, bias, cfg->n_routed_experts, gamma,
+                                  (hipStream_t)stream),
+          "bias update");
+  return MOE_OK;
+}
+
 moe_status moe_quantize_act(const moe_config* cfg, int64_t rows, const void* x, uint8_t* xq,
                             float* xs, void* stream) {
   CHECK(check_cfg(cfg));

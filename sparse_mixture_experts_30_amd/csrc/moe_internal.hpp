@@ -161,4 +161,8 @@ hipError_t launch_ffn_fp8(const FfnDims& d, const uint8_t* xq, const float* xs,
 hipError_t launch_combine(const void* y, const void* ys, const int32_t* pos, const float* w,
                           void* out, int64_t T, int H, int K, bool bf16, hipStream_t s);
 
+// Selection-bias update from per-expert counts (one workgroup, E <= 512).
+hipError_t launch_bias_update(const int32_t* counts, float* bias, int E, float gamma,
+                              hipStream_t s);
+
 }  // namespace moe

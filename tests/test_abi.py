@@ -93,6 +93,15 @@ def test_argument_validation():
     assert L.moe_quantize_act(ctypes.byref(_cfg(act="f32", wdtype="f32")), 4, FAKE, FAKE, FAKE,
                               None) == moe.MOE_ERR_UNSUPPORTED
     assert L.moe_get_device_error(None, 0, None) == moe.MOE_ERR_WORKSPACE
+    # bias update: the step must be finite and >= 0; both arrays are required
+    for gamma in (-1e-3, float("nan"), float("inf")):
+        assert L.moe_bias_update(ctypes.byref(cfg), FAKE, gamma, FAKE,
+                                 None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_bias_update(ctypes.byref(cfg), None, 1e-3, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_bias_update(ctypes.byref(cfg), FAKE, 1e-3, None, None) == moe.MOE_ERR_INVALID_ARG
+    bad = _cfg()
+    bad.n_group = 3
+    assert L.moe_bias_update(ctypes.byref(bad), FAKE, 1e-3, FAKE, None) != moe.MOE_OK
 
 
 def test_workspace_bytes_grows_with_tokens():
