@@ -38,6 +38,7 @@ KERNEL_SOURCES = {
     "grouped_gemm_bf16_packed": ("ffn_bf16_packed.hip", "moe_internal.hpp"),
     "grouped_gemm_bf16_packed_x2": ("ffn_bf16_packed.hip", "moe_internal.hpp"),
     "grouped_gemm_bf16_packed_few": ("ffn_bf16_packed.hip", "moe_internal.hpp"),
+    "grouped_gemm_bf16_packed_wide": ("ffn_bf16_packed.hip", "moe_internal.hpp"),
     "grouped_gemm_fp8_packed": ("ffn_fp8_packed.hip", "moe_internal.hpp"),
     "grouped_gemm_bf16": ("ffn_bf16.hip", "moe_internal.hpp"),
     "grouped_gemm_fp8": ("ffn_fp8.hip", "moe_internal.hpp"),

@@ -95,22 +95,37 @@ __device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ ((r ^ (r 
 
 // The work of one tile with NRB 32-row blocks (compile time, so the MFMA
 // loop has no branches and the fragment reads of a k slice can all be in
-// flight together).
-template <bool kGateUp, int NRB, int D, bool kStream, int kBM>
+// flight together).  NCB is the number of 32-column weight blocks per wave:
+//   NCB = 2: the tile is one packed tile (256 weight rows); wave w takes its
+//            own quarter (packed wave slot w).
+//   NCB = 4: the tile is two adjacent packed tiles (512 weight rows); wave w
+//            takes slots 2 (w % 2) and 2 (w % 2) + 1 of packed tile
+//            2 ntile + w / 2, two contiguous 8 KiB pieces per step.  Each
+//            activation fragment read from LDS then feeds four MFMAs
+//            instead of two, halving the LDS read traffic per MFMA.
+template <bool kGateUp, int NRB, int D, bool kStream, int kBM, int NCB = 2>
 __device__ __forceinline__ void packed_tile(const PackedArgs& p, u32x4* sA, int g, int row0,
                                             int nrows, int ntile) {
+  static_assert(NCB == 2 || NCB == 4, "column blocks per wave");
+  constexpr int NB = 4 * NCB;   // weight fragments per wave per step
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 31, lh = lane >> 5;
   const bool sh = (g == p.E);
   const int ncol = sh ? p.ncol_s : p.ncol_r;
-  const int n0 = ntile * (kGateUp ? 128 : 256);
+  const int nt = sh ? p.nt_s : p.nt_r;
+  // packed tile of this wave and its first wave slot in that tile
+  int wtile = NCB == 2 ? ntile : 2 * ntile + (wave >> 1);
+  const bool wvalid = wtile < nt;   // the second half of a ragged wide tile
+  wtile = min(wtile, nt - 1);
+  const int slot0 = NCB == 2 ? wave : 2 * (wave & 1);
+  const int n0 = wtile * (kGateUp ? 128 : 256);
   const int kdim = sh ? p.kdim_s : p.kdim_r;
   const int nsteps = kdim / BK;
   const int last = nsteps - 1;
   const uint16_t* A = sh ? p.a_s : p.a_r;
   const int64_t lda = sh ? p.lda_s : p.lda_r;
   const u32x4* bw = (sh ? p.b_s : p.b_r + (int64_t)g * p.nt_r * nsteps * FRAG) +
-                    (int64_t)ntile * nsteps * FRAG + wave * 512 + lane;
+                    (int64_t)wtile * nsteps * FRAG + slot0 * 512 + lane;
 
   // Activation rows staged by this thread: r = tid/8 + 32 j (j < NRB),
   // chunk tid % 8 (rows past the tile's end re-read the first row).
@@ -133,19 +148,26 @@ __device__ __forceinline__ void packed_tile(const PackedArgs& p, u32x4* sA, int 
   auto astore = [&](const u32x4 (&st)[NRB], int j, int buf) {
     sA[buf * kBM * 8 + swz((tid >> 3) + 32 * j, ch)] = st[j];
   };
-  u32x4 rb[D][8];     // weight fragments [slot][cb * 4 + kk]
-  auto bload = [&](u32x4 (&dst)[8], int step) {
+  u32x4 rb[D][NB];    // weight fragments [slot][c * 4 + kk], c = column block
+  // Issued in the order the step refills them (slice by slice), so that the
+  // wait counts the compiler merges at the loop head match on both paths.
+  auto bload = [&](u32x4 (&dst)[NB], int step) {
     const u32x4* src = bw + (int64_t)min(step, last) * FRAG;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      dst[i] = kStream ? __builtin_nontemporal_load(src + i * 64) : src[i * 64];
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int c = 0; c < NCB; ++c) {
+        const int i = c * 4 + kk;
+        dst[i] = kStream ? __builtin_nontemporal_load(src + i * 64) : src[i * 64];
+        __builtin_amdgcn_sched_barrier(0);   // keep the issue order
+      }
   };
 
-  f32x16 acc[NRB][2];
+  f32x16 acc[NRB][NCB];
 #pragma unroll
   for (int r = 0; r < NRB; ++r)
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int c = 0; c < NCB; ++c)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[r][c][i] = 0.0f;
 
@@ -158,7 +180,7 @@ __device__ __forceinline__ void packed_tile(const PackedArgs& p, u32x4* sA, int 
   // the next step move from registers `st` to LDS buffer `nbuf` and `st` is
   // refilled with step `ld`; after the slice's last MFMA its two weight
   // fragments, no longer needed, are refilled with step `bld`.
-  auto step_body = [&](int buf, u32x4 (&b)[8], u32x4 (&st)[NRB], int nbuf, int ld, int bld) {
+  auto step_body = [&](int buf, u32x4 (&b)[NB], u32x4 (&st)[NRB], int nbuf, int ld, int bld) {
     const u32x4* as = sA + buf * kBM * 8;
     const u32x4* bsrc = bw + (int64_t)min(bld, last) * FRAG;
     bf16x8 a[2][NRB];
@@ -166,17 +188,20 @@ __device__ __forceinline__ void packed_tile(const PackedArgs& p, u32x4* sA, int 
     for (int r = 0; r < NRB; ++r) a[0][r] = as_bf16x8(as[swz(r * 32 + lr, 4 * lh)]);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const bf16x8 b0 = as_bf16x8(b[kk]);
-      const bf16x8 b1 = as_bf16x8(b[4 + kk]);
+      bf16x8 bf[NCB];
+#pragma unroll
+      for (int c = 0; c < NCB; ++c) bf[c] = as_bf16x8(b[c * 4 + kk]);
       // activation chunk operations of this slice, in order
       constexpr int kOps = 2 * ((NRB + 3) / 4);
       int nop = 0;
 #pragma unroll
       for (int r = 0; r < NRB; ++r) {
-        acc[r][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk & 1][r], b0, acc[r][0], 0, 0, 0);
+        acc[r][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk & 1][r], bf[0], acc[r][0], 0, 0, 0);
         if (kk < 3) a[(kk + 1) & 1][r] = as_bf16x8(as[swz(r * 32 + lr, 4 * lh + kk + 1)]);
-        acc[r][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk & 1][r], b1, acc[r][1], 0, 0, 0);
-        // one activation operation per pair (all of them by the last pair)
+#pragma unroll
+        for (int c = 1; c < NCB; ++c)
+          acc[r][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk & 1][r], bf[c], acc[r][c], 0, 0, 0);
+        // one activation operation per group (all of them by the last group)
         const int upto = (r == NRB - 1) ? kOps : r + 1;
 #pragma unroll
         for (; nop < upto && nop < kOps; ++nop) {
@@ -187,9 +212,10 @@ __device__ __forceinline__ void packed_tile(const PackedArgs& p, u32x4* sA, int 
           }
         }
         if (r == NRB - 1) {
-          b[kk] = kStream ? __builtin_nontemporal_load(bsrc + kk * 64) : bsrc[kk * 64];
-          b[4 + kk] = kStream ? __builtin_nontemporal_load(bsrc + (4 + kk) * 64)
-                              : bsrc[(4 + kk) * 64];
+#pragma unroll
+          for (int c = 0; c < NCB; ++c)
+            b[c * 4 + kk] = kStream ? __builtin_nontemporal_load(bsrc + (c * 4 + kk) * 64)
+                                    : bsrc[(c * 4 + kk) * 64];
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -204,7 +230,10 @@ __device__ __forceinline__ void packed_tile(const PackedArgs& p, u32x4* sA, int 
   // merged over both paths, then wait only for the step about to be used.
   auto aload_all = [&](u32x4 (&st)[NRB], int step) {
 #pragma unroll
-    for (int j = 0; j < NRB; ++j) aload(st, j, step);
+    for (int j = 0; j < NRB; ++j) {
+      aload(st, j, step);
+      __builtin_amdgcn_sched_barrier(0);   // keep the issue order
+    }
   };
   aload_all(ra[0], 0);
 #pragma unroll
@@ -239,6 +268,8 @@ __device__ __forceinline__ void packed_tile(const PackedArgs& p, u32x4* sA, int 
     if (s + u < nsteps) step(s + u, u);
 
   // Epilogue: lane holds column lane%32, rows 8*(i/4) + 4*(lane/32) + i%4.
+  // Column block c of the wave is (packed slot slot0 + c / 2, block c % 2).
+  if (!wvalid) return;
   uint16_t* C = sh ? p.c_s : p.c_r;
   const int64_t ldc = sh ? p.ldc_s : p.ldc_r;
 #pragma unroll
@@ -249,16 +280,19 @@ __device__ __forceinline__ void packed_tile(const PackedArgs& p, u32x4* sA, int 
       if (row >= nrows) continue;
       uint16_t* crow = C + (int64_t)(row0 + row) * ldc;
       if (kGateUp) {
-        const int col = n0 + wave * 32 + lr;
-        if (col < ncol) {
-          const float gv = acc[r][0][i], uv = acc[r][1][i];
-          crow[col] = (uint16_t)f32_to_bf16_bits(gv / (1.0f + __expf(-gv)) * uv);
+#pragma unroll
+        for (int j = 0; j < NCB / 2; ++j) {
+          const int col = n0 + (slot0 + j) * 32 + lr;
+          if (col < ncol) {
+            const float gv = acc[r][2 * j][i], uv = acc[r][2 * j + 1][i];
+            crow[col] = (uint16_t)f32_to_bf16_bits(gv / (1.0f + __expf(-gv)) * uv);
+          }
         }
       } else {
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-          const int col = n0 + wave * 64 + cb * 32 + lr;
-          if (col < ncol) crow[col] = (uint16_t)f32_to_bf16_bits(acc[r][cb][i]);
+        for (int c = 0; c < NCB; ++c) {
+          const int col = n0 + (slot0 + (c >> 1)) * 64 + (c & 1) * 32 + lr;
+          if (col < ncol) crow[col] = (uint16_t)f32_to_bf16_bits(acc[r][c][i]);
         }
       }
     }
@@ -332,6 +366,47 @@ __global__ void __launch_bounds__(NT, 2) grouped_gemm_bf16_packed_x2(PackedArgs 
     case 2 * n: packed_tile<kGateUp, n, 1, false, BM2>(p, smem, g, row0, nrows, ntile); \
       break;                                                                        \
     case 2 * n + 1: packed_tile<kGateUp, n, 1, true, BM2>(p, smem, g, row0, nrows, ntile); \
+      break;
+    MOE_TILE_CASE(1)
+    MOE_TILE_CASE(2)
+    MOE_TILE_CASE(3)
+    MOE_TILE_CASE(4)
+#undef MOE_TILE_CASE
+    default:
+      break;
+  }
+}
+
+// Wide tiles for the gate/up projection of large batches (from 256 routed
+// rows per expert on average, where the matrix work dominates): 128 rows x
+// 512 weight rows, one workgroup per CU, each wave 128 rows x 128 weight rows
+// (four column blocks, so every activation fragment read from LDS feeds four
+// MFMAs).  The down projection keeps the two-workgroup kernel, which is
+// faster there.
+constexpr int kWideMinRows = 256;
+constexpr int BMW = kMinTileRows;
+constexpr size_t kLdsW = (size_t)2 * BMW * 8 * sizeof(u32x4);   // 32 KiB
+
+template <bool kGateUp>
+__global__ void __launch_bounds__(NT, 1) grouped_gemm_bf16_packed_wide(PackedArgs p) {
+  extern __shared__ u32x4 smem[];
+  const int64_t work = (int64_t)p.tiles[0] * p.ntn;
+  const int64_t per = (work + kNumXcd - 1) / kNumXcd;
+  const int64_t q = blockIdx.x / kNumXcd;
+  const int64_t w = (int64_t)(blockIdx.x % kNumXcd) * per + q;
+  if (q >= per || w >= work) return;
+  int ntile;
+  const int32_t* ent = decode_work(p.tiles, w, p.ntn, ntile);
+  const int g = ent[0], row0 = ent[1], nrows = ent[2];
+  if (2 * ntile >= ((g == p.E) ? p.nt_s : p.nt_r)) return;
+  const bool stream = ent[4] == 1;
+  switch (((nrows + 31) >> 5) * 2 + (stream ? 1 : 0)) {
+#define MOE_TILE_CASE(n)                                                                     \
+    case 2 * n:                                                                              \
+      packed_tile<kGateUp, n, 2, false, BMW, 4>(p, smem, g, row0, nrows, ntile);             \
+      break;                                                                                 \
+    case 2 * n + 1:                                                                          \
+      packed_tile<kGateUp, n, 2, true, BMW, 4>(p, smem, g, row0, nrows, ntile);              \
       break;
     MOE_TILE_CASE(1)
     MOE_TILE_CASE(2)
@@ -503,9 +578,13 @@ hipError_t launch_ffn_bf16_packed(const FfnDims& d, const uint16_t* x, const int
                                   int32_t* tiles, uint16_t* y, uint16_t* ys, hipStream_t s) {
   hipError_t e = set_attrs_packed();
   if (e != hipSuccess) return e;
-  e = launch_build_tiles(offsets, d.E, d.T, d.Is > 0, BM, tiles, s);
+  // Every group has at most T rows (a token picks an expert at most once).
+  const int few = d.T <= 32 ? 1 : d.T <= 64 ? 2 : 0;
+  const bool wide = !few && d.N >= (int64_t)kWideMinRows * d.E;
+  const int bm1 = wide ? BMW : BM;
+  e = launch_build_tiles(offsets, d.E, d.T, d.Is > 0, bm1, tiles, s);
   if (e != hipSuccess) return e;
-  const int64_t mt = ffn_max_mtiles(d.N, d.T, d.E, BM);
+  const int64_t mt = ffn_max_mtiles(d.N, d.T, d.E, bm1);
   uint16_t* hs = h + d.N * d.I;
   auto grid = [](int64_t max_work) {
     return (unsigned)(((max_work + kNumXcd - 1) / kNumXcd) * kNumXcd);
@@ -530,9 +609,13 @@ hipError_t launch_ffn_bf16_packed(const FfnDims& d, const uint16_t* x, const int
   a1.c_s = hs;
   a1.ldc_r = d.I;
   a1.ldc_s = d.Is;
-  // Every group has at most T rows (a token picks an expert at most once).
-  const int few = d.T <= 32 ? 1 : d.T <= 64 ? 2 : 0;
-  if (few == 1)
+  if (wide) {
+    PackedArgs w1 = a1;
+    w1.ntn = (a1.ntn + 1) / 2;
+    MOE_TIMED_LAUNCH(s, "grouped_gemm_bf16_packed_wide<true>",
+      hipLaunchKernelGGL(grouped_gemm_bf16_packed_wide<true>, dim3(grid(mt * w1.ntn)), dim3(NT),
+                         kLdsW, s, w1));
+  } else if (few == 1)
     MOE_TIMED_LAUNCH(s, "grouped_gemm_bf16_packed_few<true, 1>",
       hipLaunchKernelGGL((grouped_gemm_bf16_packed_few<true, 1>),
                          dim3(grid(mt * a1.ntn * kFewSlots)), dim3(64), 0, s, a1));
@@ -575,8 +658,9 @@ hipError_t launch_ffn_bf16_packed(const FfnDims& d, const uint16_t* x, const int
       hipLaunchKernelGGL((grouped_gemm_bf16_packed_few<false, 2>),
                          dim3(grid(mt * a2.ntn * kFewSlots)), dim3(64), 0, s, a2));
   else {
-    // The down projection uses 128-row tiles, two workgroups per CU.
-    e = launch_build_tiles(offsets, d.E, d.T, d.Is > 0, BM2, tiles, s);
+    // The down projection uses 128-row tiles, two workgroups per CU (with
+    // wide tiles the list is already at 128 rows).
+    if (!wide) e = launch_build_tiles(offsets, d.E, d.T, d.Is > 0, BM2, tiles, s);
     if (e != hipSuccess) return e;
     const int64_t mt2 = ffn_max_mtiles(d.N, d.T, d.E, BM2);
     MOE_TIMED_LAUNCH(s, "grouped_gemm_bf16_packed_x2<false>",

@@ -238,7 +238,13 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
 constexpr int SEL_WAVES = 4;
 constexpr int SEL_MAXV = 8;   // E <= 512 = 64 lanes x 8
 
-// One wavefront per token.  Lane l holds experts e = l + 64 v.
+// One wavefront selects for one token; lane l holds experts e = l + 64 v.
+// SW = 1: a workgroup holds SEL_WAVES tokens.  SW = SEL_WAVES (deep k
+// splits, small batches): a workgroup holds one token, its waves first sum
+// contiguous quarters of the splits (four times the loads in flight, over
+// four times the CUs), the quarters are added in wave order through LDS
+// (a fixed order: the result does not depend on timing), and wave 0 selects.
+template <int SW>
 __global__ void __launch_bounds__(SEL_WAVES * 64)
 select_kernel(const float* __restrict__ part, int ksplit, const float* __restrict__ bias,
               float* __restrict__ logits_out, int32_t* __restrict__ idx_out,
@@ -246,10 +252,64 @@ select_kernel(const float* __restrict__ part, int ksplit, const float* __restric
   __shared__ float s_c[SEL_WAVES][512];
   __shared__ float s_s[SEL_WAVES][512];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t t = (int64_t)blockIdx.x * SEL_WAVES + wave;
-  if (t >= T) return;
+  const int64_t t = SW == 1 ? (int64_t)blockIdx.x * SEL_WAVES + wave : (int64_t)blockIdx.x;
+  if (t >= T) return;   // uniform over the workgroup when SW > 1
   const int Eg = E / G;
   const int V = (E + 63) / 64;
+  const int s_begin = SW == 1 ? 0 : (int)((int64_t)ksplit * wave / SW);
+  const int s_end = SW == 1 ? ksplit : (int)((int64_t)ksplit * (wave + 1) / SW);
+
+  // Logits: the k-split partial sums of [s_begin, s_end) added in split
+  // order.  The loads of a batch of splits (for all of this lane's experts)
+  // are issued together and then added in order, so a deep split costs few
+  // memory round trips.
+  float lgs[SEL_MAXV];
+  {
+    constexpr int SB = 4;    // splits per batch
+    const int64_t stride = T * E;
+#pragma unroll
+    for (int v = 0; v < SEL_MAXV; ++v) {
+      const int e = lane + 64 * v;
+      lgs[v] = (v < V && e < E) ? part[(int64_t)s_begin * stride + t * E + e] : 0.0f;
+    }
+    for (int s0 = s_begin + 1; s0 < s_end; s0 += SB) {
+      float pv[SB][SEL_MAXV];
+#pragma unroll
+      for (int j = 0; j < SB; ++j)
+#pragma unroll
+        for (int v = 0; v < SEL_MAXV; ++v) {
+          const int e = lane + 64 * v;
+          pv[j][v] = (s0 + j < s_end && v < V && e < E)
+                         ? part[(int64_t)(s0 + j) * stride + t * E + e] : 0.0f;
+        }
+#pragma unroll
+      for (int j = 0; j < SB; ++j)
+#pragma unroll
+        for (int v = 0; v < SEL_MAXV; ++v)
+          if (s0 + j < s_end) lgs[v] += pv[j][v];
+    }
+  }
+  if (SW > 1) {
+    // quarters added in wave order; wave 0 goes on alone (no workgroup
+    // barrier below this point)
+#pragma unroll
+    for (int v = 0; v < SEL_MAXV; ++v) {
+      const int e = lane + 64 * v;
+      if (v < V && e < E) s_c[wave][e] = lgs[v];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int v = 0; v < SEL_MAXV; ++v) {
+      const int e = lane + 64 * v;
+      if (v < V && e < E) {
+        float acc = s_c[0][e];
+#pragma unroll
+        for (int w = 1; w < SW; ++w) acc += s_c[w][e];
+        lgs[v] = acc;
+      }
+    }
+  }
 
   float c[SEL_MAXV], s32[SEL_MAXV];
 #pragma unroll
@@ -258,8 +318,7 @@ select_kernel(const float* __restrict__ part, int ksplit, const float* __restric
     c[v] = -INFINITY;
     s32[v] = 0.0f;
     if (v < V && e < E) {
-      float lg = part[t * E + e];
-      for (int s = 1; s < ksplit; ++s) lg += part[(int64_t)s * T * E + t * E + e];
+      const float lg = lgs[v];
       if (logits_out) logits_out[t * E + e] = lg;
       double sd = 1.0 / (1.0 + exp(-(double)lg));
       s32[v] = (float)sd;
@@ -338,11 +397,17 @@ int gate_ksplit(int64_t T, int H, int E) {
   const int nsteps = H / GBK;
   if (H % GBK || nsteps < 1) return 1;
   const int64_t tiles = ((T + GBM - 1) / GBM) * ((gate_expert_blocks(E) + GEB - 1) / GEB);
-  // Enough k splits for ~512 workgroups; small batches split k finely so
-  // that the weight stream is spread over many CUs.
-  // Splits divide the k steps evenly, so that every split has work.
+  // Splits divide the k steps evenly, at least two steps each, so that
+  // every split has work, and keep the grid within ~512 workgroups.  Small
+  // batches split k finely so that the weight stream is spread over many
+  // CUs: the power-of-two count that reaches ~512 workgroups, or more (up to
+  // 64) while the partial sums written and re-read (ks T E fp32) stay below
+  // the split weight's 6 E H bytes.
+  auto ok = [&](int c) { return nsteps % c == 0 && nsteps / c >= 2 && tiles * c <= 512; };
   int ks = 1;
-  while (ks < 32 && tiles * ks < 512 && nsteps % (ks * 2) == 0 && nsteps / (ks * 2) >= 2) ks *= 2;
+  while (ks < 32 && ok(ks * 2)) ks *= 2;
+  for (int c = ks + 1; c <= 64; ++c)
+    if (ok(c) && (int64_t)c * T * 4 <= (int64_t)H * 6) ks = c;
   return ks;
 }
 
@@ -379,10 +444,16 @@ hipError_t launch_gate_logits(const void* x, bool x_bf16, const float* gate_w, v
 hipError_t launch_select(const float* partials, int ksplit, const float* bias, float* logits_out,
                          int32_t* idx, float* w, int64_t T, int E, int G, int TG, int K,
                          float rho, hipStream_t s) {
-  dim3 grid((unsigned)((T + SEL_WAVES - 1) / SEL_WAVES));
-  MOE_TIMED_LAUNCH(s, "select_kernel",
-    hipLaunchKernelGGL(select_kernel, grid, dim3(SEL_WAVES * 64), 0, s, partials, ksplit, bias,
-                       logits_out, idx, w, T, E, G, TG, K, rho));
+  if (ksplit >= 16) {
+    MOE_TIMED_LAUNCH(s, "select_kernel",
+      hipLaunchKernelGGL(select_kernel<SEL_WAVES>, dim3((unsigned)T), dim3(SEL_WAVES * 64), 0, s,
+                         partials, ksplit, bias, logits_out, idx, w, T, E, G, TG, K, rho));
+  } else {
+    dim3 grid((unsigned)((T + SEL_WAVES - 1) / SEL_WAVES));
+    MOE_TIMED_LAUNCH(s, "select_kernel",
+      hipLaunchKernelGGL(select_kernel<1>, grid, dim3(SEL_WAVES * 64), 0, s, partials, ksplit,
+                         bias, logits_out, idx, w, T, E, G, TG, K, rho));
+  }
   return hipGetLastError();
 }
 

@@ -37,8 +37,14 @@ TALL_FP8 = synth.C5.replace(name="fp8-T1024-H512-E8-K2", T=1024, H=512, E=8, G=2
 DECODE48 = synth.C3.replace(name="bf16-T48-H512-E16", T=48, H=512, E=16, G=4, TG=2, K=4, I=256,
                             Is=128, rho=2.5)
 
+# >= 256 rows per expert (wide 128 x 512 tiles) with ragged widths: 3 h-tiles
+# of 128 (the second wide tile half empty), a shared width of 2 tiles, and a
+# hidden size of 3 row tiles of 256 for the down projection
+WIDE_RAGGED = synth.C3.replace(name="bf16-T1100-H768-E4-K1-I384-Is256", T=1100, H=768, E=4,
+                               G=2, TG=1, K=1, I=384, Is=256, rho=1.3)
+
 LAYER_CASES = [C1, SMALL_BF16, RAGGED_BF16, TALL_BF16, K1_NOSHARED, TINY_T1, DECODE48, SMALL_FP8,
-               TALL_FP8]
+               TALL_FP8, WIDE_RAGGED]
 
 
 def _tol(cfg):
@@ -55,7 +61,19 @@ def inputs(cfg):
     return _inputs[cfg.name]
 
 
-@pytest.mark.parametrize("cfg", [C1, SMALL_BF16, RAGGED_BF16, K1_NOSHARED, TINY_T1],
+# 12 k steps of 64 split 6 ways (a split count that is not a power of two)
+GATE_SPLIT6 = synth.C3.replace(name="bf16-T32-H768-E64-split6", T=32, H=768, E=64, G=8, TG=4,
+                               K=8, I=128, Is=128, rho=2.5)
+
+
+# 36 k steps split 18 ways: the split sums are shared by a token's four waves
+# (uneven quarters of 4 and 5 splits)
+GATE_SPLIT18 = synth.C3.replace(name="bf16-T8-H2304-E64-split18", T=8, H=2304, E=64, G=8, TG=4,
+                                K=8, I=128, Is=128, rho=2.5)
+
+
+@pytest.mark.parametrize("cfg", [C1, SMALL_BF16, RAGGED_BF16, K1_NOSHARED, TINY_T1, GATE_SPLIT6,
+                                 GATE_SPLIT18],
                          ids=lambda c: c.name)
 def test_gate(cfg):
     log(f"gate {cfg.name}")
@@ -110,7 +128,7 @@ def test_permute_flags_out_of_range_index():
 FFN_CASES = [(C1, False), (SMALL_BF16, False), (RAGGED_BF16, False), (TALL_BF16, False),
              (K1_NOSHARED, False), (SMALL_FP8, False), (SMALL_BF16, True), (RAGGED_BF16, True),
              (TALL_BF16, True), (K1_NOSHARED, True), (DECODE48, True), (DECODE48, False),
-             (SMALL_FP8, True), (TALL_FP8, True), (TALL_FP8, False)]
+             (SMALL_FP8, True), (TALL_FP8, True), (TALL_FP8, False), (WIDE_RAGGED, True)]
 
 
 def _case_id(c):
