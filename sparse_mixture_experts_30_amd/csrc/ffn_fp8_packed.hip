@@ -207,10 +207,15 @@ __device__ __forceinline__ void fp8_tile(const Packed8Args& p, u32x4* smem, int 
   // scaled accumulation of block r - 1, so MFMA latency hides behind VALU
   // work; token-staging operations and, after the last block, the weight
   // refill of this slot are spread between the blocks.
+  // Weight block scales of the step, loaded one step ahead (scalar loads
+  // waited for in the same step would stall it).
+  float sbn0 = bs0[0], sbn1 = bs1[0];
   auto step_body = [&](int buf, int u, int step) {
     const u32x4* as = sA + buf * BM * 8;
     const float* ss = sS + buf * BM;
-    const float sb0 = bs0[step], sb1 = bs1[step];
+    const float sb0 = sbn0, sb1 = sbn1;
+    sbn0 = bs0[min(step + 1, last)];
+    sbn1 = bs1[min(step + 1, last)];
     const int nst = (u + 1) & 1;      // register stage holding step + 1
     f32x16 part[2][2];
     float sc[2][2];
