@@ -241,6 +241,57 @@ def test_quantize_act_bit_exact():
     np.testing.assert_array_equal(host(xq), q_ref)
 
 
+# Edge cases of the routing shape, through the whole layer (packed bf16):
+#   the largest expert count (512: eight experts per lane in the select),
+#   one group (group-limited routing reduces to plain top-k),
+#   every group kept (TG = G), the smallest group (2 experts), and top-k
+#   equal to every expert of the kept groups.
+EDGE_CASES = [
+    synth.C3.replace(name="bf16-T96-H256-E512-G16-TG4-K8", T=96, H=256, E=512, G=16, TG=4, K=8,
+                     I=128, Is=128, rho=2.5),
+    synth.C3.replace(name="bf16-T80-H256-E32-G1-K6", T=80, H=256, E=32, G=1, TG=1, K=6, I=128,
+                     Is=128, rho=1.5),
+    synth.C3.replace(name="bf16-T80-H256-E32-G4-TG4-K5", T=80, H=256, E=32, G=4, TG=4, K=5,
+                     I=128, Is=128, rho=1.5),
+    synth.C3.replace(name="bf16-T80-H256-E16-G8-TG3-K2", T=80, H=256, E=16, G=8, TG=3, K=2,
+                     I=128, Is=0, rho=1.5),
+    synth.C3.replace(name="bf16-T80-H256-E16-G8-TG3-K6-all", T=80, H=256, E=16, G=8, TG=3, K=6,
+                     I=128, Is=128, rho=1.5),
+]
+
+
+@pytest.mark.parametrize("cfg", EDGE_CASES, ids=lambda c: c.name)
+def test_forward_routing_edge_cases(cfg):
+    log(f"edge {cfg.name}")
+    inp, dev = inputs(cfg)
+    dev = sd.packed_copy(dev)
+    r = run_forward(cfg, dev, cfg.T)
+    check_routing(cfg, inp["x"], inp["gate_w"], inp["bias"], r["logits"], r["idx"], r["w"],
+                  cfg.name)
+    idx_c, _ = oracle.route_f32(cfg, r["logits"], inp["bias"])
+    rc, _, rp, _ = oracle.permute(idx_c, cfg.E)
+    np.testing.assert_array_equal(r["counts"], rc)
+    np.testing.assert_array_equal(r["perm"], rp)
+    if cfg.K == cfg.TG * (cfg.E // cfg.G):
+        # every expert of the kept groups is chosen, on tokens where all of
+        # them have a positive choice score (a masked expert scores 0.0 and
+        # may beat a negative one)
+        Eg = cfg.E // cfg.G
+        c = 1 / (1 + np.exp(-r["logits"].astype(np.float64))) + inp["bias"].astype(np.float64)
+        checked = 0
+        for t in range(cfg.T):
+            groups = sorted(set((r["idx"][t] // Eg).tolist()))
+            kept = [g * Eg + j for g in groups for j in range(Eg)]
+            if len(groups) == cfg.TG and np.all(c[t, kept] > 0):
+                assert sorted(r["idx"][t].tolist()) == kept
+                checked += 1
+        assert checked >= 0.9 * cfg.T
+    ref, nalt = layer_reference(cfg, inp, r["idx"], np.arange(cfg.T))
+    rel = rel_l2(r["out"], ref)
+    log(f"  out relL2={rel:.3e}, near-tie tokens={nalt}")
+    assert rel <= _tol(cfg)
+
+
 def test_forward_deterministic():
     cfg = RAGGED_BF16
     inp, dev = inputs(cfg)
