@@ -132,7 +132,7 @@ def main():
         print(json.dumps({"copy_calibration_bytes": 1 << 30, "copies": 5}))
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
 
     import numpy as np
