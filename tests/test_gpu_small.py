@@ -292,6 +292,46 @@ def test_forward_routing_edge_cases(cfg):
     assert rel <= _tol(cfg)
 
 
+def test_forward_graph_replay():
+    """moe_forward captured into a HIP graph (torch.cuda.CUDAGraph) replays
+    bit-identically to eager execution, several times, with eager forwards
+    and synchronisations between the replays (the path issues no memset or
+    host synchronisation, so it can be captured)."""
+    cfg = SMALL_BF16
+    inp, dev = inputs(cfg)
+    dev = sd.packed_copy(dev)
+    T = cfg.T
+    C = sd.moe_config(cfg)
+    W = sd.weights_struct(dev)
+    ws = sd.workspace(cfg, T)
+    out = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=DEV)
+    idx = torch.empty((T, cfg.K), dtype=torch.int32, device=DEV)
+    sync()
+
+    def fwd():
+        moe.moe_forward(C, T, dev["x"], W, out, ws, topk_idx=idx,
+                        stream=torch.cuda.current_stream())
+
+    fwd()
+    sync()
+    ref, ref_idx = out.clone(), idx.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fwd()
+    sync()
+    for rep in range(4):
+        out.fill_(0)
+        idx.fill_(-1)
+        sync()
+        g.replay()
+        sync()
+        assert torch.equal(out, ref), f"replay {rep}"
+        assert torch.equal(idx, ref_idx), f"replay {rep}"
+        fwd()          # eager work between replays
+        sync()
+        assert torch.equal(out, ref)
+
+
 def test_forward_deterministic():
     cfg = RAGGED_BF16
     inp, dev = inputs(cfg)
