@@ -67,6 +67,9 @@ def lib():
         L.oracle_ffn.restype = ctypes.c_int
         L.oracle_combine.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp]
         L.oracle_combine.restype = None
+        L.oracle_ffn_backward.argtypes = [ctypes.POINTER(Cfg), i32, i64, vp, vp, i32, vp, vp, vp,
+                                          vp, vp, i32, vp, vp, vp]
+        L.oracle_ffn_backward.restype = ctypes.c_int
         L.oracle_bias_update.argtypes = [i32, vp, ctypes.c_float, vp, vp]
         L.oracle_bias_update.restype = ctypes.c_int
         _lib = L
@@ -244,3 +247,28 @@ def bias_update(counts: np.ndarray, gamma: float, bias: np.ndarray) -> np.ndarra
     if rc:
         raise ValueError("oracle_bias_update rejected its arguments")
     return out
+
+
+def ffn_backward(cfg, inp: dict, expert: int, tokens, dy, want=("dx", "dw13", "dw2")):
+    """Exact (fp64) backward of one SwiGLU expert (-1: shared) over rows with
+    inputs x[tokens[r]] and output gradients dy [n, H] -> dict of dx [n, H],
+    dw13 [2 n_e, H], dw2 [H, n_e] (the weight gradients summed over the rows)."""
+    x = _c(inp["x"])
+    tokens = _c(tokens, np.int64)
+    dy = _c(dy, np.float64)
+    n = len(tokens)
+    H = cfg.H
+    ne = cfg.Is if expert < 0 else cfg.I
+    wd = {"f32": F32, "bf16": BF16}[cfg.wdtype]
+    xd = F32 if cfg.act == "f32" else BF16
+    g = lambda k: None if inp.get(k) is None else _c(inp[k])
+    out = {"dx": np.empty((n, H)) if "dx" in want else None,
+           "dw13": np.empty((2 * ne, H)) if "dw13" in want else None,
+           "dw2": np.empty((H, ne)) if "dw2" in want else None}
+    rc = lib().oracle_ffn_backward(ctypes.byref(cfg_of(cfg)), int(expert), n, _p(tokens), _p(x),
+                                   xd, _p(dy), _p(g("w13")), _p(g("w2")), _p(g("ws13")),
+                                   _p(g("ws2")), wd, _p(out["dx"]), _p(out["dw13"]),
+                                   _p(out["dw2"]))
+    if rc:
+        raise ValueError("oracle_ffn_backward rejected its arguments")
+    return {k: v for k, v in out.items() if v is not None}

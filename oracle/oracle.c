@@ -614,3 +614,92 @@ int oracle_bias_update(int32_t E, const int32_t *counts, float gamma, const floa
     }
     return 0;
 }
+
+/* ---- expert FFN backward (training) ------------------------------------ */
+
+/* Backward of one SwiGLU expert (R5) over n rows, in double.  Row r has the
+ * input x_r = x[tokens[r]] and the output gradient dy_r = dy[r*H .. +H).
+ * With [g; u] = W13 x, h = silu(g) u, y = W2 h, the exact derivatives are
+ *   dh   = W2^T dy                 dh_i = sum_m dy_m W2[m][i]
+ *   dg   = dh u silu'(g),          silu'(g) = s (1 + g (1 - s)), s = 1/(1+e^-g)
+ *   du   = dh silu(g)
+ *   dx_r = W13^T [dg; du]          dx_k = sum_i dg_i W13[i][k] + du_i W13[n+i][k]
+ *   dW2  = sum_r dy_r h_r^T        [H, n]
+ *   dW13 = sum_r [dg; du]_r x_r^T  [2n, H]
+ * e is the expert (-1: the shared expert, width Is).  Outputs (any may be
+ * NULL): dx [n, H], dw13 [2 n_e, H], dw2 [H, n_e], n_e = I or Is.  Weights
+ * are fp32 or bf16.  Returns 1 for a bad expert, dtype or allocation. */
+int oracle_ffn_backward(const oracle_cfg *c, int32_t e, int64_t n, const int64_t *tokens,
+                        const void *x, int32_t x_dtype, const double *dy, const void *w13,
+                        const void *w2, const void *ws13, const void *ws2, int32_t w_dtype,
+                        double *dx, double *dw13, double *dw2)
+{
+    const int32_t H = c->H, E = c->E;
+    if (e < -1 || e >= E || (e == -1 && c->Is == 0) || w_dtype == OR_E4M3)
+        return 1;
+    const int32_t ne = e < 0 ? c->Is : c->I;
+    const void *W13 = e < 0 ? ws13 : expert_base(w13, w_dtype, e, (int64_t)2 * ne * H);
+    const void *W2 = e < 0 ? ws2 : expert_base(w2, w_dtype, e, (int64_t)H * ne);
+    double *xs = malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * H);
+    double *g = malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * ne);
+    double *u = malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * ne);
+    double *h = malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * ne);
+    double *da = malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * 2 * ne);
+    if (!xs || !g || !u || !h || !da) {
+        free(xs); free(g); free(u); free(h); free(da);
+        return 1;
+    }
+    /* forward quantities and the row gradients */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n; ++r) {
+        double *xr = xs + r * H;
+        for (int32_t k = 0; k < H; ++k)
+            xr[k] = mat_at(x, NULL, x_dtype, H, tokens[r], k);
+        for (int32_t i = 0; i < ne; ++i) {
+            double gs = 0.0, us = 0.0;
+            for (int32_t k = 0; k < H; ++k) {
+                gs += mat_at(W13, NULL, w_dtype, H, i, k) * xr[k];
+                us += mat_at(W13, NULL, w_dtype, H, ne + i, k) * xr[k];
+            }
+            g[r * ne + i] = gs;
+            u[r * ne + i] = us;
+            double sg = 1.0 / (1.0 + exp(-gs));
+            h[r * ne + i] = gs * sg * us;
+            double dh = 0.0;
+            for (int32_t m = 0; m < H; ++m)
+                dh += dy[r * H + m] * mat_at(W2, NULL, w_dtype, ne, m, i);
+            da[r * 2 * ne + i] = dh * us * sg * (1.0 + gs * (1.0 - sg));
+            da[r * 2 * ne + ne + i] = dh * gs * sg;
+        }
+        if (dx) {
+            for (int32_t k = 0; k < H; ++k) {
+                double acc = 0.0;
+                for (int32_t q = 0; q < 2 * ne; ++q)
+                    acc += da[r * 2 * ne + q] * mat_at(W13, NULL, w_dtype, H, q, k);
+                dx[r * H + k] = acc;
+            }
+        }
+    }
+    if (dw2) {
+#pragma omp parallel for schedule(static)
+        for (int32_t m = 0; m < H; ++m)
+            for (int32_t i = 0; i < ne; ++i) {
+                double acc = 0.0;
+                for (int64_t r = 0; r < n; ++r)
+                    acc += dy[r * H + m] * h[r * ne + i];
+                dw2[(int64_t)m * ne + i] = acc;
+            }
+    }
+    if (dw13) {
+#pragma omp parallel for schedule(static)
+        for (int32_t q = 0; q < 2 * ne; ++q)
+            for (int32_t k = 0; k < H; ++k) {
+                double acc = 0.0;
+                for (int64_t r = 0; r < n; ++r)
+                    acc += da[r * 2 * ne + q] * xs[r * H + k];
+                dw13[(int64_t)q * H + k] = acc;
+            }
+    }
+    free(xs); free(g); free(u); free(h); free(da);
+    return 0;
+}

@@ -539,3 +539,83 @@ def test_bias_update_balances_a_skewed_router():
         bias = oracle.bias_update(counts, 0.005, bias)
     assert start > 2.0
     assert np.mean(history[-50:]) < 1.25
+
+
+# ---------------------------------------------------------------- expert FFN backward
+
+FD_CFG = synth.C1.replace(name="fd-T6-H16-E4-I8", T=6, H=16, E=4, G=2, TG=1, K=1, I=8, Is=8,
+                          rho=1.0)
+
+
+@pytest.fixture(scope="module")
+def fd_inputs():
+    return synth.gen_inputs(FD_CFG)
+
+
+def _loss(cfg, inp, expert, tokens, dy):
+    """L = sum_r <dy_r, FFN(x_{tokens[r]})> in fp64."""
+    y = oracle.ffn(cfg, inp, tokens, np.full(len(tokens), expert, np.int32))
+    return float((y * dy).sum())
+
+
+@pytest.mark.parametrize("expert", [2, -1])
+def test_ffn_backward_matches_finite_differences(fd_inputs, expert):
+    # Central differences of L with exact fp32 perturbations (2^-12 added to
+    # values near 0.3 is exact), error O(eps^2): every entry of dW13, dW2 and
+    # of the input gradient (a token used by two rows gets both rows' dx).
+    cfg, inp = FD_CFG, fd_inputs
+    tokens = np.array([0, 3, 5, 3], np.int64)
+    rng = np.random.default_rng(11)
+    dy = rng.standard_normal((len(tokens), cfg.H))
+    b = oracle.ffn_backward(cfg, inp, expert, tokens, dy)
+    eps = np.float32(2.0 ** -12)
+    k13, k2 = ("ws13", "ws2") if expert < 0 else ("w13", "w2")
+
+    def fd(key, index):
+        plus, minus = dict(inp), dict(inp)
+        a = inp[key].copy(); a[index] += eps; plus[key] = a
+        a = inp[key].copy(); a[index] -= eps; minus[key] = a
+        return (_loss(cfg, plus, expert, tokens, dy) - _loss(cfg, minus, expert, tokens, dy)) / (
+            2 * float(eps))
+
+    e = expert
+    w13_shape = b["dw13"].shape
+    fd13 = np.array([[fd(k13, (i, j) if e < 0 else (e, i, j)) for j in range(w13_shape[1])]
+                     for i in range(w13_shape[0])])
+    np.testing.assert_allclose(b["dw13"], fd13, rtol=1e-5, atol=1e-8)
+    fd2 = np.array([[fd(k2, (i, j) if e < 0 else (e, i, j)) for j in range(b["dw2"].shape[1])]
+                    for i in range(b["dw2"].shape[0])])
+    np.testing.assert_allclose(b["dw2"], fd2, rtol=1e-5, atol=1e-8)
+    for t in np.unique(tokens):
+        fdx = np.array([fd("x", (t, j)) for j in range(cfg.H)])
+        np.testing.assert_allclose(b["dx"][tokens == t].sum(0), fdx, rtol=1e-5, atol=1e-8)
+
+
+def test_ffn_backward_linear_in_dy_and_additive_over_rows(fd_inputs):
+    cfg, inp = FD_CFG, fd_inputs
+    rng = np.random.default_rng(12)
+    t1, t2 = np.array([1, 2], np.int64), np.array([4, 0, 5], np.int64)
+    d1, d2 = rng.standard_normal((2, cfg.H)), rng.standard_normal((3, cfg.H))
+    b1 = oracle.ffn_backward(cfg, inp, 1, t1, d1)
+    b2 = oracle.ffn_backward(cfg, inp, 1, t2, d2)
+    both = oracle.ffn_backward(cfg, inp, 1, np.concatenate([t1, t2]), np.concatenate([d1, d2]))
+    np.testing.assert_allclose(both["dw13"], b1["dw13"] + b2["dw13"], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(both["dw2"], b1["dw2"] + b2["dw2"], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(both["dx"], np.concatenate([b1["dx"], b2["dx"]]), rtol=1e-12)
+    scaled = oracle.ffn_backward(cfg, inp, 1, t1, -3.0 * d1)
+    for k in ("dx", "dw13", "dw2"):
+        np.testing.assert_allclose(scaled[k], -3.0 * b1[k], rtol=1e-12, atol=1e-14)
+
+
+def test_ffn_backward_zero_up_rows_give_zero_grads_but_gate_rows(fd_inputs):
+    # With the up rows of W13 zero, u = 0: h = 0 so dW2 = 0, the gate rows get
+    # no gradient (dg = dh u silu' = 0) and only the up rows get one.
+    cfg, inp = FD_CFG, dict(fd_inputs)
+    w13 = inp["w13"].copy()
+    w13[:, cfg.I:, :] = 0.0
+    inp["w13"] = w13
+    dy = np.random.default_rng(13).standard_normal((3, cfg.H))
+    b = oracle.ffn_backward(cfg, inp, 0, np.array([0, 1, 2]), dy)
+    assert np.all(b["dw2"] == 0.0)
+    assert np.all(b["dw13"][:cfg.I] == 0.0)
+    assert np.any(b["dw13"][cfg.I:] != 0.0)
