@@ -183,6 +183,37 @@ moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const mo
 moe_status moe_quantize_act(const moe_config* cfg, int64_t rows, const void* x, uint8_t* xq,
                             float* xs, void* stream);
 
+/* Backward of the grouped SwiGLU expert FFN, for training.  The experts are
+ * SwiGLU FFNs (mqxn.cn/news/19449, section 3.1) over the routed rows and the
+ * always-active shared expert ("从 1024 块 GPU 到 558 万美元：拆解 DeepSeek-V3 的
+ * 算法-系统协同设计", section 2.2); this computes their exact derivatives.  With
+ * [g; u] = W13 x_row, h = silu(g) u, y_row = W2 h and the output gradient
+ * dy_row of each row:
+ *   dh = dy W2;  dg = dh u silu'(g);  du = dh silu(g);  dx_row = [dg du] W13;
+ *   dW2 = sum over the expert's rows of dy^T h;  dW13 = sum of [dg du]^T x_row.
+ * [g; u] is recomputed from x (fp32 accumulation); [dg du] and h are rounded
+ * to bf16 before the GEMMs that consume them; every GEMM accumulates in fp32.
+ *   x [T, H] bf16; perm [T*K] and offsets [E+1] as written by moe_permute.
+ *   w: row-major bf16 weights (packed = 0): w13 [E, 2I, H], w2 [E, H, I],
+ *      ws13 [2Is, H], ws2 [H, Is].
+ *   dy [T*K, H] bf16: gradient of the routed expert outputs in the sorted row
+ *      order of moe_expert_ffn's y (for the layer output: row pos[t*K+k] is
+ *      topk_w[t,k] * dOut[t]); dy_shared [T, H]: gradient of y_shared.
+ *   dx [T*K, H], dx_shared [T, H] out bf16 (nullable, both or neither):
+ *      gradient of each row's input (sum the rows of a token for dx_t).
+ *   dw13 [E, 2I, H], dw2 [E, H, I], dws13, dws2 out bf16: weight gradients
+ *      (zero for an expert without rows).
+ * Workspace: moe_expert_ffn_backward_workspace_bytes(cfg, T) bytes (0 for a
+ * configuration it does not handle), 256-byte aligned.  bf16 activations and
+ * weights only (MOE_ERR_UNSUPPORTED otherwise, or for packed weights). */
+size_t moe_expert_ffn_backward_workspace_bytes(const moe_config* cfg, int64_t T);
+moe_status moe_expert_ffn_backward(const moe_config* cfg, int64_t T, const void* x,
+                                   const int32_t* perm, const int32_t* offsets,
+                                   const moe_weights* w, const void* dy, const void* dy_shared,
+                                   void* dx, void* dx_shared, void* dw13, void* dw2,
+                                   void* dws13, void* dws2, void* ws, size_t ws_bytes,
+                                   void* stream);
+
 /* Load-balancing update of the selection bias.  The bias takes part only in
  * choosing experts and is steered by the experts' observed load instead of
  * a gradient ("从 1024 块 GPU 到 558 万美元：拆解 DeepSeek-V3 的算法-系统协同设计",

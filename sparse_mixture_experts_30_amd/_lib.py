@@ -18,7 +18,8 @@ MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 EXPORTS = ("moe_workspace_bytes", "moe_gate", "moe_permute", "moe_expert_ffn", "moe_combine",
            "moe_forward", "moe_quantize_act", "moe_packed_bytes", "moe_pack_weight",
            "moe_get_device_error", "moe_strerror", "moe_last_error", "moe_kernel_timer_enable",
-           "moe_kernel_timer_read", "moe_bias_update")
+           "moe_kernel_timer_read", "moe_bias_update", "moe_expert_ffn_backward",
+           "moe_expert_ffn_backward_workspace_bytes")
 MOE_W13, MOE_W2, MOE_WS13, MOE_WS2 = 0, 1, 2, 3
 
 
@@ -66,6 +67,9 @@ def lib():
             "moe_forward": (ctypes.c_int, [cfgp, i64, vp, wp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
             "moe_quantize_act": (ctypes.c_int, [cfgp, i64, vp, vp, vp, vp]),
             "moe_bias_update": (ctypes.c_int, [cfgp, vp, ctypes.c_float, vp, vp]),
+            "moe_expert_ffn_backward_workspace_bytes": (sz, [cfgp, i64]),
+            "moe_expert_ffn_backward": (ctypes.c_int, [cfgp, i64, vp, vp, vp, wp, vp, vp, vp, vp, vp,
+                                                       vp, vp, vp, vp, sz, vp]),
             "moe_packed_bytes": (sz, [cfgp, ctypes.c_int]),
             "moe_pack_weight": (ctypes.c_int, [cfgp, ctypes.c_int, vp, vp, vp]),
             "moe_get_device_error": (ctypes.c_int, [vp, sz, vp]),
@@ -160,6 +164,19 @@ def moe_forward(cfg, T, x, w: MoeWeights, out, ws, logits=None, topk_idx=None, t
 def moe_quantize_act(cfg, rows, x, xq, xs, stream=None):
     _check(lib().moe_quantize_act(ctypes.byref(cfg), rows, _ptr(x), _ptr(xq), _ptr(xs),
                                   _stream(stream)))
+
+
+def moe_expert_ffn_backward_workspace_bytes(cfg: MoeConfig, T: int) -> int:
+    return lib().moe_expert_ffn_backward_workspace_bytes(ctypes.byref(cfg), T)
+
+
+def moe_expert_ffn_backward(cfg, T, x, perm, offsets, w: MoeWeights, dy, dy_shared, dx, dx_shared,
+                            dw13, dw2, dws13, dws2, ws, stream=None):
+    _check(lib().moe_expert_ffn_backward(ctypes.byref(cfg), T, _ptr(x), _ptr(perm), _ptr(offsets),
+                                         ctypes.byref(w), _ptr(dy), _ptr(dy_shared), _ptr(dx),
+                                         _ptr(dx_shared), _ptr(dw13), _ptr(dw2), _ptr(dws13),
+                                         _ptr(dws2), _ptr(ws), _nbytes(ws) if ws is not None else 0,
+                                         _stream(stream)))
 
 
 def moe_bias_update(cfg, counts, gamma, bias, stream=None):

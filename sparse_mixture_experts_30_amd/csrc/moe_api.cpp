@@ -369,6 +369,63 @@ moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const mo
   return MOE_OK;
 }
 
+size_t moe_expert_ffn_backward_workspace_bytes(const moe_config* cfg, int64_t T) {
+  if (check_cfg(cfg) != MOE_OK || check_T(T, cfg) != MOE_OK) return 0;
+  if (cfg->weight_dtype != MOE_BF16 || cfg->act_dtype != MOE_BF16) return 0;
+  moe::FfnDims d{T, T * cfg->num_experts_per_tok, cfg->hidden_size, cfg->moe_intermediate_size,
+                 cfg->shared_intermediate_size, cfg->n_routed_experts,
+                 cfg->num_experts_per_tok};
+  return moe::ffn_backward_ws_bytes(d);
+}
+
+moe_status moe_expert_ffn_backward(const moe_config* cfg, int64_t T, const void* x,
+                                   const int32_t* perm, const int32_t* offsets,
+                                   const moe_weights* w, const void* dy, const void* dy_shared,
+                                   void* dx, void* dx_shared, void* dw13, void* dw2,
+                                   void* dws13, void* dws2, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  CHECK(check_cfg(cfg));
+  CHECK(check_T(T, cfg));
+  if (cfg->weight_dtype != MOE_BF16 || cfg->act_dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "the expert backward takes bf16 activations and weights");
+  if (T == 0) return MOE_OK;
+  NONNULL(w);
+  if (w->packed)
+    return fail(MOE_ERR_UNSUPPORTED, "the expert backward reads row-major weights (packed = 0)");
+  NONNULL(x);
+  NONNULL(perm);
+  NONNULL(offsets);
+  NONNULL(w->w13);
+  NONNULL(w->w2);
+  NONNULL(dy);
+  NONNULL(dw13);
+  NONNULL(dw2);
+  const bool sh = cfg->shared_intermediate_size > 0;
+  if (sh) {
+    NONNULL(w->ws13);
+    NONNULL(w->ws2);
+    NONNULL(dy_shared);
+    NONNULL(dws13);
+    NONNULL(dws2);
+  }
+  moe::FfnDims d{T, T * cfg->num_experts_per_tok, cfg->hidden_size, cfg->moe_intermediate_size,
+                 cfg->shared_intermediate_size, cfg->n_routed_experts,
+                 cfg->num_experts_per_tok};
+  const size_t need = moe::ffn_backward_ws_bytes(d);
+  if (!ws || ws_bytes < need || ((uintptr_t)ws & 255))
+    return fail(MOE_ERR_WORKSPACE, "workspace must be 256-byte aligned and >= %zu bytes", need);
+  HIPCALL(moe::launch_ffn_backward(d, (const uint16_t*)x, perm, offsets,
+                                   (const uint16_t*)w->w13, (const uint16_t*)w->w2,
+                                   (const uint16_t*)(sh ? w->ws13 : nullptr),
+                                   (const uint16_t*)(sh ? w->ws2 : nullptr), (const uint16_t*)dy,
+                                   (const uint16_t*)(sh ? dy_shared : nullptr), (uint16_t*)dx,
+                                   (uint16_t*)(sh ? dx_shared : nullptr), (uint16_t*)dw13,
+                                   (uint16_t*)dw2, (uint16_t*)(sh ? dws13 : nullptr),
+                                   (uint16_t*)(sh ? dws2 : nullptr), ws, (hipStream_t)stream),
+          "expert backward");
+  return MOE_OK;
+}
+
 moe_status moe_bias_update(const moe_config* cfg, const int32_t* counts, float gamma,
                            float* bias, void* stream) {
   CHECK(check_cfg(cfg));

@@ -161,6 +161,17 @@ hipError_t launch_ffn_fp8(const FfnDims& d, const uint8_t* xq, const float* xs,
 hipError_t launch_combine(const void* y, const void* ys, const int32_t* pos, const float* w,
                           void* out, int64_t T, int H, int K, bool bf16, hipStream_t s);
 
+// Backward of the grouped SwiGLU expert FFN (ffn_backward.hip): row-major
+// bf16 weights; dy/dys are the gradients of the expert output rows (routed
+// rows in expert-sorted order, then the shared expert's T rows).
+size_t ffn_backward_ws_bytes(const FfnDims& d);
+hipError_t launch_ffn_backward(const FfnDims& d, const uint16_t* x, const int32_t* perm,
+                               const int32_t* offsets, const uint16_t* w13, const uint16_t* w2,
+                               const uint16_t* ws13, const uint16_t* ws2, const uint16_t* dy,
+                               const uint16_t* dys, uint16_t* dx, uint16_t* dxs, uint16_t* dw13,
+                               uint16_t* dw2, uint16_t* dws13, uint16_t* dws2, void* ws,
+                               hipStream_t s);
+
 // Selection-bias update from per-expert counts (one workgroup, E <= 512).
 hipError_t launch_bias_update(const int32_t* counts, float* bias, int E, float gamma,
                               hipStream_t s);

@@ -102,6 +102,20 @@ def test_argument_validation():
     bad = _cfg()
     bad.n_group = 3
     assert L.moe_bias_update(ctypes.byref(bad), FAKE, 1e-3, FAKE, None) != moe.MOE_OK
+    # expert backward: bf16 row-major weights only; required arrays; workspace
+    def bwd(c, w, dy=FAKE, ws=FAKE * 256, ws_bytes=1 << 40):
+        return L.moe_expert_ffn_backward(ctypes.byref(c), 4, FAKE, FAKE, FAKE, ctypes.byref(w), dy,
+                                         FAKE, None, None, FAKE, FAKE, FAKE, FAKE, ws, ws_bytes,
+                                         None)
+    wrow = moe.weights(w13=FAKE, w2=FAKE, ws13=FAKE, ws2=FAKE)
+    assert bwd(cfg, moe.weights(w13=FAKE, w2=FAKE, ws13=FAKE, ws2=FAKE, packed=1)) == \
+        moe.MOE_ERR_UNSUPPORTED
+    assert bwd(_cfg(wdtype="fp8"), wrow) == moe.MOE_ERR_UNSUPPORTED
+    assert bwd(cfg, wrow, dy=None) == moe.MOE_ERR_INVALID_ARG
+    assert bwd(cfg, wrow, ws_bytes=100) == moe.MOE_ERR_WORKSPACE
+    assert bwd(cfg, wrow, ws=FAKE * 256 + 4) == moe.MOE_ERR_WORKSPACE
+    assert moe.moe_expert_ffn_backward_workspace_bytes(_cfg(wdtype="fp8"), 16) == 0
+    assert moe.moe_expert_ffn_backward_workspace_bytes(cfg, 16) > 0
 
 
 def test_workspace_bytes_grows_with_tokens():
