@@ -118,6 +118,8 @@ def main():
                     help="just run warmup + steps (for rocprofv3), print the JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="copy 1 GiB device-to-device 5 times (HBM counter calibration)")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the expert-FFN backward measurement of the bf16 layer workloads")
     ap.add_argument("--row-major", action="store_true",
                     help="use the row-major weight layout instead of the packed one")
     args = ap.parse_args()
@@ -159,8 +161,13 @@ def main():
         inp = synth.gen_inputs(cfg)
     log(f"[bench] generated in {time.time() - t0:.1f}s; uploading")
     d = sd.to_device(inp)
+    # The expert-FFN backward (training) reads row-major bf16 weights: kept
+    # for the bf16 layer workloads of at least 1024 tokens.
+    with_bwd = (not args.no_backward and not gate_only and cfg.wdtype == "bf16" and
+                cfg.act == "bf16" and T >= 1024)
+    drow = d if with_bwd else None
     if cfg.wdtype != "f32" and not args.row_major and not gate_only:
-        d = sd.packed_copy(d)   # the row-major device copies are released here
+        d = sd.packed_copy(d)   # the row-major device copies are released here unless kept
     W = None if gate_only else sd.weights_struct(d)
     C = sd.moe_config(cfg)
     ws = sd.workspace(cfg, T)
@@ -266,6 +273,55 @@ def main():
                    "calls_per_s": round(nbu / (eb0.elapsed_time(eb1) * 1e-3), 1),
                    "bytes_per_launch": 12 * E, "bound": "launch latency (one workgroup)"}
 
+    # Backward of the expert FFNs for this batch's routing (training): output
+    # gradients of the routed rows and the shared expert -> input and weight
+    # gradients.  Not part of the layer step; reported beside it.
+    backward = None
+    if drow is not None:
+        gen = torch.Generator(device=dev).manual_seed(23)
+        dyb = torch.randn((T * K, H), generator=gen, device=dev).to(torch.bfloat16)
+        dysb = torch.randn((T, H), generator=gen, device=dev).to(torch.bfloat16) if Is else None
+        bf = dict(dtype=torch.bfloat16, device=dev)
+        dxb = torch.empty((T * K, H), **bf)
+        dxsb = torch.empty((T, H), **bf) if Is else None
+        dw13 = torch.empty((E, 2 * I, H), **bf)
+        dw2 = torch.empty((E, H, I), **bf)
+        dws13 = torch.empty((2 * Is, H), **bf) if Is else None
+        dws2 = torch.empty((H, Is), **bf) if Is else None
+        wsb = torch.empty(moe.moe_expert_ffn_backward_workspace_bytes(C, T), dtype=torch.uint8,
+                          device=dev)
+        Wrow = sd.weights_struct(drow)
+
+        def bwd():
+            moe.moe_expert_ffn_backward(C, T, drow["x"], perm, offs, Wrow, dyb, dysb, dxb, dxsb,
+                                        dw13, dw2, dws13, dws2, wsb, stream=stream)
+
+        bwd()
+        torch.cuda.synchronize()
+        moe.moe_kernel_timer_read()
+        moe.moe_kernel_timer_enable(True)
+        bwd()
+        torch.cuda.synchronize()
+        moe.moe_kernel_timer_enable(False)
+        bk = {k: round(v[0] / v[1], 4) for k, v in moe.moe_kernel_timer_read().items()}
+        nb = 5
+        eb0.record(stream)
+        for _ in range(nb):
+            bwd()
+        eb1.record(stream)
+        torch.cuda.synchronize()
+        bms = eb0.elapsed_time(eb1) / nb
+        rows_i = T * K * I + T * Is
+        bflop = 16.0 * rows_i * H     # recompute 4, dh 2, dx 4, dW2 2, dW13 4 (x rows*I*H)
+        # weights read once and their gradients written once, x, dy, dx once
+        bbytes = 2 * (active * 3 * H * I * 2 + 3 * H * Is * 2) + 3 * (T * K + T) * H * 2
+        backward = {"ms": round(bms, 3), "tflops": round(bflop / (bms * 1e-3) / 1e12, 1),
+                    "mfma_frac": round(bflop / (bms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                    "hbm_gbs": round(bbytes / (bms * 1e-3) / 1e9, 1),
+                    "hbm_frac": round(bbytes / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "algorithmic_flop": bflop, "algorithmic_bytes": bbytes, "kernels_ms": bk}
+        del dyb, dysb, dxb, dxsb, dw13, dw2, dws13, dws2, wsb
+
     # Algorithmic work (routed rows only; active experts' weights only).
     wbytes = 1 if cfg.wdtype == "fp8" else (2 if cfg.wdtype == "bf16" else 4)
     abytes = 2 if cfg.act == "bf16" else 4
@@ -339,6 +395,7 @@ def main():
         "kernels_ms": {k: round(v, 4) for k, v in sorted(kernels_ms.items())},
         "expert_ffn": ffn,
         "bias_update": bias_update,
+        "expert_backward": backward,
         "roofline": roof,
     }
 

@@ -70,6 +70,9 @@ def lib():
         L.oracle_ffn_backward.argtypes = [ctypes.POINTER(Cfg), i32, i64, vp, vp, i32, vp, vp, vp,
                                           vp, vp, i32, vp, vp, vp]
         L.oracle_ffn_backward.restype = ctypes.c_int
+        L.oracle_ffn_backward_entries.argtypes = [ctypes.POINTER(Cfg), i32, i64, vp, vp, i32, vp,
+                                                  vp, vp, vp, vp, i32, i64, vp, vp, vp, vp]
+        L.oracle_ffn_backward_entries.restype = ctypes.c_int
         L.oracle_bias_update.argtypes = [i32, vp, ctypes.c_float, vp, vp]
         L.oracle_bias_update.restype = ctypes.c_int
         _lib = L
@@ -272,3 +275,23 @@ def ffn_backward(cfg, inp: dict, expert: int, tokens, dy, want=("dx", "dw13", "d
     if rc:
         raise ValueError("oracle_ffn_backward rejected its arguments")
     return {k: v for k, v in out.items() if v is not None}
+
+
+def ffn_backward_entries(cfg, inp: dict, expert: int, tokens, dy, which, rows, cols):
+    """Selected entries of the expert's weight gradients (fp64), one by one:
+    which[q] = 0 -> dW13[rows[q], cols[q]], 1 -> dW2[rows[q], cols[q]]."""
+    x = _c(inp["x"])
+    tokens = _c(tokens, np.int64)
+    dy = _c(dy, np.float64)
+    which, rows, cols = (_c(a, np.int32) for a in (which, rows, cols))
+    wd = {"f32": F32, "bf16": BF16}[cfg.wdtype]
+    xd = F32 if cfg.act == "f32" else BF16
+    g = lambda k: None if inp.get(k) is None else _c(inp[k])
+    out = np.empty(len(which), np.float64)
+    rc = lib().oracle_ffn_backward_entries(ctypes.byref(cfg_of(cfg)), int(expert), len(tokens),
+                                           _p(tokens), _p(x), xd, _p(dy), _p(g("w13")),
+                                           _p(g("w2")), _p(g("ws13")), _p(g("ws2")), wd,
+                                           len(which), _p(which), _p(rows), _p(cols), _p(out))
+    if rc:
+        raise ValueError("oracle_ffn_backward_entries rejected its arguments")
+    return out

@@ -703,3 +703,56 @@ int oracle_ffn_backward(const oracle_cfg *c, int32_t e, int64_t n, const int64_t
     free(xs); free(g); free(u); free(h); free(da);
     return 0;
 }
+
+/* Selected entries of the same weight gradients, one by one, for rows too
+ * many for the full matrices (each entry costs O(n H)).  Entry q is
+ * dW13[rr[q]][cc[q]] when which[q] == 0 and dW2[rr[q]][cc[q]] when
+ * which[q] == 1, with the definitions of oracle_ffn_backward:
+ *   dW13[i][k]      = sum_r dg_r[i] x_r[k],  dW13[n+i][k] = sum_r du_r[i] x_r[k]
+ *   dW2[m][i]       = sum_r dy_r[m] h_r[i]
+ * where g_r[i], u_r[i] and dh_r[i] are recomputed for the entry's column i. */
+int oracle_ffn_backward_entries(const oracle_cfg *c, int32_t e, int64_t n, const int64_t *tokens,
+                                const void *x, int32_t x_dtype, const double *dy, const void *w13,
+                                const void *w2, const void *ws13, const void *ws2,
+                                int32_t w_dtype, int64_t nq, const int32_t *which,
+                                const int32_t *rr, const int32_t *cc, double *out)
+{
+    const int32_t H = c->H, E = c->E;
+    if (e < -1 || e >= E || (e == -1 && c->Is == 0) || w_dtype == OR_E4M3)
+        return 1;
+    const int32_t ne = e < 0 ? c->Is : c->I;
+    const void *W13 = e < 0 ? ws13 : expert_base(w13, w_dtype, e, (int64_t)2 * ne * H);
+    const void *W2 = e < 0 ? ws2 : expert_base(w2, w_dtype, e, (int64_t)H * ne);
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int64_t q = 0; q < nq; ++q) {
+        const int32_t r0 = rr[q], c0 = cc[q];
+        const int dw13 = which[q] == 0;
+        if ((dw13 && (r0 < 0 || r0 >= 2 * ne || c0 < 0 || c0 >= H)) ||
+            (!dw13 && (r0 < 0 || r0 >= H || c0 < 0 || c0 >= ne))) {
+            bad = 1;
+            continue;
+        }
+        const int32_t i = dw13 ? r0 % ne : c0;     /* the FFN column involved */
+        double acc = 0.0;
+        for (int64_t r = 0; r < n; ++r) {
+            double gs = 0.0, us = 0.0, dh = 0.0;
+            for (int32_t k = 0; k < H; ++k) {
+                double xv = mat_at(x, NULL, x_dtype, H, tokens[r], k);
+                gs += mat_at(W13, NULL, w_dtype, H, i, k) * xv;
+                us += mat_at(W13, NULL, w_dtype, H, ne + i, k) * xv;
+            }
+            double sg = 1.0 / (1.0 + exp(-gs));
+            if (dw13) {
+                for (int32_t m = 0; m < H; ++m)
+                    dh += dy[r * H + m] * mat_at(W2, NULL, w_dtype, ne, m, i);
+                double d = r0 < ne ? dh * us * sg * (1.0 + gs * (1.0 - sg)) : dh * gs * sg;
+                acc += d * mat_at(x, NULL, x_dtype, H, tokens[r], c0);
+            } else {
+                acc += dy[r * H + r0] * (gs * sg * us);
+            }
+        }
+        out[q] = acc;
+    }
+    return bad;
+}

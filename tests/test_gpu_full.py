@@ -23,6 +23,7 @@ pytestmark = pytest.mark.gpu
 class _Weights:
     """Full V3-shape expert weights, generated once per dtype (host + device)."""
     cache = {}
+    row = {}       # row-major bf16 device weights (the backward reads this layout)
 
     @classmethod
     def get(cls, wdtype):
@@ -37,6 +38,8 @@ class _Weights:
                 synth.gen_shared_weights(cfg)
             log(f"  generated in {time.time() - t0:.1f}s; uploading")
             dev_w = {k: sd.tensor(v) for k, v in host_w.items()}
+            if wdtype == "bf16":
+                cls.row[wdtype] = dict(dev_w)
             # the benchmark's configuration: packed weights
             dev_w = sd.packed_copy(dict(dev_w, cfg=cfg))
             dev_w.pop("cfg")
@@ -128,3 +131,90 @@ def test_layer_v3_fp8_T8192_sampled():
     q_ref, s_ref = oracle.quant_rows(synth.bf16_to_f32(inp["x"]))
     np.testing.assert_array_equal(host(xs), s_ref)
     np.testing.assert_array_equal(host(xq), q_ref)
+
+
+def test_expert_backward_v3_bf16_T4096_sampled():
+    """Backward of the expert FFNs at the full V3 shape, with the routing the
+    gate gives 4096 tokens and the row-major bf16 weights the benchmark's
+    backward reads: sampled rows of dx (routed and shared), sampled entries
+    of dW13 and dW2 for sampled experts and the shared expert, each set
+    within 2e-2 relative L2 of the fp64 oracle; every output finite and
+    experts without rows exactly zero."""
+    cfg = synth.C3
+    inp, dev = _inputs(cfg)
+    row = dict(dev, **_Weights.row["bf16"])
+    row.pop("packed", None)
+    T, H, E, K, I, Is = cfg.T, cfg.H, cfg.E, cfg.K, cfg.I, cfg.Is
+    N = T * K
+    log(f"{cfg.name}: backward of the expert FFNs")
+    _, idx, _ = run_gate(cfg, dev, T)
+    counts, offsets, perm, _, status = run_permute(cfg, idx)
+    assert status == moe.MOE_OK and counts.sum() == N
+    rng = np.random.default_rng(29)
+    dy_b = torch.from_numpy(rng.standard_normal((N, H), dtype=np.float32)).to(torch.bfloat16)
+    dys_b = torch.from_numpy(rng.standard_normal((T, H), dtype=np.float32)).to(torch.bfloat16)
+    dy_np = dy_b.float().numpy()
+    dys_np = dys_b.float().numpy()
+
+    C = sd.moe_config(cfg)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    bf = dict(dtype=torch.bfloat16, device=DEV)
+    dx, dxs = torch.empty((N, H), **bf), torch.empty((T, H), **bf)
+    dw13, dw2 = torch.empty((E, 2 * I, H), **bf), torch.empty((E, H, I), **bf)
+    dws13, dws2 = torch.empty((2 * Is, H), **bf), torch.empty((H, Is), **bf)
+    ws = torch.empty(moe.moe_expert_ffn_backward_workspace_bytes(C, T), dtype=torch.uint8,
+                     device=DEV)
+    moe.moe_expert_ffn_backward(C, T, row["x"], t(perm), t(offsets), sd.weights_struct(row),
+                                dy_b.to(DEV), dys_b.to(DEV), dx, dxs, dw13, dw2, dws13, dws2, ws)
+    sync()
+    for name, a in (("dx", dx), ("dx_shared", dxs), ("dW13", dw13), ("dW2", dw2),
+                    ("dW13_shared", dws13), ("dW2_shared", dws2)):
+        assert bool(torch.isfinite(a).all()), name
+    empty = np.flatnonzero(counts == 0)
+    for e in empty:
+        assert not bool(dw13[e].any()) and not bool(dw2[e].any()), f"expert {e} without rows"
+
+    t0 = time.time()
+    # dx: sampled routed rows (each row's gradient depends on that row alone)
+    rows = np.unique(synth.words(40, 31, synth.T_TEST, 52).astype(np.int64) % N)
+    g_dx = host(dx[t(rows)])
+    expert_of = np.searchsorted(offsets, rows, side="right") - 1
+    ref = np.empty_like(g_dx, dtype=np.float64)
+    for j, (r, e) in enumerate(zip(rows, expert_of)):
+        ref[j] = oracle.ffn_backward(cfg, inp, int(e), perm[r:r + 1] // K, dy_np[r:r + 1],
+                                     want=("dx",))["dx"][0]
+    worst = max(rel_l2(g_dx[j], ref[j]) for j in range(len(rows)))
+    log(f"  dx: {len(rows)} rows, worst row relL2 {worst:.3e}")
+    assert worst <= 2e-2
+    toks = _samples(T, 16, 53)
+    g = host(dxs[t(toks)])
+    ref = oracle.ffn_backward(cfg, inp, -1, toks, dys_np[toks], want=("dx",))["dx"]
+    worst = max(rel_l2(g[j], ref[j]) for j in range(len(toks)))
+    log(f"  shared dx: {len(toks)} tokens, worst row relL2 {worst:.3e}")
+    assert worst <= 2e-2
+
+    # weight gradients: sampled entries of the busiest, the least busy
+    # (with rows) and seeded other experts, and of the shared expert
+    busy = np.flatnonzero(counts > 0)
+    picks = {int(np.argmax(counts)), int(busy[np.argmin(counts[busy])])}
+    picks |= {int(busy[i]) for i in synth.words(4, 37, synth.T_TEST, 54) % len(busy)}
+    nq = 48
+    for e in sorted(picks) + [-1]:
+        ne = Is if e < 0 else I
+        r = synth.words(4 * nq, 41 + e, synth.T_TEST, 55).astype(np.int64)
+        which = np.repeat([0, 1], nq)
+        rr = np.concatenate([r[:nq] % (2 * ne), r[nq:2 * nq] % H])
+        cc = np.concatenate([r[2 * nq:3 * nq] % H, r[3 * nq:] % ne])
+        if e < 0:
+            tok, dyr = np.arange(T), dys_np
+            g13, g2 = host(dws13), host(dws2)
+        else:
+            r0, r1 = int(offsets[e]), int(offsets[e + 1])
+            tok, dyr = perm[r0:r1] // K, dy_np[r0:r1]
+            g13, g2 = host(dw13[e]), host(dw2[e])
+        ref = oracle.ffn_backward_entries(cfg, inp, e, tok, dyr, which, rr, cc)
+        got = np.concatenate([g13[rr[:nq], cc[:nq]], g2[rr[nq:], cc[nq:]]])
+        e13, e2 = rel_l2(got[:nq], ref[:nq]), rel_l2(got[nq:], ref[nq:])
+        log(f"  expert {e} ({len(tok)} rows): dW13 relL2 {e13:.3e}, dW2 relL2 {e2:.3e}")
+        assert e13 <= 2e-2 and e2 <= 2e-2, e
+    log(f"  oracle {time.time() - t0:.1f}s; experts without rows: {len(empty)}")

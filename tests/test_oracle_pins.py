@@ -619,3 +619,19 @@ def test_ffn_backward_zero_up_rows_give_zero_grads_but_gate_rows(fd_inputs):
     assert np.all(b["dw2"] == 0.0)
     assert np.all(b["dw13"][:cfg.I] == 0.0)
     assert np.any(b["dw13"][cfg.I:] != 0.0)
+
+
+@pytest.mark.parametrize("expert", [1, -1])
+def test_ffn_backward_entries_equal_full_gradients(fd_inputs, expert):
+    cfg, inp = FD_CFG, fd_inputs
+    tokens = np.array([2, 0, 5, 5, 1], np.int64)
+    dy = np.random.default_rng(14).standard_normal((len(tokens), cfg.H))
+    full = oracle.ffn_backward(cfg, inp, expert, tokens, dy)
+    ne = cfg.Is if expert < 0 else cfg.I
+    which = np.array([0] * (2 * ne * cfg.H) + [1] * (cfg.H * ne))
+    r13, c13 = np.divmod(np.arange(2 * ne * cfg.H), cfg.H)
+    r2, c2 = np.divmod(np.arange(cfg.H * ne), ne)
+    got = oracle.ffn_backward_entries(cfg, inp, expert, tokens, dy, which,
+                                      np.concatenate([r13, r2]), np.concatenate([c13, c2]))
+    np.testing.assert_allclose(got[:2 * ne * cfg.H], full["dw13"].ravel(), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(got[2 * ne * cfg.H:], full["dw2"].ravel(), rtol=1e-12, atol=1e-14)
