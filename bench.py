@@ -118,6 +118,8 @@ def main():
                     help="just run warmup + steps (for rocprofv3), print the JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="copy 1 GiB device-to-device 5 times (HBM counter calibration)")
+    ap.add_argument("--single-stream", action="store_true",
+                    help="time moe_forward on one stream instead of moe_forward_overlap")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the expert-FFN backward measurement of the bf16 layer workloads")
     ap.add_argument("--row-major", action="store_true",
@@ -185,12 +187,23 @@ def main():
     perm = torch.empty(T * K, dtype=torch.int32, device=dev)
     pos = torch.empty(T * K, dtype=torch.int32, device=dev)
 
+    # The layer step: moe_forward_overlap (the shared expert's GEMMs on a
+    # second stream, joined before the combine), or moe_forward on one stream.
+    shared_stream = torch.cuda.Stream()
+    overlap = not args.single_stream and not gate_only
+
+    def forward(two_streams):
+        if two_streams:
+            moe.moe_forward_overlap(C, T, d["x"], W, out, ws, shared_stream, stream=stream)
+        else:
+            moe.moe_forward(C, T, d["x"], W, out, ws, stream=stream)
+
     def step():
         if gate_only:
             moe.moe_gate(C, T, d["x"], d["gate_w"], d["bias"], lg, idx, wt, ws, stream=stream)
             moe.moe_permute(C, T, idx, counts, offs, perm, pos, ws, stream=stream)
         else:
-            moe.moe_forward(C, T, d["x"], W, out, ws, stream=stream)
+            forward(overlap)
 
     for _ in range(args.warmup):
         step()
@@ -224,6 +237,22 @@ def main():
     dom_ms /= dom_launches
     ms = ev0.elapsed_time(ev1) / args.steps
     log(f"[bench] {ms:.3f} ms/step; dominant kernel {dominant}: {dom_ms:.3f} ms/launch")
+
+    # The other forward path (one stream vs two), timed the same way.
+    other = None
+    if not gate_only:
+        for _ in range(2):
+            forward(not overlap)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            forward(not overlap)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        oms = ev0.elapsed_time(ev1) / args.steps
+        other = {"entry_point": "moe_forward" if overlap else "moe_forward_overlap",
+                 "ms": round(oms, 4), "tokens_per_s": round(T / (oms * 1e-3), 1)}
+        log(f"[bench] {other['entry_point']}: {oms:.3f} ms/step")
 
     # Per-phase timing with the separate entry points (same kernels, same
     # stream), HIP events between phases.
@@ -394,6 +423,9 @@ def main():
         "phases_ms": {p: round(v, 4) for p, v in acc.items()},
         "kernels_ms": {k: round(v, 4) for k, v in sorted(kernels_ms.items())},
         "expert_ffn": ffn,
+        "entry_point": None if gate_only else ("moe_forward_overlap" if overlap
+                                               else "moe_forward"),
+        "other_entry_point": other,
         "bias_update": bias_update,
         "expert_backward": backward,
         "roofline": roof,

@@ -168,10 +168,38 @@ moe_status moe_combine(const moe_config* cfg, int64_t T, const void* y, const vo
 /* The whole layer: gate, permute, expert FFNs, combine, enqueued in that
  * order.  out [T, H] act_dtype.  logits [T,E], topk_idx/topk_w [T,K],
  * counts [E] and perm [T*K] are optional copies of the intermediate results
- * (NULL: kept in the workspace only). */
+ * (NULL: kept in the workspace only).
+ * Decode batches (1 <= T <= 32) take a shorter schedule of the same steps:
+ * the gate as fp32 dot products straight from the fp32 gate weight over a
+ * few k ranges, the same selection kernel, then one workgroup that permutes
+ * and lays out the GEMM tiles.  The logits then differ from moe_gate's in
+ * rounding only (both are fp32 accumulations of the exact products); the
+ * choice is made from the logits written. */
 moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const moe_weights* w,
                        void* out, float* logits, int32_t* topk_idx, float* topk_w,
                        int32_t* counts, int32_t* perm, void* ws, size_t ws_bytes, void* stream);
+
+/* moe_forward with the shared expert on a second stream, the single-GPU
+ * part of the dual micro-batch overlap ("深入理解 DeepSeek-V3…", section 3.1):
+ * the always-active shared expert ("从 1024 块 GPU 到 558 万美元：拆解 DeepSeek-V3
+ * 的算法-系统协同设计", section 2.2) does not depend on the routing, so its GEMMs
+ * start on shared_stream at once and run beside the gate, the permutation
+ * and the routed experts on stream; stream waits for them before the
+ * combine.  Same arguments and outputs as moe_forward, bit for bit (the
+ * shared expert's tiles are the same kernels with the same arithmetic).
+ *   shared_stream: a stream of the same device, not stream.  Work enqueued on
+ *   it before the call runs before the shared expert; when the call returns,
+ *   every output is ordered on stream (shared_stream is not needed again).
+ * fp32 weights (and configs without a shared expert) run wholly on stream.
+ * The library keeps two HIP events per device and host thread for the fork
+ * and the join (created on first use).  The call may be captured into a
+ * HIP graph on stream.
+ * Errors: MOE_ERR_INVALID_ARG if shared_stream is NULL or equals stream; the
+ * rest as moe_forward. */
+moe_status moe_forward_overlap(const moe_config* cfg, int64_t T, const void* x,
+                               const moe_weights* w, void* out, float* logits, int32_t* topk_idx,
+                               float* topk_w, int32_t* counts, int32_t* perm, void* ws,
+                               size_t ws_bytes, void* stream, void* shared_stream);
 
 /* FP8 activation quantiser ("深入理解 DeepSeek-V3…", section 3.2: 1x128
  * activation tiles).  For each row of x [rows, H] (bf16, H % 128 == 0) and

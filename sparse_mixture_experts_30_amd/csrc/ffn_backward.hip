@@ -299,7 +299,7 @@ hipError_t launch_ffn_backward(const FfnDims& d, const uint16_t* x, const int32_
   base += al((size_t)(N * I + (sh ? T : 0) * Is) * 2);
   int32_t* tiles = (int32_t*)base;
 
-  hipError_t e = launch_build_tiles(offsets, E, T, sh, BBM, tiles, s);
+  hipError_t e = launch_build_tiles(offsets, E, T, true, sh, BBM, tiles, s);
   if (e != hipSuccess) return e;
   const int64_t mt = ffn_max_mtiles(N, T, E, BBM);
 

@@ -255,10 +255,9 @@ hipError_t launch_ffn_bf16(const FfnDims& d, const uint16_t* x, const int32_t* p
                            int32_t* tiles, uint16_t* y, uint16_t* ys, hipStream_t s) {
   hipError_t e = set_attrs();
   if (e != hipSuccess) return e;
-  const bool has_shared = d.Is > 0;
-  e = launch_build_tiles(offsets, d.E, d.T, has_shared, BM, tiles, s);
+  e = ffn_build_tiles(d, offsets, BM, tiles, s);
   if (e != hipSuccess) return e;
-  const int64_t mt = ffn_max_mtiles(d.N, d.T, d.E, BM);
+  const int64_t mt = ffn_grid_mtiles(d, BM);
   uint16_t* hs = h + d.N * d.I;
 
   GemmArgs a1{};

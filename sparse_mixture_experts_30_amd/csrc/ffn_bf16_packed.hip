@@ -582,9 +582,9 @@ hipError_t launch_ffn_bf16_packed(const FfnDims& d, const uint16_t* x, const int
   const int few = d.T <= 32 ? 1 : d.T <= 64 ? 2 : 0;
   const bool wide = !few && d.N >= (int64_t)kWideMinRows * d.E;
   const int bm1 = wide ? BMW : BM;
-  e = launch_build_tiles(offsets, d.E, d.T, d.Is > 0, bm1, tiles, s);
+  e = ffn_build_tiles(d, offsets, bm1, tiles, s);
   if (e != hipSuccess) return e;
-  const int64_t mt = ffn_max_mtiles(d.N, d.T, d.E, bm1);
+  const int64_t mt = ffn_grid_mtiles(d, bm1);
   uint16_t* hs = h + d.N * d.I;
   auto grid = [](int64_t max_work) {
     return (unsigned)(((max_work + kNumXcd - 1) / kNumXcd) * kNumXcd);
@@ -660,9 +660,9 @@ hipError_t launch_ffn_bf16_packed(const FfnDims& d, const uint16_t* x, const int
   else {
     // The down projection uses 128-row tiles, two workgroups per CU (with
     // wide tiles the list is already at 128 rows).
-    if (!wide) e = launch_build_tiles(offsets, d.E, d.T, d.Is > 0, BM2, tiles, s);
+    if (!wide) e = ffn_build_tiles(d, offsets, BM2, tiles, s);
     if (e != hipSuccess) return e;
-    const int64_t mt2 = ffn_max_mtiles(d.N, d.T, d.E, BM2);
+    const int64_t mt2 = ffn_grid_mtiles(d, BM2);
     MOE_TIMED_LAUNCH(s, "grouped_gemm_bf16_packed_x2<false>",
       hipLaunchKernelGGL(grouped_gemm_bf16_packed_x2<false>, dim3(grid(mt2 * a2.ntn)), dim3(NT),
                          kLdsP2, s, a2));

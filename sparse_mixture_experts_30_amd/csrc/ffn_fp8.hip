@@ -365,9 +365,9 @@ hipError_t launch_ffn_fp8(const FfnDims& d, const uint8_t* xq, const float* xs,
                           uint16_t* y, uint16_t* ys, hipStream_t s) {
   hipError_t e = set_attrs8();
   if (e != hipSuccess) return e;
-  e = launch_build_tiles(offsets, d.E, d.T, d.Is > 0, BM, tiles, s);
+  e = ffn_build_tiles(d, offsets, BM, tiles, s);
   if (e != hipSuccess) return e;
-  const int64_t mt = ffn_max_mtiles(d.N, d.T, d.E, BM);
+  const int64_t mt = ffn_grid_mtiles(d, BM);
   uint8_t* hq_s = hq + d.N * d.I;
   float* hs_s = hs + d.N * (d.I / 128);
 

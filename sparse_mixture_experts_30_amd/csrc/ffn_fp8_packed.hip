@@ -452,9 +452,9 @@ hipError_t launch_ffn_fp8_packed(const FfnDims& d, const uint8_t* xq, const floa
                                  uint16_t* y, uint16_t* ys, hipStream_t s) {
   hipError_t e = set_attrs_fp8_packed();
   if (e != hipSuccess) return e;
-  e = launch_build_tiles(offsets, d.E, d.T, d.Is > 0, BM, tiles, s);
+  e = ffn_build_tiles(d, offsets, BM, tiles, s);
   if (e != hipSuccess) return e;
-  const int64_t mt = ffn_max_mtiles(d.N, d.T, d.E, BM);
+  const int64_t mt = ffn_grid_mtiles(d, BM);
   auto grid = [](int64_t max_work) {
     return (unsigned)(((max_work + kNumXcd - 1) / kNumXcd) * kNumXcd);
   };

@@ -15,14 +15,16 @@ namespace moe {
 namespace {
 
 __global__ void __launch_bounds__(1024)
-build_tiles_kernel(const int32_t* __restrict__ offsets, int E, int64_t T, int has_shared,
-                   int BM, int32_t* __restrict__ tiles) {
+build_tiles_kernel(const int32_t* __restrict__ offsets, int E, int64_t T, int has_routed,
+                   int has_shared, int BM, int32_t* __restrict__ tiles) {
   __shared__ int32_t s[1024];
   const int g = threadIdx.x;
   int32_t n = 0, r0 = 0;
   if (g < E) {
-    r0 = offsets[g];
-    n = offsets[g + 1] - r0;
+    if (has_routed) {
+      r0 = offsets[g];
+      n = offsets[g + 1] - r0;
+    }
   } else if (g == E && has_shared) {
     n = (int32_t)T;
   }
@@ -53,11 +55,23 @@ int64_t ffn_max_mtiles(int64_t N, int64_t T, int E, int BM) {
   return (N + BM - 1) / BM + E + (T + BM - 1) / BM;
 }
 
-hipError_t launch_build_tiles(const int32_t* offsets, int E, int64_t T, bool has_shared, int BM,
-                              int32_t* tiles, hipStream_t s) {
+hipError_t launch_build_tiles(const int32_t* offsets, int E, int64_t T, bool has_routed,
+                              bool has_shared, int BM, int32_t* tiles, hipStream_t s) {
   MOE_TIMED_LAUNCH(s, "build_tiles_kernel",
     hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, E, T,
-                       has_shared ? 1 : 0, BM, tiles));
+                       has_routed ? 1 : 0, has_shared ? 1 : 0, BM, tiles));
   return hipGetLastError();
+}
+
+int64_t ffn_grid_mtiles(const FfnDims& d, int BM) {
+  const bool routed = d.groups & kGroupRouted, shared = (d.groups & kGroupShared) && d.Is > 0;
+  return (routed ? (d.N + BM - 1) / BM + d.E : 0) + (shared ? (d.T + BM - 1) / BM : 0);
+}
+
+hipError_t ffn_build_tiles(const FfnDims& d, const int32_t* offsets, int BM, int32_t* tiles,
+                           hipStream_t s) {
+  if (d.tiles_ready && d.T <= BM) return hipSuccess;
+  return launch_build_tiles(offsets, d.E, d.T, d.groups & kGroupRouted,
+                            (d.groups & kGroupShared) && d.Is > 0, BM, tiles, s);
 }
 }  // namespace moe

@@ -15,6 +15,7 @@
 // per call by a small kernel that also lays the three parts out in MFMA
 // fragment order; the GEMM then streams them straight into registers.
 #include "moe_internal.hpp"
+#include "select_device.hpp"
 
 #include <float.h>
 
@@ -222,21 +223,7 @@ gate_logits_f32_kernel(const float* __restrict__ x, const float* __restrict__ wg
   if (t < T && e < E) out[t * E + e] = acc;
 }
 
-// Wave-level argmax of (v, i): larger v wins, equal v -> lower i.
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    float ov = __shfl_xor(v, off, 64);
-    int oi = __shfl_xor(i, off, 64);
-    if (ov > v || (ov == v && oi < i)) {
-      v = ov;
-      i = oi;
-    }
-  }
-}
-
 constexpr int SEL_WAVES = 4;
-constexpr int SEL_MAXV = 8;   // E <= 512 = 64 lanes x 8
 
 // One wavefront selects for one token; lane l holds experts e = l + 64 v.
 // SW = 1: a workgroup holds SEL_WAVES tokens.  SW = SEL_WAVES (deep k
@@ -254,25 +241,19 @@ select_kernel(const float* __restrict__ part, int ksplit, const float* __restric
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t t = SW == 1 ? (int64_t)blockIdx.x * SEL_WAVES + wave : (int64_t)blockIdx.x;
   if (t >= T) return;   // uniform over the workgroup when SW > 1
-  const int Eg = E / G;
   const int V = (E + 63) / 64;
   const int s_begin = SW == 1 ? 0 : (int)((int64_t)ksplit * wave / SW);
   const int s_end = SW == 1 ? ksplit : (int)((int64_t)ksplit * (wave + 1) / SW);
 
   // Logits: the k-split partial sums of [s_begin, s_end) added in split
-  // order.  The loads of a batch of splits (for all of this lane's experts)
-  // are issued together and then added in order, so a deep split costs few
-  // memory round trips.
-  float lgs[SEL_MAXV];
+  // order.  The loads of a batch of eight splits (for all of this lane's
+  // experts) are issued together and then added in order, so a deep split
+  // costs few memory round trips.
+  float lgs[SEL_MAXV] = {};
   {
-    constexpr int SB = 4;    // splits per batch
+    constexpr int SB = 8;    // splits per batch
     const int64_t stride = T * E;
-#pragma unroll
-    for (int v = 0; v < SEL_MAXV; ++v) {
-      const int e = lane + 64 * v;
-      lgs[v] = (v < V && e < E) ? part[(int64_t)s_begin * stride + t * E + e] : 0.0f;
-    }
-    for (int s0 = s_begin + 1; s0 < s_end; s0 += SB) {
+    for (int s0 = s_begin; s0 < s_end; s0 += SB) {
       float pv[SB][SEL_MAXV];
 #pragma unroll
       for (int j = 0; j < SB; ++j)
@@ -285,8 +266,10 @@ select_kernel(const float* __restrict__ part, int ksplit, const float* __restric
 #pragma unroll
       for (int j = 0; j < SB; ++j)
 #pragma unroll
-        for (int v = 0; v < SEL_MAXV; ++v)
-          if (s0 + j < s_end) lgs[v] += pv[j][v];
+        for (int v = 0; v < SEL_MAXV; ++v) {
+          if (s0 + j == s_begin) lgs[v] = pv[j][v];          // the first split starts the sum
+          else if (s0 + j < s_end) lgs[v] += pv[j][v];
+        }
     }
   }
   if (SW > 1) {
@@ -311,84 +294,9 @@ select_kernel(const float* __restrict__ part, int ksplit, const float* __restric
     }
   }
 
-  float c[SEL_MAXV], s32[SEL_MAXV];
-#pragma unroll
-  for (int v = 0; v < SEL_MAXV; ++v) {
-    int e = lane + 64 * v;
-    c[v] = -INFINITY;
-    s32[v] = 0.0f;
-    if (v < V && e < E) {
-      const float lg = lgs[v];
-      if (logits_out) logits_out[t * E + e] = lg;
-      double sd = 1.0 / (1.0 + exp(-(double)lg));
-      s32[v] = (float)sd;
-      c[v] = s32[v] + bias[e];
-      s_c[wave][e] = c[v];
-      s_s[wave][e] = s32[v];
-    }
-  }
-  __syncwarp();
-
-  // Group score: sum of the two largest choice scores of group `lane`.
-  float g = -INFINITY;
-  if (lane < G) {
-    float m1 = -INFINITY, m2 = -INFINITY;
-    for (int j = 0; j < Eg; ++j) {
-      float v = s_c[wave][lane * Eg + j];
-      if (v > m1) {
-        m2 = m1;
-        m1 = v;
-      } else if (v > m2) {
-        m2 = v;
-      }
-    }
-    g = m1 + m2;
-  }
-  // Keep the TG best groups.
-  uint64_t keep = 0;
-  for (int r = 0; r < TG; ++r) {
-    float v = g;
-    int i = (lane < G && !((keep >> lane) & 1ull)) ? lane : 0x7fffffff;
-    if (i == 0x7fffffff) v = -INFINITY;
-    wave_argmax(v, i);
-    keep |= 1ull << i;
-  }
-  // Masked choice scores: 0.0 outside the kept groups.
-#pragma unroll
-  for (int v = 0; v < SEL_MAXV; ++v) {
-    int e = lane + 64 * v;
-    if (v < V && e < E && !((keep >> (e / Eg)) & 1ull)) c[v] = 0.0f;
-  }
-  // Top K, descending, ties to the lower expert id.
-  float my_s = 0.0f;
-  int my_e = 0;
-  uint32_t taken = 0;
-  for (int k = 0; k < K; ++k) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int v = 0; v < SEL_MAXV; ++v) {
-      int e = lane + 64 * v;
-      if (v < V && e < E && !((taken >> v) & 1u) && c[v] > bv) {
-        bv = c[v];
-        bi = e;
-      }
-    }
-    wave_argmax(bv, bi);
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    if (lane == k) {
-      my_e = bi;
-      my_s = s_s[wave][bi];
-    }
-  }
-  // Weights: unbiased scores, normalised over the K slots (K > 1), times rho.
-  float sum = 0.0f;
-  for (int k = 0; k < K; ++k) sum += __shfl(my_s, k, 64);
-  if (lane < K) {
-    float wv = (K > 1) ? my_s / (sum + 1e-20f) : my_s;
-    idx_out[t * K + lane] = my_e;
-    w_out[t * K + lane] = wv * rho;
-  }
+  select_token(lgs, lane, bias, s_c[wave], s_s[wave], E, G, TG, K, rho,
+               logits_out ? logits_out + t * E : nullptr, idx_out + t * K, w_out + t * K,
+               nullptr);
 }
 
 }  // namespace

@@ -76,9 +76,10 @@ size_t act_bytes(const moe_config* c) { return c->act_dtype == MOE_BF16 ? 2 : 4;
 
 // Workspace segments (byte offsets, 256-aligned).
 struct Layout {
-  size_t err, part, gsplit, idx, w, counts, offsets, perm, pos, hist, tiles, h, hs, xq, xs, y, ys,
-      total;
+  size_t err, part, gsplit, idx, w, counts, offsets, perm, pos, hist, tiles, tiles2, h, hs, xq,
+      xs, y, ys, total;
   int ksplit;
+  bool decode;   // decode routing (gate, selection, permutation, tile list in three launches)
 };
 
 Layout layout(const moe_config* c, int64_t T) {
@@ -88,6 +89,8 @@ Layout layout(const moe_config* c, int64_t T) {
   const int64_t N = T * K;
   const bool fp8 = c->weight_dtype == MOE_FP8_E4M3;
   L.ksplit = c->act_dtype == MOE_BF16 ? moe::gate_ksplit(T, (int)H, (int)E) : 1;
+  L.decode = moe::decode_route_ok(T, (int)H, (int)E, (int)K);
+  const int64_t nparts = std::max<int64_t>(L.ksplit, L.decode ? moe::decode_ksplit((int)H, (int)E) : 1);
   size_t o = 0;
   auto take = [&](size_t bytes) {
     size_t at = o;
@@ -95,7 +98,7 @@ Layout layout(const moe_config* c, int64_t T) {
     return at;
   };
   L.err = take(sizeof(int32_t));
-  L.part = take((size_t)L.ksplit * T * E * 4);
+  L.part = take((size_t)nparts * T * E * 4);
   L.gsplit = c->act_dtype == MOE_BF16 ? take(moe::gate_split_bytes((int)H, (int)E)) : o;
   L.idx = take((size_t)N * 4);
   L.w = take((size_t)N * 4);
@@ -106,6 +109,7 @@ Layout layout(const moe_config* c, int64_t T) {
   L.hist = take((size_t)moe::permute_nblk(N) * (E + 1) * 4);
   moe::FfnDims d{T, N, (int)H, (int)I, (int)Is, (int)E, (int)K};
   L.tiles = take(moe::ffn_tiles_bytes(d));
+  L.tiles2 = take(moe::ffn_tiles_bytes(d));   // the shared expert's list on a second stream
   const size_t hel = (size_t)(N * I + T * Is);
   if (fp8) {
     L.h = take(hel);
@@ -178,11 +182,18 @@ moe_status run_permute(const moe_config* c, int64_t T, const int32_t* idx, int32
   return MOE_OK;
 }
 
+// groups: which groups to compute (moe::kGroupRouted / kGroupShared);
+// tiles: the tile list to use (built here unless tiles_ready); quantize: fp8
+// weights only, quantise x first (else xq / xs already hold it).
 moe_status run_ffn(const moe_config* c, int64_t T, const void* x, const int32_t* perm,
                    const int32_t* offsets, const moe_weights* wt, void* y, void* ys, void* ws,
-                   const Layout& L, hipStream_t s) {
+                   const Layout& L, hipStream_t s, int groups = moe::kGroupsAll,
+                   int32_t* tiles = nullptr, bool tiles_ready = false, bool quantize = true) {
   moe::FfnDims d{T, T * c->num_experts_per_tok, c->hidden_size, c->moe_intermediate_size,
                  c->shared_intermediate_size, c->n_routed_experts, c->num_experts_per_tok};
+  d.groups = groups;
+  d.tiles_ready = tiles_ready;
+  if (!tiles) tiles = at<int32_t>(ws, L.tiles);
   switch (c->weight_dtype) {
     case MOE_F32:
       HIPCALL(moe::launch_ffn_f32(d, (const float*)x, perm, offsets, (const float*)wt->w13,
@@ -195,14 +206,14 @@ moe_status run_ffn(const moe_config* c, int64_t T, const void* x, const int32_t*
       if (wt->packed) {
         HIPCALL(moe::launch_ffn_bf16_packed(d, (const uint16_t*)x, perm, offsets, wt->w13, wt->w2,
                                             wt->ws13, wt->ws2, at<uint16_t>(ws, L.h),
-                                            at<int32_t>(ws, L.tiles), (uint16_t*)y,
+                                            tiles, (uint16_t*)y,
                                             (uint16_t*)ys, s),
                 "ffn bf16 packed");
       } else {
         HIPCALL(moe::launch_ffn_bf16(d, (const uint16_t*)x, perm, offsets,
                                      (const uint16_t*)wt->w13, (const uint16_t*)wt->w2,
                                      (const uint16_t*)wt->ws13, (const uint16_t*)wt->ws2,
-                                     at<uint16_t>(ws, L.h), at<int32_t>(ws, L.tiles),
+                                     at<uint16_t>(ws, L.h), tiles,
                                      (uint16_t*)y, (uint16_t*)ys, s),
                 "ffn bf16");
       }
@@ -210,13 +221,14 @@ moe_status run_ffn(const moe_config* c, int64_t T, const void* x, const int32_t*
     case MOE_FP8_E4M3: {
       uint8_t* xq = at<uint8_t>(ws, L.xq);
       float* xs = at<float>(ws, L.xs);
-      HIPCALL(moe::launch_quant_rows((const uint16_t*)x, T, c->hidden_size, xq, xs, s),
-              "quantise x");
+      if (quantize)
+        HIPCALL(moe::launch_quant_rows((const uint16_t*)x, T, c->hidden_size, xq, xs, s),
+                "quantise x");
       if (wt->packed) {
         HIPCALL(moe::launch_ffn_fp8_packed(d, xq, xs, perm, offsets, wt->w13, wt->w13_scale,
                                            wt->w2, wt->w2_scale, wt->ws13, wt->ws13_scale, wt->ws2,
                                            wt->ws2_scale, at<uint8_t>(ws, L.h), at<float>(ws, L.hs),
-                                           at<int32_t>(ws, L.tiles), (uint16_t*)y, (uint16_t*)ys,
+                                           tiles, (uint16_t*)y, (uint16_t*)ys,
                                            s),
                 "ffn fp8 packed");
         break;
@@ -225,7 +237,7 @@ moe_status run_ffn(const moe_config* c, int64_t T, const void* x, const int32_t*
                                   (const uint8_t*)wt->w2, wt->w2_scale, (const uint8_t*)wt->ws13,
                                   wt->ws13_scale, (const uint8_t*)wt->ws2, wt->ws2_scale,
                                   at<uint8_t>(ws, L.h), at<float>(ws, L.hs),
-                                  at<int32_t>(ws, L.tiles), (uint16_t*)y, (uint16_t*)ys, s),
+                                  tiles, (uint16_t*)y, (uint16_t*)ys, s),
               "ffn fp8");
       break;
     }
@@ -258,6 +270,92 @@ moe_status check_weights(const moe_config* c, const moe_weights* w, bool need_ga
       NONNULL(w->ws2_scale);
     }
   }
+  return MOE_OK;
+}
+
+
+// Events that order a call's work across its two streams, one pair per
+// device and host thread (created on first use, reused by every later call:
+// a wait takes the event's most recent record at the time it is enqueued).
+struct ForkJoin {
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+
+hipError_t fork_join_events(ForkJoin** out) {
+  constexpr int kMaxDevices = 64;
+  thread_local ForkJoin ev[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  ForkJoin& f = ev[dev];
+  if (!f.fork && (e = hipEventCreateWithFlags(&f.fork, hipEventDisableTiming)) != hipSuccess)
+    return e;
+  if (!f.join && (e = hipEventCreateWithFlags(&f.join, hipEventDisableTiming)) != hipSuccess)
+    return e;
+  *out = &f;
+  return hipSuccess;
+}
+
+// The layer on stream s.  With s2 (not null), the shared expert's GEMMs run
+// on s2, forked from s at the start and joined back before the combine.
+moe_status forward_impl(const moe_config* cfg, int64_t T, const void* x, const moe_weights* w,
+                        void* out, float* logits, int32_t* topk_idx, float* topk_w,
+                        int32_t* counts, int32_t* perm, void* ws, size_t ws_bytes,
+                        hipStream_t s, hipStream_t s2) {
+  CHECK(check_cfg(cfg));
+  CHECK(check_T(T, cfg));
+  if (T == 0) return MOE_OK;
+  NONNULL(x);
+  NONNULL(out);
+  CHECK(check_weights(cfg, w, true));
+  const Layout L = layout(cfg, T);
+  CHECK(check_ws(ws, ws_bytes, L));
+  int32_t* idx = topk_idx ? topk_idx : at<int32_t>(ws, L.idx);
+  float* wt = topk_w ? topk_w : at<float>(ws, L.w);
+  int32_t* cnt = counts ? counts : at<int32_t>(ws, L.counts);
+  int32_t* pm = perm ? perm : at<int32_t>(ws, L.perm);
+  int32_t* offs = at<int32_t>(ws, L.offsets);
+  int32_t* pos = at<int32_t>(ws, L.pos);
+  int32_t* tiles = at<int32_t>(ws, L.tiles);
+  void* y = at<void>(ws, L.y);
+  const bool sh = cfg->shared_intermediate_size > 0;
+  void* ys = sh ? at<void>(ws, L.ys) : nullptr;
+  const bool fp8 = cfg->weight_dtype == MOE_FP8_E4M3;
+  // The fp32 expert kernels compute every group in one launch.
+  const bool split = s2 && sh && cfg->weight_dtype != MOE_F32;
+
+  ForkJoin* ev = nullptr;
+  if (split) {
+    HIPCALL(fork_join_events(&ev), "fork/join events");
+    if (fp8)   // x is quantised once, before the fork, for both streams
+      HIPCALL(moe::launch_quant_rows((const uint16_t*)x, T, cfg->hidden_size, at<uint8_t>(ws, L.xq),
+                                     at<float>(ws, L.xs), s),
+              "quantise x");
+    HIPCALL(hipEventRecord(ev->fork, s), "fork");
+    HIPCALL(hipStreamWaitEvent(s2, ev->fork, 0), "fork");
+    CHECK(run_ffn(cfg, T, x, pm, offs, w, y, ys, ws, L, s2, moe::kGroupShared,
+                  at<int32_t>(ws, L.tiles2), false, false));
+    HIPCALL(hipEventRecord(ev->join, s2), "join");
+  }
+  const int groups = split ? moe::kGroupRouted : moe::kGroupsAll;
+  if (L.decode) {
+    HIPCALL(moe::launch_decode_route(x, cfg->act_dtype == MOE_BF16, w->gate_w, w->bias,
+                                     at<float>(ws, L.part), logits, idx, wt, T, cfg->hidden_size,
+                                     cfg->n_routed_experts, cfg->n_group, cfg->topk_group,
+                                     cfg->num_experts_per_tok, cfg->routed_scaling_factor, cnt,
+                                     offs, pm, pos, at<int32_t>(ws, L.err), tiles, true,
+                                     (groups & moe::kGroupShared) && sh, s),
+            "decode routing");
+  } else {
+    CHECK(run_gate(cfg, T, x, w->gate_w, w->bias, logits, idx, wt, ws, L, s));
+    CHECK(run_permute(cfg, T, idx, cnt, offs, pm, pos, ws, L, s));
+  }
+  CHECK(run_ffn(cfg, T, x, pm, offs, w, y, ys, ws, L, s, groups, tiles, L.decode, !split));
+  if (split) HIPCALL(hipStreamWaitEvent(s, ev->join, 0), "join");
+  HIPCALL(moe::launch_combine(y, ys, pos, wt, out, T, cfg->hidden_size, cfg->num_experts_per_tok,
+                              cfg->act_dtype == MOE_BF16, s),
+          "combine");
   return MOE_OK;
 }
 
@@ -343,30 +441,18 @@ moe_status moe_combine(const moe_config* cfg, int64_t T, const void* y, const vo
 moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const moe_weights* w,
                        void* out, float* logits, int32_t* topk_idx, float* topk_w,
                        int32_t* counts, int32_t* perm, void* ws, size_t ws_bytes, void* stream) {
-  CHECK(check_cfg(cfg));
-  CHECK(check_T(T, cfg));
-  if (T == 0) return MOE_OK;
-  NONNULL(x);
-  NONNULL(out);
-  CHECK(check_weights(cfg, w, true));
-  const Layout L = layout(cfg, T);
-  CHECK(check_ws(ws, ws_bytes, L));
-  hipStream_t s = (hipStream_t)stream;
-  int32_t* idx = topk_idx ? topk_idx : at<int32_t>(ws, L.idx);
-  float* wt = topk_w ? topk_w : at<float>(ws, L.w);
-  int32_t* cnt = counts ? counts : at<int32_t>(ws, L.counts);
-  int32_t* pm = perm ? perm : at<int32_t>(ws, L.perm);
-  int32_t* offs = at<int32_t>(ws, L.offsets);
-  int32_t* pos = at<int32_t>(ws, L.pos);
-  void* y = at<void>(ws, L.y);
-  void* ys = cfg->shared_intermediate_size > 0 ? at<void>(ws, L.ys) : nullptr;
-  CHECK(run_gate(cfg, T, x, w->gate_w, w->bias, logits, idx, wt, ws, L, s));
-  CHECK(run_permute(cfg, T, idx, cnt, offs, pm, pos, ws, L, s));
-  CHECK(run_ffn(cfg, T, x, pm, offs, w, y, ys, ws, L, s));
-  HIPCALL(moe::launch_combine(y, ys, pos, wt, out, T, cfg->hidden_size, cfg->num_experts_per_tok,
-                              cfg->act_dtype == MOE_BF16, s),
-          "combine");
-  return MOE_OK;
+  return forward_impl(cfg, T, x, w, out, logits, topk_idx, topk_w, counts, perm, ws, ws_bytes,
+                      (hipStream_t)stream, nullptr);
+}
+
+moe_status moe_forward_overlap(const moe_config* cfg, int64_t T, const void* x,
+                               const moe_weights* w, void* out, float* logits, int32_t* topk_idx,
+                               float* topk_w, int32_t* counts, int32_t* perm, void* ws,
+                               size_t ws_bytes, void* stream, void* shared_stream) {
+  if (!shared_stream || shared_stream == stream)
+    return fail(MOE_ERR_INVALID_ARG, "shared_stream must be a stream other than stream");
+  return forward_impl(cfg, T, x, w, out, logits, topk_idx, topk_w, counts, perm, ws, ws_bytes,
+                      (hipStream_t)stream, (hipStream_t)shared_stream);
 }
 
 size_t moe_expert_ffn_backward_workspace_bytes(const moe_config* cfg, int64_t T) {

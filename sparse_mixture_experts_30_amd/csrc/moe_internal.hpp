@@ -90,6 +90,18 @@ hipError_t launch_select(const float* partials, int ksplit, const float* bias, f
                          int32_t* idx, float* w, int64_t T, int E, int G, int TG, int K,
                          float rho, hipStream_t s);
 
+// Decode routing (decode.hip): gate, selection, permutation and the tile
+// list of the expert GEMMs in three launches, for 1 <= T <= kDecodeMaxT.
+constexpr int kDecodeMaxT = 32;
+bool decode_route_ok(int64_t T, int H, int E, int K);
+int decode_ksplit(int H, int E);   // partial sums [ksplit, T, E] in `partials`
+hipError_t launch_decode_route(const void* x, bool x_bf16, const float* gate_w,
+                               const float* bias, float* partials, float* logits_out,
+                               int32_t* idx, float* w, int64_t T, int H, int E, int G, int TG,
+                               int K, float rho, int32_t* counts, int32_t* offsets,
+                               int32_t* perm, int32_t* pos, int32_t* err, int32_t* tiles,
+                               bool has_routed, bool has_shared, hipStream_t s);
+
 int permute_nblk(int64_t N);
 hipError_t launch_permute(const int32_t* idx, int64_t N, int E, int32_t* hist, int32_t* counts,
                           int32_t* offsets, int32_t* perm, int32_t* pos, int32_t* err,
@@ -98,9 +110,11 @@ hipError_t launch_permute(const int32_t* idx, int64_t N, int E, int32_t* hist, i
 // Expert FFN tile schedule (see ffn_sched.hip for the entry format).  The
 // smallest M-tile height any GEMM uses sizes the list in the workspace.
 constexpr int kMinTileRows = 128;
+// Groups of an expert-FFN launch: the routed experts, the shared expert.
+constexpr int kGroupRouted = 1, kGroupShared = 2, kGroupsAll = 3;
 int64_t ffn_max_mtiles(int64_t N, int64_t T, int E, int BM);
-hipError_t launch_build_tiles(const int32_t* offsets, int E, int64_t T, bool has_shared, int BM,
-                              int32_t* tiles, hipStream_t s);
+hipError_t launch_build_tiles(const int32_t* offsets, int E, int64_t T, bool has_routed,
+                              bool has_shared, int BM, int32_t* tiles, hipStream_t s);
 
 // Work item w (0 <= w < tiles[0] * ntn) of a grouped GEMM with ntn N-tiles:
 // returns the M-tile entry and the N-tile.  Inside a group the N-tile index
@@ -121,8 +135,16 @@ struct FfnDims {
   int64_t T;       // tokens
   int64_t N;       // routed rows T*K
   int H, I, Is, E, K;
+  int groups = kGroupsAll;   // which groups the launch computes
+  bool tiles_ready = false;  // the tile list is already built (decode routing)
 };
 size_t ffn_tiles_bytes(const FfnDims& d);
+// M-tiles a launch over d's groups can have (sizes its grid).
+int64_t ffn_grid_mtiles(const FfnDims& d, int BM);
+// The tile list of d's groups with M-tiles of BM rows, unless d says it is
+// ready and no group can exceed one tile (T <= BM).
+hipError_t ffn_build_tiles(const FfnDims& d, const int32_t* offsets, int BM, int32_t* tiles,
+                           hipStream_t s);
 hipError_t launch_ffn_bf16(const FfnDims& d, const uint16_t* x, const int32_t* perm,
                            const int32_t* offsets, const uint16_t* w13, const uint16_t* w2,
                            const uint16_t* ws13, const uint16_t* ws2, uint16_t* h,

@@ -14,6 +14,7 @@
 //      equal ids before it (wave ballots on the id bits, then a prefix over the
 //      waves), added to the running base.
 #include "moe_internal.hpp"
+#include "permute_device.hpp"
 
 namespace moe {
 
@@ -21,7 +22,6 @@ namespace {
 
 constexpr int PCHUNK = 2048;   // flat indices per block
 constexpr int PTHREADS = 256;
-constexpr int PMAXE = 512;
 
 __global__ void __launch_bounds__(PTHREADS)
 hist_kernel(const int32_t* __restrict__ idx, int64_t N, int E, int32_t* __restrict__ hist) {
@@ -147,72 +147,8 @@ __global__ void __launch_bounds__(PMAXE)
 permute_small_kernel(const int32_t* __restrict__ idx, int N, int E, int32_t* __restrict__ counts,
                      int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
                      int32_t* __restrict__ pos, int32_t* __restrict__ err) {
-  constexpr int W = PMAXE / 64;
-  __shared__ int32_t h[PMAXE + 1];   // h[E] counts ids outside [0, E)
-  __shared__ int32_t s[PMAXE];
-  __shared__ int32_t running[PMAXE];
-  __shared__ int32_t wcnt[W][PMAXE];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int e = tid; e <= E; e += PMAXE) h[e] = 0;
-  for (int e = tid; e < PMAXE; e += PMAXE)
-#pragma unroll
-    for (int w = 0; w < W; ++w) wcnt[w][e] = 0;
-  __syncthreads();
-  for (int f = tid; f < N; f += PMAXE) {
-    const int e = idx[f];
-    atomicAdd(&h[(e >= 0 && e < E) ? e : E], 1);
-  }
-  __syncthreads();
-  const int32_t mine = (tid < E) ? h[tid] : 0;
-  if (tid < E) counts[tid] = mine;
-  if (tid == 0) *err = h[E] ? 1 : 0;
-  s[tid] = mine;
-  __syncthreads();
-  for (int off = 1; off < PMAXE; off <<= 1) {
-    const int32_t v = (tid >= off) ? s[tid - off] : 0;
-    __syncthreads();
-    s[tid] += v;
-    __syncthreads();
-  }
-  const int32_t excl = s[tid] - mine;
-  if (tid < E) {
-    offsets[tid] = excl;
-    running[tid] = excl;
-  }
-  if (tid == E - 1) offsets[E] = s[tid];
-  __syncthreads();
-  // Stable scatter, PMAXE elements at a time in index order (as scatter_kernel).
-  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int sub = 0; sub < N; sub += PMAXE) {
-    const int f = sub + tid;
-    int e = (f < N) ? idx[f] : -1;
-    const bool valid = (e >= 0 && e < E);
-    if (!valid) e = -1;
-    uint64_t peers = ~0ull;
-#pragma unroll
-    for (int bit = 0; bit < 10; ++bit) {
-      const bool b = (e >> bit) & 1;
-      const uint64_t m = __ballot(b);
-      peers &= b ? m : ~m;
-    }
-    const int rank = __popcll(peers & lt);
-    const bool leader = (peers & lt) == 0;
-    const int cnt = __popcll(peers);
-    if (valid && leader) wcnt[wave][e] = cnt;
-    __syncthreads();
-    if (valid) {
-      int p = running[e] + rank;
-      for (int w = 0; w < wave; ++w) p += wcnt[w][e];
-      perm[p] = f;
-      pos[f] = p;
-    }
-    __syncthreads();
-    if (valid && leader) {
-      atomicAdd(&running[e], cnt);
-      wcnt[wave][e] = 0;
-    }
-    __syncthreads();
-  }
+  __shared__ PermuteLds<PMAXE> L;
+  block_permute<PMAXE>(L, idx, N, E, counts, offsets, perm, pos, err);
 }
 
 }  // namespace

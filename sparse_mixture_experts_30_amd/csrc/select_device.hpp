@@ -1,0 +1,129 @@
+// Per-token expert selection by one wavefront (page "从 1024 块 GPU 到 558 万美元：
+// 拆解 DeepSeek-V3 的算法-系统协同设计", section 2.2, MoEGate): sigmoid scores,
+// the selection-only bias, the group score as the sum of a group's two
+// largest choice scores, the topk_group best groups, the top_k best experts
+// inside them (0.0 for experts outside), and the weights from the unbiased
+// scores, normalised over the chosen experts when top_k > 1, times
+// routed_scaling_factor.
+#pragma once
+
+#include "moe_internal.hpp"
+
+namespace moe {
+
+constexpr int SEL_MAXV = 8;   // E <= 512 = 64 lanes x 8
+
+// Wave-level argmax of (v, i): larger v wins, equal v -> lower i.
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    float ov = __shfl_xor(v, off, 64);
+    int oi = __shfl_xor(i, off, 64);
+    if (ov > v || (ov == v && oi < i)) {
+      v = ov;
+      i = oi;
+    }
+  }
+}
+
+// Lane l holds the logits of experts e = l + 64 v (v < ceil(E / 64)).  s_c
+// and s_s are this wavefront's LDS rows of at least E floats.  Writes the
+// logits row (if logits_row is not null), the K chosen ids and weights; the
+// ids also go to idx_lds when it is not null.
+__device__ __forceinline__ void select_token(const float (&lgs)[SEL_MAXV], int lane,
+                                             const float* __restrict__ bias, float* s_c,
+                                             float* s_s, int E, int G, int TG, int K, float rho,
+                                             float* logits_row, int32_t* idx_row, float* w_row,
+                                             int32_t* idx_lds) {
+  const int Eg = E / G;
+  const int V = (E + 63) / 64;
+  float c[SEL_MAXV], s32[SEL_MAXV];
+#pragma unroll
+  for (int v = 0; v < SEL_MAXV; ++v) {
+    const int e = lane + 64 * v;
+    c[v] = -INFINITY;
+    s32[v] = 0.0f;
+    if (v < V && e < E) {
+      const float lg = lgs[v];
+      if (logits_row) logits_row[e] = lg;
+      const double sd = 1.0 / (1.0 + exp(-(double)lg));
+      s32[v] = (float)sd;
+      c[v] = s32[v] + bias[e];
+      s_c[e] = c[v];
+      s_s[e] = s32[v];
+    }
+  }
+  __syncwarp();
+
+  // Group score: sum of the two largest choice scores of group `lane`.
+  // The scores are read eight at a time (independent LDS loads) and taken
+  // in index order.
+  float g = -INFINITY;
+  if (lane < G) {
+    float m1 = -INFINITY, m2 = -INFINITY;
+    for (int j0 = 0; j0 < Eg; j0 += 8) {
+      float v8[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v8[j] = (j0 + j < Eg) ? s_c[lane * Eg + j0 + j] : -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float v = v8[j];
+        if (v > m1) {
+          m2 = m1;
+          m1 = v;
+        } else if (v > m2) {
+          m2 = v;
+        }
+      }
+    }
+    g = m1 + m2;
+  }
+  // Keep the TG best groups.
+  uint64_t keep = 0;
+  for (int r = 0; r < TG; ++r) {
+    float v = g;
+    int i = (lane < G && !((keep >> lane) & 1ull)) ? lane : 0x7fffffff;
+    if (i == 0x7fffffff) v = -INFINITY;
+    wave_argmax(v, i);
+    keep |= 1ull << i;
+  }
+  // Masked choice scores: 0.0 outside the kept groups.
+#pragma unroll
+  for (int v = 0; v < SEL_MAXV; ++v) {
+    const int e = lane + 64 * v;
+    if (v < V && e < E && !((keep >> (e / Eg)) & 1ull)) c[v] = 0.0f;
+  }
+  // Top K, descending, ties to the lower expert id.
+  float my_s = 0.0f;
+  int my_e = 0;
+  uint32_t taken = 0;
+  for (int k = 0; k < K; ++k) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int v = 0; v < SEL_MAXV; ++v) {
+      const int e = lane + 64 * v;
+      if (v < V && e < E && !((taken >> v) & 1u) && c[v] > bv) {
+        bv = c[v];
+        bi = e;
+      }
+    }
+    wave_argmax(bv, bi);
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    if (lane == k) {
+      my_e = bi;
+      my_s = s_s[bi];
+    }
+  }
+  // Weights: unbiased scores, normalised over the K slots (K > 1), times rho.
+  float sum = 0.0f;
+  for (int k = 0; k < K; ++k) sum += __shfl(my_s, k, 64);
+  if (lane < K) {
+    const float wv = (K > 1) ? my_s / (sum + 1e-20f) : my_s;
+    idx_row[lane] = my_e;
+    w_row[lane] = wv * rho;
+    if (idx_lds) idx_lds[lane] = my_e;
+  }
+}
+
+}  // namespace moe

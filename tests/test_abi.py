@@ -84,6 +84,16 @@ def test_argument_validation():
                             FAKE * 256, 1 << 40, None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_forward(ctypes.byref(cfg), 4, FAKE, ctypes.byref(w), FAKE, None, None, None,
                          None, None, FAKE * 256, 1 << 40, None) == moe.MOE_ERR_INVALID_ARG
+    # the overlapped forward needs a second stream distinct from the first
+    wf = moe.weights(gate_w=FAKE, bias=FAKE, w13=FAKE, w2=FAKE, ws13=FAKE, ws2=FAKE)
+    for s1, s2 in ((None, None), (FAKE, FAKE)):
+        assert L.moe_forward_overlap(ctypes.byref(cfg), 4, FAKE, ctypes.byref(wf), FAKE, None,
+                                     None, None, None, None, FAKE * 256, 1 << 40, s1,
+                                     s2) == moe.MOE_ERR_INVALID_ARG
+    assert "shared_stream" in moe.moe_last_error()
+    assert L.moe_forward_overlap(ctypes.byref(cfg), 4, FAKE, ctypes.byref(w), FAKE, None, None,
+                                 None, None, None, FAKE * 256, 1 << 40, None,
+                                 FAKE) == moe.MOE_ERR_INVALID_ARG   # shared weights missing
     assert L.moe_combine(ctypes.byref(cfg), 4, FAKE, None, FAKE, FAKE, FAKE, None) == \
         moe.MOE_ERR_INVALID_ARG                                          # y_shared NULL, Is > 0
     cfg8 = _cfg(wdtype="fp8")

@@ -1,0 +1,201 @@
+"""GPU parity of the decode schedule of moe_forward (1 <= T <= 32: the gate
+as fp32 dot products over a few k ranges, the selection, then one workgroup
+that permutes and lays out the tile list) and of moe_forward_overlap (the shared expert on a second
+stream), against the fp64 oracle and against moe_forward itself."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import sparse_mixture_experts_30_amd as moe
+from synth import device as sd
+
+from gpu_util import DEV, check_routing, host, layer_reference, log, rel_l2, run_forward, sync
+
+pytestmark = pytest.mark.gpu
+
+DECODE_CASES = [
+    # several tiles of N for the GEMMs, every expert count of a V3-like gate
+    synth.C3.replace(name="dec-bf16-T32-H1024-E64-K8", T=32, H=1024, E=64, G=8, TG=4, K=8, I=256,
+                     Is=256, rho=2.5),
+    # 512 experts: eight per lane in the selection, four k ranges in the gate
+    synth.C3.replace(name="dec-bf16-T32-H256-E512-G16-K8", T=32, H=256, E=512, G=16, TG=4, K=8,
+                     I=128, Is=128, rho=2.5),
+    # ragged batch, one group (plain top-k), no shared expert
+    synth.C3.replace(name="dec-bf16-T19-H512-E32-G1-K6-noshared", T=19, H=512, E=32, G=1, TG=1,
+                     K=6, I=128, Is=0, rho=1.5),
+    # every expert chosen by every token: 2048 flat ids, the largest list
+    synth.C3.replace(name="dec-bf16-T32-H256-E64-G1-K64", T=32, H=256, E=64, G=1, TG=1, K=64,
+                     I=64, Is=64, rho=1.0),
+    # k ranges of 72 elements: the gate's loop ends with a chunk of 8
+    synth.C3.replace(name="dec-bf16-T5-H576-E256-K8", T=5, H=576, E=256, G=8, TG=4, K=8, I=64,
+                     Is=64, rho=2.5),
+    synth.C5.replace(name="dec-fp8-T24-H1024-E32-K4", T=24, H=1024, E=32, G=4, TG=2, K=4, I=256,
+                     Is=384, rho=2.5),
+    synth.C1.replace(name="dec-f32-T20-H128-E16", T=20),
+]
+
+_inputs = {}
+
+
+def inputs(cfg):
+    if cfg.name not in _inputs:
+        inp = synth.gen_inputs(cfg)
+        _inputs[cfg.name] = (inp, sd.to_device(inp))
+    return _inputs[cfg.name]
+
+
+def _tol(cfg):
+    return {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2}[cfg.wdtype]
+
+
+@pytest.mark.parametrize("packed", [True, False], ids=["packed", "rowmajor"])
+@pytest.mark.parametrize("cfg", DECODE_CASES, ids=lambda c: c.name)
+def test_decode_forward(cfg, packed):
+    if packed and cfg.wdtype == "f32":
+        pytest.skip("the packed layout is for bf16 and e4m3 weights")
+    log(f"decode {cfg.name} packed={packed}")
+    inp, dev = inputs(cfg)
+    if packed:
+        dev = sd.packed_copy(dev)
+    r = run_forward(cfg, dev, cfg.T)
+    check_routing(cfg, inp["x"], inp["gate_w"], inp["bias"], r["logits"], r["idx"], r["w"],
+                  cfg.name)
+    idx_c, _ = oracle.route_f32(cfg, r["logits"], inp["bias"])
+    rc, _, rp, _ = oracle.permute(idx_c, cfg.E)
+    np.testing.assert_array_equal(r["counts"], rc)
+    np.testing.assert_array_equal(r["perm"], rp)
+    ref, nalt = layer_reference(cfg, inp, r["idx"], np.arange(cfg.T))
+    rel = rel_l2(r["out"], ref)
+    log(f"  out relL2={rel:.3e} (tol {_tol(cfg)}), near-tie tokens={nalt}")
+    assert rel <= _tol(cfg)
+
+
+def test_decode_schedule_launches():
+    """T <= 32 runs the decode routing kernels and not the batch path's gate,
+    permutation or tile list; T = 33 runs the batch path."""
+    cfg = DECODE_CASES[0]
+    inp, dev = inputs(cfg)
+    dev = sd.packed_copy(dev)
+    for T, want, absent in ((32, ("gate_decode_kernel", "select_kernel", "route_decode_kernel"),
+                             ("gate_split_kernel", "gate_logits_bf16_kernel",
+                              "permute_small_kernel", "build_tiles_kernel")),
+                            (33, ("gate_logits_bf16_kernel", "select_kernel",
+                                  "permute_small_kernel", "build_tiles_kernel"),
+                             ("gate_decode_kernel", "route_decode_kernel"))):
+        x = sd.tensor(np.ascontiguousarray(np.resize(inp["x"], (T, cfg.H))))
+        moe.moe_kernel_timer_read()
+        moe.moe_kernel_timer_enable(True)
+        ws = sd.workspace(cfg, T)
+        out = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=DEV)
+        moe.moe_forward(sd.moe_config(cfg), T, x, sd.weights_struct(dev), out, ws)
+        sync()
+        moe.moe_kernel_timer_enable(False)
+        kt = moe.moe_kernel_timer_read()
+        log(f"  T={T}: {sorted(kt)}")
+        for name in want:
+            assert name in kt and kt[name][1] == 1, (T, name)
+        for name in absent:
+            assert name not in kt, (T, name)
+
+
+OVERLAP_CASES = [
+    (DECODE_CASES[0], True),
+    (DECODE_CASES[5], False),      # fp8 row-major, decode
+    (synth.C3.replace(name="ovl-bf16-T300-H1024-E64", T=300, H=1024, E=64, G=8, TG=4, K=8, I=256,
+                      Is=256, rho=2.5), True),
+    (synth.C3.replace(name="ovl-bf16-T300-H1024-E64", T=300, H=1024, E=64, G=8, TG=4, K=8, I=256,
+                      Is=256, rho=2.5), False),
+    (synth.C5.replace(name="ovl-fp8-T200-H1024-E32", T=200, H=1024, E=32, G=4, TG=2, K=4, I=256,
+                      Is=384, rho=2.5), True),
+    # >= 256 rows per expert: the wide GEMM tiles
+    (synth.C3.replace(name="ovl-bf16-T1100-H768-E4-K1", T=1100, H=768, E=4, G=2, TG=1, K=1,
+                      I=384, Is=256, rho=1.3), True),
+    (DECODE_CASES[2], True),       # no shared expert: wholly on the first stream
+    (DECODE_CASES[6], False),      # fp32: wholly on the first stream
+]
+
+
+def _forward_outputs(cfg, dev, T, shared_stream=None):
+    C = sd.moe_config(cfg)
+    W = sd.weights_struct(dev)
+    ws = sd.workspace(cfg, T)
+    o = {"out": torch.empty((T, cfg.H), dtype=torch.bfloat16 if cfg.act == "bf16"
+                            else torch.float32, device=DEV),
+         "logits": torch.empty((T, cfg.E), dtype=torch.float32, device=DEV),
+         "idx": torch.empty((T, cfg.K), dtype=torch.int32, device=DEV),
+         "w": torch.empty((T, cfg.K), dtype=torch.float32, device=DEV),
+         "counts": torch.empty(cfg.E, dtype=torch.int32, device=DEV),
+         "perm": torch.empty(T * cfg.K, dtype=torch.int32, device=DEV)}
+    args = dict(logits=o["logits"], topk_idx=o["idx"], topk_w=o["w"], counts=o["counts"],
+                perm=o["perm"])
+    if shared_stream is None:
+        moe.moe_forward(C, T, dev["x"], W, o["out"], ws, **args)
+    else:
+        moe.moe_forward_overlap(C, T, dev["x"], W, o["out"], ws, shared_stream, **args)
+    sync()
+    return {k: host(v) for k, v in o.items()}
+
+
+def _case_id(case):
+    cfg, packed = case
+    return f"{cfg.name}-{'packed' if packed else 'rowmajor'}"
+
+
+@pytest.mark.parametrize("case", OVERLAP_CASES, ids=_case_id)
+def test_forward_overlap_bit_identical(case):
+    cfg, packed = case
+    log(f"overlap {cfg.name} packed={packed}")
+    _, dev = inputs(cfg)
+    if packed:
+        dev = sd.packed_copy(dev)
+    ref = _forward_outputs(cfg, dev, cfg.T)
+    s2 = torch.cuda.Stream()
+    for rep in range(2):
+        got = _forward_outputs(cfg, dev, cfg.T, shared_stream=s2)
+        for k in ref:
+            assert np.array_equal(got[k], ref[k]), (rep, k)
+
+
+def test_forward_overlap_graph_replay():
+    """moe_forward_overlap captured into a HIP graph (the second stream joins
+    the capture through the fork event) replays bit-identically to eager
+    moe_forward, several times, with eager calls between the replays."""
+    cfg = OVERLAP_CASES[2][0]
+    _, dev = inputs(cfg)
+    dev = sd.packed_copy(dev)
+    T = cfg.T
+    C = sd.moe_config(cfg)
+    W = sd.weights_struct(dev)
+    ws = sd.workspace(cfg, T)
+    out = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=DEV)
+    idx = torch.empty((T, cfg.K), dtype=torch.int32, device=DEV)
+    s2 = torch.cuda.Stream()
+    sync()
+    moe.moe_forward(C, T, dev["x"], W, out, ws, topk_idx=idx)
+    sync()
+    ref, ref_idx = out.clone(), idx.clone()
+
+    def fwd():
+        moe.moe_forward_overlap(C, T, dev["x"], W, out, ws, s2, topk_idx=idx,
+                                stream=torch.cuda.current_stream())
+
+    fwd()
+    sync()
+    assert torch.equal(out, ref) and torch.equal(idx, ref_idx)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fwd()
+    sync()
+    for rep in range(4):
+        out.fill_(0)
+        idx.fill_(-1)
+        sync()
+        g.replay()
+        sync()
+        assert torch.equal(out, ref), f"replay {rep}"
+        assert torch.equal(idx, ref_idx), f"replay {rep}"
+        fwd()
+        sync()
+        assert torch.equal(out, ref)
