@@ -118,8 +118,8 @@ def main():
                     help="just run warmup + steps (for rocprofv3), print the JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="copy 1 GiB device-to-device 5 times (HBM counter calibration)")
-    ap.add_argument("--single-stream", action="store_true",
-                    help="time moe_forward on one stream instead of moe_forward_overlap")
+    ap.add_argument("--overlap", action="store_true",
+                    help="time moe_forward_overlap (shared expert on a second stream) as the step")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the expert-FFN backward measurement of the bf16 layer workloads")
     ap.add_argument("--row-major", action="store_true",
@@ -187,10 +187,10 @@ def main():
     perm = torch.empty(T * K, dtype=torch.int32, device=dev)
     pos = torch.empty(T * K, dtype=torch.int32, device=dev)
 
-    # The layer step: moe_forward_overlap (the shared expert's GEMMs on a
-    # second stream, joined before the combine), or moe_forward on one stream.
+    # The layer step: moe_forward on one stream, or (--overlap)
+    # moe_forward_overlap, the shared expert's GEMMs on a second stream.
     shared_stream = torch.cuda.Stream()
-    overlap = not args.single_stream and not gate_only
+    overlap = args.overlap and not gate_only
 
     def forward(two_streams):
         if two_streams:
