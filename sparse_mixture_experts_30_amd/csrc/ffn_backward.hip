@@ -9,21 +9,30 @@
 // exact derivatives are
 //   dh = dy W2,   dg = dh u silu'(g),   du = dh silu(g),
 //   dx_row = [dg du] W13,   dW2 = sum_rows dy^T h,   dW13 = sum_rows [dg du]^T x.
-// Five grouped GEMMs compute them, all on one tile routine:
+// Five grouped GEMMs compute them:
 //   GU   [g u] = x_rows W13^T      rows x 2I, k = H    (recompute, fp32 out)
 //   DH   dh    = dy W2             rows x I,  k = H    (epilogue: SwiGLU backward)
 //   DX   dx    = da W13            rows x H,  k = 2I
 //   DW2  dW2   = dy^T h            H x I,     k = the expert's rows
 //   DW13 dW13  = da^T x_rows       2I x H,    k = the expert's rows
-// The MFMA wants both operands with 8 consecutive k values per lane.  Tiles
-// go through LDS in one layout, [row][k] with k contiguous (32 per row, the
-// 16-byte chunk c of row r stored at chunk c ^ ((r / 4) % 4), so that 16
-// consecutive rows read at one chunk hit 16 different bank groups).  An
-// operand whose k runs along memory rows (the weights of DH and DX, both
-// operands of the weight gradients) is transposed on its way into LDS: each
-// thread loads 8 consecutive elements of one k row and writes them as 8
-// 2-byte LDS stores.
+// GU is the forward's row-major gate/up GEMM (ffn_bf16.hip) storing g and
+// u.  The other four share one tile routine.
+//
+// The MFMA wants both operands with 8 consecutive k values per lane, so
+// tiles go through LDS as [row][k] with k contiguous (64 per row in eight
+// XOR-swizzled 16-byte chunks).  In DH
+// and DX the weight's k runs along its memory rows: each thread loads 8
+// consecutive elements of one k row and writes them as 8 2-byte LDS
+// stores.  The weight gradients contract over the expert's rows, which run
+// along memory rows in every operand; instead of transposing in LDS, their
+// operands are written once in transposed form ([column][row], k
+// contiguous): x (gathered through perm) and dy by a transpose kernel, [dg
+// du] and h by DH's epilogue.  Each routed expert's rows start at a column
+// that is a multiple of 32 (pcol), the gap filled with zeros, so the weight
+// gradient GEMMs read whole 16-byte chunks (a last half step of 32 columns
+// is zero-filled).
 #include "moe_internal.hpp"
+#include "permute_device.hpp"
 
 #include <algorithm>
 
@@ -31,121 +40,123 @@ namespace moe {
 
 namespace {
 
-constexpr int BBM = 128, BBN = 128, BBK = 32, BNT = 256;
+constexpr int BBM = 128, BBN = 128, BNT = 256;
+constexpr int kPad = 32;   // column alignment of each expert in the transposed operands
 
-enum : int { A_ROWS = 0, A_COLS = 1 };           // A(m,k): row m k-contiguous / k rows m-contiguous
-enum : int { B_NK = 0, B_KN = 1 };               // B(k,n): row n k-contiguous / k rows n-contiguous
-enum : int { E_GU = 0, E_DH = 1, E_STORE = 2 };  // epilogues
+enum : int { B_NK = 0, B_KN = 1 };   // B(k,n): row n k-contiguous / k rows n-contiguous
+enum : int { E_DH = 1, E_STORE = 2 };
+
+// Epilogue destinations; the tile's row m0 + m and column n0 + n.
+struct Epi {
+  uint16_t* c;              // E_STORE: C(m, n) at c + m * ldc + n
+  int64_t ldc;
+  const float* gu;          // E_DH: [g u] rows (fp32), [dg du] rows (bf16), and the
+  int64_t ldgu;             // transposed [dg du] and h at column m (zero up to mpad)
+  uint16_t* da;
+  int64_t ldda;
+  uint16_t* daT;
+  uint16_t* hT;
+  int64_t ldT;
+  int mpad;
+};
 
 struct BwdArgs {
-  // dims [routed, shared]; M of row-tiled GEMMs is the tile's row count
-  int M[2], N[2], K[2];
+  // [routed, shared]
+  int N[2], K[2];
   const uint16_t* a[2];
   int64_t lda[2];
-  int64_t astride;          // per routed expert (0: row-space operand)
   const uint16_t* b[2];
   int64_t ldb[2];
-  int64_t bstride;
-  int a_gather, b_gather;   // routed row j -> token perm[j] / K (x as the operand)
-  int b_rows;               // B_KN row index: 1 = the group's row space, 0 = a weight row
-  const int32_t* perm;
-  int topk;
-  void* c[2];
+  int64_t bstride;          // routed weight per expert (row-tiled B)
+  uint16_t* c[2];
   int64_t ldc[2];
-  int64_t cstride;          // per routed expert (weight gradients)
-  const float* gu[2];       // E_DH: [g u] rows, fp32
+  int64_t cstride;          // routed weight gradient per expert
+  const float* gu[2];
   int64_t ldgu[2];
-  uint16_t* da[2];          // E_DH outputs: [dg du] bf16 and h bf16
+  uint16_t* da[2];
   int64_t ldda[2];
-  uint16_t* h[2];
-  int64_t ldh[2];
+  uint16_t* daT[2];
+  uint16_t* hT[2];
+  int64_t ldT[2];
   const int32_t* tiles;     // row-tiled: tile list and N-tiles per M-tile
   int ntn;
-  const int32_t* offsets;   // weight-tiled: rows of each expert
+  const int32_t* offsets;
+  const int32_t* pcol;      // padded first column of each routed expert, [E + 1]
   int E;
-  int64_t T;
+  int64_t T, Tp;
+  int M[2];                 // weight-tiled: gradient rows
   int mt, nt;               // weight-tiled: M- and N-tiles per group
 };
 
-__device__ __forceinline__ int lds_at(int r, int k) {
-  return r * BBK + ((((k >> 3) ^ (r >> 2)) & 3) << 3) + (k & 7);
+// Physical 16-byte chunk of logical chunk c in LDS row r, for rows of BK k
+// (BK / 8 chunks): 16 consecutive rows read at one logical chunk fall in 16
+// distinct bank groups.
+template <int BK>
+__device__ __forceinline__ int swz(int r, int c) {
+  if (BK == 64) return r * 8 + (c ^ ((r ^ (r >> 3)) & 7));
+  return r * 4 + (c ^ ((r >> 2) & 3));
 }
 
-// One 128 x 128 tile of group g (s = 0 routed, 1 shared).  Row-tiled:
-// rows row0 + [m0, m0 + Mv) of the row space.  Weight-tiled: rows [m0,
-// m0 + 128) of an M x N weight gradient, k over the group's rows row0 + [0, Kv).
-template <int AM, int BMD, int EPI, bool WG>
-__device__ void bwd_tile(const BwdArgs& p, uint16_t* sA, uint16_t* sB, int g, int s, int64_t row0,
-                         int m0, int Mv, int n0, int Nv, int Kv) {
+// One 128 x 128 tile: C(m, n) = sum_k A(m, k) B(k, n) for rows [m0, m0 +
+// 128) below Mv and columns [n0, n0 + 128) below Nv, k in [0, Kv) (a
+// multiple of 32; with BK = 64 a last half step is zero-filled).  A(m, k) =
+// A[m * lda + k]; B(k, n) = B[n * ldb + k] (B_NK) or B[k * ldb + n] (B_KN).
+// k steps of BK through two LDS buffers and two register stages: at step s
+// the LDS holds step s and the registers steps s + 1 and s + 2, so every
+// load has two steps of MFMAs to arrive.  BK = 64 suits long k (the row
+// GEMMs); BK = 32 halves the LDS (more workgroups per CU) for the short k
+// of the weight gradients.
+template <int BK, int BMD, int EPI>
+__device__ __forceinline__ void bwd_tile(u32x4 (*lds)[(BBM + BBN) * (BK / 8)],
+                                         const uint16_t* __restrict__ A, int64_t lda,
+                                         const uint16_t* __restrict__ B, int64_t ldb, int m0,
+                                         int Mv, int n0, int Nv, int Kv, const Epi& ep) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 31, lh = lane >> 5;
   const int wm = wave >> 1, wn = wave & 1;
-  const uint16_t* A = p.a[s] + (s == 0 ? (int64_t)g * p.astride : 0);
-  const uint16_t* B = p.b[s] + (s == 0 ? (int64_t)g * p.bstride : 0);
-  const int64_t lda = p.lda[s], ldb = p.ldb[s];
+  constexpr int CH = BK / 8;           // 16-byte chunks per LDS row
+  constexpr int NS = BK / 16;          // chunks per thread and operand = 16-wide k slices
+  const int nsteps = (Kv + BK - 1) / BK;
 
-  // row-space row -> the row of the operand (x is read through perm)
-  auto xrow = [&](int64_t r, bool gather) -> int64_t {
-    return (gather && s == 0) ? (int64_t)(p.perm[r] / p.topk) : r;
+  // Thread's rows: A (and B_NK) row tid / CH + (256 / CH) j, chunk tid % CH;
+  // B_KN: k row tid / 16 + 16 j, n chunk tid % 16.
+  struct Stage {
+    u32x4 a[NS], b[NS];
   };
-
-  // Per thread and step: two 16-byte chunks of A and two of B.
-  u32x4 ra[2], rb[2];
-  auto load = [&](int k0) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int c = tid + BNT * j;
-      u32x4 v = {0, 0, 0, 0};
-      if (AM == A_ROWS) {
-        const int m = c >> 2, kc = c & 3;
-        if (m < Mv) {
-          const int64_t r = xrow(row0 + m0 + m, p.a_gather);
-          v = *reinterpret_cast<const u32x4*>(A + r * lda + k0 + kc * 8);
-        }
-      } else {
-        const int k = c >> 4, mc = c & 15;
-        if (k0 + k < Kv && m0 + mc * 8 < Mv)
-          v = *reinterpret_cast<const u32x4*>(A + (row0 + k0 + k) * lda + m0 + mc * 8);
-      }
-      ra[j] = v;
-      v = (u32x4){0, 0, 0, 0};
-      if (BMD == B_NK) {
-        const int n = c >> 2, kc = c & 3;
-        if (n0 + n < Nv) v = *reinterpret_cast<const u32x4*>(B + (int64_t)(n0 + n) * ldb + k0 + kc * 8);
-      } else {
-        const int k = c >> 4, nc = c & 15;
-        if (k0 + k < Kv && n0 + nc * 8 < Nv) {
-          const int64_t r = p.b_rows ? xrow(row0 + k0 + k, p.b_gather) : (int64_t)(k0 + k);
-          v = *reinterpret_cast<const u32x4*>(B + r * ldb + n0 + nc * 8);
-        }
-      }
-      rb[j] = v;
+  const int ch = tid % CH;
+  auto gload = [&](Stage& st, int j, int step) {
+    if (step >= nsteps) return;   // past the last step: the stage is never used
+    const int k0 = step * BK;
+    const int m = tid / CH + (BNT / CH) * j;
+    const bool kin = k0 + ch * 8 < Kv;
+    st.a[j] = (m0 + m < Mv && kin)
+                  ? *reinterpret_cast<const u32x4*>(A + (int64_t)(m0 + m) * lda + k0 + ch * 8)
+                  : (u32x4){0, 0, 0, 0};
+    if (BMD == B_NK) {
+      st.b[j] = (n0 + m < Nv && kin)
+                    ? *reinterpret_cast<const u32x4*>(B + (int64_t)(n0 + m) * ldb + k0 + ch * 8)
+                    : (u32x4){0, 0, 0, 0};
+    } else {
+      const int k = (tid >> 4) + 16 * j, nc = tid & 15;
+      st.b[j] = (n0 + nc * 8 < Nv && k0 + k < Kv)
+                    ? *reinterpret_cast<const u32x4*>(B + (int64_t)(k0 + k) * ldb + n0 + nc * 8)
+                    : (u32x4){0, 0, 0, 0};
     }
   };
-  auto store = [&]() {
+  auto sstore = [&](const Stage& st, int j, int buf) {
+    u32x4* sA = lds[buf];
+    u32x4* sB = lds[buf] + BBM * CH;
+    const int m = tid / CH + (BNT / CH) * j;
+    sA[swz<BK>(m, ch)] = st.a[j];
+    if (BMD == B_NK) {
+      sB[swz<BK>(m, ch)] = st.b[j];
+    } else {
+      const int k = (tid >> 4) + 16 * j, nc = tid & 15;
+      uint16_t* sb = reinterpret_cast<uint16_t*>(sB);
+      const uint32_t w[4] = {st.b[j].x, st.b[j].y, st.b[j].z, st.b[j].w};
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int c = tid + BNT * j;
-      if (AM == A_ROWS) {
-        const int m = c >> 2, kc = c & 3;
-        *reinterpret_cast<u32x4*>(sA + lds_at(m, kc * 8)) = ra[j];
-      } else {
-        const int k = c >> 4, mc = c & 15;
-        const uint32_t w[4] = {ra[j].x, ra[j].y, ra[j].z, ra[j].w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          sA[lds_at(mc * 8 + i, k)] = (uint16_t)(w[i >> 1] >> (16 * (i & 1)));
-      }
-      if (BMD == B_NK) {
-        const int n = c >> 2, kc = c & 3;
-        *reinterpret_cast<u32x4*>(sB + lds_at(n, kc * 8)) = rb[j];
-      } else {
-        const int k = c >> 4, nc = c & 15;
-        const uint32_t w[4] = {rb[j].x, rb[j].y, rb[j].z, rb[j].w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          sB[lds_at(nc * 8 + i, k)] = (uint16_t)(w[i >> 1] >> (16 * (i & 1)));
-      }
+      for (int i = 0; i < 8; ++i)
+        sb[swz<BK>(nc * 8 + i, k >> 3) * 8 + (k & 7)] = (uint16_t)(w[i >> 1] >> (16 * (i & 1)));
     }
   };
 
@@ -157,34 +168,49 @@ __device__ void bwd_tile(const BwdArgs& p, uint16_t* sA, uint16_t* sB, int g, in
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
-  const int nsteps = (Kv + BBK - 1) / BBK;
-  if (nsteps > 0) {
-    load(0);
-    store();
-    __syncthreads();
-  }
-  for (int st = 0; st < nsteps; ++st) {
-    if (st + 1 < nsteps) load((st + 1) * BBK);
+  // One step: MFMAs on LDS buffer `buf`; between its four 16-wide k slices
+  // the next step moves from registers `st` to buffer `nbuf`, and `st` is
+  // refilled with step `ld`.
+  auto step_body = [&](int buf, Stage& st, int nbuf, int ld) {
+    const u32x4* sA = lds[buf];
+    const u32x4* sB = lds[buf] + BBM * CH;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < NS; ++kk) {
+      const int c = 2 * kk + lh;
       bf16x8 af[2], bfr[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const int ar = wm * 64 + i * 32 + lr;
-        af[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(sA + lds_at(ar, kk * 16 + lh * 8)));
-        const int br = wn * 64 + i * 32 + lr;
-        bfr[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(sB + lds_at(br, kk * 16 + lh * 8)));
+        af[i] = as_bf16x8(sA[swz<BK>(wm * 64 + i * 32 + lr, c)]);
+        bfr[i] = as_bf16x8(sB[swz<BK>(wn * 64 + i * 32 + lr, c)]);
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      sstore(st, kk, nbuf);
+      gload(st, kk, ld);
     }
+  };
+
+  if (nsteps > 0) {
+    Stage R0, R1;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) gload(R0, j, 0);
+#pragma unroll
+    for (int j = 0; j < NS; ++j) sstore(R0, j, 0);
+#pragma unroll
+    for (int j = 0; j < NS; ++j) gload(R1, j, 1);
+#pragma unroll
+    for (int j = 0; j < NS; ++j) gload(R0, j, 2);
     __syncthreads();
-    if (st + 1 < nsteps) {
-      store();
+    for (int st = 0; st < nsteps; st += 2) {
+      step_body(0, R1, 1, st + 3);     // step st; stage st+1 to LDS; load st+3
       __syncthreads();
+      if (st + 1 < nsteps) {
+        step_body(1, R0, 0, st + 4);   // step st+1; stage st+2 to LDS; load st+4
+        __syncthreads();
+      }
     }
   }
 
@@ -193,38 +219,56 @@ __device__ void bwd_tile(const BwdArgs& p, uint16_t* sA, uint16_t* sB, int g, in
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + wn * 64 + j * 32 + lr;
+      if (n >= Nv) continue;
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int m = m0 + wm * 64 + i * 32 + 8 * (q >> 2) + 4 * lh + (q & 3);
-        const int n = n0 + wn * 64 + j * 32 + lr;
-        if (m >= (WG ? Mv : m0 + Mv) || n >= Nv) continue;
-        const float v = acc[i][j][q];
-        if (WG) {
-          uint16_t* C = (uint16_t*)p.c[s] + (s == 0 ? (int64_t)g * p.cstride : 0);
-          C[(int64_t)m * p.ldc[s] + n] = (uint16_t)f32_to_bf16_bits(v);
-        } else if (EPI == E_GU) {
-          float* C = (float*)p.c[s];
-          C[(row0 + m) * p.ldc[s] + n] = v;
-        } else if (EPI == E_DH) {
-          const float* gu = p.gu[s] + (row0 + m) * p.ldgu[s];
-          const float gv = gu[n], uv = gu[Nv + n];
-          const float sg = 1.0f / (1.0f + __expf(-gv));
-          uint16_t* da = p.da[s] + (row0 + m) * p.ldda[s];
-          da[n] = (uint16_t)f32_to_bf16_bits(v * uv * sg * (1.0f + gv * (1.0f - sg)));
-          da[Nv + n] = (uint16_t)f32_to_bf16_bits(v * gv * sg);
-          p.h[s][(row0 + m) * p.ldh[s] + n] = (uint16_t)f32_to_bf16_bits(gv * sg * uv);
+      for (int qq = 0; qq < 4; ++qq) {
+        const int mb = m0 + wm * 64 + i * 32 + 8 * qq + 4 * lh;   // 4 rows mb .. mb + 3
+        if (EPI == E_STORE) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (mb + r < Mv)
+              ep.c[(int64_t)(mb + r) * ep.ldc + n] =
+                  (uint16_t)f32_to_bf16_bits(acc[i][j][4 * qq + r]);
         } else {
-          uint16_t* C = (uint16_t*)p.c[s];
-          C[(row0 + m) * p.ldc[s] + n] = (uint16_t)f32_to_bf16_bits(v);
+          float dg[4], du[4], hv[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            dg[r] = du[r] = hv[r] = 0.0f;
+            const int m = mb + r;
+            if (m < Mv) {
+              const float v = acc[i][j][4 * qq + r];
+              const float* gu = ep.gu + (int64_t)m * ep.ldgu;
+              const float gv = gu[n], uv = gu[Nv + n];
+              const float sg = 1.0f / (1.0f + __expf(-gv));
+              dg[r] = v * uv * sg * (1.0f + gv * (1.0f - sg));
+              du[r] = v * gv * sg;
+              hv[r] = gv * sg * uv;
+              uint16_t* da = ep.da + (int64_t)m * ep.ldda;
+              da[n] = (uint16_t)f32_to_bf16_bits(dg[r]);
+              da[Nv + n] = (uint16_t)f32_to_bf16_bits(du[r]);
+            }
+          }
+          if (mb < ep.mpad) {   // four consecutive columns of the transposed rows
+            const uint2 pg = {pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
+            const uint2 pu = {pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
+            const uint2 ph = {pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
+            *reinterpret_cast<uint2*>(ep.daT + (int64_t)n * ep.ldT + mb) = pg;
+            *reinterpret_cast<uint2*>(ep.daT + (int64_t)(Nv + n) * ep.ldT + mb) = pu;
+            *reinterpret_cast<uint2*>(ep.hT + (int64_t)n * ep.ldT + mb) = ph;
+          }
         }
       }
+    }
 }
 
-// Row-tiled GEMMs (GU, DH, DX): work item = (M-tile of the tile list, N-tile).
-template <int AM, int BMD, int EPI>
+// Row-tiled GEMMs (DH, DX): work item = (M-tile of the tile list, N-tile).
+// A is the tile's rows (dy or [dg du]), B the group's weight (k rows).
+template <int EPI>
 __global__ void __launch_bounds__(BNT) bwd_rows_kernel(BwdArgs p) {
-  __shared__ uint16_t lds[(BBM + BBN) * BBK];   // 16 KiB: A tile, then B tile
+  constexpr int BK = 64;
+  __shared__ u32x4 lds[2][(BBM + BBN) * (BK / 8)];   // 64 KiB
   const int64_t work = (int64_t)p.tiles[0] * p.ntn;
   const int64_t per = (work + kNumXcd - 1) / kNumXcd;
   const int64_t q = blockIdx.x / kNumXcd;
@@ -235,15 +279,35 @@ __global__ void __launch_bounds__(BNT) bwd_rows_kernel(BwdArgs p) {
   const int g = ent[0], row0 = ent[1], nrows = ent[2];
   const int s = (g == p.E) ? 1 : 0;
   if (ntile * BBN >= p.N[s]) return;
-  bwd_tile<AM, BMD, EPI, false>(p, lds, lds + BBM * BBK, g, s, row0, 0, nrows, ntile * BBN, p.N[s],
-                                p.K[s]);
+  const uint16_t* A = p.a[s] + (int64_t)row0 * p.lda[s];
+  const uint16_t* B = p.b[s] + (s == 0 ? (int64_t)g * p.bstride : 0);
+  Epi ep{};
+  if (EPI == E_STORE) {
+    ep.c = p.c[s] + (int64_t)row0 * p.ldc[s];
+    ep.ldc = p.ldc[s];
+  } else {
+    // transposed columns: the shared expert's rows are its tokens; a routed
+    // expert's rows start at its padded column
+    const int64_t col = s ? row0 : p.pcol[g] + (row0 - p.offsets[g]);
+    ep.gu = p.gu[s] + (int64_t)row0 * p.ldgu[s];
+    ep.ldgu = p.ldgu[s];
+    ep.da = p.da[s] + (int64_t)row0 * p.ldda[s];
+    ep.ldda = p.ldda[s];
+    ep.daT = p.daT[s] + col;
+    ep.hT = p.hT[s] + col;
+    ep.ldT = p.ldT[s];
+    ep.mpad = (nrows + kPad - 1) / kPad * kPad;
+  }
+  bwd_tile<BK, B_KN, EPI>(lds, A, p.lda[s], B, p.ldb[s], 0, nrows, ntile * BBN, p.N[s], p.K[s],
+                          ep);
 }
 
-// Weight-gradient GEMMs (DW2, DW13): work item = (group, M-tile, N-tile),
-// k over the group's rows (an expert without rows gets a zero gradient).
-template <int AM, int BMD>
-__global__ void __launch_bounds__(BNT) bwd_weights_kernel(BwdArgs p) {
-  __shared__ uint16_t lds[(BBM + BBN) * BBK];
+// Weight-gradient GEMMs (DW2, DW13): work item = (group, M-tile, N-tile); A
+// and B are transposed operands, k over the group's padded columns (an
+// expert without rows gets a zero gradient).
+__global__ void __launch_bounds__(BNT) bwd_wgrad_kernel(BwdArgs p) {
+  constexpr int BK = 32;
+  __shared__ u32x4 lds[2][(BBM + BBN) * (BK / 8)];   // 32 KiB
   const int64_t per_g = (int64_t)p.mt * p.nt;
   const int64_t groups = p.E + (p.M[1] > 0 ? 1 : 0);
   const int64_t work = groups * per_g;
@@ -256,26 +320,121 @@ __global__ void __launch_bounds__(BNT) bwd_weights_kernel(BwdArgs p) {
   const int mtile = rest / p.nt, ntile = rest % p.nt;
   const int s = (g == p.E) ? 1 : 0;
   if (mtile * BBM >= p.M[s] || ntile * BBN >= p.N[s]) return;
-  const int64_t row0 = s ? 0 : p.offsets[g];
-  const int rows = s ? (int)p.T : p.offsets[g + 1] - p.offsets[g];
-  bwd_tile<AM, BMD, E_STORE, true>(p, lds, lds + BBM * BBK, g, s, row0, mtile * BBM, p.M[s],
-                                   ntile * BBN, p.N[s], rows);
+  const int64_t col = s ? 0 : p.pcol[g];
+  const int kv = s ? (int)p.Tp : p.pcol[g + 1] - p.pcol[g];
+  Epi ep{};
+  ep.c = p.c[s] + (s == 0 ? (int64_t)g * p.cstride : 0);
+  ep.ldc = p.ldc[s];
+  bwd_tile<BK, B_NK, E_STORE>(lds, p.a[s] + col, p.lda[s], p.b[s] + col, p.ldb[s], mtile * BBM,
+                          p.M[s], ntile * BBN, p.N[s], kv, ep);
+}
+
+// pcol[e] = sum over e' < e of the row count of e' rounded up to kPad, for
+// e <= E (one workgroup of 1024 threads, E < 1024).
+__global__ void __launch_bounds__(1024)
+pad_columns_kernel(const int32_t* __restrict__ offsets, int E, int32_t* __restrict__ pcol) {
+  __shared__ int32_t wsum[16];
+  const int e = threadIdx.x;
+  const int32_t c = e < E ? (offsets[e + 1] - offsets[e] + kPad - 1) / kPad * kPad : 0;
+  const int32_t incl = block_inclusive_scan<1024>(c, wsum);
+  if (e <= E) pcol[e] = incl - c;
+}
+
+// dst[h][c0 + jj] = src[row(jj)][h] for a block of 32 columns and 64 h, zero
+// where the column has no row.  Routed (pcol != null): column block c0 lies
+// in the expert e with pcol[e] <= c0 < pcol[e + 1]; its column j is row
+// offsets[e] + j of the sorted order, read from src row perm[...] / topk
+// when gathering (topk > 0) or from that row itself.  Shared: column t is
+// row t, for t < T.
+constexpr int TR_COLS = 32, TR_H = 64, TR_LD = 72;   // LDS row stride (elements)
+
+__global__ void __launch_bounds__(256)
+transpose_kernel(const uint16_t* __restrict__ src, int H, const int32_t* __restrict__ perm,
+                 int topk, const int32_t* __restrict__ offsets,
+                 const int32_t* __restrict__ pcol, int E, int64_t T, uint16_t* __restrict__ dst,
+                 int64_t ldd) {
+  __shared__ uint16_t tile[TR_COLS * TR_LD];
+  const int tid = threadIdx.x;
+  const int64_t c0 = (int64_t)blockIdx.x * TR_COLS;
+  const int h0 = blockIdx.y * TR_H;
+  int64_t first = 0, count = 0;   // sorted rows of this column block
+  if (pcol) {
+    if (c0 >= pcol[E]) return;     // uniform
+    int lo = 0, hi = E - 1;        // largest e with pcol[e] <= c0
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pcol[mid] <= c0) lo = mid; else hi = mid - 1;
+    }
+    const int64_t j0 = c0 - pcol[lo];
+    first = offsets[lo] + j0;
+    count = offsets[lo + 1] - offsets[lo] - j0;
+  } else {
+    first = c0;
+    count = T - c0;
+  }
+  // load: thread -> (column jj, 8 consecutive h)
+  {
+    const int jj = tid >> 3, hc = tid & 7;
+    u32x4 v = {0, 0, 0, 0};
+    if (jj < count) {
+      const int64_t j = first + jj;
+      const int64_t row = (pcol && topk > 0) ? (int64_t)(perm[j] / topk) : j;
+      v = *reinterpret_cast<const u32x4*>(src + row * H + h0 + hc * 8);
+    }
+    *reinterpret_cast<u32x4*>(tile + jj * TR_LD + hc * 8) = v;
+  }
+  __syncthreads();
+  // store: thread -> (h, 8 consecutive columns)
+  {
+    const int h = tid >> 2, cc = tid & 3;
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = (uint32_t)tile[(cc * 8 + 2 * i) * TR_LD + h] |
+             ((uint32_t)tile[(cc * 8 + 2 * i + 1) * TR_LD + h] << 16);
+    *reinterpret_cast<u32x4*>(dst + (int64_t)(h0 + h) * ldd + c0 + cc * 8) =
+        (u32x4){w[0], w[1], w[2], w[3]};
+  }
 }
 
 unsigned grid_for(int64_t work) {
   return (unsigned)(((work + kNumXcd - 1) / kNumXcd) * kNumXcd);
 }
 
+// Workspace segments (bytes, 256-aligned).
+struct BwdLayout {
+  size_t gu, da, daT, hT, xT, dyT, pcol, tiles, total;
+  int64_t NP, Tp;   // transposed row strides: routed columns, shared columns
+};
+
+BwdLayout bwd_layout(const FfnDims& d) {
+  BwdLayout L{};
+  const int64_t rs = d.Is > 0 ? d.T : 0;
+  // every expert's padded width is below its rows + kPad; the stride stays
+  // a multiple of kPad (16-byte aligned rows)
+  L.NP = (d.N + kPad - 1) / kPad * kPad + (int64_t)kPad * d.E;
+  L.Tp = (rs + kPad - 1) / kPad * kPad;
+  size_t o = 0;
+  auto take = [&](size_t b) {
+    const size_t at = o;
+    o += (b + 255) / 256 * 256;
+    return at;
+  };
+  L.gu = take((size_t)(d.N * 2 * d.I + rs * 2 * d.Is) * 4);
+  L.da = take((size_t)(d.N * 2 * d.I + rs * 2 * d.Is) * 2);
+  L.daT = take((size_t)(2 * d.I * L.NP + 2 * d.Is * L.Tp) * 2);
+  L.hT = take((size_t)(d.I * L.NP + d.Is * L.Tp) * 2);
+  L.xT = take((size_t)d.H * (L.NP + L.Tp) * 2);
+  L.dyT = take((size_t)d.H * (L.NP + L.Tp) * 2);
+  L.pcol = take((size_t)(d.E + 1) * 4);
+  L.tiles = take(ffn_tiles_bytes(d));
+  L.total = o;
+  return L;
+}
+
 }  // namespace
 
-size_t ffn_backward_ws_bytes(const FfnDims& d) {
-  const int64_t rows_r = d.N, rows_s = d.Is > 0 ? d.T : 0;
-  auto al = [](size_t b) { return (b + 255) / 256 * 256; };
-  return al((size_t)(rows_r * 2 * d.I + rows_s * 2 * d.Is) * 4) +      // gu fp32
-         al((size_t)(rows_r * 2 * d.I + rows_s * 2 * d.Is) * 2) +      // da bf16
-         al((size_t)(rows_r * d.I + rows_s * d.Is) * 2) +              // h bf16
-         al(ffn_tiles_bytes(d));
-}
+size_t ffn_backward_ws_bytes(const FfnDims& d) { return bwd_layout(d).total; }
 
 hipError_t launch_ffn_backward(const FfnDims& d, const uint16_t* x, const int32_t* perm,
                                const int32_t* offsets, const uint16_t* w13, const uint16_t* w2,
@@ -286,58 +445,77 @@ hipError_t launch_ffn_backward(const FfnDims& d, const uint16_t* x, const int32_
   const int64_t N = d.N, T = d.T;
   const int H = d.H, I = d.I, Is = d.Is, E = d.E;
   const bool sh = Is > 0;
-  auto al = [](size_t b) { return (b + 255) / 256 * 256; };
+  const BwdLayout L = bwd_layout(d);
   char* base = (char*)ws;
-  float* gu_r = (float*)base;
+  float* gu_r = (float*)(base + L.gu);
   float* gu_s = gu_r + N * 2 * I;
-  base += al((size_t)(N * 2 * I + (sh ? T : 0) * 2 * Is) * 4);
-  uint16_t* da_r = (uint16_t*)base;
+  uint16_t* da_r = (uint16_t*)(base + L.da);
   uint16_t* da_s = da_r + N * 2 * I;
-  base += al((size_t)(N * 2 * I + (sh ? T : 0) * 2 * Is) * 2);
-  uint16_t* h_r = (uint16_t*)base;
-  uint16_t* h_s = h_r + N * I;
-  base += al((size_t)(N * I + (sh ? T : 0) * Is) * 2);
-  int32_t* tiles = (int32_t*)base;
+  uint16_t* daT_r = (uint16_t*)(base + L.daT);
+  uint16_t* daT_s = daT_r + 2 * I * L.NP;
+  uint16_t* hT_r = (uint16_t*)(base + L.hT);
+  uint16_t* hT_s = hT_r + I * L.NP;
+  uint16_t* xT_r = (uint16_t*)(base + L.xT);
+  uint16_t* xT_s = xT_r + H * L.NP;
+  uint16_t* dyT_r = (uint16_t*)(base + L.dyT);
+  uint16_t* dyT_s = dyT_r + H * L.NP;
+  int32_t* pcol = (int32_t*)(base + L.pcol);
+  int32_t* tiles = (int32_t*)(base + L.tiles);
 
-  hipError_t e = launch_build_tiles(offsets, E, T, true, sh, BBM, tiles, s);
+  // GU: [g u] = x_rows W13^T (rows x 2I, k = H), fp32, with the forward's
+  // row-major gate/up GEMM.
+  hipError_t e = launch_gate_up_bf16(d, x, perm, offsets, w13, ws13, tiles, gu_r, gu_s, s);
+  if (e != hipSuccess) return e;
+  e = launch_build_tiles(offsets, E, T, true, sh, BBM, tiles, s);
   if (e != hipSuccess) return e;
   const int64_t mt = ffn_max_mtiles(N, T, E, BBM);
 
-  BwdArgs p{};
-  p.perm = perm;
-  p.topk = d.K;
-  p.tiles = tiles;
-  p.offsets = offsets;
-  p.E = E;
-  p.T = T;
-
-  // GU: [g u] = x_rows W13^T (rows x 2I, k = H), fp32.
+  // Padded columns, then x (gathered) and dy in transposed form.
+  MOE_TIMED_LAUNCH(s, "pad_columns_kernel",
+    hipLaunchKernelGGL(pad_columns_kernel, dim3(1), dim3(1024), 0, s, offsets, E, pcol));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   {
-    BwdArgs q = p;
-    q.N[0] = 2 * I; q.N[1] = 2 * Is; q.K[0] = q.K[1] = H;
-    q.a[0] = q.a[1] = x; q.lda[0] = q.lda[1] = H; q.a_gather = 1;
-    q.b[0] = w13; q.b[1] = ws13; q.ldb[0] = q.ldb[1] = H; q.bstride = (int64_t)2 * I * H;
-    q.c[0] = gu_r; q.c[1] = gu_s; q.ldc[0] = 2 * I; q.ldc[1] = 2 * Is;
-    q.ntn = (std::max(2 * I, 2 * Is) + BBN - 1) / BBN;
-    MOE_TIMED_LAUNCH(s, "bwd_rows_kernel<gu>",
-      hipLaunchKernelGGL((bwd_rows_kernel<A_ROWS, B_NK, E_GU>), dim3(grid_for(mt * q.ntn)),
-                         dim3(BNT), 0, s, q));
+    const dim3 gr((unsigned)((L.NP + TR_COLS - 1) / TR_COLS), H / TR_H);
+    MOE_TIMED_LAUNCH(s, "transpose_kernel<x>",
+      hipLaunchKernelGGL(transpose_kernel, gr, dim3(256), 0, s, x, H, perm, d.K, offsets, pcol, E,
+                         T, xT_r, L.NP));
+    MOE_TIMED_LAUNCH(s, "transpose_kernel<dy>",
+      hipLaunchKernelGGL(transpose_kernel, gr, dim3(256), 0, s, dy, H, perm, 0, offsets, pcol, E,
+                         T, dyT_r, L.NP));
+    if (sh) {
+      const dim3 gs((unsigned)(L.Tp / TR_COLS), H / TR_H);
+      MOE_TIMED_LAUNCH(s, "transpose_kernel<x>",
+        hipLaunchKernelGGL(transpose_kernel, gs, dim3(256), 0, s, x, H, nullptr, 0, nullptr,
+                           nullptr, E, T, xT_s, L.Tp));
+      MOE_TIMED_LAUNCH(s, "transpose_kernel<dy>",
+        hipLaunchKernelGGL(transpose_kernel, gs, dim3(256), 0, s, dys, H, nullptr, 0, nullptr,
+                           nullptr, E, T, dyT_s, L.Tp));
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  // DH: dh = dy W2 (rows x I, k = H); epilogue writes [dg du] and h.
+
+  BwdArgs p{};
+  p.tiles = tiles;
+  p.offsets = offsets;
+  p.pcol = pcol;
+  p.E = E;
+  p.T = T;
+  p.Tp = L.Tp;
+
+  // DH: dh = dy W2 (rows x I, k = H); epilogue writes [dg du] (rows and
+  // transposed) and h (transposed).
   {
     BwdArgs q = p;
     q.N[0] = I; q.N[1] = Is; q.K[0] = q.K[1] = H;
     q.a[0] = dy; q.a[1] = dys; q.lda[0] = q.lda[1] = H;
     q.b[0] = w2; q.b[1] = ws2; q.ldb[0] = I; q.ldb[1] = Is; q.bstride = (int64_t)H * I;
-    q.b_rows = 0;
     q.gu[0] = gu_r; q.gu[1] = gu_s; q.ldgu[0] = 2 * I; q.ldgu[1] = 2 * Is;
     q.da[0] = da_r; q.da[1] = da_s; q.ldda[0] = 2 * I; q.ldda[1] = 2 * Is;
-    q.h[0] = h_r; q.h[1] = h_s; q.ldh[0] = I; q.ldh[1] = Is;
+    q.daT[0] = daT_r; q.daT[1] = daT_s; q.hT[0] = hT_r; q.hT[1] = hT_s;
+    q.ldT[0] = L.NP; q.ldT[1] = L.Tp;
     q.ntn = (std::max(I, Is) + BBN - 1) / BBN;
     MOE_TIMED_LAUNCH(s, "bwd_rows_kernel<dh>",
-      hipLaunchKernelGGL((bwd_rows_kernel<A_ROWS, B_KN, E_DH>), dim3(grid_for(mt * q.ntn)),
-                         dim3(BNT), 0, s, q));
+      hipLaunchKernelGGL(bwd_rows_kernel<E_DH>, dim3(grid_for(mt * q.ntn)), dim3(BNT), 0, s, q));
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // DX: dx_rows = [dg du] W13 (rows x H, k = 2I).
@@ -346,45 +524,40 @@ hipError_t launch_ffn_backward(const FfnDims& d, const uint16_t* x, const int32_
     q.N[0] = q.N[1] = H; q.K[0] = 2 * I; q.K[1] = 2 * Is;
     q.a[0] = da_r; q.a[1] = da_s; q.lda[0] = 2 * I; q.lda[1] = 2 * Is;
     q.b[0] = w13; q.b[1] = ws13; q.ldb[0] = q.ldb[1] = H; q.bstride = (int64_t)2 * I * H;
-    q.b_rows = 0;
     q.c[0] = dx; q.c[1] = dxs; q.ldc[0] = q.ldc[1] = H;
     q.ntn = (H + BBN - 1) / BBN;
     MOE_TIMED_LAUNCH(s, "bwd_rows_kernel<dx>",
-      hipLaunchKernelGGL((bwd_rows_kernel<A_ROWS, B_KN, E_STORE>), dim3(grid_for(mt * q.ntn)),
-                         dim3(BNT), 0, s, q));
+      hipLaunchKernelGGL(bwd_rows_kernel<E_STORE>, dim3(grid_for(mt * q.ntn)), dim3(BNT), 0, s,
+                         q));
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  // DW2: dW2 = dy^T h (H x I, k = the expert's rows).
+  // DW2: dW2 = dy^T h (H x I, k = the expert's rows): A = dy^T, B = h^T.
   {
     BwdArgs q = p;
-    q.M[0] = q.M[1] = H; q.N[0] = I; q.N[1] = sh ? Is : 0;
-    q.a[0] = dy; q.a[1] = dys; q.lda[0] = q.lda[1] = H; q.astride = 0;
-    q.b[0] = h_r; q.b[1] = h_s; q.ldb[0] = I; q.ldb[1] = Is; q.bstride = 0;
-    q.b_rows = 1; q.b_gather = 0;
+    q.M[0] = H; q.M[1] = sh ? H : 0; q.N[0] = I; q.N[1] = Is;
+    q.a[0] = dyT_r; q.a[1] = dyT_s; q.lda[0] = L.NP; q.lda[1] = L.Tp;
+    q.b[0] = hT_r; q.b[1] = hT_s; q.ldb[0] = L.NP; q.ldb[1] = L.Tp;
     q.c[0] = dw2; q.c[1] = dws2; q.ldc[0] = I; q.ldc[1] = Is; q.cstride = (int64_t)H * I;
-    if (!sh) q.M[1] = 0;
     q.mt = (H + BBM - 1) / BBM;
     q.nt = (std::max(I, Is) + BBN - 1) / BBN;
     const int64_t work = (int64_t)(E + (sh ? 1 : 0)) * q.mt * q.nt;
-    MOE_TIMED_LAUNCH(s, "bwd_weights_kernel<dw2>",
-      hipLaunchKernelGGL((bwd_weights_kernel<A_COLS, B_KN>), dim3(grid_for(work)), dim3(BNT), 0,
-                         s, q));
+    MOE_TIMED_LAUNCH(s, "bwd_wgrad_kernel<dw2>",
+      hipLaunchKernelGGL(bwd_wgrad_kernel, dim3(grid_for(work)), dim3(BNT), 0, s, q));
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  // DW13: dW13 = [dg du]^T x_rows (2I x H, k = the expert's rows).
+  // DW13: dW13 = [dg du]^T x_rows (2I x H, k = the expert's rows): A =
+  // [dg du]^T, B = x_rows^T.
   {
     BwdArgs q = p;
     q.M[0] = 2 * I; q.M[1] = sh ? 2 * Is : 0; q.N[0] = q.N[1] = H;
-    q.a[0] = da_r; q.a[1] = da_s; q.lda[0] = 2 * I; q.lda[1] = 2 * Is; q.astride = 0;
-    q.b[0] = q.b[1] = x; q.ldb[0] = q.ldb[1] = H; q.bstride = 0;
-    q.b_rows = 1; q.b_gather = 1;
+    q.a[0] = daT_r; q.a[1] = daT_s; q.lda[0] = L.NP; q.lda[1] = L.Tp;
+    q.b[0] = xT_r; q.b[1] = xT_s; q.ldb[0] = L.NP; q.ldb[1] = L.Tp;
     q.c[0] = dw13; q.c[1] = dws13; q.ldc[0] = q.ldc[1] = H; q.cstride = (int64_t)2 * I * H;
     q.mt = (std::max(2 * I, 2 * Is) + BBM - 1) / BBM;
     q.nt = (H + BBN - 1) / BBN;
     const int64_t work = (int64_t)(E + (sh ? 1 : 0)) * q.mt * q.nt;
-    MOE_TIMED_LAUNCH(s, "bwd_weights_kernel<dw13>",
-      hipLaunchKernelGGL((bwd_weights_kernel<A_COLS, B_KN>), dim3(grid_for(work)), dim3(BNT), 0,
-                         s, q));
+    MOE_TIMED_LAUNCH(s, "bwd_wgrad_kernel<dw13>",
+      hipLaunchKernelGGL(bwd_wgrad_kernel, dim3(grid_for(work)), dim3(BNT), 0, s, q));
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;

@@ -66,7 +66,10 @@ struct Stage {
 // fall in distinct banks.
 __device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ ((r ^ (r >> 3)) & 7)); }
 
-template <bool kGateUp>
+// kStoreGU (with kGateUp): the epilogue stores g and u themselves in fp32,
+// row r of a group at c + r * ldc (g in columns [0, ncol), u in
+// [ncol, 2 ncol)), for the backward of the FFN.
+template <bool kGateUp, bool kStoreGU = false>
 __global__ void __launch_bounds__(NT, 1) grouped_gemm_bf16(GemmArgs p) {
   extern __shared__ u32x4 smem[];
   u32x4* sA = smem;                   // [2][BM * 8]
@@ -207,7 +210,14 @@ __global__ void __launch_bounds__(NT, 1) grouped_gemm_bf16(GemmArgs p) {
       const int row = r * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
       if (row >= nrows) continue;
       uint16_t* crow = C + (int64_t)(row0 + row) * ldc;
-      if (kGateUp) {
+      if (kGateUp && kStoreGU) {
+        const int col = n0 + wave * 32 + lr;
+        if (col < ncol) {
+          float* grow = reinterpret_cast<float*>(sh ? p.c_s : p.c_r) + (int64_t)(row0 + row) * ldc;
+          grow[col] = acc[r][0][i];
+          grow[ncol + col] = acc[r][1][i];
+        }
+      } else if (kGateUp) {
         const int col = n0 + wave * 32 + lr;
         if (col < ncol) {
           const float gv = acc[r][0][i], uv = acc[r][1][i];
@@ -233,6 +243,9 @@ hipError_t set_attrs() {
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
   if (e != hipSuccess) return e;
   e = hipFuncSetAttribute((const void*)grouped_gemm_bf16<false>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+  if (e != hipSuccess) return e;
+  e = hipFuncSetAttribute((const void*)grouped_gemm_bf16<true, true>,
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
   if (e == hipSuccess) g_attr_set = true;
   return e;
@@ -305,6 +318,38 @@ hipError_t launch_ffn_bf16(const FfnDims& d, const uint16_t* x, const int32_t* p
   a2.ldc_r = a2.ldc_s = d.H;
   MOE_TIMED_LAUNCH(s, "grouped_gemm_bf16<false>",
     hipLaunchKernelGGL(grouped_gemm_bf16<false>, dim3(grid_for(mt * a2.ntn)), dim3(NT), kLds, s, a2));
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_up_bf16(const FfnDims& d, const uint16_t* x, const int32_t* perm,
+                               const int32_t* offsets, const uint16_t* w13, const uint16_t* ws13,
+                               int32_t* tiles, float* gu, float* gus, hipStream_t s) {
+  hipError_t e = set_attrs();
+  if (e != hipSuccess) return e;
+  e = ffn_build_tiles(d, offsets, BM, tiles, s);
+  if (e != hipSuccess) return e;
+  const int64_t mt = ffn_grid_mtiles(d, BM);
+  GemmArgs a{};
+  a.tiles = tiles;
+  a.ntn = (int)((std::max(d.I, d.Is) + BNB / 2 - 1) / (BNB / 2));
+  a.E = d.E;
+  a.K = d.K;
+  a.a_r = a.a_s = x;
+  a.lda_r = a.lda_s = d.H;
+  a.perm = perm;
+  a.kdim_r = a.kdim_s = d.H;
+  a.b_r = w13;
+  a.b_es = (int64_t)2 * d.I * d.H;
+  a.b_s = ws13;
+  a.ncol_r = d.I;
+  a.ncol_s = d.Is;
+  a.c_r = reinterpret_cast<uint16_t*>(gu);
+  a.c_s = reinterpret_cast<uint16_t*>(gus);
+  a.ldc_r = 2 * d.I;
+  a.ldc_s = 2 * d.Is;
+  MOE_TIMED_LAUNCH(s, "grouped_gemm_bf16<gate_up>",
+    hipLaunchKernelGGL((grouped_gemm_bf16<true, true>), dim3(grid_for(mt * a.ntn)), dim3(NT), kLds,
+                       s, a));
   return hipGetLastError();
 }
 
