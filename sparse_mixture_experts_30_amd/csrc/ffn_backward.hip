@@ -30,7 +30,8 @@
 // du] and h by DH's epilogue.  Each routed expert's rows start at a column
 // that is a multiple of 32 (pcol), the gap filled with zeros, so the weight
 // gradient GEMMs read whole 16-byte chunks (a last half step of 32 columns
-// is zero-filled).
+// is zero-filled).  Every row stride of the workspace is an odd multiple of
+// 128 bytes.
 #include "moe_internal.hpp"
 #include "permute_device.hpp"
 
@@ -41,6 +42,7 @@ namespace moe {
 namespace {
 
 constexpr int BBM = 128, BBN = 128, BNT = 256;
+constexpr int WTM = 256;   // weight-gradient tile rows
 constexpr int kPad = 32;   // column alignment of each expert in the transposed operands
 
 enum : int { B_NK = 0, B_KN = 1 };   // B(k,n): row n k-contiguous / k rows n-contiguous
@@ -97,17 +99,18 @@ __device__ __forceinline__ int swz(int r, int c) {
   return r * 4 + (c ^ ((r >> 2) & 3));
 }
 
-// One 128 x 128 tile: C(m, n) = sum_k A(m, k) B(k, n) for rows [m0, m0 +
-// 128) below Mv and columns [n0, n0 + 128) below Nv, k in [0, Kv) (a
+// One TM x 128 tile: C(m, n) = sum_k A(m, k) B(k, n) for rows [m0, m0 +
+// TM) below Mv and columns [n0, n0 + 128) below Nv, k in [0, Kv) (a
 // multiple of 32; with BK = 64 a last half step is zero-filled).  A(m, k) =
 // A[m * lda + k]; B(k, n) = B[n * ldb + k] (B_NK) or B[k * ldb + n] (B_KN).
-// k steps of BK through two LDS buffers and two register stages: at step s
-// the LDS holds step s and the registers steps s + 1 and s + 2, so every
-// load has two steps of MFMAs to arrive.  BK = 64 suits long k (the row
-// GEMMs); BK = 32 halves the LDS (more workgroups per CU) for the short k
-// of the weight gradients.
-template <int BK, int BMD, int EPI>
-__device__ __forceinline__ void bwd_tile(u32x4 (*lds)[(BBM + BBN) * (BK / 8)],
+// Four waves, 2 x 2, each TM / 2 x 64.  k steps of BK through two LDS
+// buffers and two register stages: at step s the LDS holds step s and the
+// registers steps s + 1 and s + 2, so every load has two steps of MFMAs to
+// arrive.  BK = 64 suits long k (the row GEMMs); the weight gradients, with
+// k the few rows of one expert, take BK = 32 and TM = 256: half the LDS per
+// step, and 85 rather than 64 flop per byte read from L2.
+template <int BK, int TM, int BMD, int EPI>
+__device__ __forceinline__ void bwd_tile(u32x4 (*lds)[(TM + BBN) * (BK / 8)],
                                          const uint16_t* __restrict__ A, int64_t lda,
                                          const uint16_t* __restrict__ B, int64_t ldb, int m0,
                                          int Mv, int n0, int Nv, int Kv, const Epi& ep) {
@@ -115,26 +118,32 @@ __device__ __forceinline__ void bwd_tile(u32x4 (*lds)[(BBM + BBN) * (BK / 8)],
   const int lr = lane & 31, lh = lane >> 5;
   const int wm = wave >> 1, wn = wave & 1;
   constexpr int CH = BK / 8;           // 16-byte chunks per LDS row
-  constexpr int NS = BK / 16;          // chunks per thread and operand = 16-wide k slices
+  constexpr int NS = BK / 16;          // 16-wide k slices per step = B chunks per thread
+  constexpr int NA = TM * CH / BNT;    // A chunks per thread
+  constexpr int MI = TM / 64;          // 32-row blocks per wave
   const int nsteps = (Kv + BK - 1) / BK;
 
   // Thread's rows: A (and B_NK) row tid / CH + (256 / CH) j, chunk tid % CH;
   // B_KN: k row tid / 16 + 16 j, n chunk tid % 16.
   struct Stage {
-    u32x4 a[NS], b[NS];
+    u32x4 a[NA], b[NS];
   };
   const int ch = tid % CH;
-  auto gload = [&](Stage& st, int j, int step) {
+  auto gload_a = [&](Stage& st, int j, int step) {
     if (step >= nsteps) return;   // past the last step: the stage is never used
     const int k0 = step * BK;
     const int m = tid / CH + (BNT / CH) * j;
-    const bool kin = k0 + ch * 8 < Kv;
-    st.a[j] = (m0 + m < Mv && kin)
+    st.a[j] = (m0 + m < Mv && k0 + ch * 8 < Kv)
                   ? *reinterpret_cast<const u32x4*>(A + (int64_t)(m0 + m) * lda + k0 + ch * 8)
                   : (u32x4){0, 0, 0, 0};
+  };
+  auto gload_b = [&](Stage& st, int j, int step) {
+    if (step >= nsteps) return;
+    const int k0 = step * BK;
     if (BMD == B_NK) {
-      st.b[j] = (n0 + m < Nv && kin)
-                    ? *reinterpret_cast<const u32x4*>(B + (int64_t)(n0 + m) * ldb + k0 + ch * 8)
+      const int n = tid / CH + (BNT / CH) * j;
+      st.b[j] = (n0 + n < Nv && k0 + ch * 8 < Kv)
+                    ? *reinterpret_cast<const u32x4*>(B + (int64_t)(n0 + n) * ldb + k0 + ch * 8)
                     : (u32x4){0, 0, 0, 0};
     } else {
       const int k = (tid >> 4) + 16 * j, nc = tid & 15;
@@ -143,13 +152,15 @@ __device__ __forceinline__ void bwd_tile(u32x4 (*lds)[(BBM + BBN) * (BK / 8)],
                     : (u32x4){0, 0, 0, 0};
     }
   };
-  auto sstore = [&](const Stage& st, int j, int buf) {
-    u32x4* sA = lds[buf];
-    u32x4* sB = lds[buf] + BBM * CH;
+  auto sstore_a = [&](const Stage& st, int j, int buf) {
     const int m = tid / CH + (BNT / CH) * j;
-    sA[swz<BK>(m, ch)] = st.a[j];
+    lds[buf][swz<BK>(m, ch)] = st.a[j];
+  };
+  auto sstore_b = [&](const Stage& st, int j, int buf) {
+    u32x4* sB = lds[buf] + TM * CH;
     if (BMD == B_NK) {
-      sB[swz<BK>(m, ch)] = st.b[j];
+      const int n = tid / CH + (BNT / CH) * j;
+      sB[swz<BK>(n, ch)] = st.b[j];
     } else {
       const int k = (tid >> 4) + 16 * j, nc = tid & 15;
       uint16_t* sb = reinterpret_cast<uint16_t*>(sB);
@@ -160,49 +171,61 @@ __device__ __forceinline__ void bwd_tile(u32x4 (*lds)[(BBM + BBN) * (BK / 8)],
     }
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[MI][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
-  // One step: MFMAs on LDS buffer `buf`; between its four 16-wide k slices
-  // the next step moves from registers `st` to buffer `nbuf`, and `st` is
+  // One step: MFMAs on LDS buffer `buf`; between its 16-wide k slices the
+  // next step moves from registers `st` to buffer `nbuf`, and `st` is
   // refilled with step `ld`.
   auto step_body = [&](int buf, Stage& st, int nbuf, int ld) {
     const u32x4* sA = lds[buf];
-    const u32x4* sB = lds[buf] + BBM * CH;
+    const u32x4* sB = lds[buf] + TM * CH;
 #pragma unroll
     for (int kk = 0; kk < NS; ++kk) {
       const int c = 2 * kk + lh;
-      bf16x8 af[2], bfr[2];
+      bf16x8 af[MI], bfr[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        af[i] = as_bf16x8(sA[swz<BK>(wm * 64 + i * 32 + lr, c)]);
-        bfr[i] = as_bf16x8(sB[swz<BK>(wn * 64 + i * 32 + lr, c)]);
-      }
+      for (int i = 0; i < MI; ++i) af[i] = as_bf16x8(sA[swz<BK>(wm * (TM / 2) + i * 32 + lr, c)]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < 2; ++j) bfr[j] = as_bf16x8(sB[swz<BK>(wn * 64 + j * 32 + lr, c)]);
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-      sstore(st, kk, nbuf);
-      gload(st, kk, ld);
+#pragma unroll
+      for (int j = kk; j < NA; j += NS) {
+        sstore_a(st, j, nbuf);
+        gload_a(st, j, ld);
+      }
+      sstore_b(st, kk, nbuf);
+      gload_b(st, kk, ld);
     }
   };
 
   if (nsteps > 0) {
     Stage R0, R1;
 #pragma unroll
-    for (int j = 0; j < NS; ++j) gload(R0, j, 0);
+    for (int j = 0; j < NA; ++j) gload_a(R0, j, 0);
 #pragma unroll
-    for (int j = 0; j < NS; ++j) sstore(R0, j, 0);
+    for (int j = 0; j < NS; ++j) gload_b(R0, j, 0);
 #pragma unroll
-    for (int j = 0; j < NS; ++j) gload(R1, j, 1);
+    for (int j = 0; j < NA; ++j) sstore_a(R0, j, 0);
 #pragma unroll
-    for (int j = 0; j < NS; ++j) gload(R0, j, 2);
+    for (int j = 0; j < NS; ++j) sstore_b(R0, j, 0);
+#pragma unroll
+    for (int j = 0; j < NA; ++j) gload_a(R1, j, 1);
+#pragma unroll
+    for (int j = 0; j < NS; ++j) gload_b(R1, j, 1);
+#pragma unroll
+    for (int j = 0; j < NA; ++j) gload_a(R0, j, 2);
+#pragma unroll
+    for (int j = 0; j < NS; ++j) gload_b(R0, j, 2);
     __syncthreads();
     for (int st = 0; st < nsteps; st += 2) {
       step_body(0, R1, 1, st + 3);     // step st; stage st+1 to LDS; load st+3
@@ -216,22 +239,45 @@ __device__ __forceinline__ void bwd_tile(u32x4 (*lds)[(BBM + BBN) * (BK / 8)],
 
   // Epilogue: lane holds column lr of each 32 x 32 block, rows
   // 8 (q / 4) + 4 lh + q % 4.
+  if (EPI == E_STORE) {
+    // Through LDS, 64 rows of each wave's TM / 2 x 64 sub-tile at a time,
+    // so that every global store writes 16 contiguous bytes (eight lanes
+    // cover one 128-byte row segment).
+    constexpr int OLD = 72;   // LDS row stride (elements): 16-byte aligned, 4-bank skew
+    uint16_t* so = reinterpret_cast<uint16_t*>(lds[0]) + wave * 64 * OLD;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int pass = 0; pass < MI / 2; ++pass) {
+      __syncthreads();   // the LDS is free (main loop, or the previous pass, is done)
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int q = 0; q < 16; ++q)
+            so[(ii * 32 + 8 * (q >> 2) + 4 * lh + (q & 3)) * OLD + j * 32 + lr] =
+                (uint16_t)f32_to_bf16_bits(acc[2 * pass + ii][j][q]);
+      __syncthreads();
+      const int rb = m0 + wm * (TM / 2) + pass * 64, cb = n0 + wn * 64;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int r = (lane >> 3) + 8 * t, c = (lane & 7) * 8;
+        if (rb + r < Mv && cb + c < Nv)
+          *reinterpret_cast<u32x4*>(ep.c + (int64_t)(rb + r) * ep.ldc + cb + c) =
+              *reinterpret_cast<const u32x4*>(so + r * OLD + c);
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int n = n0 + wn * 64 + j * 32 + lr;
       if (n >= Nv) continue;
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
-        const int mb = m0 + wm * 64 + i * 32 + 8 * qq + 4 * lh;   // 4 rows mb .. mb + 3
-        if (EPI == E_STORE) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (mb + r < Mv)
-              ep.c[(int64_t)(mb + r) * ep.ldc + n] =
-                  (uint16_t)f32_to_bf16_bits(acc[i][j][4 * qq + r]);
-        } else {
+        const int mb = m0 + wm * (TM / 2) + i * 32 + 8 * qq + 4 * lh;   // rows mb .. mb + 3
+        {
           float dg[4], du[4], hv[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -298,35 +344,45 @@ __global__ void __launch_bounds__(BNT) bwd_rows_kernel(BwdArgs p) {
     ep.ldT = p.ldT[s];
     ep.mpad = (nrows + kPad - 1) / kPad * kPad;
   }
-  bwd_tile<BK, B_KN, EPI>(lds, A, p.lda[s], B, p.ldb[s], 0, nrows, ntile * BBN, p.N[s], p.K[s],
+  bwd_tile<BK, BBM, B_KN, EPI>(lds, A, p.lda[s], B, p.ldb[s], 0, nrows, ntile * BBN, p.N[s], p.K[s],
                           ep);
 }
 
-// Weight-gradient GEMMs (DW2, DW13): work item = (group, M-tile, N-tile); A
-// and B are transposed operands, k over the group's padded columns (an
-// expert without rows gets a zero gradient).
-__global__ void __launch_bounds__(BNT) bwd_wgrad_kernel(BwdArgs p) {
+// Weight-gradient GEMMs (DW2, DW13): work item = (group, 256-row M-tile,
+// N-tile); A and B are transposed operands, k over the group's padded
+// columns (an expert without rows gets a zero gradient).  The tiles are
+// short (k = one expert's rows), so a fixed grid of two workgroups per CU
+// loops over them instead of one launch per tile: workgroup i of an XCD
+// takes tiles i, i + n, i + 2n, ... of that XCD's contiguous range, so the
+// XCD's workgroups work on neighbouring tiles (one expert's operands) at a
+// time.
+constexpr int kWgradPerCu = 2;
+
+__global__ void __launch_bounds__(BNT, kWgradPerCu) bwd_wgrad_kernel(BwdArgs p) {
   constexpr int BK = 32;
-  __shared__ u32x4 lds[2][(BBM + BBN) * (BK / 8)];   // 32 KiB
+  __shared__ u32x4 lds[2][(WTM + BBN) * (BK / 8)];   // 48 KiB
   const int64_t per_g = (int64_t)p.mt * p.nt;
   const int64_t groups = p.E + (p.M[1] > 0 ? 1 : 0);
   const int64_t work = groups * per_g;
   const int64_t per = (work + kNumXcd - 1) / kNumXcd;
-  const int64_t q = blockIdx.x / kNumXcd;
-  const int64_t w = (int64_t)(blockIdx.x % kNumXcd) * per + q;
-  if (q >= per || w >= work) return;
-  const int g = (int)(w / per_g);
-  const int rest = (int)(w % per_g);
-  const int mtile = rest / p.nt, ntile = rest % p.nt;
-  const int s = (g == p.E) ? 1 : 0;
-  if (mtile * BBM >= p.M[s] || ntile * BBN >= p.N[s]) return;
-  const int64_t col = s ? 0 : p.pcol[g];
-  const int kv = s ? (int)p.Tp : p.pcol[g + 1] - p.pcol[g];
-  Epi ep{};
-  ep.c = p.c[s] + (s == 0 ? (int64_t)g * p.cstride : 0);
-  ep.ldc = p.ldc[s];
-  bwd_tile<BK, B_NK, E_STORE>(lds, p.a[s] + col, p.lda[s], p.b[s] + col, p.ldb[s], mtile * BBM,
-                          p.M[s], ntile * BBN, p.N[s], kv, ep);
+  const int64_t nper = gridDim.x / kNumXcd;
+  const int64_t begin = (int64_t)(blockIdx.x % kNumXcd) * per;
+  const int64_t end = min(work, begin + per);
+  for (int64_t w = begin + blockIdx.x / kNumXcd; w < end; w += nper) {
+    const int g = (int)(w / per_g);
+    const int rest = (int)(w % per_g);
+    const int mtile = rest / p.nt, ntile = rest % p.nt;
+    const int s = (g == p.E) ? 1 : 0;
+    if (mtile * WTM >= p.M[s] || ntile * BBN >= p.N[s]) continue;   // uniform
+    const int64_t col = s ? 0 : p.pcol[g];
+    const int kv = s ? (int)p.Tp : p.pcol[g + 1] - p.pcol[g];
+    Epi ep{};
+    ep.c = p.c[s] + (s == 0 ? (int64_t)g * p.cstride : 0);
+    ep.ldc = p.ldc[s];
+    bwd_tile<BK, WTM, B_NK, E_STORE>(lds, p.a[s] + col, p.lda[s], p.b[s] + col, p.ldb[s],
+                                     mtile * WTM, p.M[s], ntile * BBN, p.N[s], kv, ep);
+    __syncthreads();   // the next tile's prologue rewrites the LDS
+  }
 }
 
 // pcol[e] = sum over e' < e of the row count of e' rounded up to kPad, for
@@ -401,31 +457,62 @@ unsigned grid_for(int64_t work) {
   return (unsigned)(((work + kNumXcd - 1) / kNumXcd) * kNumXcd);
 }
 
-// Workspace segments (bytes, 256-aligned).
+// Workgroups of the looping weight-gradient kernel: kWgradPerCu per CU of
+// the current device, at most one per tile, a multiple of the XCD count.
+unsigned wgrad_grid(int64_t work) {
+  static int cus = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      n = 256;
+    return n > 0 ? n : 256;
+  }();
+  return grid_for(std::min<int64_t>(work, (int64_t)cus * kWgradPerCu));
+}
+
+// Row stride (elements) of at least n whose size in bytes is an odd
+// multiple of 128: successive rows of a tile then fall in different memory
+// channels (a power-of-two stride would put them all in a few).
+int64_t spread_ld(int64_t n, int elem_bytes) {
+  const int64_t q = 128 / elem_bytes;
+  int64_t ld = (n + q - 1) / q * q;
+  if ((ld / q) % 2 == 0) ld += q;
+  return ld;
+}
+
+// Workspace segments (bytes, 256-aligned) and row strides (elements).
 struct BwdLayout {
   size_t gu, da, daT, hT, xT, dyT, pcol, tiles, total;
-  int64_t NP, Tp;   // transposed row strides: routed columns, shared columns
+  int64_t NP, Tp;            // transposed columns: routed (capacity), shared
+  int64_t ldr, lds;          // transposed row strides: routed, shared
+  int64_t ldgu_r, ldgu_s;    // [g u] rows (fp32)
+  int64_t ldda_r, ldda_s;    // [dg du] rows (bf16)
 };
 
 BwdLayout bwd_layout(const FfnDims& d) {
   BwdLayout L{};
   const int64_t rs = d.Is > 0 ? d.T : 0;
-  // every expert's padded width is below its rows + kPad; the stride stays
-  // a multiple of kPad (16-byte aligned rows)
+  // every expert's padded width is below its rows + kPad
   L.NP = (d.N + kPad - 1) / kPad * kPad + (int64_t)kPad * d.E;
   L.Tp = (rs + kPad - 1) / kPad * kPad;
+  L.ldr = spread_ld(L.NP, 2);
+  L.lds = spread_ld(L.Tp, 2);
+  L.ldgu_r = spread_ld(2 * d.I, 4);
+  L.ldgu_s = spread_ld(2 * d.Is, 4);
+  L.ldda_r = spread_ld(2 * d.I, 2);
+  L.ldda_s = spread_ld(2 * d.Is, 2);
   size_t o = 0;
   auto take = [&](size_t b) {
     const size_t at = o;
     o += (b + 255) / 256 * 256;
     return at;
   };
-  L.gu = take((size_t)(d.N * 2 * d.I + rs * 2 * d.Is) * 4);
-  L.da = take((size_t)(d.N * 2 * d.I + rs * 2 * d.Is) * 2);
-  L.daT = take((size_t)(2 * d.I * L.NP + 2 * d.Is * L.Tp) * 2);
-  L.hT = take((size_t)(d.I * L.NP + d.Is * L.Tp) * 2);
-  L.xT = take((size_t)d.H * (L.NP + L.Tp) * 2);
-  L.dyT = take((size_t)d.H * (L.NP + L.Tp) * 2);
+  L.gu = take((size_t)(d.N * L.ldgu_r + rs * L.ldgu_s) * 4);
+  L.da = take((size_t)(d.N * L.ldda_r + rs * L.ldda_s) * 2);
+  L.daT = take((size_t)(2 * d.I * L.ldr + 2 * d.Is * L.lds) * 2);
+  L.hT = take((size_t)(d.I * L.ldr + d.Is * L.lds) * 2);
+  L.xT = take((size_t)d.H * (L.ldr + L.lds) * 2);
+  L.dyT = take((size_t)d.H * (L.ldr + L.lds) * 2);
   L.pcol = take((size_t)(d.E + 1) * 4);
   L.tiles = take(ffn_tiles_bytes(d));
   L.total = o;
@@ -448,23 +535,24 @@ hipError_t launch_ffn_backward(const FfnDims& d, const uint16_t* x, const int32_
   const BwdLayout L = bwd_layout(d);
   char* base = (char*)ws;
   float* gu_r = (float*)(base + L.gu);
-  float* gu_s = gu_r + N * 2 * I;
+  float* gu_s = gu_r + N * L.ldgu_r;
   uint16_t* da_r = (uint16_t*)(base + L.da);
-  uint16_t* da_s = da_r + N * 2 * I;
+  uint16_t* da_s = da_r + N * L.ldda_r;
   uint16_t* daT_r = (uint16_t*)(base + L.daT);
-  uint16_t* daT_s = daT_r + 2 * I * L.NP;
+  uint16_t* daT_s = daT_r + 2 * I * L.ldr;
   uint16_t* hT_r = (uint16_t*)(base + L.hT);
-  uint16_t* hT_s = hT_r + I * L.NP;
+  uint16_t* hT_s = hT_r + I * L.ldr;
   uint16_t* xT_r = (uint16_t*)(base + L.xT);
-  uint16_t* xT_s = xT_r + H * L.NP;
+  uint16_t* xT_s = xT_r + H * L.ldr;
   uint16_t* dyT_r = (uint16_t*)(base + L.dyT);
-  uint16_t* dyT_s = dyT_r + H * L.NP;
+  uint16_t* dyT_s = dyT_r + H * L.ldr;
   int32_t* pcol = (int32_t*)(base + L.pcol);
   int32_t* tiles = (int32_t*)(base + L.tiles);
 
   // GU: [g u] = x_rows W13^T (rows x 2I, k = H), fp32, with the forward's
   // row-major gate/up GEMM.
-  hipError_t e = launch_gate_up_bf16(d, x, perm, offsets, w13, ws13, tiles, gu_r, gu_s, s);
+  hipError_t e = launch_gate_up_bf16(d, x, perm, offsets, w13, ws13, tiles, gu_r, L.ldgu_r, gu_s,
+                                     L.ldgu_s, s);
   if (e != hipSuccess) return e;
   e = launch_build_tiles(offsets, E, T, true, sh, BBM, tiles, s);
   if (e != hipSuccess) return e;
@@ -478,18 +566,18 @@ hipError_t launch_ffn_backward(const FfnDims& d, const uint16_t* x, const int32_
     const dim3 gr((unsigned)((L.NP + TR_COLS - 1) / TR_COLS), H / TR_H);
     MOE_TIMED_LAUNCH(s, "transpose_kernel<x>",
       hipLaunchKernelGGL(transpose_kernel, gr, dim3(256), 0, s, x, H, perm, d.K, offsets, pcol, E,
-                         T, xT_r, L.NP));
+                         T, xT_r, L.ldr));
     MOE_TIMED_LAUNCH(s, "transpose_kernel<dy>",
       hipLaunchKernelGGL(transpose_kernel, gr, dim3(256), 0, s, dy, H, perm, 0, offsets, pcol, E,
-                         T, dyT_r, L.NP));
+                         T, dyT_r, L.ldr));
     if (sh) {
       const dim3 gs((unsigned)(L.Tp / TR_COLS), H / TR_H);
       MOE_TIMED_LAUNCH(s, "transpose_kernel<x>",
         hipLaunchKernelGGL(transpose_kernel, gs, dim3(256), 0, s, x, H, nullptr, 0, nullptr,
-                           nullptr, E, T, xT_s, L.Tp));
+                           nullptr, E, T, xT_s, L.lds));
       MOE_TIMED_LAUNCH(s, "transpose_kernel<dy>",
         hipLaunchKernelGGL(transpose_kernel, gs, dim3(256), 0, s, dys, H, nullptr, 0, nullptr,
-                           nullptr, E, T, dyT_s, L.Tp));
+                           nullptr, E, T, dyT_s, L.lds));
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
@@ -509,10 +597,10 @@ hipError_t launch_ffn_backward(const FfnDims& d, const uint16_t* x, const int32_
     q.N[0] = I; q.N[1] = Is; q.K[0] = q.K[1] = H;
     q.a[0] = dy; q.a[1] = dys; q.lda[0] = q.lda[1] = H;
     q.b[0] = w2; q.b[1] = ws2; q.ldb[0] = I; q.ldb[1] = Is; q.bstride = (int64_t)H * I;
-    q.gu[0] = gu_r; q.gu[1] = gu_s; q.ldgu[0] = 2 * I; q.ldgu[1] = 2 * Is;
-    q.da[0] = da_r; q.da[1] = da_s; q.ldda[0] = 2 * I; q.ldda[1] = 2 * Is;
+    q.gu[0] = gu_r; q.gu[1] = gu_s; q.ldgu[0] = L.ldgu_r; q.ldgu[1] = L.ldgu_s;
+    q.da[0] = da_r; q.da[1] = da_s; q.ldda[0] = L.ldda_r; q.ldda[1] = L.ldda_s;
     q.daT[0] = daT_r; q.daT[1] = daT_s; q.hT[0] = hT_r; q.hT[1] = hT_s;
-    q.ldT[0] = L.NP; q.ldT[1] = L.Tp;
+    q.ldT[0] = L.ldr; q.ldT[1] = L.lds;
     q.ntn = (std::max(I, Is) + BBN - 1) / BBN;
     MOE_TIMED_LAUNCH(s, "bwd_rows_kernel<dh>",
       hipLaunchKernelGGL(bwd_rows_kernel<E_DH>, dim3(grid_for(mt * q.ntn)), dim3(BNT), 0, s, q));
@@ -522,7 +610,7 @@ hipError_t launch_ffn_backward(const FfnDims& d, const uint16_t* x, const int32_
   if (dx || dxs) {
     BwdArgs q = p;
     q.N[0] = q.N[1] = H; q.K[0] = 2 * I; q.K[1] = 2 * Is;
-    q.a[0] = da_r; q.a[1] = da_s; q.lda[0] = 2 * I; q.lda[1] = 2 * Is;
+    q.a[0] = da_r; q.a[1] = da_s; q.lda[0] = L.ldda_r; q.lda[1] = L.ldda_s;
     q.b[0] = w13; q.b[1] = ws13; q.ldb[0] = q.ldb[1] = H; q.bstride = (int64_t)2 * I * H;
     q.c[0] = dx; q.c[1] = dxs; q.ldc[0] = q.ldc[1] = H;
     q.ntn = (H + BBN - 1) / BBN;
@@ -535,14 +623,14 @@ hipError_t launch_ffn_backward(const FfnDims& d, const uint16_t* x, const int32_
   {
     BwdArgs q = p;
     q.M[0] = H; q.M[1] = sh ? H : 0; q.N[0] = I; q.N[1] = Is;
-    q.a[0] = dyT_r; q.a[1] = dyT_s; q.lda[0] = L.NP; q.lda[1] = L.Tp;
-    q.b[0] = hT_r; q.b[1] = hT_s; q.ldb[0] = L.NP; q.ldb[1] = L.Tp;
+    q.a[0] = dyT_r; q.a[1] = dyT_s; q.lda[0] = L.ldr; q.lda[1] = L.lds;
+    q.b[0] = hT_r; q.b[1] = hT_s; q.ldb[0] = L.ldr; q.ldb[1] = L.lds;
     q.c[0] = dw2; q.c[1] = dws2; q.ldc[0] = I; q.ldc[1] = Is; q.cstride = (int64_t)H * I;
-    q.mt = (H + BBM - 1) / BBM;
+    q.mt = (H + WTM - 1) / WTM;
     q.nt = (std::max(I, Is) + BBN - 1) / BBN;
     const int64_t work = (int64_t)(E + (sh ? 1 : 0)) * q.mt * q.nt;
     MOE_TIMED_LAUNCH(s, "bwd_wgrad_kernel<dw2>",
-      hipLaunchKernelGGL(bwd_wgrad_kernel, dim3(grid_for(work)), dim3(BNT), 0, s, q));
+      hipLaunchKernelGGL(bwd_wgrad_kernel, dim3(wgrad_grid(work)), dim3(BNT), 0, s, q));
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // DW13: dW13 = [dg du]^T x_rows (2I x H, k = the expert's rows): A =
@@ -550,14 +638,14 @@ hipError_t launch_ffn_backward(const FfnDims& d, const uint16_t* x, const int32_
   {
     BwdArgs q = p;
     q.M[0] = 2 * I; q.M[1] = sh ? 2 * Is : 0; q.N[0] = q.N[1] = H;
-    q.a[0] = daT_r; q.a[1] = daT_s; q.lda[0] = L.NP; q.lda[1] = L.Tp;
-    q.b[0] = xT_r; q.b[1] = xT_s; q.ldb[0] = L.NP; q.ldb[1] = L.Tp;
+    q.a[0] = daT_r; q.a[1] = daT_s; q.lda[0] = L.ldr; q.lda[1] = L.lds;
+    q.b[0] = xT_r; q.b[1] = xT_s; q.ldb[0] = L.ldr; q.ldb[1] = L.lds;
     q.c[0] = dw13; q.c[1] = dws13; q.ldc[0] = q.ldc[1] = H; q.cstride = (int64_t)2 * I * H;
-    q.mt = (std::max(2 * I, 2 * Is) + BBM - 1) / BBM;
+    q.mt = (std::max(2 * I, 2 * Is) + WTM - 1) / WTM;
     q.nt = (H + BBN - 1) / BBN;
     const int64_t work = (int64_t)(E + (sh ? 1 : 0)) * q.mt * q.nt;
     MOE_TIMED_LAUNCH(s, "bwd_wgrad_kernel<dw13>",
-      hipLaunchKernelGGL(bwd_wgrad_kernel, dim3(grid_for(work)), dim3(BNT), 0, s, q));
+      hipLaunchKernelGGL(bwd_wgrad_kernel, dim3(wgrad_grid(work)), dim3(BNT), 0, s, q));
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;

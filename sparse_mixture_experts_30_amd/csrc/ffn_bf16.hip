@@ -323,7 +323,8 @@ hipError_t launch_ffn_bf16(const FfnDims& d, const uint16_t* x, const int32_t* p
 
 hipError_t launch_gate_up_bf16(const FfnDims& d, const uint16_t* x, const int32_t* perm,
                                const int32_t* offsets, const uint16_t* w13, const uint16_t* ws13,
-                               int32_t* tiles, float* gu, float* gus, hipStream_t s) {
+                               int32_t* tiles, float* gu, int64_t ldgu, float* gus,
+                               int64_t ldgus, hipStream_t s) {
   hipError_t e = set_attrs();
   if (e != hipSuccess) return e;
   e = ffn_build_tiles(d, offsets, BM, tiles, s);
@@ -345,8 +346,8 @@ hipError_t launch_gate_up_bf16(const FfnDims& d, const uint16_t* x, const int32_
   a.ncol_s = d.Is;
   a.c_r = reinterpret_cast<uint16_t*>(gu);
   a.c_s = reinterpret_cast<uint16_t*>(gus);
-  a.ldc_r = 2 * d.I;
-  a.ldc_s = 2 * d.Is;
+  a.ldc_r = ldgu;
+  a.ldc_s = ldgus;
   MOE_TIMED_LAUNCH(s, "grouped_gemm_bf16<gate_up>",
     hipLaunchKernelGGL((grouped_gemm_bf16<true, true>), dim3(grid_for(mt * a.ntn)), dim3(NT), kLds,
                        s, a));

@@ -149,11 +149,13 @@ hipError_t launch_ffn_bf16(const FfnDims& d, const uint16_t* x, const int32_t* p
                            const int32_t* offsets, const uint16_t* w13, const uint16_t* w2,
                            const uint16_t* ws13, const uint16_t* ws2, uint16_t* h,
                            int32_t* tiles, uint16_t* y, uint16_t* ys, hipStream_t s);
-// [g u] = x_rows W13^T in fp32 (routed rows in expert order, then the
-// shared expert's T rows at gus), with the row-major GEMM1 of ffn_bf16.hip.
+// [g u] = x_rows W13^T in fp32 (routed rows in expert order, row stride
+// ldgu; the shared expert's T rows at gus, stride ldgus), with the
+// row-major GEMM1 of ffn_bf16.hip.
 hipError_t launch_gate_up_bf16(const FfnDims& d, const uint16_t* x, const int32_t* perm,
                                const int32_t* offsets, const uint16_t* w13, const uint16_t* ws13,
-                               int32_t* tiles, float* gu, float* gus, hipStream_t s);
+                               int32_t* tiles, float* gu, int64_t ldgu, float* gus,
+                               int64_t ldgus, hipStream_t s);
 // Packed weight layout (ffn_bf16_packed.hip).
 size_t packed_bytes(bool gate_up, int64_t experts, int n, int kd);
 hipError_t launch_pack(bool gate_up, const uint16_t* src, void* dst, int64_t experts, int n,
