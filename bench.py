@@ -115,7 +115,8 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=384,
                     help="tokens of the workload run through the fp64 oracle (0 = skip)")
     ap.add_argument("--profile-only", action="store_true",
-                    help="just run warmup + steps (for rocprofv3), print the JSON line")
+                    help="for rocprofv3: warmup + steps and the per-kernel breakdown only (no "
+                         "oracle, no second entry point, no backward), print the JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="copy 1 GiB device-to-device 5 times (HBM counter calibration)")
     ap.add_argument("--overlap", action="store_true",
@@ -165,8 +166,8 @@ def main():
     d = sd.to_device(inp)
     # The expert-FFN backward (training) reads row-major bf16 weights: kept
     # for the bf16 layer workloads of at least 1024 tokens.
-    with_bwd = (not args.no_backward and not gate_only and cfg.wdtype == "bf16" and
-                cfg.act == "bf16" and T >= 1024)
+    with_bwd = (not args.no_backward and not args.profile_only and not gate_only and
+                cfg.wdtype == "bf16" and cfg.act == "bf16" and T >= 1024)
     drow = d if with_bwd else None
     if cfg.wdtype != "f32" and not args.row_major and not gate_only:
         d = sd.packed_copy(d)   # the row-major device copies are released here unless kept
@@ -238,21 +239,30 @@ def main():
     ms = ev0.elapsed_time(ev1) / args.steps
     log(f"[bench] {ms:.3f} ms/step; dominant kernel {dominant}: {dom_ms:.3f} ms/launch")
 
-    # The other forward path (one stream vs two), timed the same way.
+    # The other forward path (one stream vs two), not in a profiled run (its
+    # launches would mix into the traced kernels' figures).  Three rounds that
+    # alternate the two paths, K steps each, so that both see the same clocks
+    # and caches; the medians are reported.
     other = None
-    if not gate_only:
+    if not gate_only and not args.profile_only:
+        times = {True: [], False: []}
         for _ in range(2):
             forward(not overlap)
-        torch.cuda.synchronize()
-        ev0.record(stream)
-        for _ in range(args.steps):
-            forward(not overlap)
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        oms = ev0.elapsed_time(ev1) / args.steps
+        for _ in range(3):
+            for path in (overlap, not overlap):
+                torch.cuda.synchronize()
+                ev0.record(stream)
+                for _ in range(args.steps):
+                    forward(path)
+                ev1.record(stream)
+                torch.cuda.synchronize()
+                times[path].append(ev0.elapsed_time(ev1) / args.steps)
+        oms = sorted(times[not overlap])[1]
         other = {"entry_point": "moe_forward" if overlap else "moe_forward_overlap",
-                 "ms": round(oms, 4), "tokens_per_s": round(T / (oms * 1e-3), 1)}
-        log(f"[bench] {other['entry_point']}: {oms:.3f} ms/step")
+                 "ms": round(oms, 4), "tokens_per_s": round(T / (oms * 1e-3), 1),
+                 "step_entry_point_ms_same_rounds": round(sorted(times[overlap])[1], 4)}
+        log(f"[bench] {other['entry_point']}: {oms:.3f} ms/step (step entry point "
+            f"{other['step_entry_point_ms_same_rounds']:.3f} ms in the same rounds)")
 
     # Per-phase timing with the separate entry points (same kernels, same
     # stream), HIP events between phases.
