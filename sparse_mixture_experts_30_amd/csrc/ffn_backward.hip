@@ -124,7 +124,9 @@ __device__ __forceinline__ void bwd_tile(u32x4 (*lds)[(TM + BBN) * (BK / 8)],
   const int nsteps = (Kv + BK - 1) / BK;
 
   // Thread's rows: A (and B_NK) row tid / CH + (256 / CH) j, chunk tid % CH;
-  // B_KN: k row tid / 16 + 16 j, n chunk tid % 16.
+  // B_KN (BK = 64): k rows 4 (tid / 16) + j, n chunk tid % 16, a 4 x 8 block
+  // that is transposed in registers and stored as eight 8-byte [n][k] runs.
+  static_assert(BMD != B_KN || BK == 64, "the k-row operand is staged in 64-k steps");
   struct Stage {
     u32x4 a[NA], b[NS];
   };
@@ -146,7 +148,7 @@ __device__ __forceinline__ void bwd_tile(u32x4 (*lds)[(TM + BBN) * (BK / 8)],
                     ? *reinterpret_cast<const u32x4*>(B + (int64_t)(n0 + n) * ldb + k0 + ch * 8)
                     : (u32x4){0, 0, 0, 0};
     } else {
-      const int k = (tid >> 4) + 16 * j, nc = tid & 15;
+      const int k = 4 * (tid >> 4) + j, nc = tid & 15;
       st.b[j] = (n0 + nc * 8 < Nv && k0 + k < Kv)
                     ? *reinterpret_cast<const u32x4*>(B + (int64_t)(k0 + k) * ldb + n0 + nc * 8)
                     : (u32x4){0, 0, 0, 0};
@@ -161,13 +163,21 @@ __device__ __forceinline__ void bwd_tile(u32x4 (*lds)[(TM + BBN) * (BK / 8)],
     if (BMD == B_NK) {
       const int n = tid / CH + (BNT / CH) * j;
       sB[swz<BK>(n, ch)] = st.b[j];
-    } else {
-      const int k = (tid >> 4) + 16 * j, nc = tid & 15;
+    } else if (j == NS - 1) {   // all four k rows are in: transpose and store
+      const int kq = tid >> 4, nc = tid & 15;
       uint16_t* sb = reinterpret_cast<uint16_t*>(sB);
-      const uint32_t w[4] = {st.b[j].x, st.b[j].y, st.b[j].z, st.b[j].w};
+      const uint32_t w[4][4] = {{st.b[0].x, st.b[0].y, st.b[0].z, st.b[0].w},
+                                {st.b[1].x, st.b[1].y, st.b[1].z, st.b[1].w},
+                                {st.b[2].x, st.b[2].y, st.b[2].z, st.b[2].w},
+                                {st.b[3].x, st.b[3].y, st.b[3].z, st.b[3].w}};
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        sb[swz<BK>(nc * 8 + i, k >> 3) * 8 + (k & 7)] = (uint16_t)(w[i >> 1] >> (16 * (i & 1)));
+      for (int i = 0; i < 8; ++i) {   // column n = 8 nc + i: k rows 4 kq .. 4 kq + 3
+        const int sh = 16 * (i & 1);
+        const uint32_t e0 = (w[0][i >> 1] >> sh) & 0xFFFFu, e1 = (w[1][i >> 1] >> sh) & 0xFFFFu;
+        const uint32_t e2 = (w[2][i >> 1] >> sh) & 0xFFFFu, e3 = (w[3][i >> 1] >> sh) & 0xFFFFu;
+        *reinterpret_cast<uint2*>(sb + swz<BK>(nc * 8 + i, kq >> 1) * 8 + (kq & 1) * 4) =
+            (uint2){e0 | (e1 << 16), e2 | (e3 << 16)};
+      }
     }
   };
 
@@ -203,8 +213,14 @@ __device__ __forceinline__ void bwd_tile(u32x4 (*lds)[(TM + BBN) * (BK / 8)],
         sstore_a(st, j, nbuf);
         gload_a(st, j, ld);
       }
-      sstore_b(st, kk, nbuf);
-      gload_b(st, kk, ld);
+      if (BMD == B_NK) {
+        sstore_b(st, kk, nbuf);
+        gload_b(st, kk, ld);
+      } else if (kk == NS - 1) {   // the k-row block is stored whole, then reloaded
+        sstore_b(st, NS - 1, nbuf);
+#pragma unroll
+        for (int j = 0; j < NS; ++j) gload_b(st, j, ld);
+      }
     }
   };
 
