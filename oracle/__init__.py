@@ -295,3 +295,61 @@ def ffn_backward_entries(cfg, inp: dict, expert: int, tokens, dy, which, rows, c
     if rc:
         raise ValueError("oracle_ffn_backward_entries rejected its arguments")
     return out
+
+
+def routing_weights(cfg, lg: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """Routing weights of the chosen experts from the logits, fp64 ("从 1024 块
+    GPU 到 558 万美元：拆解 DeepSeek-V3 的算法-系统协同设计", section 2.2, MoEGate): the
+    unbiased sigmoid scores s of the chosen experts, divided by their sum (plus
+    1e-20) when top_k > 1, times routed_scaling_factor -> [T, K]."""
+    lg = np.asarray(lg, np.float64)
+    idx = np.asarray(idx)
+    s = 1.0 / (1.0 + np.exp(-np.take_along_axis(lg, idx.astype(np.int64), axis=1)))
+    if cfg.K > 1:
+        s = s / (s.sum(axis=1, keepdims=True) + 1e-20)
+    return s * cfg.rho
+
+
+def layer_backward(cfg, inp: dict, idx: np.ndarray, dout: np.ndarray) -> dict:
+    """Exact fp64 gradients of L = sum_t <dout_t, out_t> for the layer with
+    its routing held at idx (the top-k choice is piecewise constant in the
+    inputs: the gradient reaches the gate only through the chosen experts'
+    weights).  out_t = shared(x_t) + sum_k w_tk FFN_idx[t,k](x_t) with w from
+    routing_weights; the bias only selects and gets no gradient.
+    Returns dx [T, H], dgate_w [E, H], dw13 [E, 2I, H], dw2 [E, H, I] and, with
+    a shared expert, dws13 [2Is, H], dws2 [H, Is]."""
+    T, H, E, K, I = inp["x"].shape[0], cfg.H, cfg.E, cfg.K, cfg.I
+    x = np.asarray(inp["x"])
+    xf = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64) if x.dtype == np.uint16 \
+        else x.astype(np.float64)
+    gw = np.asarray(inp["gate_w"], np.float64)
+    dout = np.asarray(dout, np.float64)
+    idx = np.asarray(idx, np.int64)
+    lg = logits(x, cfg.act, inp["gate_w"])
+    s = 1.0 / (1.0 + np.exp(-np.take_along_axis(lg, idx, axis=1)))          # [T, K]
+    w = routing_weights(cfg, lg, idx)
+    tok = np.repeat(np.arange(T), K)
+    y = ffn(cfg, inp, tok, idx.ravel().astype(np.int32)).reshape(T, K, H)  # expert outputs
+    dw = np.einsum("th,tkh->tk", dout, y)
+    if K > 1:   # w_k = rho s_k / D, D = sum_j s_j + 1e-20
+        D = s.sum(axis=1, keepdims=True) + 1e-20
+        ds = cfg.rho * (dw / D - (dw * s).sum(axis=1, keepdims=True) / D ** 2)
+    else:
+        ds = cfg.rho * dw
+    dlg = ds * s * (1.0 - s)                                                 # d logit of the chosen
+    out = {"dgate_w": np.zeros((E, H)), "dw13": np.zeros((E, 2 * I, H)), "dw2": np.zeros((E, H, I))}
+    np.add.at(out["dgate_w"], idx.ravel(), dlg.ravel()[:, None] * xf[tok])
+    dx = np.einsum("tk,tkh->th", dlg, gw[idx])
+    for e in range(E):
+        rows = np.flatnonzero(idx.ravel() == e)
+        if len(rows) == 0:
+            continue
+        b = ffn_backward(cfg, inp, e, tok[rows], w.ravel()[rows, None] * dout[tok[rows]])
+        out["dw13"][e], out["dw2"][e] = b["dw13"], b["dw2"]
+        np.add.at(dx, tok[rows], b["dx"])
+    if cfg.Is:
+        b = ffn_backward(cfg, inp, -1, np.arange(T), dout)
+        out["dws13"], out["dws2"] = b["dw13"], b["dw2"]
+        dx += b["dx"]
+    out["dx"] = dx
+    return out

@@ -635,3 +635,67 @@ def test_ffn_backward_entries_equal_full_gradients(fd_inputs, expert):
                                       np.concatenate([r13, r2]), np.concatenate([c13, c2]))
     np.testing.assert_allclose(got[:2 * ne * cfg.H], full["dw13"].ravel(), rtol=1e-12, atol=1e-14)
     np.testing.assert_allclose(got[2 * ne * cfg.H:], full["dw2"].ravel(), rtol=1e-12, atol=1e-14)
+
+
+# Layer backward with the routing held fixed (a top-k choice is piecewise
+# constant): central differences of L = sum_t <dout_t, out_t>, where out comes
+# from the oracle's forward with the routing weights recomputed from the
+# perturbed logits.  Every perturbation must leave the routing unchanged.
+LB_CFGS = [synth.C1.replace(name="lbwd-T6-H16-E4-K2", T=6, H=16, E=4, G=2, TG=1, K=2, I=8, Is=8,
+                            rho=2.5),
+           synth.C1.replace(name="lbwd-T5-H16-E4-K1-noshared", T=5, H=16, E=4, G=2, TG=2, K=1,
+                            I=8, Is=0, rho=1.7)]
+
+
+def _layer_loss(cfg, inp, idx, dout):
+    lg = oracle.logits(inp["x"], cfg.act, inp["gate_w"])
+    idx2, _, _ = oracle.route_f64(cfg, lg, inp["bias"])
+    assert np.array_equal(idx2, idx), "perturbation changed the routing"
+    out = oracle.layer(cfg, inp, idx, oracle.routing_weights(cfg, lg, idx))
+    return float((out * dout).sum())
+
+
+@pytest.mark.parametrize("cfg", LB_CFGS, ids=lambda c: c.name)
+def test_layer_backward_matches_finite_differences(cfg):
+    inp = synth.gen_inputs(cfg)
+    lg = oracle.logits(inp["x"], cfg.act, inp["gate_w"])
+    idx, w, margin = oracle.route_f64(cfg, lg, inp["bias"])
+    assert margin.min() > 1e-3
+    # the weights the backward differentiates are the router's own
+    np.testing.assert_array_equal(oracle.routing_weights(cfg, lg, idx), w)
+    dout = np.random.default_rng(21).standard_normal((cfg.T, cfg.H))
+    b = oracle.layer_backward(cfg, inp, idx, dout)
+    eps = np.float32(2.0 ** -12)
+
+    def fd(key, index):
+        plus, minus = dict(inp), dict(inp)
+        a = inp[key].copy(); a[index] += eps; plus[key] = a
+        a = inp[key].copy(); a[index] -= eps; minus[key] = a
+        return (_layer_loss(cfg, plus, idx, dout) - _layer_loss(cfg, minus, idx, dout)) / (
+            2 * float(eps))
+
+    keys = [("x", "dx"), ("gate_w", "dgate_w"), ("w13", "dw13"), ("w2", "dw2")]
+    if cfg.Is:
+        keys += [("ws13", "dws13"), ("ws2", "dws2")]
+    for key, gkey in keys:
+        num = np.array([fd(key, ix) for ix in np.ndindex(*inp[key].shape)]).reshape(inp[key].shape)
+        # central differences carry an O(eps^2) curvature term: 1e-5 of the
+        # gradient's scale covers it, and a dropped term or wrong sign is O(1)
+        np.testing.assert_allclose(b[gkey], num, rtol=1e-5, atol=1e-5 * np.abs(num).max(),
+                                   err_msg=gkey)
+
+
+def test_layer_backward_gate_gradient_zero_when_weights_cannot_move():
+    # top-1 with rho: w = rho * s, so the gate gets dlogit = rho <dout, y> s (1 - s);
+    # with dout orthogonal to every chosen expert's output the gate gradient
+    # vanishes while the experts' gradients do not.
+    cfg = LB_CFGS[1]
+    inp = synth.gen_inputs(cfg)
+    lg = oracle.logits(inp["x"], cfg.act, inp["gate_w"])
+    idx, _, _ = oracle.route_f64(cfg, lg, inp["bias"])
+    y = oracle.ffn(cfg, inp, np.arange(cfg.T), idx[:, 0])
+    dout = np.random.default_rng(22).standard_normal((cfg.T, cfg.H))
+    dout -= (np.einsum("th,th->t", dout, y) / np.einsum("th,th->t", y, y))[:, None] * y
+    b = oracle.layer_backward(cfg, inp, idx, dout)
+    np.testing.assert_allclose(b["dgate_w"], 0.0, atol=1e-12)
+    assert np.abs(b["dw2"]).max() > 1e-3
