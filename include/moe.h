@@ -242,6 +242,43 @@ moe_status moe_expert_ffn_backward(const moe_config* cfg, int64_t T, const void*
                                    void* dws13, void* dws2, void* ws, size_t ws_bytes,
                                    void* stream);
 
+/* Backward of the whole layer, for training, with the routing held at the
+ * forward's choice (the top-k selection is piecewise constant: the gradient
+ * reaches the gate through the chosen experts' weights only, and the
+ * selection-only bias gets none).  The forward is that of moe_forward
+ * ("从 1024 块 GPU 到 558 万美元：拆解 DeepSeek-V3 的算法-系统协同设计", section 2.2,
+ * MoEGate, and the combine of section 2.3): out_t = shared(x_t) +
+ * sum_k w_tk y_tk with w_k = rho s_k / (sum_j s_j + 1e-20) (top_k > 1) or
+ * rho s_k, s = sigmoid(logits) of the chosen experts, logits = x Wg^T.
+ * Given dout [T, H], with D = sum_j s_j + 1e-20:
+ *   dy_tk = w_tk dout_t (the routed rows' gradients, rounded to bf16),
+ *   dw_tk = <dout_t, y_tk>,  ds_k = rho (dw_k / D - sum_j dw_j s_j / D^2)
+ *   (rho dw_k for top-1),  dlogit_tk = ds_k s_k (1 - s_k),
+ *   dgate_w[e] = sum over the rows routed to e of dlogit x_t (fp32),
+ *   dx_t = sum_k dlogit_tk Wg[idx_tk] + the experts' input gradients
+ *   (moe_expert_ffn_backward, with the shared expert's output gradient dout).
+ *   x [T, H] bf16; w: gate_w [E, H] fp32 and row-major bf16 expert weights
+ *      (packed = 0) as in moe_expert_ffn_backward;
+ *   logits [T, E] fp32, topk_idx / topk_w [T, K], perm [T*K], offsets [E+1],
+ *      pos [T*K]: the forward's (moe_gate, moe_permute);
+ *   y [T*K, H] bf16: the routed expert outputs of the forward in sorted row
+ *      order (moe_expert_ffn's y);
+ *   dout [T, H] bf16: the gradient of the layer output.
+ *   Outputs (written whole): dx [T, H] bf16, dgate_w [E, H] fp32, dw13,
+ *   dw2 (and dws13, dws2 with a shared expert) bf16 as in
+ *   moe_expert_ffn_backward.
+ * Workspace: moe_backward_workspace_bytes(cfg, T) bytes (0 for a config the
+ * backward does not take), 256-byte aligned.
+ * Errors: MOE_ERR_UNSUPPORTED for non-bf16 configs or packed weights;
+ * MOE_ERR_INVALID_ARG for a missing array; MOE_ERR_WORKSPACE. */
+size_t moe_backward_workspace_bytes(const moe_config* cfg, int64_t T);
+moe_status moe_backward(const moe_config* cfg, int64_t T, const void* x, const moe_weights* w,
+                        const float* logits, const int32_t* topk_idx, const float* topk_w,
+                        const int32_t* perm, const int32_t* offsets, const int32_t* pos,
+                        const void* y, const void* dout, void* dx, float* dgate_w, void* dw13,
+                        void* dw2, void* dws13, void* dws2, void* ws, size_t ws_bytes,
+                        void* stream);
+
 /* Load-balancing update of the selection bias.  The bias takes part only in
  * choosing experts and is steered by the experts' observed load instead of
  * a gradient ("从 1024 块 GPU 到 558 万美元：拆解 DeepSeek-V3 的算法-系统协同设计",

@@ -19,7 +19,8 @@ EXPORTS = ("moe_workspace_bytes", "moe_gate", "moe_permute", "moe_expert_ffn", "
            "moe_forward", "moe_forward_overlap", "moe_quantize_act", "moe_packed_bytes", "moe_pack_weight",
            "moe_get_device_error", "moe_strerror", "moe_last_error", "moe_kernel_timer_enable",
            "moe_kernel_timer_read", "moe_bias_update", "moe_expert_ffn_backward",
-           "moe_expert_ffn_backward_workspace_bytes")
+           "moe_expert_ffn_backward_workspace_bytes", "moe_backward",
+           "moe_backward_workspace_bytes")
 MOE_W13, MOE_W2, MOE_WS13, MOE_WS2 = 0, 1, 2, 3
 
 
@@ -72,6 +73,9 @@ def lib():
             "moe_expert_ffn_backward_workspace_bytes": (sz, [cfgp, i64]),
             "moe_expert_ffn_backward": (ctypes.c_int, [cfgp, i64, vp, vp, vp, wp, vp, vp, vp, vp, vp,
                                                        vp, vp, vp, vp, sz, vp]),
+            "moe_backward_workspace_bytes": (sz, [cfgp, i64]),
+            "moe_backward": (ctypes.c_int, [cfgp, i64, vp, wp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                            vp, vp, vp, vp, vp, vp, sz, vp]),
             "moe_packed_bytes": (sz, [cfgp, ctypes.c_int]),
             "moe_pack_weight": (ctypes.c_int, [cfgp, ctypes.c_int, vp, vp, vp]),
             "moe_get_device_error": (ctypes.c_int, [vp, sz, vp]),
@@ -171,6 +175,19 @@ def moe_forward_overlap(cfg, T, x, w: MoeWeights, out, ws, shared_stream, logits
                                      _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _ptr(counts),
                                      _ptr(perm), _ptr(ws), _nbytes(ws) if ws is not None else 0,
                                      _stream(stream), _stream(shared_stream)))
+
+
+def moe_backward_workspace_bytes(cfg, T) -> int:
+    return lib().moe_backward_workspace_bytes(ctypes.byref(cfg), T)
+
+
+def moe_backward(cfg, T, x, w: MoeWeights, logits, topk_idx, topk_w, perm, offsets, pos, y, dout,
+                 dx, dgate_w, dw13, dw2, dws13, dws2, ws, stream=None):
+    _check(lib().moe_backward(ctypes.byref(cfg), T, _ptr(x), ctypes.byref(w), _ptr(logits),
+                              _ptr(topk_idx), _ptr(topk_w), _ptr(perm), _ptr(offsets), _ptr(pos),
+                              _ptr(y), _ptr(dout), _ptr(dx), _ptr(dgate_w), _ptr(dw13),
+                              _ptr(dw2), _ptr(dws13), _ptr(dws2), _ptr(ws),
+                              _nbytes(ws) if ws is not None else 0, _stream(stream)))
 
 
 def moe_quantize_act(cfg, rows, x, xq, xs, stream=None):

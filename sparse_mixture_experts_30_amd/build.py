@@ -18,7 +18,8 @@ BUILD = os.path.join(ROOT, "_build")
 
 SOURCES = ["gate.hip", "permute.hip", "ffn_sched.hip", "ffn_bf16.hip", "ffn_bf16_packed.hip",
            "ffn_fp8.hip", "ffn_fp8_packed.hip",
-           "ffn_f32.hip", "combine.hip", "bias.hip", "ffn_backward.hip", "decode.hip", "moe_api.cpp",
+           "ffn_f32.hip", "combine.hip", "bias.hip", "ffn_backward.hip", "decode.hip",
+           "layer_backward.hip", "moe_api.cpp",
            "timer.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

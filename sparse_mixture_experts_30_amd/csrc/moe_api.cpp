@@ -10,6 +10,7 @@
 #include <algorithm>
 
 #include "moe_internal.hpp"
+#include "backward.hpp"
 
 namespace {
 
@@ -509,6 +510,70 @@ moe_status moe_expert_ffn_backward(const moe_config* cfg, int64_t T, const void*
                                    (uint16_t*)dw2, (uint16_t*)(sh ? dws13 : nullptr),
                                    (uint16_t*)(sh ? dws2 : nullptr), ws, (hipStream_t)stream),
           "expert backward");
+  return MOE_OK;
+}
+
+size_t moe_backward_workspace_bytes(const moe_config* cfg, int64_t T) {
+  if (check_cfg(cfg) != MOE_OK || check_T(T, cfg) != MOE_OK) return 0;
+  if (cfg->weight_dtype != MOE_BF16 || cfg->act_dtype != MOE_BF16) return 0;
+  moe::FfnDims d{T, T * cfg->num_experts_per_tok, cfg->hidden_size, cfg->moe_intermediate_size,
+                 cfg->shared_intermediate_size, cfg->n_routed_experts,
+                 cfg->num_experts_per_tok};
+  return moe::layer_backward_ws_bytes(d);
+}
+
+moe_status moe_backward(const moe_config* cfg, int64_t T, const void* x, const moe_weights* w,
+                        const float* logits, const int32_t* topk_idx, const float* topk_w,
+                        const int32_t* perm, const int32_t* offsets, const int32_t* pos,
+                        const void* y, const void* dout, void* dx, float* dgate_w, void* dw13,
+                        void* dw2, void* dws13, void* dws2, void* ws, size_t ws_bytes,
+                        void* stream) {
+  CHECK(check_cfg(cfg));
+  CHECK(check_T(T, cfg));
+  if (cfg->weight_dtype != MOE_BF16 || cfg->act_dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "the layer backward takes bf16 activations and weights");
+  if (T == 0) return MOE_OK;
+  NONNULL(w);
+  if (w->packed)
+    return fail(MOE_ERR_UNSUPPORTED, "the layer backward reads row-major weights (packed = 0)");
+  NONNULL(x);
+  NONNULL(w->gate_w);
+  NONNULL(w->w13);
+  NONNULL(w->w2);
+  NONNULL(logits);
+  NONNULL(topk_idx);
+  NONNULL(topk_w);
+  NONNULL(perm);
+  NONNULL(offsets);
+  NONNULL(pos);
+  NONNULL(y);
+  NONNULL(dout);
+  NONNULL(dx);
+  NONNULL(dgate_w);
+  NONNULL(dw13);
+  NONNULL(dw2);
+  const bool sh = cfg->shared_intermediate_size > 0;
+  if (sh) {
+    NONNULL(w->ws13);
+    NONNULL(w->ws2);
+    NONNULL(dws13);
+    NONNULL(dws2);
+  }
+  moe::FfnDims d{T, T * cfg->num_experts_per_tok, cfg->hidden_size, cfg->moe_intermediate_size,
+                 cfg->shared_intermediate_size, cfg->n_routed_experts,
+                 cfg->num_experts_per_tok};
+  const size_t need = moe::layer_backward_ws_bytes(d);
+  if (!ws || ws_bytes < need || ((uintptr_t)ws & 255))
+    return fail(MOE_ERR_WORKSPACE, "workspace must be 256-byte aligned and >= %zu bytes", need);
+  HIPCALL(moe::launch_layer_backward(
+              d, (const uint16_t*)x, w->gate_w, logits, topk_idx, topk_w, perm, offsets, pos,
+              (const uint16_t*)y, (const uint16_t*)dout, (const uint16_t*)w->w13,
+              (const uint16_t*)w->w2, (const uint16_t*)(sh ? w->ws13 : nullptr),
+              (const uint16_t*)(sh ? w->ws2 : nullptr), cfg->routed_scaling_factor,
+              (uint16_t*)dx, dgate_w, (uint16_t*)dw13, (uint16_t*)dw2,
+              (uint16_t*)(sh ? dws13 : nullptr), (uint16_t*)(sh ? dws2 : nullptr), ws,
+              (hipStream_t)stream),
+          "layer backward");
   return MOE_OK;
 }
 

@@ -125,6 +125,22 @@ def test_argument_validation():
     assert bwd(cfg, wrow, ws_bytes=100) == moe.MOE_ERR_WORKSPACE
     assert bwd(cfg, wrow, ws=FAKE * 256 + 4) == moe.MOE_ERR_WORKSPACE
     assert moe.moe_expert_ffn_backward_workspace_bytes(_cfg(wdtype="fp8"), 16) == 0
+    # layer backward: the same dtype and layout rules; every forward array is required
+    def lbwd(c, w, logits=FAKE, dgw=FAKE, ws=FAKE * 256, ws_bytes=1 << 40):
+        return L.moe_backward(ctypes.byref(c), 4, FAKE, ctypes.byref(w), logits, FAKE, FAKE, FAKE,
+                              FAKE, FAKE, FAKE, FAKE, FAKE, dgw, FAKE, FAKE, FAKE, FAKE, ws,
+                              ws_bytes, None)
+    wg = moe.weights(gate_w=FAKE, w13=FAKE, w2=FAKE, ws13=FAKE, ws2=FAKE)
+    assert lbwd(_cfg(wdtype="fp8"), wg) == moe.MOE_ERR_UNSUPPORTED
+    assert lbwd(cfg, moe.weights(gate_w=FAKE, w13=FAKE, w2=FAKE, ws13=FAKE, ws2=FAKE,
+                                 packed=1)) == moe.MOE_ERR_UNSUPPORTED
+    assert lbwd(cfg, wrow) == moe.MOE_ERR_INVALID_ARG                    # no gate weight
+    assert lbwd(cfg, wg, logits=None) == moe.MOE_ERR_INVALID_ARG
+    assert lbwd(cfg, wg, dgw=None) == moe.MOE_ERR_INVALID_ARG
+    assert lbwd(cfg, wg, ws_bytes=100) == moe.MOE_ERR_WORKSPACE
+    assert moe.moe_backward_workspace_bytes(_cfg(wdtype="fp8"), 16) == 0
+    assert moe.moe_backward_workspace_bytes(cfg, 16) > moe.moe_expert_ffn_backward_workspace_bytes(
+        cfg, 16)
     assert moe.moe_expert_ffn_backward_workspace_bytes(cfg, 16) > 0
 
 
