@@ -312,10 +312,12 @@ def main():
                    "calls_per_s": round(nbu / (eb0.elapsed_time(eb1) * 1e-3), 1),
                    "bytes_per_launch": 12 * E, "bound": "launch latency (one workgroup)"}
 
-    # Backward of the expert FFNs for this batch's routing (training): output
-    # gradients of the routed rows and the shared expert -> input and weight
-    # gradients.  Not part of the layer step; reported beside it.
-    backward = None
+    # Backward (training), reported beside the layer step, on this batch's
+    # routing: the expert FFNs alone (output gradients of the routed rows and
+    # of the shared expert -> input and weight gradients), and the whole
+    # layer (the gradient of the layer output -> dx, the gate weight's and
+    # every expert weight's gradients).
+    backward = layer_backward = None
     if drow is not None:
         gen = torch.Generator(device=dev).manual_seed(23)
         dyb = torch.randn((T * K, H), generator=gen, device=dev).to(torch.bfloat16)
@@ -327,39 +329,57 @@ def main():
         dw2 = torch.empty((E, H, I), **bf)
         dws13 = torch.empty((2 * Is, H), **bf) if Is else None
         dws2 = torch.empty((H, Is), **bf) if Is else None
-        wsb = torch.empty(moe.moe_expert_ffn_backward_workspace_bytes(C, T), dtype=torch.uint8,
-                          device=dev)
         Wrow = sd.weights_struct(drow)
 
-        def bwd():
-            moe.moe_expert_ffn_backward(C, T, drow["x"], perm, offs, Wrow, dyb, dysb, dxb, dxsb,
-                                        dw13, dw2, dws13, dws2, wsb, stream=stream)
+        def timed(fn):
+            """(ms per call over 5 calls, per-kernel ms of one call)."""
+            fn()
+            torch.cuda.synchronize()
+            moe.moe_kernel_timer_read()
+            moe.moe_kernel_timer_enable(True)
+            fn()
+            torch.cuda.synchronize()
+            moe.moe_kernel_timer_enable(False)
+            kms = {k: round(v[0] / v[1], 4) for k, v in moe.moe_kernel_timer_read().items()}
+            eb0.record(stream)
+            for _ in range(5):
+                fn()
+            eb1.record(stream)
+            torch.cuda.synchronize()
+            return eb0.elapsed_time(eb1) / 5, kms
 
-        bwd()
-        torch.cuda.synchronize()
-        moe.moe_kernel_timer_read()
-        moe.moe_kernel_timer_enable(True)
-        bwd()
-        torch.cuda.synchronize()
-        moe.moe_kernel_timer_enable(False)
-        bk = {k: round(v[0] / v[1], 4) for k, v in moe.moe_kernel_timer_read().items()}
-        nb = 5
-        eb0.record(stream)
-        for _ in range(nb):
-            bwd()
-        eb1.record(stream)
-        torch.cuda.synchronize()
-        bms = eb0.elapsed_time(eb1) / nb
+        def figures(bms, flop, nbytes, kms):
+            return {"ms": round(bms, 3), "tflops": round(flop / (bms * 1e-3) / 1e12, 1),
+                    "mfma_frac": round(flop / (bms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                    "hbm_gbs": round(nbytes / (bms * 1e-3) / 1e9, 1),
+                    "hbm_frac": round(nbytes / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "algorithmic_flop": flop, "algorithmic_bytes": nbytes, "kernels_ms": kms}
+
         rows_i = T * K * I + T * Is
         bflop = 16.0 * rows_i * H     # recompute 4, dh 2, dx 4, dW2 2, dW13 4 (x rows*I*H)
         # weights read once and their gradients written once, x, dy, dx once
         bbytes = 2 * (active * 3 * H * I * 2 + 3 * H * Is * 2) + 3 * (T * K + T) * H * 2
-        backward = {"ms": round(bms, 3), "tflops": round(bflop / (bms * 1e-3) / 1e12, 1),
-                    "mfma_frac": round(bflop / (bms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-                    "hbm_gbs": round(bbytes / (bms * 1e-3) / 1e9, 1),
-                    "hbm_frac": round(bbytes / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                    "algorithmic_flop": bflop, "algorithmic_bytes": bbytes, "kernels_ms": bk}
-        del dyb, dysb, dxb, dxsb, dw13, dw2, dws13, dws2, wsb
+        wsb = torch.empty(moe.moe_expert_ffn_backward_workspace_bytes(C, T), dtype=torch.uint8,
+                          device=dev)
+        bms, bk = timed(lambda: moe.moe_expert_ffn_backward(
+            C, T, drow["x"], perm, offs, Wrow, dyb, dysb, dxb, dxsb, dw13, dw2, dws13, dws2, wsb,
+            stream=stream))
+        backward = figures(bms, bflop, bbytes, bk)
+        del wsb
+
+        # the layer: y (the routed expert outputs) from the phase timing above
+        dout = torch.randn((T, H), generator=gen, device=dev).to(torch.bfloat16)
+        dxl = torch.empty((T, H), **bf)
+        dgw = torch.empty((E, H), dtype=torch.float32, device=dev)
+        wsl = torch.empty(moe.moe_backward_workspace_bytes(C, T), dtype=torch.uint8, device=dev)
+        lms, lk = timed(lambda: moe.moe_backward(
+            C, T, drow["x"], Wrow, lg, idx, wt, perm, offs, pos, y, dout, dxl, dgw, dw13, dw2,
+            dws13, dws2, wsl, stream=stream))
+        # + the combine's dot products, the gate's weight gradient and dx: 6 T K H;
+        # + y and dout read, the gate weight read and its gradient written
+        layer_backward = figures(lms, bflop + 6.0 * T * K * H,
+                                 bbytes + (T * K + T) * H * 2 + 2 * E * H * 4, lk)
+        del dyb, dysb, dxb, dxsb, dw13, dw2, dws13, dws2, wsl, dout, dxl, dgw
 
     # Algorithmic work (routed rows only; active experts' weights only).
     wbytes = 1 if cfg.wdtype == "fp8" else (2 if cfg.wdtype == "bf16" else 4)
@@ -438,6 +458,7 @@ def main():
         "other_entry_point": other,
         "bias_update": bias_update,
         "expert_backward": backward,
+        "layer_backward": layer_backward,
         "roofline": roof,
     }
 

@@ -310,14 +310,22 @@ def routing_weights(cfg, lg: np.ndarray, idx: np.ndarray) -> np.ndarray:
     return s * cfg.rho
 
 
-def layer_backward(cfg, inp: dict, idx: np.ndarray, dout: np.ndarray) -> dict:
+def layer_backward(cfg, inp: dict, idx: np.ndarray, dout: np.ndarray, tokens=None,
+                   want=("dx", "dgate_w", "dw")) -> dict:
     """Exact fp64 gradients of L = sum_t <dout_t, out_t> for the layer with
     its routing held at idx (the top-k choice is piecewise constant in the
     inputs: the gradient reaches the gate only through the chosen experts'
     weights).  out_t = shared(x_t) + sum_k w_tk FFN_idx[t,k](x_t) with w from
     routing_weights; the bias only selects and gets no gradient.
-    Returns dx [T, H], dgate_w [E, H], dw13 [E, 2I, H], dw2 [E, H, I] and, with
-    a shared expert, dws13 [2Is, H], dws2 [H, Is]."""
+    Returns dx [T, H], dgate_w [E, H], and with "dw" wanted dw13 [E, 2I, H],
+    dw2 [E, H, I] and, with a shared expert, dws13 [2Is, H], dws2 [H, Is].
+    With tokens (indices into x, idx and dout), L sums over those tokens only:
+    dx holds their rows, and dgate_w[e] is exact for an expert e all of whose
+    tokens are listed."""
+    if tokens is not None:
+        tokens = np.asarray(tokens, np.int64)
+        inp = dict(inp, x=np.asarray(inp["x"])[tokens])
+        idx, dout = np.asarray(idx)[tokens], np.asarray(dout)[tokens]
     T, H, E, K, I = inp["x"].shape[0], cfg.H, cfg.E, cfg.K, cfg.I
     x = np.asarray(inp["x"])
     xf = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64) if x.dtype == np.uint16 \
@@ -337,19 +345,26 @@ def layer_backward(cfg, inp: dict, idx: np.ndarray, dout: np.ndarray) -> dict:
     else:
         ds = cfg.rho * dw
     dlg = ds * s * (1.0 - s)                                                 # d logit of the chosen
-    out = {"dgate_w": np.zeros((E, H)), "dw13": np.zeros((E, 2 * I, H)), "dw2": np.zeros((E, H, I))}
+    wdw = "dw" in want
+    parts = ("dx", "dw13", "dw2") if wdw else ("dx",)
+    out = {"dgate_w": np.zeros((E, H))}
+    if wdw:
+        out["dw13"], out["dw2"] = np.zeros((E, 2 * I, H)), np.zeros((E, H, I))
     np.add.at(out["dgate_w"], idx.ravel(), dlg.ravel()[:, None] * xf[tok])
     dx = np.einsum("tk,tkh->th", dlg, gw[idx])
-    for e in range(E):
+    if "dx" not in want and not wdw:
+        return out
+    for e in np.unique(idx):
         rows = np.flatnonzero(idx.ravel() == e)
-        if len(rows) == 0:
-            continue
-        b = ffn_backward(cfg, inp, e, tok[rows], w.ravel()[rows, None] * dout[tok[rows]])
-        out["dw13"][e], out["dw2"][e] = b["dw13"], b["dw2"]
+        b = ffn_backward(cfg, inp, int(e), tok[rows], w.ravel()[rows, None] * dout[tok[rows]],
+                         want=parts)
+        if wdw:
+            out["dw13"][e], out["dw2"][e] = b["dw13"], b["dw2"]
         np.add.at(dx, tok[rows], b["dx"])
     if cfg.Is:
-        b = ffn_backward(cfg, inp, -1, np.arange(T), dout)
-        out["dws13"], out["dws2"] = b["dw13"], b["dw2"]
+        b = ffn_backward(cfg, inp, -1, np.arange(T), dout, want=parts)
+        if wdw:
+            out["dws13"], out["dws2"] = b["dw13"], b["dw2"]
         dx += b["dx"]
     out["dx"] = dx
     return out

@@ -218,3 +218,82 @@ def test_expert_backward_v3_bf16_T4096_sampled():
         log(f"  expert {e} ({len(tok)} rows): dW13 relL2 {e13:.3e}, dW2 relL2 {e2:.3e}")
         assert e13 <= 2e-2 and e2 <= 2e-2, e
     log(f"  oracle {time.time() - t0:.1f}s; experts without rows: {len(empty)}")
+
+
+def test_layer_backward_v3_bf16_T4096_sampled():
+    """Backward of the whole layer at the full V3 shape, on the routing the
+    forward chose for 4096 tokens (the benchmark's configuration): sampled dx
+    rows, the gate weight's gradient row of the expert with the fewest rows,
+    and sampled weight-gradient entries of one routed expert and of the
+    shared expert, each within 2e-2 relative L2 of the fp64 oracle."""
+    cfg = synth.C3
+    inp, dev = _inputs(cfg)
+    row = dict(dev, **_Weights.row["bf16"])
+    row.pop("packed", None)
+    T, H, E, K, I, Is = cfg.T, cfg.H, cfg.E, cfg.K, cfg.I, cfg.Is
+    N = T * K
+    C = sd.moe_config(cfg)
+    log(f"{cfg.name}: backward of the layer")
+    ws = sd.workspace(cfg, T)
+    f32, i32 = dict(dtype=torch.float32, device=DEV), dict(dtype=torch.int32, device=DEV)
+    bf = dict(dtype=torch.bfloat16, device=DEV)
+    lg, idx, w = torch.empty((T, E), **f32), torch.empty((T, K), **i32), torch.empty((T, K), **f32)
+    counts, offsets = torch.empty(E, **i32), torch.empty(E + 1, **i32)
+    perm, pos = torch.empty(N, **i32), torch.empty(N, **i32)
+    y, ys = torch.empty((N, H), **bf), torch.empty((T, H), **bf)
+    moe.moe_gate(C, T, dev["x"], dev["gate_w"], dev["bias"], lg, idx, w, ws)
+    moe.moe_permute(C, T, idx, counts, offsets, perm, pos, ws)
+    moe.moe_expert_ffn(C, T, dev["x"], perm, offsets, sd.weights_struct(dev), y, ys, ws)
+    rng = np.random.default_rng(37)
+    dout_b = torch.from_numpy(rng.standard_normal((T, H), dtype=np.float32)).to(torch.bfloat16)
+    dout_np = dout_b.float().numpy()
+    dx, dgw = torch.empty((T, H), **bf), torch.empty((E, H), **f32)
+    dw13, dw2 = torch.empty((E, 2 * I, H), **bf), torch.empty((E, H, I), **bf)
+    dws13, dws2 = torch.empty((2 * Is, H), **bf), torch.empty((H, Is), **bf)
+    wsb = torch.empty(moe.moe_backward_workspace_bytes(C, T), dtype=torch.uint8, device=DEV)
+    moe.moe_backward(C, T, row["x"], sd.weights_struct(row), lg, idx, w, perm, offsets, pos, y,
+                     dout_b.to(DEV), dx, dgw, dw13, dw2, dws13, dws2, wsb)
+    sync()
+    for name, a in (("dx", dx), ("dgate_w", dgw), ("dW13", dw13), ("dW2", dw2),
+                    ("dW13_shared", dws13), ("dW2_shared", dws2)):
+        assert bool(torch.isfinite(a).all()), name
+    idx_h, w_h, cnt, offs_h, perm_h = host(idx), host(w), host(counts), host(offsets), host(perm)
+
+    t0 = time.time()
+    toks = _samples(T, 8, 57)
+    ref = oracle.layer_backward(cfg, inp, idx_h, dout_np, tokens=toks, want=("dx",))["dx"]
+    g = host(dx[torch.from_numpy(toks).to(DEV)])
+    worst = max(rel_l2(g[j], ref[j]) for j in range(len(toks)))
+    log(f"  dx: {len(toks)} tokens, worst row relL2 {worst:.3e}")
+    assert worst <= 2e-2
+
+    busy = np.flatnonzero(cnt > 0)
+    e = int(busy[np.argmin(cnt[busy])])
+    etoks = np.flatnonzero((idx_h == e).any(axis=1))
+    ref = oracle.layer_backward(cfg, inp, idx_h, dout_np, tokens=etoks, want=("dgate_w",))
+    r = rel_l2(host(dgw[e]), ref["dgate_w"][e])
+    log(f"  dgate_w row of expert {e} ({len(etoks)} tokens): relL2 {r:.3e}")
+    assert r <= 2e-2
+
+    # weight gradients: the routed rows' output gradients are w * dout
+    nq = 48
+    for ex in (e, -1):
+        ne = Is if ex < 0 else I
+        q = synth.words(4 * nq, 61 + ex, synth.T_TEST, 58).astype(np.int64)
+        which = np.repeat([0, 1], nq)
+        rr = np.concatenate([q[:nq] % (2 * ne), q[nq:2 * nq] % H])
+        cc = np.concatenate([q[2 * nq:3 * nq] % H, q[3 * nq:] % ne])
+        if ex < 0:
+            tok, dyr = np.arange(T), dout_np
+            g13, g2 = host(dws13), host(dws2)
+        else:
+            f = perm_h[offs_h[ex]:offs_h[ex + 1]]
+            tok = f // K
+            dyr = w_h.ravel()[f][:, None] * dout_np[tok]
+            g13, g2 = host(dw13[ex]), host(dw2[ex])
+        ref = oracle.ffn_backward_entries(cfg, inp, ex, tok, dyr, which, rr, cc)
+        got = np.concatenate([g13[rr[:nq], cc[:nq]], g2[rr[nq:], cc[nq:]]])
+        e13, e2 = rel_l2(got[:nq], ref[:nq]), rel_l2(got[nq:], ref[nq:])
+        log(f"  expert {ex} ({len(tok)} rows): dW13 relL2 {e13:.3e}, dW2 relL2 {e2:.3e}")
+        assert e13 <= 2e-2 and e2 <= 2e-2, ex
+    log(f"  oracle {time.time() - t0:.1f}s")

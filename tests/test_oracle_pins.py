@@ -699,3 +699,20 @@ def test_layer_backward_gate_gradient_zero_when_weights_cannot_move():
     b = oracle.layer_backward(cfg, inp, idx, dout)
     np.testing.assert_allclose(b["dgate_w"], 0.0, atol=1e-12)
     assert np.abs(b["dw2"]).max() > 1e-3
+
+
+def test_layer_backward_token_subsets_agree_with_the_whole():
+    # dx rows depend on their own token only; an expert's gate gradient on
+    # the tokens routed to it only
+    cfg = LB_CFGS[0]
+    inp = synth.gen_inputs(cfg)
+    lg = oracle.logits(inp["x"], cfg.act, inp["gate_w"])
+    idx, _, _ = oracle.route_f64(cfg, lg, inp["bias"])
+    dout = np.random.default_rng(23).standard_normal((cfg.T, cfg.H))
+    full = oracle.layer_backward(cfg, inp, idx, dout)
+    sub = oracle.layer_backward(cfg, inp, idx, dout, tokens=[4, 1], want=("dx",))
+    np.testing.assert_allclose(sub["dx"], full["dx"][[4, 1]], rtol=1e-12, atol=1e-14)
+    e = int(idx[0, 0])
+    toks = np.flatnonzero((idx == e).any(axis=1))
+    sub = oracle.layer_backward(cfg, inp, idx, dout, tokens=toks, want=("dgate_w",))
+    np.testing.assert_allclose(sub["dgate_w"][e], full["dgate_w"][e], rtol=1e-12, atol=1e-14)
