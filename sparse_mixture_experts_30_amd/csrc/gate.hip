@@ -246,14 +246,19 @@ select_kernel(const float* __restrict__ part, int ksplit, const float* __restric
   const int s_end = SW == 1 ? ksplit : (int)((int64_t)ksplit * (wave + 1) / SW);
 
   // Logits: the k-split partial sums of [s_begin, s_end) added in split
-  // order.  The loads of a batch of eight splits (for all of this lane's
-  // experts) are issued together and then added in order, so a deep split
-  // costs few memory round trips.
-  float lgs[SEL_MAXV] = {};
+  // order.  The loads of a batch of splits (for all of this lane's experts)
+  // are issued together and then added in order, so a deep split costs few
+  // memory round trips.
+  float lgs[SEL_MAXV];
   {
-    constexpr int SB = 8;    // splits per batch
+    constexpr int SB = 4;    // splits per batch
     const int64_t stride = T * E;
-    for (int s0 = s_begin; s0 < s_end; s0 += SB) {
+#pragma unroll
+    for (int v = 0; v < SEL_MAXV; ++v) {
+      const int e = lane + 64 * v;
+      lgs[v] = (v < V && e < E) ? part[(int64_t)s_begin * stride + t * E + e] : 0.0f;
+    }
+    for (int s0 = s_begin + 1; s0 < s_end; s0 += SB) {
       float pv[SB][SEL_MAXV];
 #pragma unroll
       for (int j = 0; j < SB; ++j)
@@ -266,10 +271,8 @@ select_kernel(const float* __restrict__ part, int ksplit, const float* __restric
 #pragma unroll
       for (int j = 0; j < SB; ++j)
 #pragma unroll
-        for (int v = 0; v < SEL_MAXV; ++v) {
-          if (s0 + j == s_begin) lgs[v] = pv[j][v];          // the first split starts the sum
-          else if (s0 + j < s_end) lgs[v] += pv[j][v];
-        }
+        for (int v = 0; v < SEL_MAXV; ++v)
+          if (s0 + j < s_end) lgs[v] += pv[j][v];
     }
   }
   if (SW > 1) {

@@ -56,24 +56,16 @@ __device__ __forceinline__ void select_token(const float (&lgs)[SEL_MAXV], int l
   __syncwarp();
 
   // Group score: sum of the two largest choice scores of group `lane`.
-  // The scores are read eight at a time (independent LDS loads) and taken
-  // in index order.
   float g = -INFINITY;
   if (lane < G) {
     float m1 = -INFINITY, m2 = -INFINITY;
-    for (int j0 = 0; j0 < Eg; j0 += 8) {
-      float v8[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v8[j] = (j0 + j < Eg) ? s_c[lane * Eg + j0 + j] : -INFINITY;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float v = v8[j];
-        if (v > m1) {
-          m2 = m1;
-          m1 = v;
-        } else if (v > m2) {
-          m2 = v;
-        }
+    for (int j = 0; j < Eg; ++j) {
+      const float v = s_c[lane * Eg + j];
+      if (v > m1) {
+        m2 = m1;
+        m1 = v;
+      } else if (v > m2) {
+        m2 = v;
       }
     }
     g = m1 + m2;
