@@ -199,3 +199,40 @@ def test_forward_overlap_graph_replay():
         fwd()
         sync()
         assert torch.equal(out, ref)
+
+
+def test_decode_forward_graph_replay():
+    """The decode schedule (T = 32) captured into a HIP graph replays
+    bit-identically to eager moe_forward, with eager calls between replays."""
+    cfg = DECODE_CASES[0]
+    _, dev = inputs(cfg)
+    dev = sd.packed_copy(dev)
+    T = cfg.T
+    C = sd.moe_config(cfg)
+    W = sd.weights_struct(dev)
+    ws = sd.workspace(cfg, T)
+    out = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=DEV)
+    idx = torch.empty((T, cfg.K), dtype=torch.int32, device=DEV)
+
+    def fwd():
+        moe.moe_forward(C, T, dev["x"], W, out, ws, topk_idx=idx,
+                        stream=torch.cuda.current_stream())
+
+    fwd()
+    sync()
+    ref, ref_idx = out.clone(), idx.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fwd()
+    sync()
+    for rep in range(4):
+        out.fill_(0)
+        idx.fill_(-1)
+        sync()
+        g.replay()
+        sync()
+        assert torch.equal(out, ref), f"replay {rep}"
+        assert torch.equal(idx, ref_idx), f"replay {rep}"
+        fwd()
+        sync()
+        assert torch.equal(out, ref)
