@@ -15,6 +15,7 @@
 // per call by a small kernel that also lays the three parts out in MFMA
 // fragment order; the GEMM then streams them straight into registers.
 #include "moe_internal.hpp"
+#include "gate_split.hpp"
 #include "select_device.hpp"
 
 #include <float.h>
@@ -28,28 +29,6 @@ constexpr int GEB = 4;     // 32-expert blocks per tile (one per wave)
 constexpr int GBK = 64;    // k per step
 constexpr int GTHREADS = 256;
 constexpr int GFRAG = 3 * 4 * 64;   // 16-byte fragments per (expert block, step)
-
-// Split 8 fp32 weights into hi/mid/lo bf16x8 operands (exact decomposition).
-__device__ __forceinline__ void split3(u32x4 p, u32x4 q, u32x4& h, u32x4& m, u32x4& l) {
-  const uint32_t v[8] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    uint32_t hb[2], mb[2], lb[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const uint32_t b = v[2 * j + u];
-      const float r1 = __uint_as_float(b) - __uint_as_float(b & 0xFFFF0000u);  // exact
-      const uint32_t b1 = __float_as_uint(r1);
-      const float r2 = r1 - __uint_as_float(b1 & 0xFFFF0000u);  // exact, <= 8 bits
-      hb[u] = b >> 16;
-      mb[u] = b1 >> 16;
-      lb[u] = __float_as_uint(r2) >> 16;
-    }
-    h[j] = hb[0] | (hb[1] << 16);
-    m[j] = mb[0] | (mb[1] << 16);
-    l[j] = lb[0] | (lb[1] << 16);
-  }
-}
 
 // wp block (eb, step) = [part 3][k slice 4][lane 64] x 16 bytes: lane l of
 // slice kk holds expert 32 eb + l%32 (zero past E) at k = 64 step +

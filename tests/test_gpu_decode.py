@@ -1,6 +1,7 @@
 """GPU parity of the decode schedule of moe_forward (1 <= T <= 32: the gate
-as fp32 dot products over a few k ranges, the selection, then one workgroup
-that permutes and lays out the tile list) and of moe_forward_overlap (the shared expert on a second
+over a few k ranges (bf16 MFMA on the exact split of the fp32 weight, or fp32
+dot products for fp32 activations), the selection, then one workgroup that
+permutes and lays out the tile list) and of moe_forward_overlap (the shared expert on a second
 stream), against the fp64 oracle and against moe_forward itself."""
 import numpy as np
 import pytest
@@ -78,12 +79,13 @@ def test_decode_schedule_launches():
     cfg = DECODE_CASES[0]
     inp, dev = inputs(cfg)
     dev = sd.packed_copy(dev)
-    for T, want, absent in ((32, ("gate_decode_kernel", "select_kernel", "route_decode_kernel"),
+    for T, want, absent in ((32, ("gate_decode_mfma_kernel", "select_kernel",
+                                  "route_decode_kernel"),
                              ("gate_split_kernel", "gate_logits_bf16_kernel",
                               "permute_small_kernel", "build_tiles_kernel")),
                             (33, ("gate_logits_bf16_kernel", "select_kernel",
                                   "permute_small_kernel", "build_tiles_kernel"),
-                             ("gate_decode_kernel", "route_decode_kernel"))):
+                             ("gate_decode_mfma_kernel", "route_decode_kernel"))):
         x = sd.tensor(np.ascontiguousarray(np.resize(inp["x"], (T, cfg.H))))
         moe.moe_kernel_timer_read()
         moe.moe_kernel_timer_enable(True)
