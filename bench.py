@@ -42,7 +42,7 @@ KERNEL_SOURCES = {
     "grouped_gemm_fp8_packed": ("ffn_fp8_packed.hip", "moe_internal.hpp"),
     "grouped_gemm_bf16": ("ffn_bf16.hip", "moe_internal.hpp"),
     "grouped_gemm_fp8": ("ffn_fp8.hip", "moe_internal.hpp"),
-    "gate_logits_bf16_kernel": ("gate.hip", "moe_internal.hpp"),
+    "gate_logits_bf16_kernel": ("gate.hip", "gate_split.hpp", "moe_internal.hpp"),
 }
 
 

@@ -428,11 +428,17 @@ __global__ void __launch_bounds__(NT, 1) grouped_gemm_bf16_packed_wide(PackedArg
 // with one wave per workgroup the few active tiles of a small batch spread
 // over all CUs instead of queueing behind each other.
 constexpr int kFewSlots = 4;   // waves (packed wave slots) per tile
+// Wave slots of the GPU at four waves per SIMD (256 CUs x 4 SIMDs x 4).
+constexpr int64_t kFewDenseSlots = 4096;
 
-template <bool kGateUp, int NRB>
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+// WPE = 2: two waves per SIMD with three steps in flight for single-block
+// tiles.  WPE = 4 (the down projection of a batch whose waves all fit in
+// one round at four per SIMD): two steps in flight, so that every wave is
+// resident at once instead of a few running in a second round.
+template <bool kGateUp, int NRB, int WPE = 2>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(WPE)))
 grouped_gemm_bf16_packed_few(PackedArgs p) {
-  constexpr int D = NRB == 1 ? 3 : 2;   // steps of weights + activations in flight
+  constexpr int D = (NRB == 1 && WPE == 2) ? 3 : 2;   // steps of weights + activations in flight
   const int64_t work = (int64_t)p.tiles[0] * p.ntn * kFewSlots;
   const int64_t per = (work + kNumXcd - 1) / kNumXcd;
   const int64_t q = blockIdx.x / kNumXcd;
@@ -649,7 +655,11 @@ hipError_t launch_ffn_bf16_packed(const FfnDims& d, const uint16_t* x, const int
   a2.c_r = y;
   a2.c_s = ys;
   a2.ldc_r = a2.ldc_s = d.H;
-  if (few == 1)
+  if (few == 1 && mt * a2.ntn * kFewSlots <= kFewDenseSlots)
+    MOE_TIMED_LAUNCH(s, "grouped_gemm_bf16_packed_few<false, 1, 4>",
+      hipLaunchKernelGGL((grouped_gemm_bf16_packed_few<false, 1, 4>),
+                         dim3(grid(mt * a2.ntn * kFewSlots)), dim3(64), 0, s, a2));
+  else if (few == 1)
     MOE_TIMED_LAUNCH(s, "grouped_gemm_bf16_packed_few<false, 1>",
       hipLaunchKernelGGL((grouped_gemm_bf16_packed_few<false, 1>),
                          dim3(grid(mt * a2.ntn * kFewSlots)), dim3(64), 0, s, a2));

@@ -10,6 +10,8 @@
 // possible count and surplus workgroups exit.
 #include "moe_internal.hpp"
 
+#include <algorithm>
+
 namespace moe {
 
 namespace {
@@ -64,8 +66,11 @@ hipError_t launch_build_tiles(const int32_t* offsets, int E, int64_t T, bool has
 }
 
 int64_t ffn_grid_mtiles(const FfnDims& d, int BM) {
+  // At most min(E, N) routed groups have rows, each with at most one
+  // partial tile.
   const bool routed = d.groups & kGroupRouted, shared = (d.groups & kGroupShared) && d.Is > 0;
-  return (routed ? (d.N + BM - 1) / BM + d.E : 0) + (shared ? (d.T + BM - 1) / BM : 0);
+  return (routed ? (d.N + BM - 1) / BM + std::min<int64_t>(d.E, d.N) : 0) +
+         (shared ? (d.T + BM - 1) / BM : 0);
 }
 
 hipError_t ffn_build_tiles(const FfnDims& d, const int32_t* offsets, int BM, int32_t* tiles,
