@@ -170,11 +170,13 @@ moe_status moe_combine(const moe_config* cfg, int64_t T, const void* y, const vo
  * counts [E] and perm [T*K] are optional copies of the intermediate results
  * (NULL: kept in the workspace only).
  * Decode batches (1 <= T <= 32) take a shorter schedule of the same steps:
- * the gate as fp32 dot products straight from the fp32 gate weight over a
- * few k ranges, the same selection kernel, then one workgroup that permutes
- * and lays out the GEMM tiles.  The logits then differ from moe_gate's in
- * rounding only (both are fp32 accumulations of the exact products); the
- * choice is made from the logits written. */
+ * the gate straight from the fp32 gate weight over a few k ranges (bf16
+ * activations: bf16 MFMA over the weight's exact bf16 split, made in
+ * registers; fp32 activations: fp32 dot products), the same selection
+ * kernel, then one workgroup that permutes and lays out the GEMM tiles.  The
+ * logits then differ from moe_gate's in rounding only (both are fp32
+ * accumulations of the exact products); the choice is made from the logits
+ * written. */
 moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const moe_weights* w,
                        void* out, float* logits, int32_t* topk_idx, float* topk_w,
                        int32_t* counts, int32_t* perm, void* ws, size_t ws_bytes, void* stream);
