@@ -40,14 +40,24 @@ combine_bf16_kernel(const uint16_t* __restrict__ y, const uint16_t* __restrict__
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
     }
-    for (int k = 0; k < K; ++k) {
-      const uint4 v = *reinterpret_cast<const uint4*>(y + (int64_t)sp[k] * H + c);
-      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-      const float wk = sw[k];
+    // The rows of up to kBatch experts are loaded together, then added in
+    // k order (one memory round trip per batch instead of one per expert).
+    constexpr int kBatch = 8;
+    for (int k0 = 0; k0 < K; k0 += kBatch) {
+      uint4 v[kBatch];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc[2 * j] = fmaf(wk, bf16_bits_to_f32(u[j] & 0xFFFFu), acc[2 * j]);
-        acc[2 * j + 1] = fmaf(wk, bf16_bits_to_f32(u[j] >> 16), acc[2 * j + 1]);
+      for (int b = 0; b < kBatch; ++b)
+        if (k0 + b < K) v[b] = *reinterpret_cast<const uint4*>(y + (int64_t)sp[k0 + b] * H + c);
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        if (k0 + b >= K) break;
+        const uint32_t u[4] = {v[b].x, v[b].y, v[b].z, v[b].w};
+        const float wk = sw[k0 + b];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[2 * j] = fmaf(wk, bf16_bits_to_f32(u[j] & 0xFFFFu), acc[2 * j]);
+          acc[2 * j + 1] = fmaf(wk, bf16_bits_to_f32(u[j] >> 16), acc[2 * j + 1]);
+        }
       }
     }
     uint4 o;
