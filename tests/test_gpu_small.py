@@ -257,6 +257,12 @@ EDGE_CASES = [
                      I=128, Is=0, rho=1.5),
     synth.C3.replace(name="bf16-T80-H256-E16-G8-TG3-K6-all", T=80, H=256, E=16, G=8, TG=3, K=6,
                      I=128, Is=128, rho=1.5),
+    # fewer routed rows than experts (the GEMM grids are sized for at most
+    # min(E, T * K) non-empty groups): two-block decode tiles, and 256-row tiles
+    synth.C3.replace(name="bf16-T40-H256-E256-K1", T=40, H=256, E=256, G=8, TG=4, K=1, I=128,
+                     Is=128, rho=2.5),
+    synth.C3.replace(name="bf16-T100-H256-E512-G16-TG4-K2", T=100, H=256, E=512, G=16, TG=4,
+                     K=2, I=128, Is=128, rho=2.5),
 ]
 
 
