@@ -64,8 +64,9 @@ __device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
 constexpr int DG_MAXK = 896;   // k range per workgroup (bounds its LDS)
 
 // part[ks][t][e] = sum over k in [ks * kchunk, min(H, (ks + 1) * kchunk)) of
-// x[t][k] * wg[e][k] (fp32 activations).  Thread (el, t): el = tid / 32 picks the expert of the
-// workgroup's eight, t = tid % 32 the token.  kchunk and H are multiples of 8.
+// x[t][k] * wg[e][k] (fp32 activations).  Thread (el, t): el = tid / 32
+// picks the expert of the workgroup's eight, t = tid % 32 the token.  kchunk
+// and H are multiples of 8.
 // LDS: the token rows (row stride kchunk / XV + 1 chunks of 16 bytes, so
 // that the 32 rows read at one k fall in different banks), then the 8 gate
 // rows.
