@@ -5,7 +5,8 @@
 //   out[t] = y_shared[t] + sum_k w[t,k] * y[pos[t*K + k]]
 // fp32 accumulation in k order; one rounding to the output type.  One
 // workgroup per token, 16-byte coalesced loads of whole rows (an HBM-bound
-// gather-add).
+// gather-add).  A position outside [0, T*K) (only a caller-made pos can hold
+// one) contributes nothing.
 #include "moe_internal.hpp"
 
 namespace moe {
@@ -17,12 +18,13 @@ constexpr int CT = 256;
 __global__ void __launch_bounds__(CT)
 combine_bf16_kernel(const uint16_t* __restrict__ y, const uint16_t* __restrict__ ys,
                     const int32_t* __restrict__ pos, const float* __restrict__ w,
-                    uint16_t* __restrict__ out, int H, int K) {
+                    uint16_t* __restrict__ out, int H, int K, int64_t N) {
   const int64_t t = blockIdx.x;
   __shared__ int32_t sp[64];
   __shared__ float sw[64];
   if (threadIdx.x < K) {
-    sp[threadIdx.x] = pos[t * K + threadIdx.x];
+    const int32_t p = pos[t * K + threadIdx.x];
+    sp[threadIdx.x] = (p >= 0 && p < N) ? p : -1;
     sw[threadIdx.x] = w[t * K + threadIdx.x];
   }
   __syncthreads();
@@ -46,11 +48,15 @@ combine_bf16_kernel(const uint16_t* __restrict__ y, const uint16_t* __restrict__
     for (int k0 = 0; k0 < K; k0 += kBatch) {
       uint4 v[kBatch];
 #pragma unroll
-      for (int b = 0; b < kBatch; ++b)
-        if (k0 + b < K) v[b] = *reinterpret_cast<const uint4*>(y + (int64_t)sp[k0 + b] * H + c);
+      for (int b = 0; b < kBatch; ++b) {
+        v[b] = make_uint4(0u, 0u, 0u, 0u);
+        if (k0 + b < K && sp[k0 + b] >= 0)
+          v[b] = *reinterpret_cast<const uint4*>(y + (int64_t)sp[k0 + b] * H + c);
+      }
 #pragma unroll
       for (int b = 0; b < kBatch; ++b) {
         if (k0 + b >= K) break;
+        if (sp[k0 + b] < 0) continue;
         const uint32_t u[4] = {v[b].x, v[b].y, v[b].z, v[b].w};
         const float wk = sw[k0 + b];
 #pragma unroll
@@ -72,12 +78,14 @@ combine_bf16_kernel(const uint16_t* __restrict__ y, const uint16_t* __restrict__
 __global__ void __launch_bounds__(CT)
 combine_f32_kernel(const float* __restrict__ y, const float* __restrict__ ys,
                    const int32_t* __restrict__ pos, const float* __restrict__ w,
-                   float* __restrict__ out, int H, int K) {
+                   float* __restrict__ out, int H, int K, int64_t N) {
   const int64_t t = blockIdx.x;
   for (int c = threadIdx.x; c < H; c += CT) {
     float acc = ys ? ys[t * H + c] : 0.0f;
-    for (int k = 0; k < K; ++k)
-      acc = fmaf(w[t * K + k], y[(int64_t)pos[t * K + k] * H + c], acc);
+    for (int k = 0; k < K; ++k) {
+      const int32_t p = pos[t * K + k];
+      if (p >= 0 && p < N) acc = fmaf(w[t * K + k], y[(int64_t)p * H + c], acc);
+    }
     out[t * H + c] = acc;
   }
 }
@@ -89,11 +97,12 @@ hipError_t launch_combine(const void* y, const void* ys, const int32_t* pos, con
   if (bf16)
     MOE_TIMED_LAUNCH(s, "combine_bf16_kernel",
       hipLaunchKernelGGL(combine_bf16_kernel, dim3((unsigned)T), dim3(CT), 0, s,
-                         (const uint16_t*)y, (const uint16_t*)ys, pos, w, (uint16_t*)out, H, K));
+                         (const uint16_t*)y, (const uint16_t*)ys, pos, w, (uint16_t*)out, H, K,
+                         T * K));
   else
     MOE_TIMED_LAUNCH(s, "combine_f32_kernel",
       hipLaunchKernelGGL(combine_f32_kernel, dim3((unsigned)T), dim3(CT), 0, s, (const float*)y,
-                         (const float*)ys, pos, w, (float*)out, H, K));
+                         (const float*)ys, pos, w, (float*)out, H, K, T * K));
   return hipGetLastError();
 }
 

@@ -584,10 +584,13 @@ hipError_t launch_ffn_bf16_packed(const FfnDims& d, const uint16_t* x, const int
                                   int32_t* tiles, uint16_t* y, uint16_t* ys, hipStream_t s) {
   hipError_t e = set_attrs_packed();
   if (e != hipSuccess) return e;
-  // Every group has at most T rows (a token picks an expert at most once).
+  // Small batches take the few-row kernels, which compute 32 * few rows per
+  // tile; their tile list is cut at that height, so a group with more rows
+  // than T (a caller's routing that names one expert twice for a token) is
+  // still covered whole.
   const int few = d.T <= 32 ? 1 : d.T <= 64 ? 2 : 0;
   const bool wide = !few && d.N >= (int64_t)kWideMinRows * d.E;
-  const int bm1 = wide ? BMW : BM;
+  const int bm1 = few ? 32 * few : wide ? BMW : BM;
   e = ffn_build_tiles(d, offsets, bm1, tiles, s);
   if (e != hipSuccess) return e;
   const int64_t mt = ffn_grid_mtiles(d, bm1);

@@ -110,6 +110,8 @@ hipError_t launch_permute(const int32_t* idx, int64_t N, int E, int32_t* hist, i
 // Expert FFN tile schedule (see ffn_sched.hip for the entry format).  The
 // smallest M-tile height any GEMM uses sizes the list in the workspace.
 constexpr int kMinTileRows = 128;
+// Tile height of the few-row kernels of batches of at most 64 tokens.
+inline int ffn_list_tile_rows(int64_t T) { return T <= 32 ? 32 : T <= 64 ? 64 : kMinTileRows; }
 // Groups of an expert-FFN launch: the routed experts, the shared expert.
 constexpr int kGroupRouted = 1, kGroupShared = 2, kGroupsAll = 3;
 int64_t ffn_max_mtiles(int64_t N, int64_t T, int E, int BM);

@@ -49,6 +49,9 @@ __device__ __forceinline__ void select_token(const float (&lgs)[SEL_MAXV], int l
       const double sd = 1.0 / (1.0 + exp(-(double)lg));
       s32[v] = (float)sd;
       c[v] = s32[v] + bias[e];
+      // A NaN choice (NaN in x or the bias) competes as -inf, so every
+      // comparison below is a total order and every pick is a valid id.
+      if (c[v] != c[v]) c[v] = -INFINITY;
       s_c[e] = c[v];
       s_s[e] = s32[v];
     }
@@ -69,6 +72,7 @@ __device__ __forceinline__ void select_token(const float (&lgs)[SEL_MAXV], int l
       }
     }
     g = m1 + m2;
+    if (g != g) g = -INFINITY;   // -inf + inf
   }
   // Keep the TG best groups.
   uint64_t keep = 0;
@@ -85,7 +89,8 @@ __device__ __forceinline__ void select_token(const float (&lgs)[SEL_MAXV], int l
     const int e = lane + 64 * v;
     if (v < V && e < E && !((keep >> (e / Eg)) & 1ull)) c[v] = 0.0f;
   }
-  // Top K, descending, ties to the lower expert id.
+  // Top K, descending, ties to the lower expert id.  A lane offers its best
+  // untaken expert even at -inf, so K <= E valid ids always exist.
   float my_s = 0.0f;
   int my_e = 0;
   uint32_t taken = 0;
@@ -95,7 +100,7 @@ __device__ __forceinline__ void select_token(const float (&lgs)[SEL_MAXV], int l
 #pragma unroll
     for (int v = 0; v < SEL_MAXV; ++v) {
       const int e = lane + 64 * v;
-      if (v < V && e < E && !((taken >> v) & 1u) && c[v] > bv) {
+      if (v < V && e < E && !((taken >> v) & 1u) && (c[v] > bv || bi == 0x7fffffff)) {
         bv = c[v];
         bi = e;
       }

@@ -24,6 +24,21 @@ def rel_l2(a, b):
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
 
 
+# fp8 layer against the oracle that also quantises x and h per 1x128 tile
+# (the kernels' own data path): the remaining error is accumulation order in
+# fp32 and the bf16 rounding of y and out, a few 1e-3; a mis-scaled tile
+# (a wrong activation or weight scale) moves a token by far more.
+FP8_QUANT_TOL = 1e-2
+
+
+def worst_row_rel(a, b):
+    """Largest per-row relative L2 error of a against b ([n, H])."""
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float((np.linalg.norm(a - b, axis=1) /
+                  np.maximum(np.linalg.norm(b, axis=1), 1e-300)).max())
+
+
 def host(t) -> np.ndarray:
     """Device tensor -> numpy (bf16 widened exactly to float32)."""
     if t.dtype == torch.bfloat16:

@@ -14,8 +14,8 @@ import synth
 import sparse_mixture_experts_30_amd as moe
 from synth import device as sd
 
-from gpu_util import (DEV, check_routing, host, layer_reference, log, rel_l2, run_forward,
-                      run_gate, run_permute, sync)
+from gpu_util import (DEV, FP8_QUANT_TOL, check_routing, host, layer_reference, log, rel_l2,
+                      run_forward, run_gate, run_permute, sync, worst_row_rel)
 
 pytestmark = pytest.mark.gpu
 
@@ -85,7 +85,7 @@ def test_gate_permute_v3_T16384():
     assert counts.sum() == cfg.T * cfg.K
 
 
-def _full_layer(cfg, n_samples=None, quant_diag=False):
+def _full_layer(cfg, n_samples=None):
     inp, dev = _inputs(cfg)
     T = cfg.T
     log(f"{cfg.name}: forward")
@@ -101,18 +101,33 @@ def _full_layer(cfg, n_samples=None, quant_diag=False):
     t0 = time.time()
     ref, nalt = layer_reference(cfg, inp, r["idx"][toks], toks)
     rel = rel_l2(r["out"][toks], ref)
+    worst = worst_row_rel(r["out"][toks], ref)
     tol = 6e-2 if cfg.wdtype == "fp8" else 2e-2
-    log(f"  out relL2={rel:.3e} on {len(toks)} tokens (tol {tol}), near-tie tokens={nalt}, "
-        f"active experts={int((r['counts'] > 0).sum())}, oracle {time.time() - t0:.1f}s")
-    assert rel <= tol
-    if quant_diag:
+    log(f"  out relL2={rel:.3e} worst token={worst:.3e} on {len(toks)} tokens (tol {tol}), "
+        f"near-tie tokens={nalt}, active experts={int((r['counts'] > 0).sum())}, "
+        f"oracle {time.time() - t0:.1f}s")
+    assert rel <= tol and worst <= 3 * tol
+    if cfg.wdtype == "fp8":
         ref2, _ = layer_reference(cfg, inp, r["idx"][toks], toks, quant_act=True)
-        log(f"  vs activation-quantised oracle relL2={rel_l2(r['out'][toks], ref2):.3e}")
+        r2 = rel_l2(r["out"][toks], ref2)
+        w2 = worst_row_rel(r["out"][toks], ref2)
+        log(f"  vs activation-quantised oracle relL2={r2:.3e} worst token={w2:.3e} "
+            f"(tol {FP8_QUANT_TOL})")
+        assert r2 <= FP8_QUANT_TOL and w2 <= 3 * FP8_QUANT_TOL
     return inp, dev, r
 
 
 def test_layer_v3_bf16_T4096_sampled():
     _full_layer(synth.C3, n_samples=64)
+
+
+def test_layer_v3_bf16_T16384_sampled():
+    """16384 tokens (512 routed rows per expert): the wide gate/up tiles at
+    H = 7168 over their whole k loop, and a workspace past 2 GiB (the upper
+    rows of y and all of y_shared lie beyond byte 2^31 of it); routing on
+    every token, outputs on sampled tokens that include the first and the
+    last."""
+    _full_layer(synth.C3X, n_samples=48)
 
 
 @pytest.mark.parametrize("cfg", [synth.C4A, synth.C4B, synth.C4C, synth.C4D],
@@ -122,7 +137,7 @@ def test_layer_v3_decode_zipf(cfg):
 
 
 def test_layer_v3_fp8_T8192_sampled():
-    inp, dev, r = _full_layer(synth.C5, n_samples=48, quant_diag=True)
+    inp, dev, r = _full_layer(synth.C5, n_samples=48)
     cfg = synth.C5
     xq = torch.empty((cfg.T, cfg.H), dtype=torch.uint8, device=DEV)
     xs = torch.empty((cfg.T, cfg.H // 128), dtype=torch.float32, device=DEV)

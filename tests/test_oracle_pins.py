@@ -428,6 +428,104 @@ def test_fp8_layer_uses_dequantised_weights():
     assert 1e-4 < rel < 0.1
 
 
+def _qdq_1x128_torch(v):
+    """1x128 quantise-dequantise of the rows of v, written independently of
+    the oracle with torch's float8_e4m3fn cast ("深入理解 DeepSeek-V3…", section
+    3.2: one scale per 1x128 activation tile): a = max |v| of the fp32 tile,
+    scale = a/448 and inverse = 448/a each rounded once to fp32 (scale 1 for
+    an all-zero tile), code = e4m3 of the fp32 product (clamped to +-448
+    first, since torch maps magnitudes past 464 to NaN), value = code *
+    scale."""
+    v = np.asarray(v, np.float64).astype(np.float32)
+    n = v.shape[-1]
+    t = v.reshape(-1, n // 128, 128)
+    a = np.abs(t).max(axis=-1, keepdims=True).astype(np.float64)
+    nz = a > 0
+    scale = np.where(nz, (a / 448.0).astype(np.float32), np.float32(1.0))
+    inv = np.where(nz, (448.0 / np.where(nz, a, 1.0)).astype(np.float32), np.float32(0.0))
+    prod = (t * inv.astype(np.float32)).astype(np.float32)
+    codes = torch.from_numpy(np.clip(prod, -448.0, 448.0)).to(torch.float8_e4m3fn)
+    return (codes.to(torch.float64).numpy() * scale.astype(np.float64)).reshape(v.shape)
+
+
+def _fp8_layer_numpy(cfg, inp, idx, w, quant_x, quant_h):
+    """The layer on dequantised e4m3 weights with numpy fp64 matmuls, each
+    GEMM input optionally passed through the 1x128 quantiser first."""
+    deq = lambda q, s: (torch.from_numpy(q).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+                        * np.kron(s.astype(np.float64), np.ones((128, 128))))
+    x = synth.bf16_to_f32(inp["x"]).astype(np.float64)
+    xq = _qdq_1x128_torch(x) if quant_x else x
+
+    def ffn(w13, w2, xr):
+        a = w13 @ xr
+        n = w13.shape[0] // 2
+        h = a[:n] / (1.0 + np.exp(-a[:n])) * a[n:]
+        if quant_h:
+            h = _qdq_1x128_torch(h[None, :])[0]
+        return w2 @ h
+
+    ws13, ws2 = deq(inp["ws13"], inp["ws13_s"]), deq(inp["ws2"], inp["ws2_s"])
+    w13 = [deq(inp["w13"][e], inp["w13_s"][e]) for e in range(cfg.E)]
+    w2 = [deq(inp["w2"][e], inp["w2_s"][e]) for e in range(cfg.E)]
+    out = np.empty((x.shape[0], cfg.H))
+    for t in range(x.shape[0]):
+        out[t] = ffn(ws13, ws2, xq[t])
+        for k in range(cfg.K):
+            out[t] += w[t, k] * ffn(w13[idx[t, k]], w2[idx[t, k]], xq[t])
+    return out
+
+
+def test_fp8_activation_quantised_mode_matches_numpy_expression():
+    """F2 (the oracle with the activations quantised as the fp8 data path
+    does): x quantised per 1x128 tile before W13, h = silu(g) * u quantised
+    per 1x128 tile after the SwiGLU and before W2 ("深入理解 DeepSeek-V3…",
+    section 3.2: every GEMM's activation input in 1x128 tiles).  Pinned to a
+    numpy/torch re-expression at 1e-10; the readings that differ from it --
+    h left unquantised, x left unquantised, neither (F1), or the quantiser
+    applied to the W2 output instead of its input -- each sit orders of
+    magnitude further away, so an oracle making any of those slips fails."""
+    cfg = synth.C5.replace(name="f2-pin", T=10, H=256, E=4, G=2, TG=1, K=2, I=256, Is=128,
+                           rho=2.5)
+    inp = synth.gen_inputs(cfg)
+    lg = oracle.logits(inp["x"], cfg.act, inp["gate_w"])
+    idx, w, _ = oracle.route_f64(cfg, lg, inp["bias"])
+    got = oracle.layer(cfg, inp, idx, w, quant_act=True)
+    ref = _fp8_layer_numpy(cfg, inp, idx, w, quant_x=True, quant_h=True)
+    rel = lambda a, b: np.linalg.norm(a - b) / np.linalg.norm(b)
+    assert rel(got, ref) < 1e-10
+    # F1 (no activation quantisation) is the same numpy expression unquantised
+    f1 = oracle.layer(cfg, inp, idx, w, quant_act=False)
+    assert rel(f1, _fp8_layer_numpy(cfg, inp, idx, w, quant_x=False, quant_h=False)) < 1e-10
+    # each wrong reading is far from F2
+    for qx, qh in ((True, False), (False, True), (False, False)):
+        assert rel(_fp8_layer_numpy(cfg, inp, idx, w, quant_x=qx, quant_h=qh), ref) > 1e-4
+
+    def ffn_quant_after_w2(w13, w2, xr):   # the quantiser on the output instead
+        a = w13 @ xr
+        n = w13.shape[0] // 2
+        h = a[:n] / (1.0 + np.exp(-a[:n])) * a[n:]
+        return _qdq_1x128_torch((w2 @ h)[None, :])[0]
+
+    deq = lambda q, s: (torch.from_numpy(q).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+                        * np.kron(s.astype(np.float64), np.ones((128, 128))))
+    xq = _qdq_1x128_torch(synth.bf16_to_f32(inp["x"]).astype(np.float64))
+    slip = np.stack([ffn_quant_after_w2(deq(inp["ws13"], inp["ws13_s"]),
+                                        deq(inp["ws2"], inp["ws2_s"]), xq[t]) +
+                     sum(w[t, k] * ffn_quant_after_w2(deq(inp["w13"][idx[t, k]],
+                                                          inp["w13_s"][idx[t, k]]),
+                                                      deq(inp["w2"][idx[t, k]],
+                                                          inp["w2_s"][idx[t, k]]), xq[t])
+                         for k in range(cfg.K)) for t in range(cfg.T)])
+    assert rel(slip, ref) > 1e-4
+    # the expert rows (moe_expert_ffn's y) follow the same expression
+    e = int(idx[0, 0])
+    y = oracle.ffn(cfg, inp, np.array([0]), np.array([e], np.int32), quant_act=True)[0]
+    a = deq(inp["w13"][e], inp["w13_s"][e]) @ xq[0]
+    h = a[:cfg.I] / (1.0 + np.exp(-a[:cfg.I])) * a[cfg.I:]
+    y_ref = deq(inp["w2"][e], inp["w2_s"][e]) @ _qdq_1x128_torch(h[None, :])[0]
+    assert np.linalg.norm(y - y_ref) / np.linalg.norm(y_ref) < 1e-10
+
+
 # ---------------------------------------------------------------- per-row FFN and the combine step
 
 def test_ffn_rows_match_numpy_and_compose_to_layer():
