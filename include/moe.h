@@ -35,8 +35,10 @@
  *   - Layouts are row-major.  Weight matrices are stored "output rows x
  *     input columns" with the input dimension contiguous.
  *   - T == 0 is a no-op returning MOE_OK.
- *   - Apart from the kernel timer below (off by default) the library holds no
- *     mutable global state; calls on different streams with different
+ *   - Global state: the kernel timer below (off by default), kernel
+ *     attributes set once per process on first use, and the two fork/join
+ *     events of moe_forward_overlap (per device and host thread).  None of
+ *     it holds results: calls on different streams with different
  *     workspaces may run concurrently.
  *   - Results are deterministic: no floating-point atomics anywhere, so two
  *     runs on the same inputs give bitwise-identical outputs.
@@ -116,7 +118,9 @@ size_t moe_workspace_bytes(const moe_config* cfg, int64_t T);
 /* Gate and selection (first page, section 2.2).
  *   x       [T, H] act_dtype
  *   gate_w  [E, H] fp32,  bias [E] fp32
- *   logits  [T, E] fp32 out, may be NULL (then kept in the workspace).  The
+ *   logits  [T, E] fp32 out, may be NULL: then they are not kept (the
+ *           workspace holds per-k-range partial sums only), so a caller that
+ *           needs them later (moe_backward does) passes this array.  The
  *           gate product is computed to fp32 accuracy: x is exact in bf16 and
  *           the fp32 gate weight is split into three bf16 parts whose
  *           products with x are exact, accumulated in fp32 on MFMA.

@@ -476,13 +476,11 @@ unsigned grid_for(int64_t work) {
 // Workgroups of the looping weight-gradient kernel: kWgradPerCu per CU of
 // the current device, at most one per tile, a multiple of the XCD count.
 unsigned wgrad_grid(int64_t work) {
-  static int cus = [] {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      n = 256;
-    return n > 0 ? n : 256;
-  }();
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
   return grid_for(std::min<int64_t>(work, (int64_t)cus * kWgradPerCu));
 }
 

@@ -274,7 +274,7 @@ __global__ void __launch_bounds__(NT, 1) grouped_gemm_fp8(Gemm8Args p) {
     // h = silu(g) * u, then 1x128 quantisation: the tile's 128 h columns of a
     // row are spread over 4 waves x 32 lanes; row max by lane shuffles, then
     // across waves through LDS (reusing the A-scale buffer).
-    float* s_amax = sAs;   // [4 waves][BM rows] fits in 2 * BM floats? use first 4*64 per pass
+    float* s_amax = sAs;   // [4 waves][32 rows] of tile maxima per pass (the A-scale buffer)
     uint8_t* HQ = sh ? p.hq_s : p.hq_r;
     float* HS = sh ? p.hs_s : p.hs_r;
     const int col = n0 + wave * 32 + lr;
