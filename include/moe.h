@@ -36,10 +36,10 @@
  *     input columns" with the input dimension contiguous.
  *   - T == 0 is a no-op returning MOE_OK.
  *   - Global state: the kernel timer below (off by default), kernel
- *     attributes set once per process on first use, and the two fork/join
- *     events of moe_forward_overlap (per device and host thread).  None of
- *     it holds results: calls on different streams with different
- *     workspaces may run concurrently.
+ *     attributes set once per process on first use, the two fork/join
+ *     events of moe_forward_overlap (per device and host thread), and the
+ *     static workspace of moe_forward_noalloc (one per device).  Calls on
+ *     different streams with different workspaces may run concurrently.
  *   - Results are deterministic: no floating-point atomics anywhere, so two
  *     runs on the same inputs give bitwise-identical outputs.
  */
@@ -206,6 +206,30 @@ moe_status moe_forward_overlap(const moe_config* cfg, int64_t T, const void* x,
                                const moe_weights* w, void* out, float* logits, int32_t* topk_idx,
                                float* topk_w, int32_t* counts, int32_t* perm, void* ws,
                                size_t ws_bytes, void* stream, void* shared_stream);
+
+/* moe_forward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments and outputs as moe_forward, bit for bit (the same
+ * kernels), without ws / ws_bytes: the workspace is a static device array
+ * of MOE_NOALLOC_SCRATCH_BYTES bytes inside the library, one per GPU, held
+ * from the library's first use on that GPU until the process ends.  The
+ * call allocates nothing (no hipMalloc, no allocating library routine).
+ *   Limit: moe_workspace_bytes(cfg, T) <= MOE_NOALLOC_SCRATCH_BYTES (at the
+ *   V3 shape, H 7168, 256 experts, top-8, bf16, FFN width 2048, that is
+ *   T <= 288);
+ *   larger batches return MOE_ERR_UNSUPPORTED and enqueue nothing.
+ *   Every call on one GPU shares that GPU's array, which keeps the last
+ *   call's contents; each call writes every part it reads before reading
+ *   it, so nothing needs clearing.  Calls that overlap on one GPU (other
+ *   streams, other threads) race on the array: the caller orders them.
+ *   The error flag of moe_get_device_error lives in that array too; the
+ *   forward's own selection always yields ids in [0, E).  The first call on
+ *   a device looks the array's address up (hipGetSymbolAddress, which loads
+ *   it): make that first call outside graph capture. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status moe_forward_noalloc(const moe_config* cfg, int64_t T, const void* x,
+                               const moe_weights* w, void* out, float* logits, int32_t* topk_idx,
+                               float* topk_w, int32_t* counts, int32_t* perm, void* stream);
 
 /* FP8 activation quantiser ("深入理解 DeepSeek-V3…", section 3.2: 1x128
  * activation tiles).  For each row of x [rows, H] (bf16, H % 128 == 0) and

@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "moe_internal.hpp"
 #include "backward.hpp"
@@ -360,6 +361,35 @@ moe_status forward_impl(const moe_config* cfg, int64_t T, const void* x, const m
   return MOE_OK;
 }
 
+// ---- the no-allocation forward ----------------------------------------------
+// Workspace of moe_forward_noalloc: one static device array, of which every GPU
+// that runs the library holds its own copy until the process ends.  In host
+// code `scratch` names a host-side stand-in, not device memory: its device
+// address comes from hipGetSymbolAddress, looked up once per device with
+// that device current, and only that address is ever handed to kernels.
+constexpr size_t kScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+hipError_t scratch_address(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -444,6 +474,24 @@ moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const mo
                        int32_t* counts, int32_t* perm, void* ws, size_t ws_bytes, void* stream) {
   return forward_impl(cfg, T, x, w, out, logits, topk_idx, topk_w, counts, perm, ws, ws_bytes,
                       (hipStream_t)stream, nullptr);
+}
+
+moe_status moe_forward_noalloc(const moe_config* cfg, int64_t T, const void* x,
+                               const moe_weights* w, void* out, float* logits, int32_t* topk_idx,
+                               float* topk_w, int32_t* counts, int32_t* perm, void* stream) {
+  CHECK(check_cfg(cfg));
+  CHECK(check_T(T, cfg));
+  if (T == 0) return MOE_OK;
+  const size_t need = layout(cfg, T).total;
+  if (need > kScratchBytes)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "moe_forward_noalloc: %lld tokens need %zu bytes of workspace, the static "
+                "scratch holds %zu (use moe_forward with a caller workspace)",
+                (long long)T, need, kScratchBytes);
+  void* ws = nullptr;
+  HIPCALL(scratch_address(&ws), "static scratch address");
+  return forward_impl(cfg, T, x, w, out, logits, topk_idx, topk_w, counts, perm, ws,
+                      kScratchBytes, (hipStream_t)stream, nullptr);
 }
 
 moe_status moe_forward_overlap(const moe_config* cfg, int64_t T, const void* x,

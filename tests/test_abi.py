@@ -172,3 +172,26 @@ def test_kernel_timer_without_launches():
     moe.moe_kernel_timer_enable(True, "grouped_gemm_bf16_packed<true>")
     moe.moe_kernel_timer_enable(False)
     assert moe.moe_kernel_timer_read() == {}
+
+
+def test_noalloc_forward_limit_and_constant():
+    """moe_forward_noalloc: the static workspace size in the header and the
+    binding agree, batches whose workspace exceeds it are refused on the
+    host (nothing enqueued, no HIP call), and T = 0 is a no-op."""
+    with open(os.path.join(ROOT, "include", "moe.h")) as f:
+        m = re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", f.read())
+    assert m and int(m.group(1)) << int(m.group(2)) == moe.MOE_NOALLOC_SCRATCH_BYTES
+    cfg = _cfg()
+    W = moe.MoeWeights()
+    for T, fits in ((256, True), (288, True), (289, False), (4096, False)):
+        assert (moe.moe_workspace_bytes(cfg, T) <= moe.MOE_NOALLOC_SCRATCH_BYTES) == fits, T
+    st = moe.lib().moe_forward_noalloc(ctypes.byref(cfg), 4096, FAKE, ctypes.byref(W), FAKE,
+                                       None, None, None, None, None, None)
+    assert st == moe.MOE_ERR_UNSUPPORTED
+    assert "static" in moe.moe_last_error()
+    st = moe.lib().moe_forward_noalloc(ctypes.byref(cfg), 0, FAKE, ctypes.byref(W), FAKE,
+                                       None, None, None, None, None, None)
+    assert st == moe.MOE_OK
+    st = moe.lib().moe_forward_noalloc(ctypes.byref(_cfg(K=0)), 4, FAKE, ctypes.byref(W), FAKE,
+                                       None, None, None, None, None, None)
+    assert st == moe.MOE_ERR_INVALID_ARG
