@@ -51,6 +51,8 @@ def lib():
         L.oracle_e4m3_encode.restype = ctypes.c_uint8
         L.oracle_quant_rows.argtypes = [i64, i32, vp, vp, vp]
         L.oracle_quant_rows.restype = None
+        L.oracle_quant_rows_pow2.argtypes = [i64, i32, vp, vp, vp]
+        L.oracle_quant_rows_pow2.restype = None
         L.oracle_logits.argtypes = [i64, i32, i32, vp, i32, vp, vp]
         L.oracle_logits.restype = None
         L.oracle_route_f64.argtypes = [ctypes.POINTER(Cfg), i64, vp, vp, vp, vp, vp]
@@ -94,7 +96,7 @@ def cfg_of(c) -> Cfg:
 
 
 def dtype_code(arr: np.ndarray, declared: str) -> int:
-    return {"f32": F32, "bf16": BF16, "fp8": E4M3}[declared]
+    return _WD[declared]
 
 
 def threads() -> int:
@@ -109,14 +111,32 @@ def e4m3_encode(v: float) -> int:
     return lib().oracle_e4m3_encode(v)
 
 
-def quant_rows(v: np.ndarray):
-    """1x128 e4m3 quantisation of a float32 [rows, cols] array -> (codes u8, scales f32)."""
+# Weight dtypes of the configs: "fp8" is e4m3 with block scales a / 448
+# (R7), "fp8e8m0" e4m3 with power-of-two block scales (R14); both decode as
+# code * scale.
+_WD = {"f32": F32, "bf16": BF16, "fp8": E4M3, "fp8e8m0": E4M3}
+# Activation quantisation mode of the fp8 data path per weight dtype.
+_QUANT_MODE = {"fp8": 1, "fp8e8m0": 2}
+
+
+def _quant_mode(cfg, quant_act) -> int:
+    if not quant_act:
+        return 0
+    if cfg.wdtype not in _QUANT_MODE:
+        raise ValueError(f"activation quantisation needs fp8 weights, not {cfg.wdtype}")
+    return _QUANT_MODE[cfg.wdtype]
+
+
+def quant_rows(v: np.ndarray, pow2: bool = False):
+    """1x128 e4m3 quantisation of a float32 [rows, cols] array -> (codes u8,
+    scales f32); pow2 selects power-of-two scales (R14) instead of a / 448."""
     v = _c(v, np.float32)
     rows, cols = v.shape
     assert cols % 128 == 0
     q = np.empty((rows, cols), np.uint8)
     s = np.empty((rows, cols // 128), np.float32)
-    lib().oracle_quant_rows(rows, cols, _p(v), _p(q), _p(s))
+    f = lib().oracle_quant_rows_pow2 if pow2 else lib().oracle_quant_rows
+    f(rows, cols, _p(v), _p(q), _p(s))
     return q, s
 
 
@@ -179,14 +199,14 @@ def layer(cfg, inp: dict, idx: np.ndarray, w: np.ndarray, tokens=None, quant_act
     tokens = np.arange(T, dtype=np.int64) if tokens is None else _c(tokens, np.int64)
     idx = _c(idx, np.int32)
     w = _c(w, np.float64)
-    wd = {"f32": F32, "bf16": BF16, "fp8": E4M3}[cfg.wdtype]
+    wd = _WD[cfg.wdtype]
     xd = F32 if cfg.act == "f32" else BF16
     g = lambda k: None if inp.get(k) is None else _c(inp[k])
     arrs = [g(k) for k in ("w13", "w13_s", "w2", "w2_s", "ws13", "ws13_s", "ws2", "ws2_s")]
     out = np.empty((len(tokens), cfg.H), np.float64)
     rc = lib().oracle_layer(ctypes.byref(cfg_of(cfg)), len(tokens), _p(tokens), _p(x), xd,
-                            _p(idx), _p(w), *[_p(a) for a in arrs], wd, int(bool(quant_act)),
-                            _p(out))
+                            _p(idx), _p(w), *[_p(a) for a in arrs], wd,
+                            _quant_mode(cfg, quant_act), _p(out))
     if rc:
         raise ValueError("oracle_layer failed (bad expert index or allocation)")
     return out
@@ -197,13 +217,13 @@ def ffn(cfg, inp: dict, tokens, experts, quant_act=False):
     x = _c(inp["x"])
     tokens = _c(tokens, np.int64)
     experts = _c(experts, np.int32)
-    wd = {"f32": F32, "bf16": BF16, "fp8": E4M3}[cfg.wdtype]
+    wd = _WD[cfg.wdtype]
     xd = F32 if cfg.act == "f32" else BF16
     g = lambda k: None if inp.get(k) is None else _c(inp[k])
     arrs = [g(k) for k in ("w13", "w13_s", "w2", "w2_s", "ws13", "ws13_s", "ws2", "ws2_s")]
     out = np.empty((len(tokens), cfg.H), np.float64)
     rc = lib().oracle_ffn(ctypes.byref(cfg_of(cfg)), len(tokens), _p(tokens), _p(experts), _p(x),
-                          xd, *[_p(a) for a in arrs], wd, int(bool(quant_act)), _p(out))
+                          xd, *[_p(a) for a in arrs], wd, _quant_mode(cfg, quant_act), _p(out))
     if rc:
         raise ValueError("oracle_ffn failed (bad expert index or allocation)")
     return out

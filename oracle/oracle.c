@@ -34,6 +34,12 @@
  *   R7  FP8 scale of a tile with max |v| = a: scale = a / 448, codes are the
  *       e4m3 values nearest v * (448 / a) (ties to even, saturating);
  *       an all-zero tile has scale 1 and zero codes.
+ *   R14 FP8 with power-of-two scales ([Insights] 3.2 asks for matrix units
+ *       that take the block scales themselves; such units take scales that
+ *       are powers of two): the scale of a tile is the smallest power of two
+ *       2^e >= a / 448 (e clamped to [-126, 127]), codes are the e4m3 values
+ *       nearest v * 2^-e (an exact product; ties to even); an all-zero tile
+ *       has scale 1 and zero codes.
  *   R11 the selection bias follows the experts' observed load ([Co-design]
  *       2.2 keeps it as a buffer updated from load statistics, not from a
  *       gradient, and prints no rule): each expert's bias moves one fixed
@@ -172,8 +178,55 @@ void oracle_quant_rows(int64_t rows, int32_t cols, const float *v, uint8_t *q, f
     }
 }
 
-/* Quantise then dequantise one row in place (double in, double out). */
-static void quant_dequant_row(double *v, int32_t n)
+/* Power-of-two scale of a tile with max |v| = a > 0 (R14): the smallest
+ * 2^e with 2^e >= a / 448.  a / 448 in double is a power of two exactly when
+ * a is 7 * 2^k (448 = 7 * 2^6), and is then computed exactly; frexp gives
+ * a / 448 = f * 2^ex with f in [0.5, 1), a power of two iff f == 0.5. */
+static int pow2_scale_exponent(double a)
+{
+    int ex;
+    double f = frexp(a / 448.0, &ex);
+    int e = (f == 0.5) ? ex - 1 : ex;
+    if (e < -126)
+        e = -126;
+    if (e > 127)
+        e = 127;
+    return e;
+}
+
+/* The same 1x128 quantiser with power-of-two scales (R14). */
+void oracle_quant_rows_pow2(int64_t rows, int32_t cols, const float *v, uint8_t *q, float *s)
+{
+    int32_t nt = cols / 128;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int32_t t = 0; t < nt; ++t) {
+            const float *p = v + r * cols + (int64_t)t * 128;
+            double a = 0.0;
+            for (int j = 0; j < 128; ++j)
+                if (fabs((double)p[j]) > a)
+                    a = fabs((double)p[j]);
+            float scale = 1.0f, inv = 0.0f;
+            if (a > 0.0) {
+                int e = pow2_scale_exponent(a);
+                scale = (float)ldexp(1.0, e);
+                inv = (float)ldexp(1.0, -e);
+            }
+            s[r * nt + t] = scale;
+            for (int j = 0; j < 128; ++j) {
+                float prod = p[j] * inv; /* exact: inv is a power of two */
+                q[r * cols + (int64_t)t * 128 + j] = oracle_e4m3_encode(prod);
+            }
+        }
+    }
+}
+
+/* Activation quantisation modes of the layer functions. */
+enum { OR_QUANT_NONE = 0, OR_QUANT_AMAX = 1, OR_QUANT_POW2 = 2 };
+
+/* Quantise then dequantise one row in place (double in, double out) with the
+ * scale rule of `mode` (R7 or R14). */
+static void quant_dequant_row(double *v, int32_t n, int32_t mode)
 {
     float tmp[128];
     uint8_t q[128];
@@ -181,7 +234,10 @@ static void quant_dequant_row(double *v, int32_t n)
     for (int32_t t = 0; t < n / 128; ++t) {
         for (int j = 0; j < 128; ++j)
             tmp[j] = (float)v[t * 128 + j];
-        oracle_quant_rows(1, 128, tmp, q, &s);
+        if (mode == OR_QUANT_POW2)
+            oracle_quant_rows_pow2(1, 128, tmp, q, &s);
+        else
+            oracle_quant_rows(1, 128, tmp, q, &s);
         for (int j = 0; j < 128; ++j)
             v[t * 128 + j] = oracle_e4m3_decode(q[j]) * (double)s;
     }
@@ -425,7 +481,8 @@ int oracle_permute(int64_t T, int32_t K, int32_t E, const int32_t *idx, int32_t 
 
 /* One SwiGLU FFN on one row (R5): a = W13 x (2n rows: gate then up),
  * h = silu(a[:n]) * a[n:], silu(z) = z / (1 + exp(-z)), y = W2 h.
- * W13 is [2n, H], W2 is [H, n].  quant_h: quantise h per 1x128 first. */
+ * W13 is [2n, H], W2 is [H, n].  quant_h: quantise h per 1x128 first, with
+ * the scale rule of that mode (OR_QUANT_AMAX: R7, OR_QUANT_POW2: R14). */
 static void ffn_row(int32_t H, int32_t n, const double *xrow, const void *w13,
                     const float *s13, const void *w2, const float *s2, int dt,
                     int quant_h, double *h, double *y)
@@ -439,7 +496,7 @@ static void ffn_row(int32_t H, int32_t n, const double *xrow, const void *w13,
         h[i] = gsum / (1.0 + exp(-gsum)) * usum;
     }
     if (quant_h)
-        quant_dequant_row(h, n);
+        quant_dequant_row(h, n, quant_h);
     for (int32_t m = 0; m < H; ++m) {
         double acc = 0.0;
         for (int32_t i = 0; i < n; ++i)
@@ -463,7 +520,8 @@ static const void *expert_base(const void *w, int dt, int64_t e, int64_t elems)
  * directly on x_t here.  w13 is [E, 2I, H], w2 [E, H, I], ws13 [2Is, H],
  * ws2 [H, Is]; e4m3 weights use 128x128 block scales (the dequantised
  * weights are the layer's weights).  quant_act: also quantise x and h per
- * 1x128 tile (diagnostic emulation of the FP8 data path).
+ * 1x128 tile as the FP8 data path does (OR_QUANT_AMAX: scales a / 448, R7;
+ * OR_QUANT_POW2: power-of-two scales, R14).
  * out is [n_tok, H]. */
 int oracle_layer(const oracle_cfg *c, int64_t n_tok, const int64_t *tokens, const void *x,
                  int32_t x_dtype, const int32_t *idx, const double *w, const void *w13,
@@ -486,7 +544,7 @@ int oracle_layer(const oracle_cfg *c, int64_t n_tok, const int64_t *tokens, cons
             for (int32_t k = 0; k < H; ++k)
                 xr[k] = mat_at(x, NULL, x_dtype, H, t, k);
             if (quant_act)
-                quant_dequant_row(xr, H);
+                quant_dequant_row(xr, H, quant_act);
             for (int32_t k = 0; k < H; ++k)
                 o[k] = 0.0;
             if (Is > 0) {
@@ -542,7 +600,7 @@ int oracle_ffn(const oracle_cfg *c, int64_t n, const int64_t *tokens, const int3
             for (int32_t k = 0; k < H; ++k)
                 xr[k] = mat_at(x, NULL, x_dtype, H, t, k);
             if (quant_act)
-                quant_dequant_row(xr, H);
+                quant_dequant_row(xr, H, quant_act);
             if (e < 0) {
                 ffn_row(H, Is, xr, ws13, ws13_s, ws2, ws2_s, w_dtype, quant_act, h, out + r * H);
             } else {

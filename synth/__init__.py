@@ -51,7 +51,7 @@ def lib():
         L.synth_normal_bf16.argtypes = [vp, i64, u64, u32, u32, d]
         L.synth_uniform_f32.argtypes = [vp, i64, u64, u32, u32, d, d]
         L.synth_words.argtypes = [vp, i64, u64, u32, u32]
-        L.synth_normal_e4m3_blocks.argtypes = [vp, vp, i64, i64, u64, u32, u32, d]
+        L.synth_normal_e4m3_blocks.argtypes = [vp, vp, i64, i64, u64, u32, u32, d, ctypes.c_int]
         for f in (L.synth_normal_f32, L.synth_normal_bf16, L.synth_uniform_f32,
                   L.synth_words, L.synth_normal_e4m3_blocks):
             f.restype = None
@@ -90,12 +90,15 @@ def words(n: int, seed: int, tensor: int, sub: int) -> np.ndarray:
 
 
 def normal_e4m3_blocks(rows: int, cols: int, seed: int, tensor: int, sub: int, std: float,
-                       q=None, s=None):
-    """e4m3 codes [rows, cols] (uint8) and fp32 scales [rows/128, cols/128]."""
+                       q=None, s=None, pow2: bool = False):
+    """e4m3 codes [rows, cols] (uint8) and fp32 scales [rows/128, cols/128]
+    (scale a/448 of the block's max |v|, or with pow2 the smallest power of
+    two not below it)."""
     assert rows % 128 == 0 and cols % 128 == 0
     q = np.empty((rows, cols), np.uint8) if q is None else q
     s = np.empty((rows // 128, cols // 128), np.float32) if s is None else s
-    lib().synth_normal_e4m3_blocks(_ptr(q), _ptr(s), rows, cols, seed, tensor, sub, std)
+    lib().synth_normal_e4m3_blocks(_ptr(q), _ptr(s), rows, cols, seed, tensor, sub, std,
+                                   1 if pow2 else 0)
     return q, s
 
 
@@ -118,7 +121,8 @@ class MoEConfig:
     Is: int
     rho: float
     act: str          # "f32" | "bf16"      (x and the layer output)
-    wdtype: str       # "f32" | "bf16" | "fp8"   (expert + shared weights)
+    wdtype: str       # "f32" | "bf16" | "fp8" | "fp8e8m0"   (expert + shared weights;
+                      #  fp8e8m0: e4m3 with power-of-two block scales)
     bias_lo: float
     bias_hi: float
     seed: int = 0
@@ -161,8 +165,10 @@ C4C = C3.replace(name="v3-decode-zipf-K1-T32", T=32, K=1,
 C4D = C4C.replace(name="v3-decode-zipf-K1-T256", T=256)
 # FP8 block-scaled layer.
 C5 = C3.replace(name="v3-layer-fp8-T8192", T=8192, wdtype="fp8")
+# The same with power-of-two block scales, which the matrix cores apply.
+C5P = C5.replace(name="v3-layer-fp8e8m0-T8192", wdtype="fp8e8m0")
 
-CONFIGS = {c.name: c for c in (C1, C2, C3, C3X, C4A, C4B, C4C, C4D, C5)}
+CONFIGS = {c.name: c for c in (C1, C2, C3, C3X, C4A, C4B, C4C, C4D, C5, C5P)}
 
 
 def load_bias_file(path: str) -> np.ndarray:
@@ -206,12 +212,13 @@ def _expert_matrix(cfg: MoEConfig, tensor: int, sub: int, rows: int, cols: int, 
         r = normal_bf16(rows * cols, cfg.seed, tensor, sub, std,
                         out=None if out is None else out.reshape(-1))
         return r.reshape(rows, cols), None
-    q, s = normal_e4m3_blocks(rows, cols, cfg.seed, tensor, sub, std, q=out, s=out_s)
+    q, s = normal_e4m3_blocks(rows, cols, cfg.seed, tensor, sub, std, q=out, s=out_s,
+                              pow2=cfg.wdtype == "fp8e8m0")
     return q, s
 
 
 def _wdt(cfg):
-    return {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}[cfg.wdtype]
+    return {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8, "fp8e8m0": np.uint8}[cfg.wdtype]
 
 
 def gen_expert_weights(cfg: MoEConfig):
@@ -222,7 +229,7 @@ def gen_expert_weights(cfg: MoEConfig):
     w13 = np.empty((E, 2 * I, H), _wdt(cfg))
     w2 = np.empty((E, H, I), _wdt(cfg))
     s13 = s2 = None
-    if cfg.wdtype == "fp8":
+    if cfg.wdtype in ("fp8", "fp8e8m0"):
         s13 = np.empty((E, 2 * I // 128, H // 128), np.float32)
         s2 = np.empty((E, H // 128, I // 128), np.float32)
     for e in range(E):

@@ -31,8 +31,11 @@
  * stored layer weights: the block's float values v are drawn as above, then
  * a = max|v| over the block, scale = a / 448 (rounded to float), and each
  * code is the OCP e4m3fn value nearest v * (448 / a) (ties to even
- * mantissa, saturated at 448).  This is weight preparation only; the layer's
- * activation quantiser lives separately in the oracle and in the kernels.
+ * mantissa, saturated at 448).  With pow2 set the block scale is instead the
+ * smallest power of two 2^e >= a / 448 and the codes are the e4m3 values
+ * nearest v * 2^-e (the weights of the power-of-two-scale FP8 variant).
+ * This is weight preparation only; the layer's activation quantiser lives
+ * separately in the oracle and in the kernels.
  */
 #include <math.h>
 #include <stdint.h>
@@ -174,9 +177,26 @@ static uint8_t e4m3_encode_gen(float v)
 /* Matrix [rows, cols] (rows, cols multiples of 128) drawn like
  * synth_normal_f32 (element r*cols + c of the stream), then stored as e4m3
  * codes q[rows*cols] with block scales s[(rows/128) * (cols/128)]. */
+/* Power-of-two block scale for a block with max |v| = amax > 0: the
+ * smallest 2^e not below amax / 448, e in [-126, 127]. */
+static int gen_pow2_exponent(float amax)
+{
+    double r = (double)amax / 448.0;
+    int e = (int)ceil(log2(r));
+    while (e > -126 && ldexp(1.0, e - 1) >= r)
+        --e;
+    while (ldexp(1.0, e) < r)
+        ++e;
+    if (e < -126)
+        e = -126;
+    if (e > 127)
+        e = 127;
+    return e;
+}
+
 void synth_normal_e4m3_blocks(uint8_t *q, float *s, int64_t rows, int64_t cols,
                               uint64_t seed, uint32_t tensor, uint32_t sub,
-                              double std)
+                              double std, int pow2)
 {
     uint64_t key = stream_key(seed, tensor, sub);
     int64_t rb = rows / 128, cb = cols / 128;
@@ -199,7 +219,11 @@ void synth_normal_e4m3_blocks(uint8_t *q, float *s, int64_t rows, int64_t cols,
             }
         }
         float scale = 1.0f, inv = 0.0f;
-        if (amax > 0.0f) {
+        if (amax > 0.0f && pow2) {
+            int e = gen_pow2_exponent(amax);
+            scale = (float)ldexp(1.0, e);
+            inv = (float)ldexp(1.0, -e);
+        } else if (amax > 0.0f) {
             scale = (float)((double)amax / 448.0);
             inv = (float)(448.0 / (double)amax);
         }

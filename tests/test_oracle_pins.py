@@ -428,21 +428,34 @@ def test_fp8_layer_uses_dequantised_weights():
     assert 1e-4 < rel < 0.1
 
 
-def _qdq_1x128_torch(v):
+def _pow2_ceil(r):
+    """Smallest power of two >= r > 0, with numpy's frexp (r = m 2^e, m in
+    [0.5, 1): r itself when m == 0.5, else 2^e)."""
+    m, e = np.frexp(r)
+    return np.ldexp(1.0, np.where(m == 0.5, e - 1, e))
+
+
+def _qdq_1x128_torch(v, pow2=False):
     """1x128 quantise-dequantise of the rows of v, written independently of
     the oracle with torch's float8_e4m3fn cast ("深入理解 DeepSeek-V3…", section
     3.2: one scale per 1x128 activation tile): a = max |v| of the fp32 tile,
     scale = a/448 and inverse = 448/a each rounded once to fp32 (scale 1 for
     an all-zero tile), code = e4m3 of the fp32 product (clamped to +-448
     first, since torch maps magnitudes past 464 to NaN), value = code *
-    scale."""
+    scale.  pow2: the scale is the smallest power of two >= a/448 and the
+    inverse its reciprocal (both exact)."""
     v = np.asarray(v, np.float64).astype(np.float32)
     n = v.shape[-1]
     t = v.reshape(-1, n // 128, 128)
     a = np.abs(t).max(axis=-1, keepdims=True).astype(np.float64)
     nz = a > 0
-    scale = np.where(nz, (a / 448.0).astype(np.float32), np.float32(1.0))
-    inv = np.where(nz, (448.0 / np.where(nz, a, 1.0)).astype(np.float32), np.float32(0.0))
+    if pow2:
+        p2 = _pow2_ceil(np.where(nz, a, 448.0) / 448.0)
+        scale = np.where(nz, p2, 1.0).astype(np.float32)
+        inv = np.where(nz, 1.0 / p2, 0.0).astype(np.float32)
+    else:
+        scale = np.where(nz, (a / 448.0).astype(np.float32), np.float32(1.0))
+        inv = np.where(nz, (448.0 / np.where(nz, a, 1.0)).astype(np.float32), np.float32(0.0))
     prod = (t * inv.astype(np.float32)).astype(np.float32)
     codes = torch.from_numpy(np.clip(prod, -448.0, 448.0)).to(torch.float8_e4m3fn)
     return (codes.to(torch.float64).numpy() * scale.astype(np.float64)).reshape(v.shape)
@@ -450,18 +463,20 @@ def _qdq_1x128_torch(v):
 
 def _fp8_layer_numpy(cfg, inp, idx, w, quant_x, quant_h):
     """The layer on dequantised e4m3 weights with numpy fp64 matmuls, each
-    GEMM input optionally passed through the 1x128 quantiser first."""
+    GEMM input optionally passed through the 1x128 quantiser first (with
+    power-of-two scales for the fp8e8m0 weights' data path)."""
+    pow2 = cfg.wdtype == "fp8e8m0"
     deq = lambda q, s: (torch.from_numpy(q).view(torch.float8_e4m3fn).to(torch.float64).numpy()
                         * np.kron(s.astype(np.float64), np.ones((128, 128))))
     x = synth.bf16_to_f32(inp["x"]).astype(np.float64)
-    xq = _qdq_1x128_torch(x) if quant_x else x
+    xq = _qdq_1x128_torch(x, pow2) if quant_x else x
 
     def ffn(w13, w2, xr):
         a = w13 @ xr
         n = w13.shape[0] // 2
         h = a[:n] / (1.0 + np.exp(-a[:n])) * a[n:]
         if quant_h:
-            h = _qdq_1x128_torch(h[None, :])[0]
+            h = _qdq_1x128_torch(h[None, :], pow2)[0]
         return w2 @ h
 
     ws13, ws2 = deq(inp["ws13"], inp["ws13_s"]), deq(inp["ws2"], inp["ws2_s"])
@@ -475,7 +490,8 @@ def _fp8_layer_numpy(cfg, inp, idx, w, quant_x, quant_h):
     return out
 
 
-def test_fp8_activation_quantised_mode_matches_numpy_expression():
+@pytest.mark.parametrize("wdtype", ["fp8", "fp8e8m0"])
+def test_fp8_activation_quantised_mode_matches_numpy_expression(wdtype):
     """F2 (the oracle with the activations quantised as the fp8 data path
     does): x quantised per 1x128 tile before W13, h = silu(g) * u quantised
     per 1x128 tile after the SwiGLU and before W2 ("深入理解 DeepSeek-V3…",
@@ -485,7 +501,8 @@ def test_fp8_activation_quantised_mode_matches_numpy_expression():
     applied to the W2 output instead of its input -- each sit orders of
     magnitude further away, so an oracle making any of those slips fails."""
     cfg = synth.C5.replace(name="f2-pin", T=10, H=256, E=4, G=2, TG=1, K=2, I=256, Is=128,
-                           rho=2.5)
+                           rho=2.5, wdtype=wdtype)
+    pow2 = wdtype == "fp8e8m0"
     inp = synth.gen_inputs(cfg)
     lg = oracle.logits(inp["x"], cfg.act, inp["gate_w"])
     idx, w, _ = oracle.route_f64(cfg, lg, inp["bias"])
@@ -504,11 +521,11 @@ def test_fp8_activation_quantised_mode_matches_numpy_expression():
         a = w13 @ xr
         n = w13.shape[0] // 2
         h = a[:n] / (1.0 + np.exp(-a[:n])) * a[n:]
-        return _qdq_1x128_torch((w2 @ h)[None, :])[0]
+        return _qdq_1x128_torch((w2 @ h)[None, :], pow2)[0]
 
     deq = lambda q, s: (torch.from_numpy(q).view(torch.float8_e4m3fn).to(torch.float64).numpy()
                         * np.kron(s.astype(np.float64), np.ones((128, 128))))
-    xq = _qdq_1x128_torch(synth.bf16_to_f32(inp["x"]).astype(np.float64))
+    xq = _qdq_1x128_torch(synth.bf16_to_f32(inp["x"]).astype(np.float64), pow2)
     slip = np.stack([ffn_quant_after_w2(deq(inp["ws13"], inp["ws13_s"]),
                                         deq(inp["ws2"], inp["ws2_s"]), xq[t]) +
                      sum(w[t, k] * ffn_quant_after_w2(deq(inp["w13"][idx[t, k]],
@@ -522,8 +539,56 @@ def test_fp8_activation_quantised_mode_matches_numpy_expression():
     y = oracle.ffn(cfg, inp, np.array([0]), np.array([e], np.int32), quant_act=True)[0]
     a = deq(inp["w13"][e], inp["w13_s"][e]) @ xq[0]
     h = a[:cfg.I] / (1.0 + np.exp(-a[:cfg.I])) * a[cfg.I:]
-    y_ref = deq(inp["w2"][e], inp["w2_s"][e]) @ _qdq_1x128_torch(h[None, :])[0]
+    y_ref = deq(inp["w2"][e], inp["w2_s"][e]) @ _qdq_1x128_torch(h[None, :], pow2)[0]
     assert np.linalg.norm(y - y_ref) / np.linalg.norm(y_ref) < 1e-10
+    # the two scale rules give different F2 layers (the mode is honoured)
+    other = cfg.replace(wdtype="fp8" if pow2 else "fp8e8m0")
+    assert rel(oracle.layer(other, inp, idx, w, quant_act=True), got) > 1e-4
+
+
+def test_quant_rows_pow2_definition():
+    """Power-of-two 1x128 scales: every scale is a power of two, the
+    smallest one with scale >= max|v| / 448 (so max|code| lies in (224, 448]),
+    codes are torch's e4m3 of v / scale (exact division), all-zero tiles get
+    scale 1 and zero codes; at max|v| = 448 * 2^k exactly the scale is 2^k,
+    one float ulp above it is 2^(k+1)."""
+    rng = np.random.default_rng(5)
+    v = (rng.standard_normal((6, 512)) * np.exp(rng.uniform(-12, 4, (6, 1)))).astype(np.float32)
+    v[2, 128:256] = 0.0
+    v[3, 0:128] *= 0.0
+    v[3, 0] = 448.0 * 2.0 ** -5                       # max exactly 448 * 2^-5
+    v[4, 256:384] = np.float32(0.5) * v[4, 256:384] / np.abs(v[4, 256:384]).max()
+    v[4, 300] = np.nextafter(np.float32(448.0 * 2.0 ** -9), np.float32(1.0))  # one ulp above
+    q, s = oracle.quant_rows(v, pow2=True)
+    m, e = np.frexp(s.astype(np.float64))
+    assert np.all(m == 0.5), "scales are powers of two"
+    t = v.reshape(6, 4, 128).astype(np.float64)
+    a = np.abs(t).max(axis=-1)
+    nz = a > 0
+    assert np.all(s[~nz] == 1.0) and np.all(q.reshape(6, 4, 128)[~nz] == 0)
+    assert np.all(s[nz] >= a[nz] / 448.0) and np.all(s[nz] / 2 < a[nz] / 448.0)
+    assert s[3, 0] == 2.0 ** -5 and s[4, 2] == 2.0 ** -8
+    ref = torch.from_numpy((t / s[..., None].astype(np.float64)).astype(np.float32))
+    ref = ref.to(torch.float8_e4m3fn).view(torch.uint8).numpy().reshape(6, 512)
+    np.testing.assert_array_equal(q, ref)
+    codes = np.vectorize(oracle.e4m3_decode)(q).reshape(6, 4, 128)
+    peak = np.abs(codes).max(axis=-1)
+    assert np.all(peak[nz] > 224.0 - 1e-9) and np.all(peak[nz] <= 448.0)
+
+
+def test_generator_pow2_e4m3_weights():
+    """fp8e8m0 weights: block scales are powers of two (the smallest not
+    below the block's max |w| / 448) and dequantise to the normal draws
+    within an e4m3 rounding step."""
+    q, s = synth.normal_e4m3_blocks(256, 384, 0, synth.T_TEST, 12, 0.05, pow2=True)
+    v = synth.normal_f32(256 * 384, 0, synth.T_TEST, 12, 0.05).reshape(256, 384)
+    m, _ = np.frexp(s.astype(np.float64))
+    assert np.all(m == 0.5)
+    a = np.abs(v.reshape(2, 128, 3, 128)).max(axis=(1, 3)).astype(np.float64)
+    assert np.all(s >= a / 448.0) and np.all(s / 2 < a / 448.0)
+    deq = (torch.from_numpy(q).view(torch.float8_e4m3fn).to(torch.float64).numpy() *
+           np.kron(s, np.ones((128, 128))))
+    np.testing.assert_allclose(deq, v, rtol=2 ** -4, atol=float(s.max()) * 2 ** -9)
 
 
 # ---------------------------------------------------------------- per-row FFN and the combine step
