@@ -40,6 +40,7 @@ KERNEL_SOURCES = {
     "grouped_gemm_bf16_packed_few": ("ffn_bf16_packed.hip", "moe_internal.hpp"),
     "grouped_gemm_bf16_packed_wide": ("ffn_bf16_packed.hip", "moe_internal.hpp"),
     "grouped_gemm_fp8_packed": ("ffn_fp8_packed.hip", "moe_internal.hpp"),
+    "grouped_gemm_fp8_mx": ("ffn_fp8_mx.hip", "moe_internal.hpp"),
     "grouped_gemm_bf16": ("ffn_bf16.hip", "moe_internal.hpp"),
     "grouped_gemm_fp8": ("ffn_fp8.hip", "moe_internal.hpp"),
     "gate_logits_bf16_kernel": ("gate.hip", "gate_split.hpp", "moe_internal.hpp"),
@@ -82,17 +83,18 @@ def kernel_work(kernel, cfg, active):
     once; None for kernels without a model here."""
     T, H, E, K, I, Is = cfg.T, cfg.H, cfg.E, cfg.K, cfg.I, cfg.Is
     N = T * K
-    wb = {"fp8": 1, "bf16": 2, "f32": 4}[cfg.wdtype]
+    fp8 = cfg.wdtype in ("fp8", "fp8e8m0")
+    wb = 1 if fp8 else {"bf16": 2, "f32": 4}[cfg.wdtype]
     ab = 2 if cfg.act == "bf16" else 4
-    hb = 1 if cfg.wdtype == "fp8" else ab       # h is kept in e4m3 on the fp8 path
-    scale = (lambda r, c: (r // 128) * (c // 128) * 4) if cfg.wdtype == "fp8" else (lambda r, c: 0)
-    hsc = ((N * I + T * Is) // 128) * 4 if cfg.wdtype == "fp8" else 0
+    hb = 1 if fp8 else ab       # h is kept in e4m3 on the fp8 path
+    scale = (lambda r, c: (r // 128) * (c // 128) * 4) if fp8 else (lambda r, c: 0)
+    hsc = ((N * I + T * Is) // 128) * 4 if fp8 else 0
     base = kernel.split("<")[0]
     gate_up = "<true" in kernel
     if base.startswith("grouped_gemm"):
         if gate_up:
             w = active * (2 * I * H * wb + scale(2 * I, H)) + (2 * Is * H * wb + scale(2 * Is, H))
-            a_in = T * H * (1 if cfg.wdtype == "fp8" else ab) + (T * (H // 128) * 4 if cfg.wdtype == "fp8" else 0)
+            a_in = T * H * (1 if fp8 else ab) + (T * (H // 128) * 4 if fp8 else 0)
             out = (N * I + T * Is) * hb + hsc
             flop = 2.0 * (N * 2 * I + T * 2 * Is) * H
         else:
@@ -382,11 +384,12 @@ def main():
         del dyb, dysb, dxb, dxsb, dw13, dw2, dws13, dws2, wsl, dout, dxl, dgw
 
     # Algorithmic work (routed rows only; active experts' weights only).
-    wbytes = 1 if cfg.wdtype == "fp8" else (2 if cfg.wdtype == "bf16" else 4)
+    fp8 = cfg.wdtype in ("fp8", "fp8e8m0")
+    wbytes = 1 if fp8 else (2 if cfg.wdtype == "bf16" else 4)
     abytes = 2 if cfg.act == "bf16" else 4
     expert_w = 3 * H * I * wbytes
     shared_w = 3 * H * Is * wbytes
-    mfma_peak = FP8_PEAK_TFLOPS if cfg.wdtype == "fp8" else BF16_PEAK_TFLOPS
+    mfma_peak = FP8_PEAK_TFLOPS if fp8 else BF16_PEAK_TFLOPS
     tok_s = T / (ms * 1e-3)
     if gate_only:
         # x and the gate weight in; routing (idx, w), counts, perm and pos out
@@ -435,7 +438,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"bf16": "bf16", "fp8": "fp8-e4m3", "f32": "f32"}[cfg.wdtype],
+        "dtype": {"bf16": "bf16", "fp8": "fp8-e4m3", "fp8e8m0": "fp8-e4m3 (power-of-two scales)",
+                  "f32": "f32"}[cfg.wdtype],
         "data": "synthetic: seeded N(0,1) tokens, N(0,1/fan_in) weights, gate N(0,1/H), bias "
                 + (f"from {os.path.basename(cfg.bias_file)} (Zipf(1.2) expert loads)"
                    if cfg.bias_file

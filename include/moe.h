@@ -65,7 +65,11 @@ typedef enum {
 typedef enum {
     MOE_F32 = 0,       /* IEEE binary32                                        */
     MOE_BF16 = 1,      /* bfloat16                                             */
-    MOE_FP8_E4M3 = 2   /* OCP e4m3fn + fp32 scale per 128x128 block (weights)  */
+    MOE_FP8_E4M3 = 2,  /* OCP e4m3fn + fp32 scale per 128x128 block (weights)  */
+    MOE_FP8_E4M3_E8M0 = 3  /* OCP e4m3fn + power-of-two fp32 scale per 128x128
+                              block (weights); the activations get
+                              power-of-two 1x128 scales too, and the matrix
+                              cores apply the scales (packed weights only)  */
 } moe_dtype;
 
 /* Layer shape: the MoEGate constructor arguments of the first page's
@@ -89,8 +93,9 @@ typedef struct {
 /* Layer weights.  The gate weight and the selection bias are always fp32.
  * w13 stacks each expert's gate projection (rows 0..I-1) over its up
  * projection (rows I..2I-1).  For MOE_FP8_E4M3 the *_scale arrays hold one
- * fp32 per 128x128 block, row-major over (row block, column block); they are
- * ignored (may be NULL) otherwise.  ws13/ws2 (+scales) may be NULL iff Is == 0.
+ * fp32 per 128x128 block, row-major over (row block, column block); for
+ * MOE_FP8_E4M3_E8M0 every scale must be a power of two (the kernels read its
+ * exponent field); the scales are ignored (may be NULL) otherwise.  ws13/ws2 (+scales) may be NULL iff Is == 0.
  * packed = 0: w13, w2, ws13, ws2 are row-major as shown; packed = 1: all four
  * were rearranged by moe_pack_weight (bf16 or e4m3 weights; scales unchanged). */
 typedef struct {
@@ -157,7 +162,11 @@ moe_status moe_permute(const moe_config* cfg, int64_t T, const int32_t* topk_idx
  * bf16 weights: bf16 MFMA, fp32 accumulation, SiLU*up fused, h kept in bf16.
  * fp8 weights: x and h quantised per 1x128 tile to e4m3 (see
  * moe_quantize_act), e4m3 MFMA, per-128-block scales applied to fp32 partial
- * sums.  f32: fp32 arithmetic throughout. */
+ * sums.  fp8 weights with power-of-two scales (MOE_FP8_E4M3_E8M0, packed):
+ * x and h quantised with power-of-two 1x128 scales, and the scaled e4m3
+ * MFMA applies both scales inside the matrix core over the whole k loop
+ * (its accumulation carries about 13 fraction bits per instruction, below
+ * the bf16 rounding of the outputs).  f32: fp32 arithmetic throughout. */
 moe_status moe_expert_ffn(const moe_config* cfg, int64_t T, const void* x, const int32_t* perm,
                           const int32_t* offsets, const moe_weights* w, void* y, void* y_shared,
                           void* ws, size_t ws_bytes, void* stream);
@@ -236,7 +245,9 @@ moe_status moe_forward_noalloc(const moe_config* cfg, int64_t T, const void* x,
  * each tile of 128 columns: a = max |v|; scale = a / 448 and inv = 448 / a,
  * each computed in double and rounded to fp32 (scale 1, inv 0 for a == 0);
  * code = nearest e4m3fn value of the fp32 product v * inv, ties to even,
- * saturated at +-448.
+ * saturated at +-448.  With weight_dtype MOE_FP8_E4M3_E8M0 the scale is
+ * instead the smallest power of two 2^e >= a / 448 (e in [-126, 127]) and
+ * inv = 2^-e, so v * inv is exact.
  *   xq [rows, H] uint8 out, xs [rows, H/128] fp32 out. */
 moe_status moe_quantize_act(const moe_config* cfg, int64_t rows, const void* x, uint8_t* xq,
                             float* xs, void* stream);

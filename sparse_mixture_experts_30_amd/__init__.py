@@ -7,7 +7,7 @@ expert FFNs).  Decode batches take a three-launch routing schedule, and the
 shared expert can run on a second stream beside the routed ones.  All compute is in the HIP kernels of
 libmoe.so; this package only marshals arguments."""
 from ._lib import (EXPORTS, MOE_BF16, MOE_ERR_DEVICE_CHECK, MOE_ERR_HIP, MOE_ERR_INVALID_ARG,
-                   MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_F32, MOE_FP8_E4M3, MOE_OK,
+                   MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_F32, MOE_FP8_E4M3, MOE_FP8_E4M3_E8M0, MOE_OK,
                    MOE_W13, MOE_W2, MOE_WS13, MOE_WS2, moe_pack_weight, moe_packed_bytes,
                    MoeConfig, MoeError, MoeWeights, SO_PATH, config, lib, moe_bias_update,
                    moe_backward, moe_backward_workspace_bytes, moe_combine, moe_expert_ffn,

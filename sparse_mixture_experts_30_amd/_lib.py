@@ -12,7 +12,7 @@ SO_PATH = os.path.join(HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP, \
     MOE_ERR_DEVICE_CHECK = range(6)
-MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_FP8_E4M3_E8M0 = 0, 1, 2, 3
 
 # Every function declared in include/moe.h.
 EXPORTS = ("moe_workspace_bytes", "moe_gate", "moe_permute", "moe_expert_ffn", "moe_combine",
@@ -124,7 +124,7 @@ def _check(status: int):
 
 
 def config(H, E, G, TG, K, I, Is, rho, act="bf16", wdtype="bf16") -> MoeConfig:
-    dt = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
+    dt = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3, "fp8e8m0": MOE_FP8_E4M3_E8M0}
     return MoeConfig(H, E, G, TG, K, I, Is, float(rho), dt[act], dt[wdtype])
 
 

@@ -17,7 +17,7 @@ OUT = os.path.join(HERE, "libmoe.so")
 BUILD = os.path.join(ROOT, "_build")
 
 SOURCES = ["gate.hip", "permute.hip", "ffn_sched.hip", "ffn_bf16.hip", "ffn_bf16_packed.hip",
-           "ffn_fp8.hip", "ffn_fp8_packed.hip",
+           "ffn_fp8.hip", "ffn_fp8_packed.hip", "ffn_fp8_mx.hip",
            "ffn_f32.hip", "combine.hip", "bias.hip", "ffn_backward.hip", "decode.hip",
            "layer_backward.hip", "moe_api.cpp",
            "timer.cpp"]

@@ -53,7 +53,26 @@ __device__ __forceinline__ void tile_scale(float amax, float& scale, float& inv)
   }
 }
 
+// Power-of-two scale of a tile with maximum amax > 0: the smallest 2^e >=
+// amax / 448 (e in [-126, 127]); amax / 448 in double is a power of two only
+// when it is computed exactly, so its mantissa bits decide.
+__device__ __forceinline__ void tile_scale_pow2(float amax, float& scale, float& inv) {
+  if (amax > 0.0f) {
+    const uint64_t b = (uint64_t)__double_as_longlong((double)amax / 448.0);
+    int e = (int)((b >> 52) & 0x7FF) - 1023;
+    if (b & 0xFFFFFFFFFFFFFull) ++e;
+    e = min(max(e, -126), 127);
+    scale = __uint_as_float((uint32_t)(e + 127) << 23);
+    inv = __uint_as_float((uint32_t)(127 - e) << 23);
+  } else {
+    scale = 1.0f;
+    inv = 0.0f;
+  }
+}
+
 // One 128-wide tile per 16 lanes (8 values each); 256 threads = 16 tiles.
+// kPow2: power-of-two scales (the matrix cores apply them), else a / 448.
+template <bool kPow2>
 __global__ void __launch_bounds__(256)
 quant_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int cols,
                   uint8_t* __restrict__ q, float* __restrict__ sc) {
@@ -80,7 +99,10 @@ quant_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int cols,
   for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
   if (!ok) return;
   float scale, inv;
-  tile_scale(m, scale, inv);
+  if (kPow2)
+    tile_scale_pow2(m, scale, inv);
+  else
+    tile_scale(m, scale, inv);
   uint32_t lo = 0, hi = 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) lo |= f32_to_e4m3(v[j] * inv) << (8 * j);
@@ -347,11 +369,15 @@ unsigned grid8(int64_t max_work) {
 }  // namespace
 
 hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int cols, uint8_t* q, float* sc,
-                             hipStream_t s) {
+                             bool pow2, hipStream_t s) {
   const int64_t tiles = rows * (cols / 128);
-  MOE_TIMED_LAUNCH(s, "quant_rows_kernel",
-    hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)((tiles + 15) / 16)), dim3(256), 0, s, x,
-                       rows, cols, q, sc));
+  const dim3 grid((unsigned)((tiles + 15) / 16));
+  if (pow2)
+    MOE_TIMED_LAUNCH(s, "quant_rows_kernel<pow2>",
+      hipLaunchKernelGGL(quant_rows_kernel<true>, grid, dim3(256), 0, s, x, rows, cols, q, sc));
+  else
+    MOE_TIMED_LAUNCH(s, "quant_rows_kernel",
+      hipLaunchKernelGGL(quant_rows_kernel<false>, grid, dim3(256), 0, s, x, rows, cols, q, sc));
   return hipGetLastError();
 }
 

@@ -32,6 +32,9 @@ moe_status hip_fail(hipError_t e, const char* where) {
 constexpr size_t kAlign = 256;
 inline size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
+// e4m3 weights, with block scales a / 448 or powers of two.
+bool is_fp8(moe_dtype w) { return w == MOE_FP8_E4M3 || w == MOE_FP8_E4M3_E8M0; }
+
 // Shape checks shared by every entry point.
 moe_status check_cfg(const moe_config* c) {
   if (!c) return fail(MOE_ERR_INVALID_ARG, "cfg is NULL");
@@ -53,7 +56,7 @@ moe_status check_cfg(const moe_config* c) {
   const moe_dtype a = c->act_dtype, w = c->weight_dtype;
   if (a != MOE_F32 && a != MOE_BF16)
     return fail(MOE_ERR_INVALID_ARG, "act_dtype must be MOE_F32 or MOE_BF16");
-  if (w != MOE_F32 && w != MOE_BF16 && w != MOE_FP8_E4M3)
+  if (w != MOE_F32 && w != MOE_BF16 && !is_fp8(w))
     return fail(MOE_ERR_INVALID_ARG, "unknown weight_dtype");
   // Valid for the method, not handled by these kernels:
   if (E > 512) return fail(MOE_ERR_UNSUPPORTED, "n_routed_experts > 512");
@@ -61,7 +64,7 @@ moe_status check_cfg(const moe_config* c) {
   if (K > 64) return fail(MOE_ERR_UNSUPPORTED, "num_experts_per_tok > 64");
   if ((a == MOE_F32) != (w == MOE_F32))
     return fail(MOE_ERR_UNSUPPORTED, "fp32 activations need fp32 weights and vice versa");
-  const int mult = (w == MOE_FP8_E4M3) ? 128 : 64;
+  const int mult = is_fp8(w) ? 128 : 64;
   if (H % mult || I % mult || Is % mult)
     return fail(MOE_ERR_UNSUPPORTED, "hidden and FFN sizes must be multiples of %d", mult);
   return MOE_OK;
@@ -89,7 +92,7 @@ Layout layout(const moe_config* c, int64_t T) {
   const int64_t H = c->hidden_size, E = c->n_routed_experts, K = c->num_experts_per_tok,
                 I = c->moe_intermediate_size, Is = c->shared_intermediate_size;
   const int64_t N = T * K;
-  const bool fp8 = c->weight_dtype == MOE_FP8_E4M3;
+  const bool fp8 = is_fp8(c->weight_dtype);
   L.ksplit = c->act_dtype == MOE_BF16 ? moe::gate_ksplit(T, (int)H, (int)E) : 1;
   L.decode = moe::decode_route_ok(T, (int)H, (int)E, (int)K);
   const int64_t nparts = std::max<int64_t>(L.ksplit, L.decode ? moe::decode_ksplit((int)H, (int)E) : 1);
@@ -220,11 +223,24 @@ moe_status run_ffn(const moe_config* c, int64_t T, const void* x, const int32_t*
                 "ffn bf16");
       }
       break;
+    case MOE_FP8_E4M3_E8M0: {
+      uint8_t* xq = at<uint8_t>(ws, L.xq);
+      float* xs = at<float>(ws, L.xs);
+      if (quantize)
+        HIPCALL(moe::launch_quant_rows((const uint16_t*)x, T, c->hidden_size, xq, xs, true, s),
+                "quantise x");
+      HIPCALL(moe::launch_ffn_fp8_mx(d, xq, xs, perm, offsets, wt->w13, wt->w13_scale, wt->w2,
+                                     wt->w2_scale, wt->ws13, wt->ws13_scale, wt->ws2,
+                                     wt->ws2_scale, at<uint8_t>(ws, L.h), at<float>(ws, L.hs),
+                                     tiles, (uint16_t*)y, (uint16_t*)ys, s),
+              "ffn fp8 (power-of-two scales)");
+      break;
+    }
     case MOE_FP8_E4M3: {
       uint8_t* xq = at<uint8_t>(ws, L.xq);
       float* xs = at<float>(ws, L.xs);
       if (quantize)
-        HIPCALL(moe::launch_quant_rows((const uint16_t*)x, T, c->hidden_size, xq, xs, s),
+        HIPCALL(moe::launch_quant_rows((const uint16_t*)x, T, c->hidden_size, xq, xs, false, s),
                 "quantise x");
       if (wt->packed) {
         HIPCALL(moe::launch_ffn_fp8_packed(d, xq, xs, perm, offsets, wt->w13, wt->w13_scale,
@@ -259,7 +275,10 @@ moe_status check_weights(const moe_config* c, const moe_weights* w, bool need_ga
   }
   NONNULL(w->w13);
   NONNULL(w->w2);
-  const bool fp8 = c->weight_dtype == MOE_FP8_E4M3;
+  const bool fp8 = is_fp8(c->weight_dtype);
+  if (c->weight_dtype == MOE_FP8_E4M3_E8M0 && !w->packed)
+    return fail(MOE_ERR_UNSUPPORTED, "e4m3 weights with power-of-two scales must be packed "
+                "(moe_pack_weight)");
   if (fp8) {
     NONNULL(w->w13_scale);
     NONNULL(w->w2_scale);
@@ -323,7 +342,7 @@ moe_status forward_impl(const moe_config* cfg, int64_t T, const void* x, const m
   void* y = at<void>(ws, L.y);
   const bool sh = cfg->shared_intermediate_size > 0;
   void* ys = sh ? at<void>(ws, L.ys) : nullptr;
-  const bool fp8 = cfg->weight_dtype == MOE_FP8_E4M3;
+  const bool fp8 = is_fp8(cfg->weight_dtype);
   // The fp32 expert kernels compute every group in one launch.
   const bool split = s2 && sh && cfg->weight_dtype != MOE_F32;
 
@@ -332,7 +351,8 @@ moe_status forward_impl(const moe_config* cfg, int64_t T, const void* x, const m
     HIPCALL(fork_join_events(&ev), "fork/join events");
     if (fp8)   // x is quantised once, before the fork, for both streams
       HIPCALL(moe::launch_quant_rows((const uint16_t*)x, T, cfg->hidden_size, at<uint8_t>(ws, L.xq),
-                                     at<float>(ws, L.xs), s),
+                                     at<float>(ws, L.xs),
+                                     cfg->weight_dtype == MOE_FP8_E4M3_E8M0, s),
               "quantise x");
     HIPCALL(hipEventRecord(ev->fork, s), "fork");
     HIPCALL(hipStreamWaitEvent(s2, ev->fork, 0), "fork");
@@ -650,6 +670,7 @@ moe_status moe_quantize_act(const moe_config* cfg, int64_t rows, const void* x, 
   NONNULL(xq);
   NONNULL(xs);
   HIPCALL(moe::launch_quant_rows((const uint16_t*)x, rows, cfg->hidden_size, xq, xs,
+                                 cfg->weight_dtype == MOE_FP8_E4M3_E8M0,
                                  (hipStream_t)stream),
           "quantise");
   return MOE_OK;
@@ -659,7 +680,7 @@ size_t moe_packed_bytes(const moe_config* cfg, moe_weight_id which) {
   if (check_cfg(cfg) != MOE_OK || cfg->weight_dtype == MOE_F32) return 0;
   const int H = cfg->hidden_size, I = cfg->moe_intermediate_size,
             Is = cfg->shared_intermediate_size, E = cfg->n_routed_experts;
-  auto bytes = cfg->weight_dtype == MOE_FP8_E4M3 ? moe::packed8_bytes : moe::packed_bytes;
+  auto bytes = is_fp8(cfg->weight_dtype) ? moe::packed8_bytes : moe::packed_bytes;
   switch (which) {
     case MOE_W13: return bytes(true, E, I, H);
     case MOE_W2: return bytes(false, E, H, I);
@@ -685,7 +706,7 @@ moe_status moe_pack_weight(const moe_config* cfg, moe_weight_id which, const voi
   const int64_t experts = (which == MOE_W13 || which == MOE_W2) ? E : 1;
   const int inter = (which == MOE_W13 || which == MOE_W2) ? I : Is;
   const int n = gate_up ? inter : H, kd = gate_up ? H : inter;
-  if (cfg->weight_dtype == MOE_FP8_E4M3)
+  if (is_fp8(cfg->weight_dtype))
     HIPCALL(moe::launch_pack8(gate_up, (const uint8_t*)src, dst, experts, n, kd,
                               (hipStream_t)stream),
             "pack weight");

@@ -115,8 +115,11 @@ inline int ffn_list_tile_rows(int64_t T) { return T <= 32 ? 32 : T <= 64 ? 64 : 
 // Groups of an expert-FFN launch: the routed experts, the shared expert.
 constexpr int kGroupRouted = 1, kGroupShared = 2, kGroupsAll = 3;
 int64_t ffn_max_mtiles(int64_t N, int64_t T, int E, int BM);
+// balanced: a group's M-tiles get equal row counts (+-1) instead of full
+// tiles and a remainder.
 hipError_t launch_build_tiles(const int32_t* offsets, int E, int64_t T, bool has_routed,
-                              bool has_shared, int BM, int32_t* tiles, hipStream_t s);
+                              bool has_shared, int BM, int32_t* tiles, hipStream_t s,
+                              bool balanced = false);
 
 // Work item w (0 <= w < tiles[0] * ntn) of a grouped GEMM with ntn N-tiles:
 // returns the M-tile entry and the N-tile.  Inside a group the N-tile index
@@ -146,7 +149,7 @@ int64_t ffn_grid_mtiles(const FfnDims& d, int BM);
 // The tile list of d's groups with M-tiles of BM rows, unless d says it is
 // ready and no group can exceed one tile (T <= BM).
 hipError_t ffn_build_tiles(const FfnDims& d, const int32_t* offsets, int BM, int32_t* tiles,
-                           hipStream_t s);
+                           hipStream_t s, bool balanced = false);
 hipError_t launch_ffn_bf16(const FfnDims& d, const uint16_t* x, const int32_t* perm,
                            const int32_t* offsets, const uint16_t* w13, const uint16_t* w2,
                            const uint16_t* ws13, const uint16_t* ws2, uint16_t* h,
@@ -180,8 +183,17 @@ hipError_t launch_ffn_fp8_packed(const FfnDims& d, const uint8_t* xq, const floa
                                  const void* ws13p, const float* ws13s, const void* ws2p,
                                  const float* ws2s, uint8_t* hq, float* hs, int32_t* tiles,
                                  uint16_t* y, uint16_t* ys, hipStream_t s);
+// 1x128 e4m3 quantisation of bf16 rows; pow2: power-of-two scales.
 hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int cols, uint8_t* q, float* sc,
-                             hipStream_t s);
+                             bool pow2, hipStream_t s);
+// e4m3 weights (packed) and activations with power-of-two block scales,
+// applied by the matrix cores (ffn_fp8_mx.hip).
+hipError_t launch_ffn_fp8_mx(const FfnDims& d, const uint8_t* xq, const float* xs,
+                             const int32_t* perm, const int32_t* offsets, const void* w13p,
+                             const float* w13s, const void* w2p, const float* w2s,
+                             const void* ws13p, const float* ws13s, const void* ws2p,
+                             const float* ws2s, uint8_t* hq, float* hs, int32_t* tiles,
+                             uint16_t* y, uint16_t* ys, hipStream_t s);
 hipError_t launch_ffn_fp8(const FfnDims& d, const uint8_t* xq, const float* xs,
                           const int32_t* perm, const int32_t* offsets, const uint8_t* w13,
                           const float* w13s, const uint8_t* w2, const float* w2s,

@@ -55,6 +55,7 @@ def _gate(cfg, T=4, ws_bytes=1 << 40, x=FAKE, gw=FAKE, b=FAKE, idx=FAKE, w=FAKE,
     (dict(K=65), moe.MOE_ERR_UNSUPPORTED),
     (dict(H=7000), moe.MOE_ERR_UNSUPPORTED),              # H % 64
     (dict(wdtype="fp8", I=2048 + 64), moe.MOE_ERR_UNSUPPORTED),  # fp8 needs % 128
+    (dict(wdtype="fp8e8m0", H=7168 - 64), moe.MOE_ERR_UNSUPPORTED),
     (dict(act="f32", wdtype="bf16"), moe.MOE_ERR_UNSUPPORTED),
 ])
 def test_config_validation(kw, status):
@@ -102,6 +103,14 @@ def test_argument_validation():
                          None, None, FAKE * 256, 1 << 40, None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_quantize_act(ctypes.byref(_cfg(act="f32", wdtype="f32")), 4, FAKE, FAKE, FAKE,
                               None) == moe.MOE_ERR_UNSUPPORTED
+    # e4m3 with power-of-two scales: packed weights only
+    cfg8p = _cfg(wdtype="fp8e8m0")
+    w8s = moe.weights(gate_w=FAKE, bias=FAKE, w13=FAKE, w13_scale=FAKE, w2=FAKE, w2_scale=FAKE,
+                      ws13=FAKE, ws13_scale=FAKE, ws2=FAKE, ws2_scale=FAKE)
+    assert L.moe_forward(ctypes.byref(cfg8p), 4, FAKE, ctypes.byref(w8s), FAKE, None, None, None,
+                         None, None, FAKE * 256, 1 << 40, None) == moe.MOE_ERR_UNSUPPORTED
+    assert "packed" in moe.moe_last_error()
+    assert moe.moe_packed_bytes(cfg8p, moe.MOE_W13) == moe.moe_packed_bytes(cfg8, moe.MOE_W13) > 0
     assert L.moe_get_device_error(None, 0, None) == moe.MOE_ERR_WORKSPACE
     # bias update: the step must be finite and >= 0; both arrays are required
     for gamma in (-1e-3, float("nan"), float("inf")):

@@ -12,7 +12,8 @@ import synth
 import sparse_mixture_experts_30_amd as moe
 from synth import device as sd
 
-from gpu_util import DEV, check_routing, host, layer_reference, log, rel_l2, run_forward, sync
+from gpu_util import (DEV, FP8_QUANT_TOL, check_routing, host, layer_reference, log, rel_l2,
+                      run_forward, sync)
 
 pytestmark = pytest.mark.gpu
 
@@ -35,6 +36,8 @@ DECODE_CASES = [
     synth.C5.replace(name="dec-fp8-T24-H1024-E32-K4", T=24, H=1024, E=32, G=4, TG=2, K=4, I=256,
                      Is=384, rho=2.5),
     synth.C1.replace(name="dec-f32-T20-H128-E16", T=20),
+    synth.C5.replace(name="dec-fp8e8m0-T24-H1024-E32-K4", T=24, H=1024, E=32, G=4, TG=2, K=4,
+                     I=256, Is=384, rho=2.5, wdtype="fp8e8m0"),
 ]
 
 _inputs = {}
@@ -48,7 +51,7 @@ def inputs(cfg):
 
 
 def _tol(cfg):
-    return {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2}[cfg.wdtype]
+    return {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2, "fp8e8m0": 6e-2}[cfg.wdtype]
 
 
 @pytest.mark.parametrize("packed", [True, False], ids=["packed", "rowmajor"])
@@ -56,6 +59,8 @@ def _tol(cfg):
 def test_decode_forward(cfg, packed):
     if packed and cfg.wdtype == "f32":
         pytest.skip("the packed layout is for bf16 and e4m3 weights")
+    if not packed and cfg.wdtype == "fp8e8m0":
+        pytest.skip("e4m3 weights with power-of-two scales are taken packed only")
     log(f"decode {cfg.name} packed={packed}")
     inp, dev = inputs(cfg)
     if packed:
@@ -71,6 +76,11 @@ def test_decode_forward(cfg, packed):
     rel = rel_l2(r["out"], ref)
     log(f"  out relL2={rel:.3e} (tol {_tol(cfg)}), near-tie tokens={nalt}")
     assert rel <= _tol(cfg)
+    if cfg.wdtype in ("fp8", "fp8e8m0"):
+        ref2, _ = layer_reference(cfg, inp, r["idx"], np.arange(cfg.T), quant_act=True)
+        r2 = rel_l2(r["out"], ref2)
+        log(f"  out vs activation-quantised oracle relL2={r2:.3e}")
+        assert r2 <= FP8_QUANT_TOL
 
 
 def test_decode_schedule_launches():

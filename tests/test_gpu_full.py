@@ -28,7 +28,7 @@ class _Weights:
     @classmethod
     def get(cls, wdtype):
         if wdtype not in cls.cache:
-            cfg = synth.C3 if wdtype == "bf16" else synth.C5
+            cfg = {"bf16": synth.C3, "fp8": synth.C5, "fp8e8m0": synth.C5P}[wdtype]
             t0 = time.time()
             log(f"generating {wdtype} V3 expert weights on the host")
             host_w = {}
@@ -102,12 +102,12 @@ def _full_layer(cfg, n_samples=None):
     ref, nalt = layer_reference(cfg, inp, r["idx"][toks], toks)
     rel = rel_l2(r["out"][toks], ref)
     worst = worst_row_rel(r["out"][toks], ref)
-    tol = 6e-2 if cfg.wdtype == "fp8" else 2e-2
+    tol = 6e-2 if cfg.wdtype in ("fp8", "fp8e8m0") else 2e-2
     log(f"  out relL2={rel:.3e} worst token={worst:.3e} on {len(toks)} tokens (tol {tol}), "
         f"near-tie tokens={nalt}, active experts={int((r['counts'] > 0).sum())}, "
         f"oracle {time.time() - t0:.1f}s")
     assert rel <= tol and worst <= 3 * tol
-    if cfg.wdtype == "fp8":
+    if cfg.wdtype in ("fp8", "fp8e8m0"):
         ref2, _ = layer_reference(cfg, inp, r["idx"][toks], toks, quant_act=True)
         r2 = rel_l2(r["out"][toks], ref2)
         w2 = worst_row_rel(r["out"][toks], ref2)
@@ -144,6 +144,23 @@ def test_layer_v3_fp8_T8192_sampled():
     moe.moe_quantize_act(sd.moe_config(cfg), cfg.T, dev["x"], xq, xs)
     sync()
     q_ref, s_ref = oracle.quant_rows(synth.bf16_to_f32(inp["x"]))
+    np.testing.assert_array_equal(host(xs), s_ref)
+    np.testing.assert_array_equal(host(xq), q_ref)
+
+
+def test_layer_v3_fp8e8m0_T8192_sampled():
+    """The FP8 layer with power-of-two block scales (applied by the matrix
+    cores) at the V3 shape, 8192 tokens: routing on every token, outputs on
+    sampled tokens against the dequantised-weight oracle and the one that
+    quantises x and h with the same power-of-two rule; x's codes and scales
+    bit-exact."""
+    inp, dev, r = _full_layer(synth.C5P, n_samples=48)
+    cfg = synth.C5P
+    xq = torch.empty((cfg.T, cfg.H), dtype=torch.uint8, device=DEV)
+    xs = torch.empty((cfg.T, cfg.H // 128), dtype=torch.float32, device=DEV)
+    moe.moe_quantize_act(sd.moe_config(cfg), cfg.T, dev["x"], xq, xs)
+    sync()
+    q_ref, s_ref = oracle.quant_rows(synth.bf16_to_f32(inp["x"]), pow2=True)
     np.testing.assert_array_equal(host(xs), s_ref)
     np.testing.assert_array_equal(host(xq), q_ref)
 

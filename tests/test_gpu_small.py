@@ -44,12 +44,22 @@ DECODE48 = synth.C3.replace(name="bf16-T48-H512-E16", T=48, H=512, E=16, G=4, TG
 WIDE_RAGGED = synth.C3.replace(name="bf16-T1100-H768-E4-K1-I384-Is256", T=1100, H=768, E=4,
                                G=2, TG=1, K=1, I=384, Is=256, rho=1.3)
 
+# e4m3 with power-of-two block scales (the matrix cores apply them; packed
+# weights only): ragged groups of 256-row tiles, and groups of two 256-row
+# tiles with 3 h-tiles (I = 384), an odd number of 128-k steps (H = 640) and
+# a shared width of one tile
+SMALL_FP8P2 = SMALL_FP8.replace(name="fp8e8m0-T200-H1024-E32", wdtype="fp8e8m0")
+TALL_FP8P2 = synth.C5.replace(name="fp8e8m0-T2100-H640-E8-K2-I384", T=2100, H=640, E=8, G=2,
+                              TG=1, K=2, I=384, Is=128, rho=1.0, wdtype="fp8e8m0")
+
 LAYER_CASES = [C1, SMALL_BF16, RAGGED_BF16, TALL_BF16, K1_NOSHARED, TINY_T1, DECODE48, SMALL_FP8,
-               TALL_FP8, WIDE_RAGGED]
+               TALL_FP8, WIDE_RAGGED, SMALL_FP8P2, TALL_FP8P2]
+# layouts each weight dtype takes: row-major (not for power-of-two fp8) and packed
+ROWMAJOR_OK = ("f32", "bf16", "fp8")
 
 
 def _tol(cfg):
-    return {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2}[cfg.wdtype]
+    return {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2, "fp8e8m0": 6e-2}[cfg.wdtype]
 
 
 _inputs = {}
@@ -129,7 +139,8 @@ def test_permute_flags_out_of_range_index():
 FFN_CASES = [(C1, False), (SMALL_BF16, False), (RAGGED_BF16, False), (TALL_BF16, False),
              (K1_NOSHARED, False), (SMALL_FP8, False), (SMALL_BF16, True), (RAGGED_BF16, True),
              (TALL_BF16, True), (K1_NOSHARED, True), (DECODE48, True), (DECODE48, False),
-             (SMALL_FP8, True), (TALL_FP8, True), (TALL_FP8, False), (WIDE_RAGGED, True)]
+             (SMALL_FP8, True), (TALL_FP8, True), (TALL_FP8, False), (WIDE_RAGGED, True),
+             (SMALL_FP8P2, True), (TALL_FP8P2, True)]
 
 
 def _case_id(c):
@@ -167,7 +178,7 @@ def test_expert_ffn(case):
         rs = rel_l2(host(ys), refs)
         log(f"  y_shared relL2={rs:.3e}")
         assert rs <= _tol(cfg)
-    if cfg.wdtype == "fp8":
+    if cfg.wdtype in ("fp8", "fp8e8m0"):
         # Against the oracle that quantises x and h per 1x128 tile as the
         # kernels do: what is left is accumulation order and the bf16 output,
         # so a mis-scaled tile or a wrong block-scale index shows here.
@@ -212,8 +223,8 @@ def test_combine(act):
         assert r <= (4e-3 if act == "bf16" else 1e-6)
 
 
-FORWARD_CASES = [(c, False) for c in LAYER_CASES] + [(c, True) for c in LAYER_CASES
-                                                     if c.wdtype != "f32"]
+FORWARD_CASES = [(c, False) for c in LAYER_CASES if c.wdtype in ROWMAJOR_OK] + \
+    [(c, True) for c in LAYER_CASES if c.wdtype != "f32"]
 
 
 @pytest.mark.parametrize("case", FORWARD_CASES, ids=_case_id)
@@ -238,22 +249,48 @@ def test_forward(case):
     log(f"  out relL2={rel:.3e} worst token={worst:.3e} (tol {_tol(cfg)}), "
         f"near-tie tokens={nalt}")
     assert rel <= _tol(cfg) and worst <= 3 * _tol(cfg)
-    if cfg.wdtype == "fp8":
+    if cfg.wdtype in ("fp8", "fp8e8m0"):
         ref2, _ = layer_reference(cfg, inp, r["idx"], np.arange(cfg.T), quant_act=True)
         r2, w2 = rel_l2(r["out"], ref2), worst_row_rel(r["out"], ref2)
         log(f"  out vs activation-quantised oracle relL2={r2:.3e} worst token={w2:.3e}")
         assert r2 <= FP8_QUANT_TOL and w2 <= 3 * FP8_QUANT_TOL
 
 
-def test_quantize_act_bit_exact():
-    cfg = SMALL_FP8
+@pytest.mark.parametrize("cfg", [SMALL_FP8, SMALL_FP8P2], ids=lambda c: c.wdtype)
+def test_quantize_act_bit_exact(cfg):
     inp, dev = inputs(cfg)
     T, H = cfg.T, cfg.H
     xq = torch.empty((T, H), dtype=torch.uint8, device=DEV)
     xs = torch.empty((T, H // 128), dtype=torch.float32, device=DEV)
     moe.moe_quantize_act(sd.moe_config(cfg), T, dev["x"], xq, xs)
     sync()
-    q_ref, s_ref = oracle.quant_rows(synth.bf16_to_f32(inp["x"]))
+    q_ref, s_ref = oracle.quant_rows(synth.bf16_to_f32(inp["x"]), pow2=cfg.wdtype == "fp8e8m0")
+    np.testing.assert_array_equal(host(xs), s_ref)
+    np.testing.assert_array_equal(host(xq), q_ref)
+
+
+def test_quantize_act_pow2_edge_values():
+    """Power-of-two scales at their boundaries: rows whose tile maximum is
+    448 * 2^k exactly (scale 2^k), one bf16 step above (2^(k+1)), an
+    all-zero tile (scale 1, zero codes), and tiny and huge magnitudes."""
+    cfg = SMALL_FP8P2.replace(T=6, H=256)
+    x = np.zeros((6, 256), np.float32)
+    rng = np.random.default_rng(3)
+    x[:, :] = rng.standard_normal((6, 256)).astype(np.float32) * 0.5
+    x[3, :128] *= 2.0 ** -100
+    x[4, 128:] *= 2.0 ** 100
+    x = ((x.view(np.uint32) >> 16) << 16).view(np.float32)   # truncated to bf16 values
+    x[0, 7] = 448.0 * 2.0 ** -3                 # exactly 448 * 2^-3
+    x[1, 9] = 448.0 * 2.0 ** -3 + 0.5           # one bf16 step above it (56 -> 56.5)
+    x[2, 128:] = 0.0
+    xb = (x.view(np.uint32) >> 16).astype(np.uint16)   # exact: the values are bf16
+    assert np.array_equal(synth.bf16_to_f32(xb), x)
+    xq = torch.empty((6, 256), dtype=torch.uint8, device=DEV)
+    xs = torch.empty((6, 2), dtype=torch.float32, device=DEV)
+    moe.moe_quantize_act(sd.moe_config(cfg), 6, sd.tensor(xb), xq, xs)
+    sync()
+    q_ref, s_ref = oracle.quant_rows(x, pow2=True)
+    assert s_ref[0, 0] == 2.0 ** -3 and s_ref[1, 0] == 2.0 ** -2 and s_ref[2, 1] == 1.0
     np.testing.assert_array_equal(host(xs), s_ref)
     np.testing.assert_array_equal(host(xq), q_ref)
 
