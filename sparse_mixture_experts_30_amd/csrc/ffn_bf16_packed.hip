@@ -591,7 +591,7 @@ hipError_t launch_ffn_bf16_packed(const FfnDims& d, const uint16_t* x, const int
   const int few = d.T <= 32 ? 1 : d.T <= 64 ? 2 : 0;
   const bool wide = !few && d.N >= (int64_t)kWideMinRows * d.E;
   const int bm1 = few ? 32 * few : wide ? BMW : BM;
-  e = ffn_build_tiles(d, offsets, bm1, tiles, s);
+  e = ffn_build_tiles(d, offsets, bm1, tiles, s, true);
   if (e != hipSuccess) return e;
   const int64_t mt = ffn_grid_mtiles(d, bm1);
   uint16_t* hs = h + d.N * d.I;
@@ -673,7 +673,7 @@ hipError_t launch_ffn_bf16_packed(const FfnDims& d, const uint16_t* x, const int
   else {
     // The down projection uses 128-row tiles, two workgroups per CU (with
     // wide tiles the list is already at 128 rows).
-    if (!wide) e = ffn_build_tiles(d, offsets, BM2, tiles, s);
+    if (!wide) e = ffn_build_tiles(d, offsets, BM2, tiles, s, true);
     if (e != hipSuccess) return e;
     const int64_t mt2 = ffn_grid_mtiles(d, BM2);
     MOE_TIMED_LAUNCH(s, "grouped_gemm_bf16_packed_x2<false>",
