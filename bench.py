@@ -20,6 +20,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -38,10 +39,14 @@ def log(msg):
 
 KERNEL_SOURCES = {
     # kernel name (as the library's timer and rocprofv3 name it) -> sources it is built from
-    "grouped_gemm_bf16_packed": ("ffn_bf16_packed.hip", "moe_internal.hpp"),
-    "grouped_gemm_bf16_packed_x2": ("ffn_bf16_packed.hip", "moe_internal.hpp"),
-    "grouped_gemm_bf16_packed_few": ("ffn_bf16_packed.hip", "moe_internal.hpp"),
-    "grouped_gemm_bf16_packed_wide": ("ffn_bf16_packed.hip", "moe_internal.hpp"),
+    "grouped_gemm_bf16_packed": ("ffn_bf16_packed.hip", "packed_few.hpp", "moe_internal.hpp"),
+    "grouped_gemm_bf16_packed_x2": ("ffn_bf16_packed.hip", "packed_few.hpp", "moe_internal.hpp"),
+    "grouped_gemm_bf16_packed_few": ("ffn_bf16_packed.hip", "packed_few.hpp", "moe_internal.hpp"),
+    "grouped_gemm_bf16_packed_wide": ("ffn_bf16_packed.hip", "packed_few.hpp",
+                                      "moe_internal.hpp"),
+    "decode_layer_kernel": ("decode_layer.hip", "combine_device.hpp", "decode_device.hpp",
+                            "gate_split.hpp", "packed_few.hpp", "permute_device.hpp",
+                            "select_device.hpp", "moe_internal.hpp"),
     "grouped_gemm_fp8_packed": ("ffn_fp8_packed.hip", "moe_internal.hpp"),
     "grouped_gemm_fp8_mx": ("ffn_fp8_mx.hip", "moe_internal.hpp"),
     "grouped_gemm_bf16": ("ffn_bf16.hip", "moe_internal.hpp"),
@@ -108,6 +113,13 @@ def kernel_work(kernel, cfg, active):
         return w + a_in + out, flop
     if base == "gate_logits_bf16_kernel":
         return T * H * ab + E * H * 4 + T * E * 4, 2.0 * T * E * H
+    if base == "decode_layer_kernel":
+        # the whole layer in one launch: the layer's own algorithmic work
+        # (x and the output once, the gate weight and bias, the active
+        # experts' and the shared expert's weights once)
+        w = (active * 3 * H * I + 3 * H * Is) * wb
+        return (w + E * H * 4 + E * 4 + 2 * T * H * ab,
+                T * (6.0 * H * (I * K + Is) + 2.0 * H * E))
     return None
 
 
@@ -126,6 +138,9 @@ def main():
                     help="copy 1 GiB device-to-device 5 times (HBM counter calibration)")
     ap.add_argument("--overlap", action="store_true",
                     help="time moe_forward_overlap (shared expert on a second stream) as the step")
+    ap.add_argument("--fused", action="store_true",
+                    help="time moe_forward_decode_fused (the decode layer in one launch) as the "
+                         "step")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the expert-FFN backward measurement of the bf16 layer workloads")
     ap.add_argument("--row-major", action="store_true",
@@ -194,13 +209,23 @@ def main():
     pos = torch.empty(T * K, dtype=torch.int32, device=dev)
 
     # The layer step: moe_forward on one stream, or (--overlap)
-    # moe_forward_overlap, the shared expert's GEMMs on a second stream.
+    # moe_forward_overlap, the shared expert's GEMMs on a second stream, or
+    # (--fused) moe_forward_decode_fused, a decode batch in one launch.
     shared_stream = torch.cuda.Stream()
-    overlap = args.overlap and not gate_only
+    fused_ok = (not gate_only and T <= 32 and cfg.act == "bf16" and cfg.wdtype == "bf16" and
+                not args.row_major)
+    entries = [] if gate_only else (["moe_forward", "moe_forward_overlap"] +
+                                    (["moe_forward_decode_fused"] if fused_ok else []))
+    if args.fused and not fused_ok:
+        sys.exit("--fused: the one-launch decode layer takes T <= 32, bf16, packed weights")
+    entry = None if gate_only else ("moe_forward_decode_fused" if args.fused else
+                                    "moe_forward_overlap" if args.overlap else "moe_forward")
 
-    def forward(two_streams):
-        if two_streams:
+    def forward(name):
+        if name == "moe_forward_overlap":
             moe.moe_forward_overlap(C, T, d["x"], W, out, ws, shared_stream, stream=stream)
+        elif name == "moe_forward_decode_fused":
+            moe.moe_forward_decode_fused(C, T, d["x"], W, out, ws, stream=stream)
         else:
             moe.moe_forward(C, T, d["x"], W, out, ws, stream=stream)
 
@@ -209,7 +234,7 @@ def main():
             moe.moe_gate(C, T, d["x"], d["gate_w"], d["bias"], lg, idx, wt, ws, stream=stream)
             moe.moe_permute(C, T, idx, counts, offs, perm, pos, ws, stream=stream)
         else:
-            forward(overlap)
+            forward(entry)
 
     for _ in range(args.warmup):
         step()
@@ -263,30 +288,37 @@ def main():
     log(f"[bench] {ms:.3f} ms/step (median, caches flushed; {warm_ms:.3f} back to back); "
         f"dominant kernel {dominant}: {dom_ms:.3f} ms/launch")
 
-    # The other forward path (one stream vs two), not in a profiled run (its
-    # launches would mix into the traced kernels' figures).  Three rounds that
-    # alternate the two paths, K steps each, so that both see the same clocks
-    # and caches; the medians are reported.
-    other = None
+    # The other forward entry points, not in a profiled run (their launches
+    # would mix into the traced kernels' figures).  Three rounds that
+    # alternate every entry point, K steps each, each step after the 1 GiB
+    # scratch write, so that all see the same clocks and cold caches; the
+    # medians of the per-step times are reported.
+    other = []
     if not gate_only and not args.profile_only:
-        times = {True: [], False: []}
-        for _ in range(2):
-            forward(not overlap)
-        for _ in range(3):
-            for path in (overlap, not overlap):
-                torch.cuda.synchronize()
-                ev0.record(stream)
-                for _ in range(args.steps):
-                    forward(path)
-                ev1.record(stream)
-                torch.cuda.synchronize()
-                times[path].append(ev0.elapsed_time(ev1) / args.steps)
-        oms = sorted(times[not overlap])[1]
-        other = {"entry_point": "moe_forward" if overlap else "moe_forward_overlap",
-                 "ms": round(oms, 4), "tokens_per_s": round(T / (oms * 1e-3), 1),
-                 "step_entry_point_ms_same_rounds": round(sorted(times[overlap])[1], 4)}
-        log(f"[bench] {other['entry_point']}: {oms:.3f} ms/step (step entry point "
-            f"{other['step_entry_point_ms_same_rounds']:.3f} ms in the same rounds)")
+        times = {e: [] for e in entries}
+        flush_o = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        for e in entries:
+            for _ in range(2):
+                forward(e)
+        for r in range(3):
+            for e in entries:
+                for i in range(args.steps):
+                    flush_o.fill_((r + i) & 0xFF)
+                    ev0.record(stream)
+                    forward(e)
+                    ev1.record(stream)
+                    torch.cuda.synchronize()
+                    times[e].append(ev0.elapsed_time(ev1))
+        del flush_o
+        med = {e: statistics.median(v) for e, v in times.items()}
+        for e in entries:
+            if e == entry:
+                continue
+            other.append({"entry_point": e, "ms": round(med[e], 4),
+                          "tokens_per_s": round(T / (med[e] * 1e-3), 1),
+                          "step_entry_point_ms_same_rounds": round(med[entry], 4)})
+            log(f"[bench] {e}: {med[e]:.3f} ms/step (step entry point {entry} "
+                f"{med[entry]:.3f} ms in the same rounds)")
 
     # Per-phase timing with the separate entry points (same kernels, same
     # stream), HIP events between phases.
@@ -482,9 +514,8 @@ def main():
         "phases_ms": {p: round(v, 4) for p, v in acc.items()},
         "kernels_ms": {k: round(v, 4) for k, v in sorted(kernels_ms.items())},
         "expert_ffn": ffn,
-        "entry_point": None if gate_only else ("moe_forward_overlap" if overlap
-                                               else "moe_forward"),
-        "other_entry_point": other,
+        "entry_point": entry,
+        "other_entry_points": other,
         "bias_update": bias_update,
         "expert_backward": backward,
         "layer_backward": layer_backward,

@@ -194,6 +194,31 @@ moe_status moe_forward(const moe_config* cfg, int64_t T, const void* x, const mo
                        void* out, float* logits, int32_t* topk_idx, float* topk_w,
                        int32_t* counts, int32_t* perm, void* ws, size_t ws_bytes, void* stream);
 
+/* moe_forward of a decode batch as ONE kernel launch ("深入理解 DeepSeek-V3…",
+ * section 3.1: batches of about 32 tokens, the always-active shared expert
+ * overlapped with the routed path): gate, selection, permutation, the routed
+ * and shared expert GEMMs and the combine run as roles of one grid whose
+ * workgroups signal each other through completion flags in ws, so that the
+ * shared expert streams its weights during the routing and an expert's down
+ * projection starts when its own gate/up projection is done.  Same
+ * arguments, workspace and results as moe_forward, bit for bit.
+ *   Takes 1 <= T <= 32 bf16 tokens with packed bf16 weights; anything else
+ *   returns MOE_ERR_UNSUPPORTED and enqueues nothing.
+ *   Under HIP graph capture it enqueues two launches: a one-thread kernel
+ *   that advances a call counter kept in ws, then the layer, so that every
+ *   replay uses fresh completion flags.
+ *   Every wait inside the kernel is bounded; a wait that gives up sets bit 2
+ *   of the device error flag (moe_get_device_error) and that call's outputs
+ *   are unreliable.  Calls that overlap on one workspace race.
+ *   Measured on MI355X it is slower than moe_forward's multi-launch decode
+ *   schedule at the V3 shape (agent-scope fences and polls under the
+ *   weight stream cost more than the launch gaps they remove), so
+ *   moe_forward does not use it. */
+moe_status moe_forward_decode_fused(const moe_config* cfg, int64_t T, const void* x,
+                                    const moe_weights* w, void* out, float* logits,
+                                    int32_t* topk_idx, float* topk_w, int32_t* counts,
+                                    int32_t* perm, void* ws, size_t ws_bytes, void* stream);
+
 /* moe_forward with the shared expert on a second stream, the single-GPU
  * part of the dual micro-batch overlap ("深入理解 DeepSeek-V3…", section 3.1):
  * the always-active shared expert ("从 1024 块 GPU 到 558 万美元：拆解 DeepSeek-V3
@@ -369,7 +394,8 @@ moe_status moe_pack_weight(const moe_config* cfg, moe_weight_id which, const voi
 /* Reads the device error flag in ws, which each moe_permute / moe_forward
  * call rewrites; synchronises `stream`.  Returns MOE_OK, MOE_ERR_DEVICE_CHECK
  * if the last permutation on this workspace saw an expert index outside
- * [0, E), or MOE_ERR_HIP. */
+ * [0, E) (flag bit 1) or if a completion wait inside moe_forward_decode_fused gave up after its bound
+ * (bit 2: the outputs of that call are unreliable), or MOE_ERR_HIP. */
 moe_status moe_get_device_error(void* ws, size_t ws_bytes, void* stream);
 
 /* Kernel timer, for measurement.  While enabled, every kernel launch of the

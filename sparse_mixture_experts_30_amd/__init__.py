@@ -13,7 +13,7 @@ from ._lib import (EXPORTS, MOE_BF16, MOE_ERR_DEVICE_CHECK, MOE_ERR_HIP, MOE_ERR
                    moe_backward, moe_backward_workspace_bytes, moe_combine, moe_expert_ffn,
                    moe_expert_ffn_backward,
                    moe_expert_ffn_backward_workspace_bytes, moe_forward, moe_forward_noalloc,
-                   moe_forward_overlap, MOE_NOALLOC_SCRATCH_BYTES,
+                   moe_forward_overlap, moe_forward_decode_fused, MOE_NOALLOC_SCRATCH_BYTES,
                    moe_gate, moe_get_device_error,
                    moe_kernel_timer_enable, moe_kernel_timer_read, moe_last_error,
                    moe_permute, moe_quantize_act, moe_strerror, moe_workspace_bytes, weights)

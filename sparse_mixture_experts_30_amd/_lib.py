@@ -16,7 +16,8 @@ MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_FP8_E4M3_E8M0 = 0, 1, 2, 3
 
 # Every function declared in include/moe.h.
 EXPORTS = ("moe_workspace_bytes", "moe_gate", "moe_permute", "moe_expert_ffn", "moe_combine",
-           "moe_forward", "moe_forward_overlap", "moe_forward_noalloc", "moe_quantize_act", "moe_packed_bytes", "moe_pack_weight",
+           "moe_forward", "moe_forward_overlap", "moe_forward_noalloc", "moe_forward_decode_fused",
+           "moe_quantize_act", "moe_packed_bytes", "moe_pack_weight",
            "moe_get_device_error", "moe_strerror", "moe_last_error", "moe_kernel_timer_enable",
            "moe_kernel_timer_read", "moe_bias_update", "moe_expert_ffn_backward",
            "moe_expert_ffn_backward_workspace_bytes", "moe_backward",
@@ -69,6 +70,8 @@ def lib():
             "moe_forward_overlap": (ctypes.c_int, [cfgp, i64, vp, wp, vp, vp, vp, vp, vp, vp, vp, sz,
                                                    vp, vp]),
             "moe_forward_noalloc": (ctypes.c_int, [cfgp, i64, vp, wp, vp, vp, vp, vp, vp, vp, vp]),
+            "moe_forward_decode_fused": (ctypes.c_int, [cfgp, i64, vp, wp, vp, vp, vp, vp, vp, vp,
+                                                        vp, sz, vp]),
             "moe_quantize_act": (ctypes.c_int, [cfgp, i64, vp, vp, vp, vp]),
             "moe_bias_update": (ctypes.c_int, [cfgp, vp, ctypes.c_float, vp, vp]),
             "moe_expert_ffn_backward_workspace_bytes": (sz, [cfgp, i64]),
@@ -166,6 +169,16 @@ def moe_forward(cfg, T, x, w: MoeWeights, out, ws, logits=None, topk_idx=None, t
     _check(lib().moe_forward(ctypes.byref(cfg), T, _ptr(x), ctypes.byref(w), _ptr(out),
                              _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _ptr(counts), _ptr(perm),
                              _ptr(ws), _nbytes(ws) if ws is not None else 0, _stream(stream)))
+
+
+def moe_forward_decode_fused(cfg, T, x, w: MoeWeights, out, ws, logits=None, topk_idx=None,
+                             topk_w=None, counts=None, perm=None, stream=None):
+    """moe_forward of a decode batch (T <= 32, bf16, packed) as one launch."""
+    _check(lib().moe_forward_decode_fused(ctypes.byref(cfg), T, _ptr(x), ctypes.byref(w),
+                                          _ptr(out), _ptr(logits), _ptr(topk_idx),
+                                          _ptr(topk_w), _ptr(counts), _ptr(perm), _ptr(ws),
+                                          _nbytes(ws) if ws is not None else 0,
+                                          _stream(stream)))
 
 
 # Bytes of the static workspace of moe_forward_noalloc (include/moe.h).

@@ -27,7 +27,7 @@
 // The batch path needs five launches for the same steps (weight split, gate
 // GEMM with a deep k split, selection, permutation, tile list).
 #include "moe_internal.hpp"
-#include "gate_split.hpp"
+#include "decode_device.hpp"
 #include "permute_device.hpp"
 
 #include <algorithm>
@@ -61,7 +61,6 @@ __device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
   v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
 }
 
-constexpr int DG_MAXK = 896;   // k range per workgroup (bounds its LDS)
 
 // part[ks][t][e] = sum over k in [ks * kchunk, min(H, (ks + 1) * kchunk)) of
 // x[t][k] * wg[e][k] (fp32 activations).  Thread (el, t): el = tid / 32
@@ -140,76 +139,15 @@ gate_decode_kernel(const XT* __restrict__ x, const float* __restrict__ wg,
   part[((int64_t)ks * T + t) * E + e] = sum;
 }
 
-// bf16 activations: the same partial sums on bf16 MFMA.  Workgroup (eb, ks)
-// takes experts 32 eb .. 32 eb + 31 and the ks-th k range; its four waves
-// split the range in 16-wide k steps.  Per step a lane loads its 8 k of one
-// token row (A operand: token lane % 32) and of one fp32 gate row (B
-// operand: expert 32 eb + lane % 32), splits the weights in registers into
-// their exact bf16 parts and accumulates the three products in fp32; every
-// load of the wave is issued before the first MFMA.  The waves' sums are
-// added in wave order through LDS.  Rows past T and experts past E re-read
-// a valid row and are not stored; k past the range is zero.
-constexpr int DM_STEPS = DG_MAXK / 4 / 16;   // 16-wide k steps per wave, at most
-
+// bf16 activations: the same partial sums on bf16 MFMA (gate_mfma_item,
+// decode_device.hpp).  Workgroup (eb, ks) takes experts 32 eb .. 32 eb + 31
+// and the ks-th k range.
 __global__ void __launch_bounds__(DG_THREADS)
 gate_decode_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ wg,
                         float* __restrict__ part, int T, int H, int E, int kchunk) {
   __shared__ float red[3][16][kWave];   // accumulators of waves 1..3
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lr = lane & 31, lh = lane >> 5;
-  const int eb = blockIdx.x, ks = blockIdx.y;
-  const int k0 = ks * kchunk;
-  const int kn = min(H, k0 + kchunk) - k0;      // a multiple of 8
-  const int nst = (kn + 15) / 16;
-  const int per = (nst + 3) / 4;                // <= DM_STEPS (kchunk <= DG_MAXK)
-  const int s0 = wave * per, s1 = min(nst, s0 + per);
-  const int t = min(lr, T - 1);
-  const int e = min(eb * 32 + lr, E - 1);
-  const uint16_t* xr = x + (int64_t)t * H + k0 + 8 * lh;
-  const float* wr = wg + (int64_t)e * H + k0 + 8 * lh;
-
-  u32x4 xa[DM_STEPS], wa[DM_STEPS], wb[DM_STEPS];
-#pragma unroll
-  for (int j = 0; j < DM_STEPS; ++j) {
-    const int st = s0 + j;
-    if (st < s1 && st * 16 + 8 * lh < kn) {
-      xa[j] = *reinterpret_cast<const u32x4*>(xr + st * 16);
-      wa[j] = *reinterpret_cast<const u32x4*>(wr + st * 16);
-      wb[j] = *reinterpret_cast<const u32x4*>(wr + st * 16 + 4);
-    } else {
-      xa[j] = wa[j] = wb[j] = (u32x4){0u, 0u, 0u, 0u};
-    }
-  }
-  f32x16 acc;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
-#pragma unroll
-  for (int j = 0; j < DM_STEPS; ++j) {
-    if (s0 + j < s1) {   // uniform over the wave
-      u32x4 h, m, l;
-      split3(wa[j], wb[j], h, m, l);
-      const bf16x8 a = as_bf16x8(xa[j]);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(h), acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(m), acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(l), acc, 0, 0, 0);
-    }
-  }
-  if (wave > 0) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) red[wave - 1][i][lane] = acc[i];
-  }
-  __syncthreads();
-  if (wave != 0) return;   // after the only barrier
-  // C layout: lane holds expert column lr and token rows 8 (i / 4) + 4 lh + i % 4.
-  const int ec = eb * 32 + lr;
-  if (ec >= E) return;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int tr = 8 * (i >> 2) + 4 * lh + (i & 3);
-    const float v = ((acc[i] + red[0][i][lane]) + red[1][i][lane]) + red[2][i][lane];
-    if (tr < T) part[((int64_t)ks * T + tr) * E + ec] = v;
-  }
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  gate_mfma_item(x, wg, part, T, H, E, kchunk, blockIdx.x, blockIdx.y, wave, true, red);
 }
 
 // One workgroup: the permutation of the T*K chosen ids, and (when tiles is

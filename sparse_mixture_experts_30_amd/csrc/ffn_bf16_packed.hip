@@ -18,6 +18,7 @@
 // kernel, with the same k assignment (lane half lh holds k in
 // [32 lh, 32 lh + 32)).
 #include "moe_internal.hpp"
+#include "packed_few.hpp"
 
 #include <algorithm>
 
@@ -26,7 +27,7 @@ namespace moe {
 namespace {
 
 constexpr int BM = 256;    // max rows per tile
-constexpr int BK = 64;     // k per step
+constexpr int BK = kPackedBK;  // k per step
 constexpr int NT = 256;    // threads
 // Pipeline depth D in steps: the weights of steps t .. t+D-1 and the
 // activation rows of steps t+1 .. t+D sit in registers (or are in flight)
@@ -34,7 +35,7 @@ constexpr int NT = 256;    // threads
 // step of lead already covers the load latency for every tile height (a
 // deeper pipeline only costs registers), so D = 2 throughout.
 constexpr int depth_for(int) { return 2; }
-constexpr int FRAG = 2048; // 16-byte fragments per packed block (32 KiB)
+constexpr int FRAG = kPackedFrag; // 16-byte fragments per packed block (32 KiB)
 constexpr size_t kLdsP = (size_t)2 * BM * 8 * sizeof(u32x4);   // 64 KiB
 
 // ---------------------------------------------------------------- packing
@@ -71,25 +72,6 @@ pack_kernel(const uint16_t* __restrict__ src, u32x4* __restrict__ dst, int64_t n
 }
 
 // ---------------------------------------------------------------- GEMM
-
-struct PackedArgs {
-  const int32_t* tiles;
-  int ntn;                      // N-tiles per M-tile (max over groups)
-  int E, K;
-  const uint16_t* a_r;
-  const uint16_t* a_s;
-  int64_t lda_r, lda_s;
-  const int32_t* perm;          // GEMM1: routed A row = perm[j] / K
-  int kdim_r, kdim_s;
-  const u32x4* b_r;             // packed routed weights
-  int nt_r;                     // output tiles per routed expert
-  const u32x4* b_s;             // packed shared weights
-  int nt_s;
-  int ncol_r, ncol_s;
-  uint16_t* c_r;
-  uint16_t* c_s;
-  int64_t ldc_r, ldc_s;
-};
 
 __device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ ((r ^ (r >> 3)) & 7)); }
 
@@ -418,19 +400,11 @@ __global__ void __launch_bounds__(NT, 1) grouped_gemm_bf16_packed_wide(PackedArg
   }
 }
 
-// Few-row variant (every group has at most 32 * NRB rows, NRB <= 2: decode
-// batches).  The activation rows are few and L2-resident, so each wave
-// loads its own MFMA operands for them straight from global memory: waves
-// are independent (no LDS, no barrier), use few registers, and two waves
-// share each SIMD, which keeps more weight loads in flight.
-//
-// Workgroups are single waves: a tile's four waves are independent, and
-// with one wave per workgroup the few active tiles of a small batch spread
-// over all CUs instead of queueing behind each other.
-constexpr int kFewSlots = 4;   // waves (packed wave slots) per tile
 // Wave slots of the GPU at four waves per SIMD (256 CUs x 4 SIMDs x 4).
 constexpr int64_t kFewDenseSlots = 4096;
 
+// Few-row variant (decode batches): one wave per workgroup, each running one
+// wave slot of one tile (few_tile); see packed_few.hpp.
 // WPE = 2: two waves per SIMD with three steps in flight for single-block
 // tiles.  WPE = 4 (the down projection of a batch whose waves all fit in
 // one round at four per SIMD): two steps in flight, so that every wave is
@@ -449,94 +423,8 @@ grouped_gemm_bf16_packed_few(PackedArgs p) {
   int ntile;
   const int32_t* ent = decode_work(p.tiles, w, p.ntn, ntile);
   const int g = ent[0], row0 = ent[1], nrows = ent[2];
-  const bool sh = (g == p.E);
-  if (ntile >= (sh ? p.nt_s : p.nt_r)) return;
-  const int lane = threadIdx.x & 63;
-  const int lr = lane & 31, lh = lane >> 5;
-  const int ncol = sh ? p.ncol_s : p.ncol_r;
-  const int n0 = ntile * (kGateUp ? 128 : 256);
-  const int kdim = sh ? p.kdim_s : p.kdim_r;
-  const int nsteps = kdim / BK;
-  const int last = nsteps - 1;
-  const uint16_t* A = sh ? p.a_s : p.a_r;
-  const int64_t lda = sh ? p.lda_s : p.lda_r;
-  const u32x4* bw = (sh ? p.b_s : p.b_r + (int64_t)g * p.nt_r * nsteps * FRAG) +
-                    (int64_t)ntile * nsteps * FRAG + wave * 512 + lane;
-  // This lane's activation rows: tile rows r * 32 + lane % 32 (rows past
-  // the end re-read the first row; their outputs are never stored); k from
-  // 32 * lane_half, as in the weight fragments.
-  const uint16_t* ap[NRB];
-#pragma unroll
-  for (int r = 0; r < NRB; ++r) {
-    const int row = r * 32 + lr;
-    const int rr = row < nrows ? row : 0;
-    const int a = (!sh && kGateUp) ? p.perm[row0 + rr] / p.K : row0 + rr;
-    ap[r] = A + (int64_t)a * lda + lh * 32;
-  }
-  u32x4 rb[D][8], ra[D][NRB][4];
-  auto load = [&](int slot, int step) {
-    const int st = min(step, last);
-    const u32x4* src = bw + (int64_t)st * FRAG;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) rb[slot][i] = __builtin_nontemporal_load(src + i * 64);
-#pragma unroll
-    for (int r = 0; r < NRB; ++r)
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        ra[slot][r][kk] = *reinterpret_cast<const u32x4*>(ap[r] + st * BK + kk * 8);
-  };
-  f32x16 acc[NRB][2];
-#pragma unroll
-  for (int r = 0; r < NRB; ++r)
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[r][c][i] = 0.0f;
-#pragma unroll
-  for (int s = 0; s < D; ++s) load(s, s);
-  for (int s = 0; s < nsteps; s += D) {
-#pragma unroll
-    for (int u = 0; u < D; ++u) {
-      if (s + u < nsteps) {
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const bf16x8 b0 = as_bf16x8(rb[u][kk]);
-          const bf16x8 b1 = as_bf16x8(rb[u][4 + kk]);
-#pragma unroll
-          for (int r = 0; r < NRB; ++r) {
-            const bf16x8 a = as_bf16x8(ra[u][r][kk]);
-            acc[r][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc[r][0], 0, 0, 0);
-            acc[r][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc[r][1], 0, 0, 0);
-          }
-        }
-      }
-      load(u, s + u + D);
-    }
-  }
-  uint16_t* C = sh ? p.c_s : p.c_r;
-  const int64_t ldc = sh ? p.ldc_s : p.ldc_r;
-#pragma unroll
-  for (int r = 0; r < NRB; ++r) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = r * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
-      if (row >= nrows) continue;
-      uint16_t* crow = C + (int64_t)(row0 + row) * ldc;
-      if (kGateUp) {
-        const int col = n0 + wave * 32 + lr;
-        if (col < ncol) {
-          const float gv = acc[r][0][i], uv = acc[r][1][i];
-          crow[col] = (uint16_t)f32_to_bf16_bits(gv / (1.0f + __expf(-gv)) * uv);
-        }
-      } else {
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-          const int col = n0 + wave * 64 + cb * 32 + lr;
-          if (col < ncol) crow[col] = (uint16_t)f32_to_bf16_bits(acc[r][cb][i]);
-        }
-      }
-    }
-  }
+  if (ntile >= (g == p.E ? p.nt_s : p.nt_r)) return;
+  few_tile<kGateUp, NRB, D>(p, g, row0, nrows, ntile, wave);
 }
 
 hipError_t set_attrs_packed() {

@@ -203,6 +203,7 @@ gate_logits_f32_kernel(const float* __restrict__ x, const float* __restrict__ wg
 }
 
 constexpr int SEL_WAVES = 4;
+static_assert(SEL_WAVES == SEL_PARTS, "a deep-split token's parts are summed by the waves");
 
 // One wavefront selects for one token; lane l holds experts e = l + 64 v.
 // SW = 1: a workgroup holds SEL_WAVES tokens.  SW = SEL_WAVES (deep k
@@ -221,39 +222,10 @@ select_kernel(const float* __restrict__ part, int ksplit, const float* __restric
   const int64_t t = SW == 1 ? (int64_t)blockIdx.x * SEL_WAVES + wave : (int64_t)blockIdx.x;
   if (t >= T) return;   // uniform over the workgroup when SW > 1
   const int V = (E + 63) / 64;
-  const int s_begin = SW == 1 ? 0 : (int)((int64_t)ksplit * wave / SW);
-  const int s_end = SW == 1 ? ksplit : (int)((int64_t)ksplit * (wave + 1) / SW);
-
-  // Logits: the k-split partial sums of [s_begin, s_end) added in split
-  // order.  The loads of a batch of splits (for all of this lane's experts)
-  // are issued together and then added in order, so a deep split costs few
-  // memory round trips.
+  const int s_begin = SW == 1 ? 0 : sel_part_begin(ksplit, wave);
+  const int s_end = SW == 1 ? ksplit : sel_part_begin(ksplit, wave + 1);
   float lgs[SEL_MAXV];
-  {
-    constexpr int SB = 4;    // splits per batch
-    const int64_t stride = T * E;
-#pragma unroll
-    for (int v = 0; v < SEL_MAXV; ++v) {
-      const int e = lane + 64 * v;
-      lgs[v] = (v < V && e < E) ? part[(int64_t)s_begin * stride + t * E + e] : 0.0f;
-    }
-    for (int s0 = s_begin + 1; s0 < s_end; s0 += SB) {
-      float pv[SB][SEL_MAXV];
-#pragma unroll
-      for (int j = 0; j < SB; ++j)
-#pragma unroll
-        for (int v = 0; v < SEL_MAXV; ++v) {
-          const int e = lane + 64 * v;
-          pv[j][v] = (s0 + j < s_end && v < V && e < E)
-                         ? part[(int64_t)(s0 + j) * stride + t * E + e] : 0.0f;
-        }
-#pragma unroll
-      for (int j = 0; j < SB; ++j)
-#pragma unroll
-        for (int v = 0; v < SEL_MAXV; ++v)
-          if (s0 + j < s_end) lgs[v] += pv[j][v];
-    }
-  }
+  sum_splits(part, T * E, t, E, lane, s_begin, s_end, lgs);
   if (SW > 1) {
     // quarters added in wave order; wave 0 goes on alone (no workgroup
     // barrier below this point)
@@ -334,7 +306,7 @@ hipError_t launch_gate_logits(const void* x, bool x_bf16, const float* gate_w, v
 hipError_t launch_select(const float* partials, int ksplit, const float* bias, float* logits_out,
                          int32_t* idx, float* w, int64_t T, int E, int G, int TG, int K,
                          float rho, hipStream_t s) {
-  if (ksplit >= 16) {
+  if (ksplit >= SEL_DEEP) {
     MOE_TIMED_LAUNCH(s, "select_kernel",
       hipLaunchKernelGGL(select_kernel<SEL_WAVES>, dim3((unsigned)T), dim3(SEL_WAVES * 64), 0, s,
                          partials, ksplit, bias, logits_out, idx, w, T, E, G, TG, K, rho));

@@ -82,7 +82,7 @@ size_t act_bytes(const moe_config* c) { return c->act_dtype == MOE_BF16 ? 2 : 4;
 // Workspace segments (byte offsets, 256-aligned).
 struct Layout {
   size_t err, part, gsplit, idx, w, counts, offsets, perm, pos, hist, tiles, tiles2, h, hs, xq,
-      xs, y, ys, total;
+      xs, y, ys, flags, total;
   int ksplit;
   bool decode;   // decode routing (gate, selection, permutation, tile list in three launches)
 };
@@ -127,6 +127,10 @@ Layout layout(const moe_config* c, int64_t T) {
   }
   L.y = take((size_t)N * H * act_bytes(c));
   L.ys = take((size_t)T * H * act_bytes(c));
+  // completion flags of the one-launch decode layer (bf16)
+  L.flags = (L.decode && c->act_dtype == MOE_BF16 && c->weight_dtype == MOE_BF16)
+                ? take(moe::decode_layer_flags_bytes((int)H, (int)E, (int)K, (int)I, (int)Is))
+                : o;
   L.total = o;
   return L;
 }
@@ -323,7 +327,7 @@ hipError_t fork_join_events(ForkJoin** out) {
 moe_status forward_impl(const moe_config* cfg, int64_t T, const void* x, const moe_weights* w,
                         void* out, float* logits, int32_t* topk_idx, float* topk_w,
                         int32_t* counts, int32_t* perm, void* ws, size_t ws_bytes,
-                        hipStream_t s, hipStream_t s2) {
+                        hipStream_t s, hipStream_t s2, bool one_launch = false) {
   CHECK(check_cfg(cfg));
   CHECK(check_T(T, cfg));
   if (T == 0) return MOE_OK;
@@ -332,6 +336,14 @@ moe_status forward_impl(const moe_config* cfg, int64_t T, const void* x, const m
   CHECK(check_weights(cfg, w, true));
   const Layout L = layout(cfg, T);
   CHECK(check_ws(ws, ws_bytes, L));
+  if (one_launch &&
+      !(L.decode && cfg->act_dtype == MOE_BF16 && cfg->weight_dtype == MOE_BF16 && w->packed &&
+        moe::decode_layer_ok(T, cfg->hidden_size, cfg->n_routed_experts,
+                             cfg->num_experts_per_tok, cfg->moe_intermediate_size,
+                             cfg->shared_intermediate_size)))
+    return fail(MOE_ERR_UNSUPPORTED,
+                "the one-launch decode layer takes 1 <= T <= %d bf16 tokens and packed bf16 "
+                "weights", moe::kDecodeMaxT);
   int32_t* idx = topk_idx ? topk_idx : at<int32_t>(ws, L.idx);
   float* wt = topk_w ? topk_w : at<float>(ws, L.w);
   int32_t* cnt = counts ? counts : at<int32_t>(ws, L.counts);
@@ -361,6 +373,18 @@ moe_status forward_impl(const moe_config* cfg, int64_t T, const void* x, const m
     HIPCALL(hipEventRecord(ev->join, s2), "join");
   }
   const int groups = split ? moe::kGroupRouted : moe::kGroupsAll;
+  if (one_launch) {
+    HIPCALL(moe::launch_decode_layer(
+                (const uint16_t*)x, w->gate_w, w->bias, w->w13, w->w2, w->ws13, w->ws2, T,
+                cfg->hidden_size, cfg->n_routed_experts, cfg->n_group, cfg->topk_group,
+                cfg->num_experts_per_tok, cfg->moe_intermediate_size,
+                cfg->shared_intermediate_size, cfg->routed_scaling_factor,
+                at<float>(ws, L.part), logits, idx, wt, cnt, offs, pm, pos,
+                at<int32_t>(ws, L.err), tiles, at<uint16_t>(ws, L.h), (uint16_t*)y,
+                (uint16_t*)ys, (uint16_t*)out, at<void>(ws, L.flags), s),
+            "decode layer");
+    return MOE_OK;
+  }
   if (L.decode) {
     HIPCALL(moe::launch_decode_route(x, cfg->act_dtype == MOE_BF16, w->gate_w, w->bias,
                                      at<float>(ws, L.part), logits, idx, wt, T, cfg->hidden_size,
@@ -512,6 +536,14 @@ moe_status moe_forward_noalloc(const moe_config* cfg, int64_t T, const void* x,
   HIPCALL(scratch_address(&ws), "static scratch address");
   return forward_impl(cfg, T, x, w, out, logits, topk_idx, topk_w, counts, perm, ws,
                       kScratchBytes, (hipStream_t)stream, nullptr);
+}
+
+moe_status moe_forward_decode_fused(const moe_config* cfg, int64_t T, const void* x,
+                                    const moe_weights* w, void* out, float* logits,
+                                    int32_t* topk_idx, float* topk_w, int32_t* counts,
+                                    int32_t* perm, void* ws, size_t ws_bytes, void* stream) {
+  return forward_impl(cfg, T, x, w, out, logits, topk_idx, topk_w, counts, perm, ws, ws_bytes,
+                      (hipStream_t)stream, nullptr, true);
 }
 
 moe_status moe_forward_overlap(const moe_config* cfg, int64_t T, const void* x,
@@ -724,6 +756,9 @@ moe_status moe_get_device_error(void* ws, size_t ws_bytes, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   HIPCALL(hipMemcpyAsync(&flag, ws, sizeof(flag), hipMemcpyDeviceToHost, s), "read error flag");
   HIPCALL(hipStreamSynchronize(s), "synchronise");
+  if (flag & 2)
+    return fail(MOE_ERR_DEVICE_CHECK,
+                "a completion wait of the one-launch decode layer timed out: outputs unreliable");
   if (flag) return fail(MOE_ERR_DEVICE_CHECK, "an expert index was outside [0, E)");
   return MOE_OK;
 }

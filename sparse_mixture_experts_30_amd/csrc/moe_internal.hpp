@@ -102,6 +102,20 @@ hipError_t launch_decode_route(const void* x, bool x_bf16, const float* gate_w,
                                int32_t* perm, int32_t* pos, int32_t* err, int32_t* tiles,
                                bool has_routed, bool has_shared, hipStream_t s);
 
+// The whole decode layer in one launch (decode_layer.hip): bf16 tokens and
+// packed bf16 weights, 1 <= T <= kDecodeMaxT; flags: a workspace region of
+// decode_layer_flags_bytes (no initial contents needed).
+bool decode_layer_ok(int64_t T, int H, int E, int K, int I, int Is);
+size_t decode_layer_flags_bytes(int H, int E, int K, int I, int Is);
+hipError_t launch_decode_layer(const uint16_t* x, const float* gate_w, const float* bias,
+                               const void* w13p, const void* w2p, const void* ws13p,
+                               const void* ws2p, int64_t T, int H, int E, int G, int TG, int K,
+                               int I, int Is, float rho, float* partials, float* logits,
+                               int32_t* idx, float* w, int32_t* counts, int32_t* offsets,
+                               int32_t* perm, int32_t* pos, int32_t* err, int32_t* tiles,
+                               uint16_t* h, uint16_t* y, uint16_t* ys, uint16_t* out,
+                               void* flags, hipStream_t s);
+
 int permute_nblk(int64_t N);
 hipError_t launch_permute(const int32_t* idx, int64_t N, int E, int32_t* hist, int32_t* counts,
                           int32_t* offsets, int32_t* perm, int32_t* pos, int32_t* err,

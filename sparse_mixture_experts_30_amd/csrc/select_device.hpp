@@ -12,6 +12,47 @@
 namespace moe {
 
 constexpr int SEL_MAXV = 8;   // E <= 512 = 64 lanes x 8
+constexpr int SEL_SB = 4;     // k splits whose loads are issued together
+constexpr int SEL_DEEP = 16;  // from this many k splits a token's sum is cut in parts
+constexpr int SEL_PARTS = 4;  // ... of contiguous splits, summed by SEL_PARTS waves
+
+// First split of part `q` of SEL_PARTS when a token's ksplit partial sums
+// are cut into contiguous parts (q = SEL_PARTS gives ksplit).
+__device__ __forceinline__ int sel_part_begin(int ksplit, int q) {
+  return (int)((int64_t)ksplit * q / SEL_PARTS);
+}
+
+// Lane l's logits of token t (experts e = l + 64 v): the k-split partial
+// sums of splits [s_begin, s_end) of part ([ksplit][T][E], split stride
+// T * E) added in split order.  The loads of SEL_SB splits (for all of the
+// lane's experts) are issued together and then added in order, so a deep
+// split costs few memory round trips.
+__device__ __forceinline__ void sum_splits(const float* __restrict__ part, int64_t stride,
+                                           int64_t t, int E, int lane, int s_begin, int s_end,
+                                           float (&lgs)[SEL_MAXV]) {
+  const int V = (E + 63) / 64;
+#pragma unroll
+  for (int v = 0; v < SEL_MAXV; ++v) {
+    const int e = lane + 64 * v;
+    lgs[v] = (v < V && e < E) ? part[(int64_t)s_begin * stride + t * E + e] : 0.0f;
+  }
+  for (int s0 = s_begin + 1; s0 < s_end; s0 += SEL_SB) {
+    float pv[SEL_SB][SEL_MAXV];
+#pragma unroll
+    for (int j = 0; j < SEL_SB; ++j)
+#pragma unroll
+      for (int v = 0; v < SEL_MAXV; ++v) {
+        const int e = lane + 64 * v;
+        pv[j][v] = (s0 + j < s_end && v < V && e < E)
+                       ? part[(int64_t)(s0 + j) * stride + t * E + e] : 0.0f;
+      }
+#pragma unroll
+    for (int j = 0; j < SEL_SB; ++j)
+#pragma unroll
+      for (int v = 0; v < SEL_MAXV; ++v)
+        if (s0 + j < s_end) lgs[v] += pv[j][v];
+  }
+}
 
 // Wave-level argmax of (v, i): larger v wins, equal v -> lower i.
 __device__ __forceinline__ void wave_argmax(float& v, int& i) {

@@ -136,6 +136,8 @@ def run_forward(cfg, dev, T, ws=None, with_routing=True):
     moe.moe_forward(sd.moe_config(cfg), T, dev["x"], W, out, ws, logits=lg, topk_idx=idx,
                     topk_w=w, counts=counts, perm=perm)
     sync()
+    # no expert index out of range, no completion wait given up
+    assert moe.moe_get_device_error(ws) == moe.MOE_OK, moe.moe_last_error()
     r = {"out": host(out)}
     if with_routing:
         r.update(logits=host(lg), idx=host(idx), w=host(w), counts=host(counts), perm=host(perm))

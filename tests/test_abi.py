@@ -97,6 +97,20 @@ def test_argument_validation():
                                  FAKE) == moe.MOE_ERR_INVALID_ARG   # shared weights missing
     assert L.moe_combine(ctypes.byref(cfg), 4, FAKE, None, FAKE, FAKE, FAKE, None) == \
         moe.MOE_ERR_INVALID_ARG                                          # y_shared NULL, Is > 0
+    # the one-launch decode layer: 1 <= T <= 32, bf16 tokens, packed bf16
+    # weights; anything else is refused on the host
+    wp = moe.weights(gate_w=FAKE, bias=FAKE, w13=FAKE, w2=FAKE, ws13=FAKE, ws2=FAKE)
+    wp.packed = 1
+    wp8 = moe.weights(gate_w=FAKE, bias=FAKE, w13=FAKE, w13_scale=FAKE, w2=FAKE, w2_scale=FAKE,
+                      ws13=FAKE, ws13_scale=FAKE, ws2=FAKE, ws2_scale=FAKE)
+    wp8.packed = 1
+    for c, ww, T in ((cfg, wf, 4), (cfg, wp, 33), (_cfg(wdtype="fp8"), wp8, 4)):
+        assert L.moe_forward_decode_fused(ctypes.byref(c), T, FAKE, ctypes.byref(ww), FAKE, None,
+                                          None, None, None, None, FAKE * 256, 1 << 40,
+                                          None) == moe.MOE_ERR_UNSUPPORTED, (T, ww.packed)
+        assert "one-launch" in moe.moe_last_error()
+    assert L.moe_forward_decode_fused(ctypes.byref(cfg), 0, None, ctypes.byref(wp), None, None,
+                                      None, None, None, None, None, 0, None) == moe.MOE_OK
     cfg8 = _cfg(wdtype="fp8")
     w8 = moe.weights(gate_w=FAKE, bias=FAKE, w13=FAKE, w2=FAKE, ws13=FAKE, ws2=FAKE)
     assert L.moe_forward(ctypes.byref(cfg8), 4, FAKE, ctypes.byref(w8), FAKE, None, None, None,

@@ -1,8 +1,10 @@
 """GPU parity of the decode schedule of moe_forward (1 <= T <= 32: the gate
 over a few k ranges (bf16 MFMA on the exact split of the fp32 weight, or fp32
 dot products for fp32 activations), the selection, then one workgroup that
-permutes and lays out the tile list) and of moe_forward_overlap (the shared expert on a second
-stream), against the fp64 oracle and against moe_forward itself."""
+permutes and lays out the tile list), of moe_forward_decode_fused (all of it,
+the expert GEMMs and the combine in one launch) and of moe_forward_overlap
+(the shared expert on a second stream), against the fp64 oracle and against
+moe_forward itself."""
 import numpy as np
 import pytest
 import torch
@@ -83,33 +85,81 @@ def test_decode_forward(cfg, packed):
         assert r2 <= FP8_QUANT_TOL
 
 
+def _launches(cfg, dev, T, fn=moe.moe_forward):
+    x = sd.tensor(np.ascontiguousarray(np.resize(inputs(cfg)[0]["x"], (T, cfg.H))))
+    moe.moe_kernel_timer_read()
+    moe.moe_kernel_timer_enable(True)
+    ws = sd.workspace(cfg, T)
+    out = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=DEV)
+    fn(sd.moe_config(cfg), T, x, sd.weights_struct(dev), out, ws)
+    sync()
+    moe.moe_kernel_timer_enable(False)
+    return moe.moe_kernel_timer_read()
+
+
+BATCH_ROUTING = ("gate_split_kernel", "gate_logits_bf16_kernel", "permute_small_kernel",
+                 "build_tiles_kernel")
+DECODE_ROUTING = ("gate_decode_mfma_kernel", "select_kernel", "route_decode_kernel")
+
+
 def test_decode_schedule_launches():
-    """T <= 32 runs the decode routing kernels and not the batch path's gate,
-    permutation or tile list; T = 33 runs the batch path."""
+    """moe_forward at T <= 32 runs the decode routing kernels and not the
+    batch path's gate, permutation or tile list (packed or row-major
+    weights); T = 33 runs the batch path; moe_forward_decode_fused is one
+    launch of the decode layer kernel."""
     cfg = DECODE_CASES[0]
-    inp, dev = inputs(cfg)
-    dev = sd.packed_copy(dev)
-    for T, want, absent in ((32, ("gate_decode_mfma_kernel", "select_kernel",
-                                  "route_decode_kernel"),
-                             ("gate_split_kernel", "gate_logits_bf16_kernel",
-                              "permute_small_kernel", "build_tiles_kernel")),
-                            (33, ("gate_logits_bf16_kernel", "select_kernel",
-                                  "permute_small_kernel", "build_tiles_kernel"),
-                             ("gate_decode_mfma_kernel", "route_decode_kernel"))):
-        x = sd.tensor(np.ascontiguousarray(np.resize(inp["x"], (T, cfg.H))))
-        moe.moe_kernel_timer_read()
-        moe.moe_kernel_timer_enable(True)
-        ws = sd.workspace(cfg, T)
-        out = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=DEV)
-        moe.moe_forward(sd.moe_config(cfg), T, x, sd.weights_struct(dev), out, ws)
-        sync()
-        moe.moe_kernel_timer_enable(False)
-        kt = moe.moe_kernel_timer_read()
-        log(f"  T={T}: {sorted(kt)}")
+    _, dev = inputs(cfg)
+    packed = sd.packed_copy(dev)
+    for T, d, want, absent in (
+            (32, packed, DECODE_ROUTING, BATCH_ROUTING + ("decode_layer_kernel",)),
+            (32, dev, DECODE_ROUTING, BATCH_ROUTING + ("decode_layer_kernel",)),
+            (33, packed, ("gate_logits_bf16_kernel", "select_kernel", "permute_small_kernel",
+                          "build_tiles_kernel"),
+             ("gate_decode_mfma_kernel", "route_decode_kernel", "decode_layer_kernel"))):
+        kt = _launches(cfg, d, T)
+        log(f"  T={T} packed={d is packed}: {sorted(kt)}")
         for name in want:
             assert name in kt and kt[name][1] == 1, (T, name)
         for name in absent:
             assert name not in kt, (T, name)
+    for T in (32, 1):
+        kt = _launches(cfg, packed, T, moe.moe_forward_decode_fused)
+        assert sorted(kt) == ["decode_layer_kernel"] and kt["decode_layer_kernel"][1] == 1, kt
+
+
+# the one-launch layer (bf16 tokens, packed bf16 weights); the gate's k ranges
+# number 16 (deep: four waves per token in the selection), 4, 8, 4, 9, 16, 8
+# and 32 (deep, an odd batch)
+LAYER_CASES = [DECODE_CASES[0], DECODE_CASES[1], DECODE_CASES[2], DECODE_CASES[3],
+               DECODE_CASES[4],
+               DECODE_CASES[0].replace(name="dec-bf16-T1-H1024-E64-K8", T=1),
+               synth.C3.replace(name="dec-bf16-T7-H512-E128-K4-I192", T=7, H=512, E=128, G=8,
+                                TG=2, K=4, I=192, Is=320, rho=2.5),
+               synth.C3.replace(name="dec-bf16-T13-H2048-E256-K8", T=13, H=2048, E=256, G=8,
+                                TG=4, K=8, I=128, Is=256, rho=2.5)]
+
+
+@pytest.mark.parametrize("cfg", LAYER_CASES, ids=lambda c: c.name)
+def test_decode_fused_matches_moe_forward(cfg):
+    """moe_forward_decode_fused gives moe_forward's bits on every output, on
+    three successive calls on one workspace (with a moe_forward call on the
+    same workspace between them), and its layer output is within the bf16
+    tolerance of the oracle."""
+    log(f"fused {cfg.name}")
+    inp, dev = inputs(cfg)
+    dev = sd.packed_copy(dev)
+    ws = sd.workspace(cfg, cfg.T)
+    ref = _forward_outputs(cfg, dev, cfg.T, ws=ws)
+    for rep in range(3):
+        got = _forward_outputs(cfg, dev, cfg.T, ws=ws, fn=moe.moe_forward_decode_fused)
+        assert moe.moe_get_device_error(ws) == moe.MOE_OK, moe.moe_last_error()
+        for k in ref:
+            assert np.array_equal(got[k], ref[k]), (rep, k)
+        _forward_outputs(cfg, dev, cfg.T, ws=ws)
+    out_ref, _ = layer_reference(cfg, inp, ref["idx"], np.arange(cfg.T))
+    rel = rel_l2(ref["out"], out_ref)
+    log(f"  out relL2={rel:.3e}")
+    assert rel <= _tol(cfg)
 
 
 OVERLAP_CASES = [
@@ -129,10 +179,10 @@ OVERLAP_CASES = [
 ]
 
 
-def _forward_outputs(cfg, dev, T, shared_stream=None):
+def _forward_outputs(cfg, dev, T, shared_stream=None, ws=None, fn=None):
     C = sd.moe_config(cfg)
     W = sd.weights_struct(dev)
-    ws = sd.workspace(cfg, T)
+    ws = sd.workspace(cfg, T) if ws is None else ws
     o = {"out": torch.empty((T, cfg.H), dtype=torch.bfloat16 if cfg.act == "bf16"
                             else torch.float32, device=DEV),
          "logits": torch.empty((T, cfg.E), dtype=torch.float32, device=DEV),
@@ -142,7 +192,9 @@ def _forward_outputs(cfg, dev, T, shared_stream=None):
          "perm": torch.empty(T * cfg.K, dtype=torch.int32, device=DEV)}
     args = dict(logits=o["logits"], topk_idx=o["idx"], topk_w=o["w"], counts=o["counts"],
                 perm=o["perm"])
-    if shared_stream is None:
+    if fn is not None:
+        fn(C, T, dev["x"], W, o["out"], ws, **args)
+    elif shared_stream is None:
         moe.moe_forward(C, T, dev["x"], W, o["out"], ws, **args)
     else:
         moe.moe_forward_overlap(C, T, dev["x"], W, o["out"], ws, shared_stream, **args)
@@ -245,6 +297,49 @@ def test_decode_forward_graph_replay():
         sync()
         assert torch.equal(out, ref), f"replay {rep}"
         assert torch.equal(idx, ref_idx), f"replay {rep}"
+        fwd()
+        sync()
+        assert torch.equal(out, ref)
+
+
+def test_decode_fused_graph_replay():
+    """moe_forward_decode_fused captured into a HIP graph (two nodes: the call
+    counter, then the layer) replays bit-identically to eager moe_forward,
+    several times, with eager fused calls on the same workspace between the
+    replays."""
+    cfg = DECODE_CASES[0]
+    _, dev = inputs(cfg)
+    dev = sd.packed_copy(dev)
+    T = cfg.T
+    C = sd.moe_config(cfg)
+    W = sd.weights_struct(dev)
+    ws = sd.workspace(cfg, T)
+    out = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=DEV)
+    idx = torch.empty((T, cfg.K), dtype=torch.int32, device=DEV)
+    moe.moe_forward(C, T, dev["x"], W, out, ws, topk_idx=idx)
+    sync()
+    ref, ref_idx = out.clone(), idx.clone()
+
+    def fwd():
+        moe.moe_forward_decode_fused(C, T, dev["x"], W, out, ws, topk_idx=idx,
+                                     stream=torch.cuda.current_stream())
+
+    fwd()
+    sync()
+    assert torch.equal(out, ref) and torch.equal(idx, ref_idx)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fwd()
+    sync()
+    for rep in range(4):
+        out.fill_(0)
+        idx.fill_(-1)
+        sync()
+        g.replay()
+        sync()
+        assert torch.equal(out, ref), f"replay {rep}"
+        assert torch.equal(idx, ref_idx), f"replay {rep}"
+        assert moe.moe_get_device_error(ws) == moe.MOE_OK, moe.moe_last_error()
         fwd()
         sync()
         assert torch.equal(out, ref)
