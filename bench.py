@@ -129,8 +129,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="v3-layer-bf16-T4096")
-    ap.add_argument("--cpu-sample", type=int, default=384,
-                    help="tokens of the workload run through the fp64 oracle (0 = skip)")
+    ap.add_argument("--cpu-sample", type=int, default=None,
+                    help="tokens of the workload run through the fp64 oracle (0 = skip; default "
+                         "384, 96 for the e4m3 layers, whose oracle also quantises: about 15 s "
+                         "of host time either way)")
     ap.add_argument("--profile-only", action="store_true",
                     help="for rocprofv3: warmup + steps and the per-kernel breakdown only (no "
                          "oracle, no second entry point, no backward), print the JSON line")
@@ -522,6 +524,8 @@ def main():
         "roofline": roof,
     }
 
+    if args.cpu_sample is None:
+        args.cpu_sample = 96 if cfg.wdtype in ("fp8", "fp8e8m0") else 384
     if args.cpu_sample > 0 and not args.profile_only:
         import oracle
         S = min(args.cpu_sample * (64 if gate_only else 1), T)
