@@ -72,6 +72,9 @@ def lib():
         L.oracle_ffn_backward.argtypes = [ctypes.POINTER(Cfg), i32, i64, vp, vp, i32, vp, vp, vp,
                                           vp, vp, i32, vp, vp, vp]
         L.oracle_ffn_backward.restype = ctypes.c_int
+        L.oracle_ffn_backward_fp8.argtypes = [ctypes.POINTER(Cfg), i32, i64, vp, vp, i32, vp,
+                                              vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp]
+        L.oracle_ffn_backward_fp8.restype = ctypes.c_int
         L.oracle_ffn_backward_entries.argtypes = [ctypes.POINTER(Cfg), i32, i64, vp, vp, i32, vp,
                                                   vp, vp, vp, vp, i32, i64, vp, vp, vp, vp]
         L.oracle_ffn_backward_entries.restype = ctypes.c_int
@@ -272,16 +275,36 @@ def bias_update(counts: np.ndarray, gamma: float, bias: np.ndarray) -> np.ndarra
     return out
 
 
-def ffn_backward(cfg, inp: dict, expert: int, tokens, dy, want=("dx", "dw13", "dw2")):
+def ffn_backward(cfg, inp: dict, expert: int, tokens, dy, want=("dx", "dw13", "dw2"),
+                 quant_act=False):
     """Exact (fp64) backward of one SwiGLU expert (-1: shared) over rows with
     inputs x[tokens[r]] and output gradients dy [n, H] -> dict of dx [n, H],
-    dw13 [2 n_e, H], dw2 [H, n_e] (the weight gradients summed over the rows)."""
+    dw13 [2 n_e, H], dw2 [H, n_e] (the weight gradients summed over the rows).
+    e4m3 weights: the backward of the dequantised weights, or with quant_act
+    the FP8 backward (R15: x, dy, [dg du], h quantised in tiles of 128 along
+    each GEMM's contraction; the rows are the expert's, in sorted order)."""
     x = _c(inp["x"])
     tokens = _c(tokens, np.int64)
     dy = _c(dy, np.float64)
     n = len(tokens)
     H = cfg.H
     ne = cfg.Is if expert < 0 else cfg.I
+    if cfg.wdtype in _QUANT_MODE:
+        xd = F32 if cfg.act == "f32" else BF16
+        g = lambda k: None if inp.get(k) is None else _c(inp[k])
+        arrs = [g(k) for k in ("w13", "w13_s", "w2", "w2_s", "ws13", "ws13_s", "ws2", "ws2_s")]
+        out = {"dx": np.empty((n, H)) if "dx" in want else None,
+               "dw13": np.empty((2 * ne, H)) if "dw13" in want else None,
+               "dw2": np.empty((H, ne)) if "dw2" in want else None}
+        rc = lib().oracle_ffn_backward_fp8(ctypes.byref(cfg_of(cfg)), int(expert), n,
+                                           _p(tokens), _p(x), xd, _p(dy),
+                                           *[_p(a) for a in arrs], _quant_mode(cfg, quant_act),
+                                           _p(out["dx"]), _p(out["dw13"]), _p(out["dw2"]))
+        if rc:
+            raise ValueError("oracle_ffn_backward_fp8 rejected its arguments")
+        return {k: v for k, v in out.items() if v is not None}
+    if quant_act:
+        raise ValueError("the quantised backward needs e4m3 weights")
     wd = {"f32": F32, "bf16": BF16}[cfg.wdtype]
     xd = F32 if cfg.act == "f32" else BF16
     g = lambda k: None if inp.get(k) is None else _c(inp[k])

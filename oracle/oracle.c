@@ -40,6 +40,15 @@
  *       2^e >= a / 448 (e clamped to [-126, 127]), codes are the e4m3 values
  *       nearest v * 2^-e (an exact product; ties to even); an all-zero tile
  *       has scale 1 and zero codes.
+ *   R15 the FP8 backward ([Insights] 3.2 fixes the granularity of FP8
+ *       training -- activations in 1x128 tiles, weights in 128x128 blocks,
+ *       fp32 accumulation -- and says no more about the backward): every
+ *       operand of a backward GEMM that is an activation or a gradient is
+ *       quantised in tiles of 128 along that GEMM's contraction dimension
+ *       (for the weight gradients, which contract over an expert's rows:
+ *       128 consecutive rows of one column); the weights keep their 128x128
+ *       blocks; the forward quantities are recomputed as the FP8 forward
+ *       computes them.
  *   R11 the selection bias follows the experts' observed load ([Co-design]
  *       2.2 keeps it as a buffer updated from load statistics, not from a
  *       gradient, and prints no rule): each expert's bias moves one fixed
@@ -759,6 +768,152 @@ int oracle_ffn_backward(const oracle_cfg *c, int32_t e, int64_t n, const int64_t
             }
     }
     free(xs); free(g); free(u); free(h); free(da);
+    return 0;
+}
+
+/* Quantise then dequantise, in place, each column of v [n, F] (row stride
+ * F) in tiles of 128 consecutive rows from row 0 (the last tile may be
+ * shorter), with the scale rule of `mode`: the column-tile form of the 1x128
+ * quantiser used by the FP8 weight gradients (R15).  A short tile is
+ * quantised as a 128-long tile padded with zeros, which changes neither its
+ * maximum nor its codes. */
+static void quant_dequant_cols(double *v, int64_t n, int32_t F, int32_t mode)
+{
+#pragma omp parallel for schedule(static)
+    for (int32_t f = 0; f < F; ++f) {
+        float tmp[128];
+        uint8_t q[128];
+        float sc;
+        for (int64_t r0 = 0; r0 < n; r0 += 128) {
+            int64_t len = n - r0 < 128 ? n - r0 : 128;
+            for (int j = 0; j < 128; ++j)
+                tmp[j] = j < len ? (float)v[(r0 + j) * F + f] : 0.0f;
+            if (mode == OR_QUANT_POW2)
+                oracle_quant_rows_pow2(1, 128, tmp, q, &sc);
+            else
+                oracle_quant_rows(1, 128, tmp, q, &sc);
+            for (int64_t j = 0; j < len; ++j)
+                v[(r0 + j) * F + f] = oracle_e4m3_decode(q[j]) * (double)sc;
+        }
+    }
+}
+
+/* The FP8 backward of one SwiGLU expert (R15) over the rows with inputs
+ * x[tokens[r]] and output gradients dy [n, H], in the order given (the
+ * expert's rows in sorted order: the column tiles of the weight gradients
+ * start at the first of them).  Q_k quantises each row in 1x128 tiles
+ * along its k elements (R7 or R14 by `mode`), Qc each column in tiles of
+ * 128 rows, and W are the dequantised e4m3 weights (code x 128x128 block
+ * scale):
+ *   [g; u] = W13 Q_H(x_r),  h = silu(g) u             (the F2 forward)
+ *   dh     = W2^T Q_H(dy_r)                           (contraction over H)
+ *   dg     = dh u silu'(g),  du = dh silu(g)
+ *   dx_r   = W13^T Q_2n([dg; du]_r)                   (contraction over 2n)
+ *   dW2    = sum_r Qc(dy)_r Qc(h)_r^T                 [H, n]
+ *   dW13   = sum_r Qc([dg; du])_r Qc(x)_r^T           [2n, H]
+ * with every sum in double.  mode OR_QUANT_NONE gives the exact backward of
+ * the dequantised weights.  w13 [E, 2I, H] with scales [E, 2I/128, H/128],
+ * w2 [E, H, I] with [E, H/128, I/128]; the shared expert's likewise.  e: the
+ * expert (-1: shared).  Returns 1 for a bad expert or shape, or allocation. */
+int oracle_ffn_backward_fp8(const oracle_cfg *c, int32_t e, int64_t n, const int64_t *tokens,
+                            const void *x, int32_t x_dtype, const double *dy,
+                            const uint8_t *w13, const float *w13_s, const uint8_t *w2,
+                            const float *w2_s, const uint8_t *ws13, const float *ws13_s,
+                            const uint8_t *ws2, const float *ws2_s, int32_t mode, double *dx,
+                            double *dw13, double *dw2)
+{
+    const int32_t H = c->H, E = c->E;
+    if (e < -1 || e >= E || (e == -1 && c->Is == 0))
+        return 1;
+    const int32_t ne = e < 0 ? c->Is : c->I;
+    if (H % 128 || ne % 128)
+        return 1;
+    const int64_t eb13 = (int64_t)(2 * ne / 128) * (H / 128), eb2 = (int64_t)(H / 128) * (ne / 128);
+    const uint8_t *W13 = e < 0 ? ws13 : w13 + (int64_t)e * 2 * ne * H;
+    const float *S13 = e < 0 ? ws13_s : w13_s + e * eb13;
+    const uint8_t *W2 = e < 0 ? ws2 : w2 + (int64_t)e * H * ne;
+    const float *S2 = e < 0 ? ws2_s : w2_s + e * eb2;
+    const size_t nn = (size_t)(n > 0 ? n : 1);
+    double *xs = malloc(sizeof(double) * nn * H);
+    double *xq = malloc(sizeof(double) * nn * H);
+    double *dyq = malloc(sizeof(double) * nn * H);
+    double *h = malloc(sizeof(double) * nn * ne);
+    double *da = malloc(sizeof(double) * nn * 2 * ne);
+    double *daq = malloc(sizeof(double) * nn * 2 * ne);
+    if (!xs || !xq || !dyq || !h || !da || !daq) {
+        free(xs); free(xq); free(dyq); free(h); free(da); free(daq);
+        return 1;
+    }
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n; ++r) {
+        double *xr = xs + r * H, *xqr = xq + r * H, *dr = dyq + r * H;
+        for (int32_t k = 0; k < H; ++k) {
+            xr[k] = mat_at(x, NULL, x_dtype, H, tokens[r], k);
+            xqr[k] = xr[k];
+            dr[k] = dy[r * H + k];
+        }
+        if (mode) {
+            quant_dequant_row(xqr, H, mode);
+            quant_dequant_row(dr, H, mode);
+        }
+        double *dar = da + r * 2 * ne;
+        for (int32_t i = 0; i < ne; ++i) {
+            double gs = 0.0, us = 0.0, dh = 0.0;
+            for (int32_t k = 0; k < H; ++k) {
+                gs += mat_at(W13, S13, OR_E4M3, H, i, k) * xqr[k];
+                us += mat_at(W13, S13, OR_E4M3, H, ne + i, k) * xqr[k];
+            }
+            for (int32_t m = 0; m < H; ++m)
+                dh += dr[m] * mat_at(W2, S2, OR_E4M3, ne, m, i);
+            double sg = 1.0 / (1.0 + exp(-gs));
+            h[r * ne + i] = gs * sg * us;
+            dar[i] = dh * us * sg * (1.0 + gs * (1.0 - sg));
+            dar[ne + i] = dh * gs * sg;
+        }
+        double *daqr = daq + r * 2 * ne;
+        memcpy(daqr, dar, sizeof(double) * 2 * ne);
+        if (mode)
+            quant_dequant_row(daqr, 2 * ne, mode);
+        if (dx) {
+            for (int32_t k = 0; k < H; ++k) {
+                double acc = 0.0;
+                for (int32_t q = 0; q < 2 * ne; ++q)
+                    acc += daqr[q] * mat_at(W13, S13, OR_E4M3, H, q, k);
+                dx[r * H + k] = acc;
+            }
+        }
+    }
+    /* the weight gradients: column tiles of 128 rows (dy, h, [dg; du], x) */
+    if (dw2 || dw13) {
+        memcpy(dyq, dy, sizeof(double) * (size_t)n * H);   /* dyq now holds Qc(dy) */
+        if (mode) {
+            quant_dequant_cols(dyq, n, H, mode);
+            quant_dequant_cols(h, n, ne, mode);
+            quant_dequant_cols(da, n, 2 * ne, mode);
+            quant_dequant_cols(xs, n, H, mode);
+        }
+    }
+    if (dw2) {
+#pragma omp parallel for schedule(static)
+        for (int32_t m = 0; m < H; ++m)
+            for (int32_t i = 0; i < ne; ++i) {
+                double acc = 0.0;
+                for (int64_t r = 0; r < n; ++r)
+                    acc += dyq[r * H + m] * h[r * ne + i];
+                dw2[(int64_t)m * ne + i] = acc;
+            }
+    }
+    if (dw13) {
+#pragma omp parallel for schedule(static)
+        for (int32_t q = 0; q < 2 * ne; ++q)
+            for (int32_t k = 0; k < H; ++k) {
+                double acc = 0.0;
+                for (int64_t r = 0; r < n; ++r)
+                    acc += da[r * 2 * ne + q] * xs[r * H + k];
+                dw13[(int64_t)q * H + k] = acc;
+            }
+    }
+    free(xs); free(xq); free(dyq); free(h); free(da); free(daq);
     return 0;
 }
 

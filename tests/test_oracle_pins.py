@@ -546,6 +546,124 @@ def test_fp8_activation_quantised_mode_matches_numpy_expression(wdtype):
     assert rel(oracle.layer(other, inp, idx, w, quant_act=True), got) > 1e-4
 
 
+def _qdq_cols_torch(v, pow2=False):
+    """Column tiles of 128 rows (the last one shorter) through the same
+    independent quantiser: rows padded with zeros to a multiple of 128 (no
+    change to a tile's maximum or codes), each column cut along the rows."""
+    n, f = v.shape
+    pad = (-n) % 128
+    vp = np.concatenate([v, np.zeros((pad, f))]) if pad else v
+    return _qdq_1x128_torch(np.ascontiguousarray(vp.T), pow2).T[:n]
+
+
+def _fp8_backward_numpy(cfg, inp, e, tokens, dy, quant, dgrad_tiles="rows", wgrad_tiles="cols",
+                        quant_h=True):
+    """The FP8 backward of one expert written out with numpy fp64 matmuls on
+    the dequantised e4m3 weights: x, dy and [dg du] quantised per 1x128 tile
+    along the contraction of the dgrad GEMMs (H, H and 2n), and for the
+    weight gradients dy, h, [dg du] and x per column in tiles of 128 of the
+    expert's rows ("深入理解 DeepSeek-V3…", section 3.2: activations and
+    gradients in tiles of 128 along the contraction, weights in 128x128
+    blocks).  dgrad_tiles / wgrad_tiles = the other axis and quant_h = False
+    give the slips the pin must tell apart."""
+    pow2 = cfg.wdtype == "fp8e8m0"
+    deq = lambda q, s: (torch.from_numpy(q).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+                        * np.kron(s.astype(np.float64), np.ones((128, 128))))
+    if e < 0:
+        w13, w2 = deq(inp["ws13"], inp["ws13_s"]), deq(inp["ws2"], inp["ws2_s"])
+    else:
+        w13, w2 = deq(inp["w13"][e], inp["w13_s"][e]), deq(inp["w2"][e], inp["w2_s"][e])
+    n = w13.shape[0] // 2
+    ident = lambda v: v
+    qr = (lambda v: _qdq_1x128_torch(v, pow2)) if quant else ident
+    qc = (lambda v: _qdq_cols_torch(v, pow2)) if quant else ident
+    qd = qr if dgrad_tiles == "rows" else qc
+    qw = qc if wgrad_tiles == "cols" else qr
+    x = synth.bf16_to_f32(inp["x"]).astype(np.float64)[tokens]
+    a = qr(x) @ w13.T
+    g, u = a[:, :n], a[:, n:]
+    sg = 1.0 / (1.0 + np.exp(-g))
+    h = g * sg * u
+    dh = qd(dy) @ w2
+    da = np.concatenate([dh * u * sg * (1.0 + g * (1.0 - sg)), dh * g * sg], axis=1)
+    return {"dx": qd(da) @ w13, "dw2": qw(dy).T @ (qw(h) if quant_h else h),
+            "dw13": qw(da).T @ qw(x)}
+
+
+@pytest.mark.parametrize("wdtype", ["fp8", "fp8e8m0"])
+def test_fp8_backward_matches_numpy_expression(wdtype):
+    """The oracle's FP8 backward (reading R15) against the numpy expression
+    above, for a routed expert and the shared expert, over 200 rows (one full
+    column tile and a short one), at 1e-10.  The readings it must not take --
+    the operands left unquantised, dgrad tiles cut along the rows instead of
+    the contraction, weight-gradient tiles cut along the features, h left
+    unquantised -- each sit orders of magnitude further away.  Unquantised,
+    the oracle is the exact backward of the dequantised weights."""
+    cfg = synth.C5.replace(name="b8-pin", T=200, H=256, E=2, G=1, TG=1, K=1, I=128, Is=256,
+                           rho=1.0, wdtype=wdtype)
+    inp = synth.gen_inputs(cfg)
+    # magnitudes that vary by powers of two along rows and along columns, so
+    # that tiles cut along either axis get different scales (with
+    # power-of-two scales, tiles of similar magnitude would share them)
+    spread = np.ldexp(1.0, (np.arange(cfg.T)[:, None] % 3) + (np.arange(cfg.H)[None, :] % 5))
+    x = synth.bf16_to_f32(inp["x"]).astype(np.float64) * spread
+    inp["x"] = (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)   # exact
+    rng = np.random.default_rng(5)
+    # worst row: the rows of small magnitude are where the tile axis shows
+    rel = lambda a, b: (np.linalg.norm(a - b, axis=1) / np.linalg.norm(b, axis=1)).max()
+    for e in (1, -1):
+        tokens = rng.permutation(cfg.T)
+        dy = synth.bf16_to_f32(synth.normal_bf16(200 * cfg.H, 4, synth.T_TEST, 2 + e, 0.05))
+        dy = dy.reshape(200, cfg.H).astype(np.float64) * np.ldexp(
+            1.0, 3 * (np.arange(200)[:, None] % 6) - 3 * (np.arange(cfg.H)[None, :] % 6))
+        got = oracle.ffn_backward(cfg, inp, e, tokens, dy, quant_act=True)
+        ref = _fp8_backward_numpy(cfg, inp, e, tokens, dy, quant=True)
+        exact = _fp8_backward_numpy(cfg, inp, e, tokens, dy, quant=False)
+        for k in ("dx", "dw13", "dw2"):
+            assert got[k].shape == ref[k].shape, k
+            assert rel(got[k], ref[k]) < 1e-10, (e, k, rel(got[k], ref[k]))
+            assert rel(exact[k], ref[k]) > 1e-4, k
+        unq = oracle.ffn_backward(cfg, inp, e, tokens, dy, quant_act=False)
+        for k in ("dx", "dw13", "dw2"):
+            assert rel(unq[k], exact[k]) < 1e-10, k
+        slip = _fp8_backward_numpy(cfg, inp, e, tokens, dy, quant=True, dgrad_tiles="cols")
+        assert rel(slip["dx"], ref["dx"]) > 1e-4
+        slip = _fp8_backward_numpy(cfg, inp, e, tokens, dy, quant=True, wgrad_tiles="rows")
+        assert rel(slip["dw2"], ref["dw2"]) > 1e-4
+        slip = _fp8_backward_numpy(cfg, inp, e, tokens, dy, quant=True, quant_h=False)
+        assert rel(slip["dw2"], ref["dw2"]) > 1e-4
+
+
+def test_fp8_backward_pow2_unquantised_equals_fp32_backward():
+    """With power-of-two block scales every dequantised weight is exact in
+    fp32, so the oracle's unquantised FP8 backward must equal its exact fp32
+    backward run on those fp32 weights (two independent weight paths: block
+    scales in the e4m3 reader, none in the fp32 one)."""
+    cfg = synth.C5.replace(name="b8-f32", T=40, H=256, E=2, G=1, TG=1, K=1, I=128, Is=128,
+                           rho=1.0, wdtype="fp8e8m0")
+    inp = synth.gen_inputs(cfg)
+    deq = lambda q, s: (torch.from_numpy(q).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+                        * np.kron(s.astype(np.float64), np.ones((128, 128))))
+    f32 = dict(inp)
+    for k in ("w13", "w2"):
+        f32[k] = np.stack([deq(inp[k][e], inp[k + "_s"][e]) for e in range(cfg.E)]
+                          ).astype(np.float32)
+        f32["ws" + k[1:]] = deq(inp["ws" + k[1:]], inp["ws" + k[1:] + "_s"]).astype(np.float32)
+    for k in ("w13", "w2"):
+        assert np.array_equal(f32[k].astype(np.float64),
+                              np.stack([deq(inp[k][e], inp[k + "_s"][e]) for e in range(cfg.E)]))
+    cfg32 = cfg.replace(wdtype="f32")
+    rng = np.random.default_rng(9)
+    tokens = rng.permutation(cfg.T)
+    dy = synth.bf16_to_f32(synth.normal_bf16(cfg.T * cfg.H, 5, synth.T_TEST, 0, 1.0)).reshape(
+        cfg.T, cfg.H).astype(np.float64)
+    for e in (0, -1):
+        a = oracle.ffn_backward(cfg, inp, e, tokens, dy, quant_act=False)
+        b = oracle.ffn_backward(cfg32, f32, e, tokens, dy)
+        for k in ("dx", "dw13", "dw2"):
+            np.testing.assert_allclose(a[k], b[k], rtol=1e-12, atol=1e-12 * np.abs(b[k]).max())
+
+
 def test_quant_rows_pow2_definition():
     """Power-of-two 1x128 scales: every scale is a power of two, the
     smallest one with scale >= max|v| / 448 (so max|code| lies in (224, 448]),
