@@ -297,9 +297,20 @@ moe_status moe_quantize_act(const moe_config* cfg, int64_t rows, const void* x, 
  *      gradient of each row's input (sum the rows of a token for dx_t).
  *   dw13 [E, 2I, H], dw2 [E, H, I], dws13, dws2 out bf16: weight gradients
  *      (zero for an expert without rows).
+ * e4m3 weights (MOE_FP8_E4M3 or MOE_FP8_E4M3_E8M0, row-major, with their
+ * 128x128 block scales): the FP8 backward ("深入理解 DeepSeek-V3…", section
+ * 3.2: operands in tiles of 128, fp32 accumulation).  [g; u] is recomputed
+ * from x quantised per 1x128 tile (the FP8 forward); dy and [dg du] are
+ * quantised per 1x128 tile along the dgrad GEMMs' contraction; for the
+ * weight gradients dy, h, [dg du] and x are quantised per column in tiles of
+ * 128 of the expert's rows (from its first row; the last tile shorter); the
+ * weights keep their blocks; every GEMM accumulates in fp32 and the outputs
+ * are bf16.  Scales as the forward's quantiser (a / 448, or powers of two
+ * for MOE_FP8_E4M3_E8M0).
  * Workspace: moe_expert_ffn_backward_workspace_bytes(cfg, T) bytes (0 for a
- * configuration it does not handle), 256-byte aligned.  bf16 activations and
- * weights only (MOE_ERR_UNSUPPORTED otherwise, or for packed weights). */
+ * configuration it does not handle), 256-byte aligned.  bf16 activations
+ * with bf16 or e4m3 weights (MOE_ERR_UNSUPPORTED otherwise, or for packed
+ * weights). */
 size_t moe_expert_ffn_backward_workspace_bytes(const moe_config* cfg, int64_t T);
 moe_status moe_expert_ffn_backward(const moe_config* cfg, int64_t T, const void* x,
                                    const int32_t* perm, const int32_t* offsets,

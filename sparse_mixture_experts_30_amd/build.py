@@ -18,7 +18,7 @@ BUILD = os.path.join(ROOT, "_build")
 
 SOURCES = ["gate.hip", "permute.hip", "ffn_sched.hip", "ffn_bf16.hip", "ffn_bf16_packed.hip",
            "ffn_fp8.hip", "ffn_fp8_packed.hip", "ffn_fp8_mx.hip",
-           "ffn_f32.hip", "combine.hip", "bias.hip", "ffn_backward.hip", "decode.hip", "decode_layer.hip",
+           "ffn_f32.hip", "combine.hip", "bias.hip", "ffn_backward.hip", "ffn_backward_fp8.hip", "decode.hip", "decode_layer.hip",
            "layer_backward.hip", "moe_api.cpp",
            "timer.cpp"]
 

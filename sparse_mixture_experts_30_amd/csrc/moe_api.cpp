@@ -558,11 +558,12 @@ moe_status moe_forward_overlap(const moe_config* cfg, int64_t T, const void* x,
 
 size_t moe_expert_ffn_backward_workspace_bytes(const moe_config* cfg, int64_t T) {
   if (check_cfg(cfg) != MOE_OK || check_T(T, cfg) != MOE_OK) return 0;
-  if (cfg->weight_dtype != MOE_BF16 || cfg->act_dtype != MOE_BF16) return 0;
+  if (cfg->act_dtype != MOE_BF16 || cfg->weight_dtype == MOE_F32) return 0;
   moe::FfnDims d{T, T * cfg->num_experts_per_tok, cfg->hidden_size, cfg->moe_intermediate_size,
                  cfg->shared_intermediate_size, cfg->n_routed_experts,
                  cfg->num_experts_per_tok};
-  return moe::ffn_backward_ws_bytes(d);
+  return is_fp8(cfg->weight_dtype) ? moe::ffn_backward_fp8_ws_bytes(d)
+                                   : moe::ffn_backward_ws_bytes(d);
 }
 
 moe_status moe_expert_ffn_backward(const moe_config* cfg, int64_t T, const void* x,
@@ -573,8 +574,10 @@ moe_status moe_expert_ffn_backward(const moe_config* cfg, int64_t T, const void*
                                    void* stream) {
   CHECK(check_cfg(cfg));
   CHECK(check_T(T, cfg));
-  if (cfg->weight_dtype != MOE_BF16 || cfg->act_dtype != MOE_BF16)
-    return fail(MOE_ERR_UNSUPPORTED, "the expert backward takes bf16 activations and weights");
+  const bool fp8 = is_fp8(cfg->weight_dtype);
+  if (cfg->act_dtype != MOE_BF16 || cfg->weight_dtype == MOE_F32)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "the expert backward takes bf16 activations with bf16 or e4m3 weights");
   if (T == 0) return MOE_OK;
   NONNULL(w);
   if (w->packed)
@@ -595,12 +598,33 @@ moe_status moe_expert_ffn_backward(const moe_config* cfg, int64_t T, const void*
     NONNULL(dws13);
     NONNULL(dws2);
   }
+  if (fp8) {
+    NONNULL(w->w13_scale);
+    NONNULL(w->w2_scale);
+    if (sh) {
+      NONNULL(w->ws13_scale);
+      NONNULL(w->ws2_scale);
+    }
+  }
   moe::FfnDims d{T, T * cfg->num_experts_per_tok, cfg->hidden_size, cfg->moe_intermediate_size,
                  cfg->shared_intermediate_size, cfg->n_routed_experts,
                  cfg->num_experts_per_tok};
-  const size_t need = moe::ffn_backward_ws_bytes(d);
+  const size_t need = fp8 ? moe::ffn_backward_fp8_ws_bytes(d) : moe::ffn_backward_ws_bytes(d);
   if (!ws || ws_bytes < need || ((uintptr_t)ws & 255))
     return fail(MOE_ERR_WORKSPACE, "workspace must be 256-byte aligned and >= %zu bytes", need);
+  if (fp8) {
+    HIPCALL(moe::launch_ffn_backward_fp8(
+                d, cfg->weight_dtype == MOE_FP8_E4M3_E8M0, (const uint16_t*)x, perm, offsets,
+                (const uint8_t*)w->w13, w->w13_scale, (const uint8_t*)w->w2, w->w2_scale,
+                (const uint8_t*)(sh ? w->ws13 : nullptr), sh ? w->ws13_scale : nullptr,
+                (const uint8_t*)(sh ? w->ws2 : nullptr), sh ? w->ws2_scale : nullptr,
+                (const uint16_t*)dy, (const uint16_t*)(sh ? dy_shared : nullptr), (uint16_t*)dx,
+                (uint16_t*)(sh ? dx_shared : nullptr), (uint16_t*)dw13, (uint16_t*)dw2,
+                (uint16_t*)(sh ? dws13 : nullptr), (uint16_t*)(sh ? dws2 : nullptr), ws,
+                (hipStream_t)stream),
+            "expert backward (e4m3)");
+    return MOE_OK;
+  }
   HIPCALL(moe::launch_ffn_backward(d, (const uint16_t*)x, perm, offsets,
                                    (const uint16_t*)w->w13, (const uint16_t*)w->w2,
                                    (const uint16_t*)(sh ? w->ws13 : nullptr),

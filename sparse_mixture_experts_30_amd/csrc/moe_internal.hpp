@@ -229,6 +229,20 @@ hipError_t launch_ffn_backward(const FfnDims& d, const uint16_t* x, const int32_
                                uint16_t* dw2, uint16_t* dws13, uint16_t* dws2, void* ws,
                                hipStream_t s);
 
+// FP8 backward of the expert FFNs (ffn_backward_fp8.hip): row-major e4m3
+// weights with fp32 128x128 block scales; pow2 selects power-of-two
+// activation and gradient scales.  Outputs as launch_ffn_backward's.
+size_t ffn_backward_fp8_ws_bytes(const FfnDims& d);
+hipError_t launch_ffn_backward_fp8(const FfnDims& d, bool pow2, const uint16_t* x,
+                                   const int32_t* perm, const int32_t* offsets,
+                                   const uint8_t* w13, const float* w13s, const uint8_t* w2,
+                                   const float* w2s, const uint8_t* ws13, const float* ws13s,
+                                   const uint8_t* ws2, const float* ws2s, const uint16_t* dy,
+                                   const uint16_t* dys, uint16_t* dx, uint16_t* dxs,
+                                   uint16_t* dw13, uint16_t* dw2, uint16_t* dws13,
+                                   uint16_t* dws2, void* ws, hipStream_t s);
+
+
 // Selection-bias update from per-expert counts (one workgroup, E <= 512).
 hipError_t launch_bias_update(const int32_t* counts, float* bias, int E, float gamma,
                               hipStream_t s);

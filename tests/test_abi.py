@@ -135,7 +135,7 @@ def test_argument_validation():
     bad = _cfg()
     bad.n_group = 3
     assert L.moe_bias_update(ctypes.byref(bad), FAKE, 1e-3, FAKE, None) != moe.MOE_OK
-    # expert backward: bf16 row-major weights only; required arrays; workspace
+    # expert backward: row-major bf16 or e4m3 weights; required arrays; workspace
     def bwd(c, w, dy=FAKE, ws=FAKE * 256, ws_bytes=1 << 40):
         return L.moe_expert_ffn_backward(ctypes.byref(c), 4, FAKE, FAKE, FAKE, ctypes.byref(w), dy,
                                          FAKE, None, None, FAKE, FAKE, FAKE, FAKE, ws, ws_bytes,
@@ -143,11 +143,20 @@ def test_argument_validation():
     wrow = moe.weights(w13=FAKE, w2=FAKE, ws13=FAKE, ws2=FAKE)
     assert bwd(cfg, moe.weights(w13=FAKE, w2=FAKE, ws13=FAKE, ws2=FAKE, packed=1)) == \
         moe.MOE_ERR_UNSUPPORTED
-    assert bwd(_cfg(wdtype="fp8"), wrow) == moe.MOE_ERR_UNSUPPORTED
+    assert bwd(_cfg(act="f32", wdtype="f32"), wrow) == moe.MOE_ERR_UNSUPPORTED
+    # e4m3 weights: the FP8 backward, which needs the block scales
+    assert bwd(_cfg(wdtype="fp8"), wrow) == moe.MOE_ERR_INVALID_ARG
+    w8 = moe.weights(w13=FAKE, w13_scale=FAKE, w2=FAKE, w2_scale=FAKE, ws13=FAKE,
+                     ws13_scale=FAKE, ws2=FAKE, ws2_scale=FAKE)
+    assert bwd(_cfg(wdtype="fp8"), w8, ws_bytes=100) == moe.MOE_ERR_WORKSPACE
+    w8.packed = 1
+    assert bwd(_cfg(wdtype="fp8e8m0"), w8) == moe.MOE_ERR_UNSUPPORTED
     assert bwd(cfg, wrow, dy=None) == moe.MOE_ERR_INVALID_ARG
     assert bwd(cfg, wrow, ws_bytes=100) == moe.MOE_ERR_WORKSPACE
     assert bwd(cfg, wrow, ws=FAKE * 256 + 4) == moe.MOE_ERR_WORKSPACE
-    assert moe.moe_expert_ffn_backward_workspace_bytes(_cfg(wdtype="fp8"), 16) == 0
+    assert moe.moe_expert_ffn_backward_workspace_bytes(_cfg(act="f32", wdtype="f32"), 16) == 0
+    for wd in ("fp8", "fp8e8m0"):
+        assert moe.moe_expert_ffn_backward_workspace_bytes(_cfg(wdtype=wd), 16) > 0
     # layer backward: the same dtype and layout rules; every forward array is required
     def lbwd(c, w, logits=FAKE, dgw=FAKE, ws=FAKE * 256, ws_bytes=1 << 40):
         return L.moe_backward(ctypes.byref(c), 4, FAKE, ctypes.byref(w), logits, FAKE, FAKE, FAKE,
