@@ -186,10 +186,11 @@ def main():
         inp = synth.gen_inputs(cfg)
     log(f"[bench] generated in {time.time() - t0:.1f}s; uploading")
     d = sd.to_device(inp)
-    # The expert-FFN backward (training) reads row-major bf16 weights: kept
-    # for the bf16 layer workloads of at least 1024 tokens.
+    # The expert-FFN backward (training) reads row-major weights (bf16, or
+    # e4m3 for the FP8 backward): kept for the layer workloads of at least
+    # 1024 tokens.
     with_bwd = (not args.no_backward and not args.profile_only and not gate_only and
-                cfg.wdtype == "bf16" and cfg.act == "bf16" and T >= 1024)
+                cfg.wdtype in ("bf16", "fp8", "fp8e8m0") and cfg.act == "bf16" and T >= 1024)
     drow = d if with_bwd else None
     if cfg.wdtype != "f32" and not args.row_major and not gate_only:
         d = sd.packed_copy(d)   # the row-major device copies are released here unless kept
@@ -406,25 +407,32 @@ def main():
             torch.cuda.synchronize()
             return eb0.elapsed_time(eb1) / 5, kms
 
+        bwd_fp8 = cfg.wdtype in ("fp8", "fp8e8m0")
+        bpeak = FP8_PEAK_TFLOPS if bwd_fp8 else BF16_PEAK_TFLOPS
+
         def figures(bms, flop, nbytes, kms):
             return {"ms": round(bms, 3), "tflops": round(flop / (bms * 1e-3) / 1e12, 1),
-                    "mfma_frac": round(flop / (bms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                    "mfma_frac": round(flop / (bms * 1e-3) / 1e12 / bpeak, 4),
                     "hbm_gbs": round(nbytes / (bms * 1e-3) / 1e9, 1),
                     "hbm_frac": round(nbytes / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                     "algorithmic_flop": flop, "algorithmic_bytes": nbytes, "kernels_ms": kms}
 
         rows_i = T * K * I + T * Is
         bflop = 16.0 * rows_i * H     # recompute 4, dh 2, dx 4, dW2 2, dW13 4 (x rows*I*H)
-        # weights read once and their gradients written once, x, dy, dx once
-        bbytes = 2 * (active * 3 * H * I * 2 + 3 * H * Is * 2) + 3 * (T * K + T) * H * 2
+        # weights read once (bf16 or e4m3) and their bf16 gradients written
+        # once, x, dy, dx once
+        wrb = 1 if bwd_fp8 else 2
+        bbytes = (wrb + 2) * (active * 3 * H * I + 3 * H * Is) + 3 * (T * K + T) * H * 2
         wsb = torch.empty(moe.moe_expert_ffn_backward_workspace_bytes(C, T), dtype=torch.uint8,
                           device=dev)
         bms, bk = timed(lambda: moe.moe_expert_ffn_backward(
             C, T, drow["x"], perm, offs, Wrow, dyb, dysb, dxb, dxsb, dw13, dw2, dws13, dws2, wsb,
             stream=stream))
         backward = figures(bms, bflop, bbytes, bk)
+        backward["dtype"] = "e4m3 operands, fp32 accumulation" if bwd_fp8 else "bf16"
         del wsb
 
+    if drow is not None and not bwd_fp8:
         # the layer: y (the routed expert outputs) from the phase timing above
         dout = torch.randn((T, H), generator=gen, device=dev).to(torch.bfloat16)
         dxl = torch.empty((T, H), **bf)
