@@ -23,7 +23,7 @@ pytestmark = pytest.mark.gpu
 class _Weights:
     """Full V3-shape expert weights, generated once per dtype (host + device)."""
     cache = {}
-    row = {}       # row-major bf16 device weights (the backward reads this layout)
+    row = {}       # row-major device weights (the backward reads this layout)
 
     @classmethod
     def get(cls, wdtype):
@@ -38,8 +38,7 @@ class _Weights:
                 synth.gen_shared_weights(cfg)
             log(f"  generated in {time.time() - t0:.1f}s; uploading")
             dev_w = {k: sd.tensor(v) for k, v in host_w.items()}
-            if wdtype == "bf16":
-                cls.row[wdtype] = dict(dev_w)
+            cls.row[wdtype] = dict(dev_w)
             # the benchmark's configuration: packed weights
             dev_w = sd.packed_copy(dict(dev_w, cfg=cfg))
             dev_w.pop("cfg")
@@ -249,6 +248,79 @@ def test_expert_backward_v3_bf16_T4096_sampled():
         e13, e2 = rel_l2(got[:nq], ref[:nq]), rel_l2(got[nq:], ref[nq:])
         log(f"  expert {e} ({len(tok)} rows): dW13 relL2 {e13:.3e}, dW2 relL2 {e2:.3e}")
         assert e13 <= 2e-2 and e2 <= 2e-2, e
+    log(f"  oracle {time.time() - t0:.1f}s; experts without rows: {len(empty)}")
+
+
+def test_expert_backward_v3_fp8e8m0_T8192_sampled():
+    """The FP8 backward of the expert FFNs at the benchmark's e4m3 workload
+    (T = 8192, V3 shape, power-of-two block scales, row-major e4m3 weights,
+    the gate's routing): sampled rows of dx (routed and shared) against the
+    oracle's FP8 backward of those rows (a row's dx depends on that row
+    alone), and the whole dW13 and dW2 of the least busy expert with rows
+    (its column tiles need all its rows) and of one more seeded expert, each
+    within 1e-2; every output finite and experts without rows exactly zero."""
+    cfg = synth.C5P
+    inp, dev = _inputs(cfg)
+    row = dict(dev, **_Weights.row["fp8e8m0"])
+    row.pop("packed", None)
+    T, H, E, K, I, Is = cfg.T, cfg.H, cfg.E, cfg.K, cfg.I, cfg.Is
+    N = T * K
+    log(f"{cfg.name}: FP8 backward of the expert FFNs")
+    _, idx, _ = run_gate(cfg, dev, T)
+    counts, offsets, perm, _, status = run_permute(cfg, idx)
+    assert status == moe.MOE_OK and counts.sum() == N
+    rng = np.random.default_rng(31)
+    dy_b = torch.from_numpy(rng.standard_normal((N, H), dtype=np.float32)).to(torch.bfloat16)
+    dys_b = torch.from_numpy(rng.standard_normal((T, H), dtype=np.float32)).to(torch.bfloat16)
+    dy_np = dy_b.float().numpy().astype(np.float64)
+    dys_np = dys_b.float().numpy().astype(np.float64)
+
+    C = sd.moe_config(cfg)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    bf = dict(dtype=torch.bfloat16, device=DEV)
+    dx, dxs = torch.empty((N, H), **bf), torch.empty((T, H), **bf)
+    dw13, dw2 = torch.empty((E, 2 * I, H), **bf), torch.empty((E, H, I), **bf)
+    dws13, dws2 = torch.empty((2 * Is, H), **bf), torch.empty((H, Is), **bf)
+    ws = torch.empty(moe.moe_expert_ffn_backward_workspace_bytes(C, T), dtype=torch.uint8,
+                     device=DEV)
+    moe.moe_expert_ffn_backward(C, T, row["x"], t(perm), t(offsets), sd.weights_struct(row),
+                                dy_b.to(DEV), dys_b.to(DEV), dx, dxs, dw13, dw2, dws13, dws2, ws)
+    sync()
+    for name, a in (("dx", dx), ("dx_shared", dxs), ("dW13", dw13), ("dW2", dw2),
+                    ("dW13_shared", dws13), ("dW2_shared", dws2)):
+        assert bool(torch.isfinite(a).all()), name
+    empty = np.flatnonzero(counts == 0)
+    for e in empty:
+        assert not bool(dw13[e].any()) and not bool(dw2[e].any()), f"expert {e} without rows"
+
+    t0 = time.time()
+    rows = np.unique(synth.words(24, 61, synth.T_TEST, 62).astype(np.int64) % N)
+    g_dx = host(dx[t(rows)])
+    expert_of = np.searchsorted(offsets, rows, side="right") - 1
+    worst = 0.0
+    for j, (r, e) in enumerate(zip(rows, expert_of)):
+        ref = oracle.ffn_backward(cfg, inp, int(e), perm[r:r + 1] // K, dy_np[r:r + 1],
+                                  want=("dx",), quant_act=True)["dx"][0]
+        worst = max(worst, rel_l2(g_dx[j], ref))
+    log(f"  dx: {len(rows)} rows, worst row relL2 {worst:.3e}")
+    assert worst <= FP8_QUANT_TOL
+    toks = _samples(T, 12, 63)
+    g = host(dxs[t(toks)])
+    ref = oracle.ffn_backward(cfg, inp, -1, toks, dys_np[toks], want=("dx",),
+                              quant_act=True)["dx"]
+    worst = max(rel_l2(g[j], ref[j]) for j in range(len(toks)))
+    log(f"  shared dx: {len(toks)} tokens, worst row relL2 {worst:.3e}")
+    assert worst <= FP8_QUANT_TOL
+    busy = np.flatnonzero(counts > 0)
+    picks = [int(busy[np.argmin(counts[busy])]),
+             int(busy[int(synth.words(1, 67, synth.T_TEST, 64)[0]) % len(busy)])]
+    for e in sorted(set(picks)):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        ref = oracle.ffn_backward(cfg, inp, e, perm[r0:r1] // K, dy_np[r0:r1],
+                                  want=("dw13", "dw2"), quant_act=True)
+        e13, e2 = rel_l2(host(dw13[e]), ref["dw13"]), rel_l2(host(dw2[e]), ref["dw2"])
+        log(f"  expert {e} ({r1 - r0} rows): dW13 relL2 {e13:.3e}, dW2 relL2 {e2:.3e}")
+        assert e13 <= FP8_QUANT_TOL and e2 <= FP8_QUANT_TOL, e
     log(f"  oracle {time.time() - t0:.1f}s; experts without rows: {len(empty)}")
 
 
