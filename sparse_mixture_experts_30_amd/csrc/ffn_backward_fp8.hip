@@ -73,7 +73,13 @@ struct B8Args {
   int ne[2];
 };
 
-template <int kMode, bool kKN, int kSB>
+// E8M0 exponent of a power-of-two fp32 scale (both have exponent bias 127).
+__device__ __forceinline__ int e8m0_bits(float s) { return (int)(__float_as_uint(s) >> 23) & 0xFF; }
+
+// kP2: power-of-two scales, applied by the scaled MFMA itself (each lane
+// passes the scale of its own A row / B row or block), so the k loop
+// accumulates in the matrix cores with no per-block vector work.
+template <int kMode, bool kKN, int kSB, bool kP2>
 __global__ void __launch_bounds__(QT) bwd8_gemm(B8Args p) {
   __shared__ uint4 sA[2][QB * 8];
   __shared__ uint4 sB[2][QB * 8];
@@ -205,33 +211,55 @@ __global__ void __launch_bounds__(QT) bwd8_gemm(B8Args p) {
       bsc = Bs[(int64_t)(n0 / QB) * (SEG(Kd) / QB) + kb0 + step];
     else if (kSB == SB_BLK_KN)
       bsc = Bs[(int64_t)(kb0 + step) * (SEG(N) / QB) + n0 / QB];
-    f32x16 part[2];
+    if (kP2) {
+      const int ea = e8m0_bits(sAs[buf][ar]);
+      int eb[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 2; ++j)
+        eb[j] = e8m0_bits(kSB == SB_ROW ? sBs[buf][64 * wn + 32 * j + lr] : bsc);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) part[j][e] = 0.0f;
+      for (int s = 0; s < 2; ++s) {
+        const int c = 4 * s + 2 * lh;
+        const i32x8 af =
+            as_i32x8(sA[buf][ar * 8 + (c ^ (ar & 7))], sA[buf][ar * 8 + ((c + 1) ^ (ar & 7))]);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int c = 4 * s + 2 * lh;
-      const i32x8 af =
-          as_i32x8(sA[buf][ar * 8 + (c ^ (ar & 7))], sA[buf][ar * 8 + ((c + 1) ^ (ar & 7))]);
+        for (int j = 0; j < 2; ++j) {
+          const int br = 64 * wn + 32 * j + lr;
+          const i32x8 bf = as_i32x8(sB[buf][br * 8 + (c ^ (br & 7))],
+                                    sB[buf][br * 8 + ((c + 1) ^ (br & 7))]);
+          acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, acc[j], 0, 0, 0, ea,
+                                                                  0, eb[j]);
+        }
+      }
+    } else {
+      f32x16 part[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) part[j][e] = 0.0f;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int c = 4 * s + 2 * lh;
+        const i32x8 af =
+            as_i32x8(sA[buf][ar * 8 + (c ^ (ar & 7))], sA[buf][ar * 8 + ((c + 1) ^ (ar & 7))]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int br = 64 * wn + 32 * j + lr;
+          const i32x8 bf = as_i32x8(sB[buf][br * 8 + (c ^ (br & 7))],
+                                    sB[buf][br * 8 + ((c + 1) ^ (br & 7))]);
+          part[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, part[j], 0, 0, 0,
+                                                                   127, 0, 127);
+        }
+      }
+      // C row 8 (e / 4) + 4 lh + e % 4 of the A block, column lr of the B block
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int br = 64 * wn + 32 * j + lr;
-        const i32x8 bf =
-            as_i32x8(sB[buf][br * 8 + (c ^ (br & 7))], sB[buf][br * 8 + ((c + 1) ^ (br & 7))]);
-        part[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, part[j], 0, 0, 0, 127,
-                                                                 0, 127);
-      }
-    }
-    // C row 8 (e / 4) + 4 lh + e % 4 of the A block, column lr of the B block
+        const float sb = kSB == SB_ROW ? sBs[buf][64 * wn + 32 * j + lr] : bsc;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const float sb = kSB == SB_ROW ? sBs[buf][64 * wn + 32 * j + lr] : bsc;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float sa = sAs[buf][32 * wm + 8 * (e >> 2) + 4 * lh + (e & 3)];
-        acc[j][e] = fmaf(part[j][e], sa * sb, acc[j][e]);
+        for (int e = 0; e < 16; ++e) {
+          const float sa = sAs[buf][32 * wm + 8 * (e >> 2) + 4 * lh + (e & 3)];
+          acc[j][e] = fmaf(part[j][e], sa * sb, acc[j][e]);
+        }
       }
     }
     if (step + 1 < nsteps) {
@@ -503,9 +531,13 @@ hipError_t q8_cols(const ColArgs& a, int64_t maxt, int fmax, bool pow2, hipStrea
 }
 
 template <int kMode, bool kKN, int kSB>
-hipError_t gemm8(const B8Args& a, dim3 grid, const char* name, hipStream_t s) {
-  MOE_TIMED_LAUNCH(s, name,
-    hipLaunchKernelGGL((bwd8_gemm<kMode, kKN, kSB>), grid, dim3(QT), 0, s, a));
+hipError_t gemm8(const B8Args& a, dim3 grid, const char* name, bool pow2, hipStream_t s) {
+  if (pow2)
+    MOE_TIMED_LAUNCH(s, name,
+      hipLaunchKernelGGL((bwd8_gemm<kMode, kKN, kSB, true>), grid, dim3(QT), 0, s, a));
+  else
+    MOE_TIMED_LAUNCH(s, name,
+      hipLaunchKernelGGL((bwd8_gemm<kMode, kKN, kSB, false>), grid, dim3(QT), 0, s, a));
   return hipGetLastError();
 }
 
@@ -584,7 +616,7 @@ hipError_t launch_ffn_backward_fp8(const FfnDims& d, bool pow2, const uint16_t* 
   a.ldc[0] = 2 * I;
   a.ldc[1] = 2 * Is;
   const dim3 grid_d((unsigned)(maxt * ntn_d));
-  B8CALL((gemm8<M_GU, false, SB_BLK_NK>(a, grid_d, "bwd8_gemm<gu>", s)));
+  B8CALL((gemm8<M_GU, false, SB_BLK_NK>(a, grid_d, "bwd8_gemm<gu>", pow2, s)));
 
   // dy rows quantised per 1x128 tile along H
   B8CALL(q8_rows<uint16_t>(dy, H, N, H, dyq_r, dys_r, pow2, s));
@@ -623,7 +655,7 @@ hipError_t launch_ffn_backward_fp8(const FfnDims& d, bool pow2, const uint16_t* 
   b.h[1] = h_s;
   b.ne[0] = I;
   b.ne[1] = Is;
-  B8CALL((gemm8<M_DH, true, SB_BLK_KN>(b, grid_d, "bwd8_gemm<dh>", s)));
+  B8CALL((gemm8<M_DH, true, SB_BLK_KN>(b, grid_d, "bwd8_gemm<dh>", pow2, s)));
 
   // [dg du] rows quantised per 1x128 tile along 2n
   B8CALL(q8_rows<float>(da_r, 2 * I, N, 2 * I, daq_r, das_r, pow2, s));
@@ -657,7 +689,7 @@ hipError_t launch_ffn_backward_fp8(const FfnDims& d, bool pow2, const uint16_t* 
     c.c[0] = dx;
     c.c[1] = dxs;
     c.ldc[0] = c.ldc[1] = H;
-    B8CALL((gemm8<M_DX, true, SB_BLK_KN>(c, grid_d, "bwd8_gemm<dx>", s)));
+    B8CALL((gemm8<M_DX, true, SB_BLK_KN>(c, grid_d, "bwd8_gemm<dx>", pow2, s)));
   }
 
   // the weight-gradient operands, quantised per column in row tiles and
@@ -733,7 +765,7 @@ hipError_t launch_ffn_backward_fp8(const FfnDims& d, bool pow2, const uint16_t* 
   w.ldc[1] = Is;
   w.cstride = (int64_t)H * I;
   const dim3 grid_w2((unsigned)((H / QB) * w.ntn), (unsigned)(E + (sh ? 1 : 0)));
-  B8CALL((gemm8<M_WG, false, SB_ROW>(w, grid_w2, "bwd8_gemm<dw2>", s)));
+  B8CALL((gemm8<M_WG, false, SB_ROW>(w, grid_w2, "bwd8_gemm<dw2>", pow2, s)));
 
   // DW13 = Qc([dg du])^T Qc(x): M = 2n, N = H
   B8Args v{};
@@ -757,7 +789,7 @@ hipError_t launch_ffn_backward_fp8(const FfnDims& d, bool pow2, const uint16_t* 
   v.cstride = (int64_t)2 * I * H;
   const dim3 grid_w13((unsigned)((2 * std::max(I, Is) / QB) * v.ntn),
                       (unsigned)(E + (sh ? 1 : 0)));
-  B8CALL((gemm8<M_WG, false, SB_ROW>(v, grid_w13, "bwd8_gemm<dw13>", s)));
+  B8CALL((gemm8<M_WG, false, SB_ROW>(v, grid_w13, "bwd8_gemm<dw13>", pow2, s)));
   return hipSuccess;
 }
 
