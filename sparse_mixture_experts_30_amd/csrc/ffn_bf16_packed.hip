@@ -285,10 +285,8 @@ template <bool kGateUp>
 __global__ void __launch_bounds__(NT, 1) grouped_gemm_bf16_packed(PackedArgs p) {
   extern __shared__ u32x4 smem[];
   const int64_t work = (int64_t)p.tiles[0] * p.ntn;
-  const int64_t per = (work + kNumXcd - 1) / kNumXcd;
-  const int64_t q = blockIdx.x / kNumXcd;
-  const int64_t w = (int64_t)(blockIdx.x % kNumXcd) * per + q;
-  if (q >= per || w >= work) return;
+  const int64_t w = xcd_chunked(blockIdx.x, work);
+  if (w < 0) return;
   int ntile;
   const int32_t* ent = decode_work(p.tiles, w, p.ntn, ntile);
   const int g = ent[0], row0 = ent[1], nrows = ent[2];
@@ -334,10 +332,8 @@ template <bool kGateUp>
 __global__ void __launch_bounds__(NT, 2) grouped_gemm_bf16_packed_x2(PackedArgs p) {
   extern __shared__ u32x4 smem[];
   const int64_t work = (int64_t)p.tiles[0] * p.ntn;
-  const int64_t per = (work + kNumXcd - 1) / kNumXcd;
-  const int64_t q = blockIdx.x / kNumXcd;
-  const int64_t w = (int64_t)(blockIdx.x % kNumXcd) * per + q;
-  if (q >= per || w >= work) return;
+  const int64_t w = xcd_chunked(blockIdx.x, work);
+  if (w < 0) return;
   int ntile;
   const int32_t* ent = decode_work(p.tiles, w, p.ntn, ntile);
   const int g = ent[0], row0 = ent[1], nrows = ent[2];
@@ -373,10 +369,8 @@ template <bool kGateUp>
 __global__ void __launch_bounds__(NT, 1) grouped_gemm_bf16_packed_wide(PackedArgs p) {
   extern __shared__ u32x4 smem[];
   const int64_t work = (int64_t)p.tiles[0] * p.ntn;
-  const int64_t per = (work + kNumXcd - 1) / kNumXcd;
-  const int64_t q = blockIdx.x / kNumXcd;
-  const int64_t w = (int64_t)(blockIdx.x % kNumXcd) * per + q;
-  if (q >= per || w >= work) return;
+  const int64_t w = xcd_chunked(blockIdx.x, work);
+  if (w < 0) return;
   int ntile;
   const int32_t* ent = decode_work(p.tiles, w, p.ntn, ntile);
   const int g = ent[0], row0 = ent[1], nrows = ent[2];
@@ -510,7 +504,7 @@ hipError_t launch_ffn_bf16_packed(const FfnDims& d, const uint16_t* x, const int
     PackedArgs w1 = a1;
     w1.ntn = (a1.ntn + 1) / 2;
     MOE_TIMED_LAUNCH(s, "grouped_gemm_bf16_packed_wide<true>",
-      hipLaunchKernelGGL(grouped_gemm_bf16_packed_wide<true>, dim3(grid(mt * w1.ntn)), dim3(NT),
+      hipLaunchKernelGGL(grouped_gemm_bf16_packed_wide<true>, dim3(xcd_grid(mt * w1.ntn)), dim3(NT),
                          kLdsW, s, w1));
   } else if (few == 1)
     MOE_TIMED_LAUNCH(s, "grouped_gemm_bf16_packed_few<true, 1>",
@@ -522,7 +516,7 @@ hipError_t launch_ffn_bf16_packed(const FfnDims& d, const uint16_t* x, const int
                          dim3(grid(mt * a1.ntn * kFewSlots)), dim3(64), 0, s, a1));
   else
     MOE_TIMED_LAUNCH(s, "grouped_gemm_bf16_packed<true>",
-      hipLaunchKernelGGL(grouped_gemm_bf16_packed<true>, dim3(grid(mt * a1.ntn)), dim3(NT), kLdsP, s,
+      hipLaunchKernelGGL(grouped_gemm_bf16_packed<true>, dim3(xcd_grid(mt * a1.ntn)), dim3(NT), kLdsP, s,
                          a1));
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -565,7 +559,7 @@ hipError_t launch_ffn_bf16_packed(const FfnDims& d, const uint16_t* x, const int
     if (e != hipSuccess) return e;
     const int64_t mt2 = ffn_grid_mtiles(d, BM2);
     MOE_TIMED_LAUNCH(s, "grouped_gemm_bf16_packed_x2<false>",
-      hipLaunchKernelGGL(grouped_gemm_bf16_packed_x2<false>, dim3(grid(mt2 * a2.ntn)), dim3(NT),
+      hipLaunchKernelGGL(grouped_gemm_bf16_packed_x2<false>, dim3(xcd_grid(mt2 * a2.ntn)), dim3(NT),
                          kLdsP2, s, a2));
   }
   return hipGetLastError();

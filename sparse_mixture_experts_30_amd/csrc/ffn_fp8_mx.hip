@@ -391,10 +391,8 @@ template <bool kGateUp>
 __global__ void __launch_bounds__(NT, 1) grouped_gemm_fp8_mx(MxArgs p) {
   extern __shared__ u32x4 smem[];
   const int64_t work = (int64_t)p.tiles[0] * p.ntn;
-  const int64_t per = (work + kNumXcd - 1) / kNumXcd;
-  const int64_t q = blockIdx.x / kNumXcd;
-  const int64_t w = (int64_t)(blockIdx.x % kNumXcd) * per + q;
-  if (q >= per || w >= work) return;
+  const int64_t w = xcd_chunked(blockIdx.x, work);
+  if (w < 0) return;
   int ntile;
   const int32_t* ent = decode_work(p.tiles, w, p.ntn, ntile);
   const int g = ent[0], row0 = ent[1], nrows = ent[2];
@@ -450,9 +448,6 @@ hipError_t launch_ffn_fp8_mx(const FfnDims& d, const uint8_t* xq, const float* x
   e = ffn_build_tiles(d, offsets, BM, tiles, s, true);
   if (e != hipSuccess) return e;
   const int64_t mt = ffn_grid_mtiles(d, BM);
-  auto grid = [](int64_t max_work) {
-    return (unsigned)(((max_work + kNumXcd - 1) / kNumXcd) * kNumXcd);
-  };
 
   MxArgs a1{};
   a1.tiles = tiles;
@@ -476,7 +471,7 @@ hipError_t launch_ffn_fp8_mx(const FfnDims& d, const uint8_t* xq, const float* x
   a1.hs_r = hs;
   a1.hs_s = hs + d.N * (d.I / 128);
   MOE_TIMED_LAUNCH(s, "grouped_gemm_fp8_mx<true>",
-    hipLaunchKernelGGL(grouped_gemm_fp8_mx<true>, dim3(grid(mt * a1.ntn)), dim3(NT), kLds, s,
+    hipLaunchKernelGGL(grouped_gemm_fp8_mx<true>, dim3(xcd_grid(mt * a1.ntn)), dim3(NT), kLds, s,
                        a1));
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -502,7 +497,7 @@ hipError_t launch_ffn_fp8_mx(const FfnDims& d, const uint8_t* xq, const float* x
   a2.c_r = y;
   a2.c_s = ys;
   MOE_TIMED_LAUNCH(s, "grouped_gemm_fp8_mx<false>",
-    hipLaunchKernelGGL(grouped_gemm_fp8_mx<false>, dim3(grid(mt * a2.ntn)), dim3(NT), kLds, s,
+    hipLaunchKernelGGL(grouped_gemm_fp8_mx<false>, dim3(xcd_grid(mt * a2.ntn)), dim3(NT), kLds, s,
                        a2));
   return hipGetLastError();
 }

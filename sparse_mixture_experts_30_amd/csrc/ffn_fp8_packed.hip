@@ -379,10 +379,8 @@ template <bool kGateUp>
 __global__ void __launch_bounds__(NT, 1) grouped_gemm_fp8_packed(Packed8Args p) {
   extern __shared__ u32x4 smem[];
   const int64_t work = (int64_t)p.tiles[0] * p.ntn;
-  const int64_t per = (work + kNumXcd - 1) / kNumXcd;
-  const int64_t q = blockIdx.x / kNumXcd;
-  const int64_t w = (int64_t)(blockIdx.x % kNumXcd) * per + q;
-  if (q >= per || w >= work) return;
+  const int64_t w = xcd_chunked(blockIdx.x, work);
+  if (w < 0) return;
   int ntile;
   const int32_t* ent = decode_work(p.tiles, w, p.ntn, ntile);
   const int g = ent[0], row0 = ent[1], nrows = ent[2];
@@ -455,9 +453,6 @@ hipError_t launch_ffn_fp8_packed(const FfnDims& d, const uint8_t* xq, const floa
   e = ffn_build_tiles(d, offsets, BM, tiles, s);
   if (e != hipSuccess) return e;
   const int64_t mt = ffn_grid_mtiles(d, BM);
-  auto grid = [](int64_t max_work) {
-    return (unsigned)(((max_work + kNumXcd - 1) / kNumXcd) * kNumXcd);
-  };
 
   Packed8Args a1{};
   a1.tiles = tiles;
@@ -481,7 +476,7 @@ hipError_t launch_ffn_fp8_packed(const FfnDims& d, const uint8_t* xq, const floa
   a1.hs_r = hs;
   a1.hs_s = hs + d.N * (d.I / 128);
   MOE_TIMED_LAUNCH(s, "grouped_gemm_fp8_packed<true>",
-    hipLaunchKernelGGL(grouped_gemm_fp8_packed<true>, dim3(grid(mt * a1.ntn)), dim3(NT), kLds, s,
+    hipLaunchKernelGGL(grouped_gemm_fp8_packed<true>, dim3(xcd_grid(mt * a1.ntn)), dim3(NT), kLds, s,
                        a1));
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -507,7 +502,7 @@ hipError_t launch_ffn_fp8_packed(const FfnDims& d, const uint8_t* xq, const floa
   a2.c_r = y;
   a2.c_s = ys;
   MOE_TIMED_LAUNCH(s, "grouped_gemm_fp8_packed<false>",
-    hipLaunchKernelGGL(grouped_gemm_fp8_packed<false>, dim3(grid(mt * a2.ntn)), dim3(NT), kLds, s,
+    hipLaunchKernelGGL(grouped_gemm_fp8_packed<false>, dim3(xcd_grid(mt * a2.ntn)), dim3(NT), kLds, s,
                        a2));
   return hipGetLastError();
 }

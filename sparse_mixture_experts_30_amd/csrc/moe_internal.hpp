@@ -54,6 +54,24 @@ __device__ __forceinline__ int xcd_contiguous(int b, int nb) {
   return (b % kNumXcd) * per + b / kNumXcd;
 }
 
+// Work item of workgroup b when chunks of kXcdChunk consecutive items go to
+// the XCDs in turn (chunk c to XCD c % kNumXcd).  Each XCD then gets an even
+// share of every part of a grouped GEMM's work list (the shared expert's
+// heavy tiles at its end included), while the neighbouring items of a chunk
+// (M-tiles that share a weight tile, N-tiles that share a group's rows) stay
+// on one XCD and its L2.  The grid is a multiple of kXcdGrid (xcd_grid);
+// returns -1 for the surplus workgroups past `work`.
+constexpr int kXcdChunk = 16;
+constexpr int64_t kXcdGrid = (int64_t)kNumXcd * kXcdChunk;
+__device__ __forceinline__ int64_t xcd_chunked(int64_t b, int64_t work) {
+  const int64_t q = b / kNumXcd;
+  const int64_t w = ((q / kXcdChunk) * kNumXcd + b % kNumXcd) * kXcdChunk + q % kXcdChunk;
+  return w < work ? w : -1;
+}
+inline unsigned xcd_grid(int64_t max_work) {
+  return (unsigned)(((max_work + kXcdGrid - 1) / kXcdGrid) * kXcdGrid);
+}
+
 // ---------------------------------------------------------------- kernel timer
 // Brackets one kernel launch with HIP events on its stream while the timer
 // (moe_kernel_timer_enable) is on; `name` must be a string literal.
