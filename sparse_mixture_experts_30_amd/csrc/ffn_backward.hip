@@ -332,10 +332,8 @@ __global__ void __launch_bounds__(BNT) bwd_rows_kernel(BwdArgs p) {
   constexpr int BK = 64;
   __shared__ u32x4 lds[2][(BBM + BBN) * (BK / 8)];   // 64 KiB
   const int64_t work = (int64_t)p.tiles[0] * p.ntn;
-  const int64_t per = (work + kNumXcd - 1) / kNumXcd;
-  const int64_t q = blockIdx.x / kNumXcd;
-  const int64_t w = (int64_t)(blockIdx.x % kNumXcd) * per + q;
-  if (q >= per || w >= work) return;
+  const int64_t w = xcd_chunked(blockIdx.x, work);
+  if (w < 0) return;
   int ntile;
   const int32_t* ent = decode_work(p.tiles, w, p.ntn, ntile);
   const int g = ent[0], row0 = ent[1], nrows = ent[2];
@@ -380,11 +378,13 @@ __global__ void __launch_bounds__(BNT, kWgradPerCu) bwd_wgrad_kernel(BwdArgs p) 
   const int64_t per_g = (int64_t)p.mt * p.nt;
   const int64_t groups = p.E + (p.M[1] > 0 ? 1 : 0);
   const int64_t work = groups * per_g;
-  const int64_t per = (work + kNumXcd - 1) / kNumXcd;
-  const int64_t nper = gridDim.x / kNumXcd;
-  const int64_t begin = (int64_t)(blockIdx.x % kNumXcd) * per;
-  const int64_t end = min(work, begin + per);
-  for (int64_t w = begin + blockIdx.x / kNumXcd; w < end; w += nper) {
+  // Workgroup b takes the items of virtual workgroups b, b + G, b + 2G, ...
+  // (G, the grid, a multiple of kXcdGrid), dealt out in XCD chunks: every
+  // XCD gets its share of each part of the list, the shared expert's long
+  // tiles at its end included.
+  for (int64_t vb = blockIdx.x;; vb += gridDim.x) {
+    const int64_t w = xcd_chunked(vb, work);
+    if (w < 0) break;
     const int g = (int)(w / per_g);
     const int rest = (int)(w % per_g);
     const int mtile = rest / p.nt, ntile = rest % p.nt;
@@ -469,19 +469,17 @@ transpose_kernel(const uint16_t* __restrict__ src, int H, const int32_t* __restr
   }
 }
 
-unsigned grid_for(int64_t work) {
-  return (unsigned)(((work + kNumXcd - 1) / kNumXcd) * kNumXcd);
-}
 
 // Workgroups of the looping weight-gradient kernel: kWgradPerCu per CU of
-// the current device, at most one per tile, a multiple of the XCD count.
+// the current device rounded down to a multiple of kXcdGrid (at least one).
 unsigned wgrad_grid(int64_t work) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       cus <= 0)
     cus = 256;
-  return grid_for(std::min<int64_t>(work, (int64_t)cus * kWgradPerCu));
+  const int64_t slots = std::max<int64_t>((int64_t)cus * kWgradPerCu / kXcdGrid, 1) * kXcdGrid;
+  return (unsigned)std::min<int64_t>(slots, xcd_grid(work));
 }
 
 // Row stride (elements) of at least n whose size in bytes is an odd
@@ -617,7 +615,7 @@ hipError_t launch_ffn_backward(const FfnDims& d, const uint16_t* x, const int32_
     q.ldT[0] = L.ldr; q.ldT[1] = L.lds;
     q.ntn = (std::max(I, Is) + BBN - 1) / BBN;
     MOE_TIMED_LAUNCH(s, "bwd_rows_kernel<dh>",
-      hipLaunchKernelGGL(bwd_rows_kernel<E_DH>, dim3(grid_for(mt * q.ntn)), dim3(BNT), 0, s, q));
+      hipLaunchKernelGGL(bwd_rows_kernel<E_DH>, dim3(xcd_grid(mt * q.ntn)), dim3(BNT), 0, s, q));
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // DX: dx_rows = [dg du] W13 (rows x H, k = 2I).
@@ -629,7 +627,7 @@ hipError_t launch_ffn_backward(const FfnDims& d, const uint16_t* x, const int32_
     q.c[0] = dx; q.c[1] = dxs; q.ldc[0] = q.ldc[1] = H;
     q.ntn = (H + BBN - 1) / BBN;
     MOE_TIMED_LAUNCH(s, "bwd_rows_kernel<dx>",
-      hipLaunchKernelGGL(bwd_rows_kernel<E_STORE>, dim3(grid_for(mt * q.ntn)), dim3(BNT), 0, s,
+      hipLaunchKernelGGL(bwd_rows_kernel<E_STORE>, dim3(xcd_grid(mt * q.ntn)), dim3(BNT), 0, s,
                          q));
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }

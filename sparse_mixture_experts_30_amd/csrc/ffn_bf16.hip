@@ -77,12 +77,10 @@ __global__ void __launch_bounds__(NT, 1) grouped_gemm_bf16(GemmArgs p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 31, lh = lane >> 5;
 
-  // Work item: XCD-contiguous over the real work count.
+  // Work item: dealt to the XCDs in chunks over the real work count.
   const int64_t work = (int64_t)p.tiles[0] * p.ntn;
-  const int64_t per = (work + kNumXcd - 1) / kNumXcd;
-  const int64_t q = blockIdx.x / kNumXcd;
-  const int64_t w = (int64_t)(blockIdx.x % kNumXcd) * per + q;
-  if (q >= per || w >= work) return;
+  const int64_t w = xcd_chunked(blockIdx.x, work);
+  if (w < 0) return;
   int ntile;
   const int32_t* ent = decode_work(p.tiles, w, p.ntn, ntile);
   const int g = ent[0], row0 = ent[1], nrows = ent[2];
@@ -251,9 +249,6 @@ hipError_t set_attrs() {
   return e;
 }
 
-unsigned grid_for(int64_t max_work) {
-  return (unsigned)(((max_work + kNumXcd - 1) / kNumXcd) * kNumXcd);
-}
 
 }  // namespace
 
@@ -294,7 +289,7 @@ hipError_t launch_ffn_bf16(const FfnDims& d, const uint16_t* x, const int32_t* p
   a1.ldc_r = d.I;
   a1.ldc_s = d.Is;
   MOE_TIMED_LAUNCH(s, "grouped_gemm_bf16<true>",
-    hipLaunchKernelGGL(grouped_gemm_bf16<true>, dim3(grid_for(mt * a1.ntn)), dim3(NT), kLds, s, a1));
+    hipLaunchKernelGGL(grouped_gemm_bf16<true>, dim3(xcd_grid(mt * a1.ntn)), dim3(NT), kLds, s, a1));
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -318,7 +313,7 @@ hipError_t launch_ffn_bf16(const FfnDims& d, const uint16_t* x, const int32_t* p
   a2.c_s = ys;
   a2.ldc_r = a2.ldc_s = d.H;
   MOE_TIMED_LAUNCH(s, "grouped_gemm_bf16<false>",
-    hipLaunchKernelGGL(grouped_gemm_bf16<false>, dim3(grid_for(mt * a2.ntn)), dim3(NT), kLds, s, a2));
+    hipLaunchKernelGGL(grouped_gemm_bf16<false>, dim3(xcd_grid(mt * a2.ntn)), dim3(NT), kLds, s, a2));
   return hipGetLastError();
 }
 
@@ -350,7 +345,7 @@ hipError_t launch_gate_up_bf16(const FfnDims& d, const uint16_t* x, const int32_
   a.ldc_r = ldgu;
   a.ldc_s = ldgus;
   MOE_TIMED_LAUNCH(s, "grouped_gemm_bf16<gate_up>",
-    hipLaunchKernelGGL((grouped_gemm_bf16<true, true>), dim3(grid_for(mt * a.ntn)), dim3(NT), kLds,
+    hipLaunchKernelGGL((grouped_gemm_bf16<true, true>), dim3(xcd_grid(mt * a.ntn)), dim3(NT), kLds,
                        s, a));
   return hipGetLastError();
 }

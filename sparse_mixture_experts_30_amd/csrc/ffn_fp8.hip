@@ -106,10 +106,8 @@ __global__ void __launch_bounds__(NT, 1) grouped_gemm_fp8(Gemm8Args p) {
   const int lr = lane & 31, lh = lane >> 5;
 
   const int64_t work = (int64_t)p.tiles[0] * p.ntn;
-  const int64_t per = (work + kNumXcd - 1) / kNumXcd;
-  const int64_t q = blockIdx.x / kNumXcd;
-  const int64_t w = (int64_t)(blockIdx.x % kNumXcd) * per + q;
-  if (q >= per || w >= work) return;
+  const int64_t w = xcd_chunked(blockIdx.x, work);
+  if (w < 0) return;
   int ntile;
   const int32_t* ent = decode_work(p.tiles, w, p.ntn, ntile);
   const int g = ent[0], row0 = ent[1], nrows = ent[2];
@@ -312,9 +310,6 @@ hipError_t set_attrs8() {
   return once;
 }
 
-unsigned grid8(int64_t max_work) {
-  return (unsigned)(((max_work + kNumXcd - 1) / kNumXcd) * kNumXcd);
-}
 
 }  // namespace
 
@@ -369,7 +364,7 @@ hipError_t launch_ffn_fp8(const FfnDims& d, const uint8_t* xq, const float* xs,
   a1.hs_r = hs;
   a1.hs_s = hs_s;
   MOE_TIMED_LAUNCH(s, "grouped_gemm_fp8<true>",
-    hipLaunchKernelGGL(grouped_gemm_fp8<true>, dim3(grid8(mt * a1.ntn)), dim3(NT), kLds8, s, a1));
+    hipLaunchKernelGGL(grouped_gemm_fp8<true>, dim3(xcd_grid(mt * a1.ntn)), dim3(NT), kLds8, s, a1));
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -395,7 +390,7 @@ hipError_t launch_ffn_fp8(const FfnDims& d, const uint8_t* xq, const float* xs,
   a2.c_r = y;
   a2.c_s = ys;
   MOE_TIMED_LAUNCH(s, "grouped_gemm_fp8<false>",
-    hipLaunchKernelGGL(grouped_gemm_fp8<false>, dim3(grid8(mt * a2.ntn)), dim3(NT), kLds8, s, a2));
+    hipLaunchKernelGGL(grouped_gemm_fp8<false>, dim3(xcd_grid(mt * a2.ntn)), dim3(NT), kLds8, s, a2));
   return hipGetLastError();
 }
 
