@@ -56,8 +56,12 @@ constexpr int FRAG = 2048;         // 16-byte fragments per packed block (32 KiB
 // (GEMM1: tile maxima [4][BM] + codes [BM][128]; GEMM2: bf16 rows of half
 // the tokens, [BM/2][256]).
 constexpr size_t kLdsMain = (size_t)2 * BM * 8 * sizeof(u32x4) + 2 * BM * sizeof(float);
-constexpr size_t kLdsEpi1 = (size_t)4 * BM * sizeof(float) + (size_t)BM * 128;
-constexpr size_t kLdsEpi2 = (size_t)(BM / 2) * 256 * sizeof(uint16_t);
+// Epilogue LDS rows are padded by 16 bytes (kQRow, kCRow), so that the 32
+// token rows a wave writes with one instruction fall in different banks.
+constexpr int kQRow = 128 + 16;    // bytes per h-code row
+constexpr int kCRow = 256 + 8;     // bf16 values per output row
+constexpr size_t kLdsEpi1 = (size_t)4 * BM * sizeof(float) + (size_t)BM * kQRow;
+constexpr size_t kLdsEpi2 = (size_t)(BM / 2) * kCRow * sizeof(uint16_t);
 constexpr size_t kLds = std::max(kLdsMain, std::max(kLdsEpi1, kLdsEpi2));   // 66 KiB
 
 // fp32 -> e4m3fn bits, round to nearest even; |v| <= 448 on this path.
@@ -304,7 +308,7 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, u32x4* smem, int g, int
     // over lane halves by a shuffle and over the 4 waves through LDS, then
     // its codes; only one block's 16 h values are live at a time.
     float* sMax = reinterpret_cast<float*>(smem);                   // [4][BM]
-    uint8_t* sQ = reinterpret_cast<uint8_t*>(smem) + 4 * BM * 4;   // [BM][128]
+    uint8_t* sQ = reinterpret_cast<uint8_t*>(smem) + 4 * BM * 4;   // [BM][kQRow]
     uint8_t* HQ = sh ? p.hq_s : p.hq_r;
     float* HS = sh ? p.hs_s : p.hs_r;
     const int nblk = ncol / 128;
@@ -340,7 +344,7 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, u32x4* smem, int g, int
 #pragma unroll
         for (int b = 0; b < 4; ++b) word |= e4m3_rne(hv[4 * q + b] * inv) << (8 * b);
         // h columns 32 wave + 8 q + 4 lh .. +4 of this tile
-        *reinterpret_cast<uint32_t*>(sQ + tok * 128 + 32 * wave + 8 * q + 4 * lh) = word;
+        *reinterpret_cast<uint32_t*>(sQ + tok * kQRow + 32 * wave + 8 * q + 4 * lh) = word;
       }
       if (wave == 0 && lh == 0 && tok < nrows) HS[(int64_t)(row0 + tok) * nblk + n0 / 128] = scale;
     }
@@ -349,11 +353,11 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, u32x4* smem, int g, int
     for (int c = tid; c < nrows * 8; c += NT) {
       const int tok = c >> 3, part = c & 7;
       *reinterpret_cast<u32x4*>(HQ + (int64_t)(row0 + tok) * ncol + n0 + 16 * part) =
-          *reinterpret_cast<const u32x4*>(sQ + tok * 128 + 16 * part);
+          *reinterpret_cast<const u32x4*>(sQ + tok * kQRow + 16 * part);
     }
   } else {
     // bf16 rows staged in LDS for 16-byte stores, half the tokens at a time.
-    uint16_t* sC = reinterpret_cast<uint16_t*>(smem);   // [BM / 2][256]
+    uint16_t* sC = reinterpret_cast<uint16_t*>(smem);   // [BM / 2][kCRow]
     uint16_t* C = sh ? p.c_s : p.c_r;
     const int width = min(256, ncol - n0);   // multiple of 8 (H % 128 == 0)
     const int per_row = width / 8;
@@ -371,7 +375,7 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, u32x4* smem, int g, int
             const int col = 64 * wave + 32 * c + 8 * q + 4 * lh;
             const uint32_t lo = pack_bf16x2(acc[r][c][4 * q], acc[r][c][4 * q + 1]);
             const uint32_t hi = pack_bf16x2(acc[r][c][4 * q + 2], acc[r][c][4 * q + 3]);
-            *reinterpret_cast<uint2*>(sC + tok * 256 + col) = make_uint2(lo, hi);
+            *reinterpret_cast<uint2*>(sC + tok * kCRow + col) = make_uint2(lo, hi);
           }
       }
       __syncthreads();
@@ -381,7 +385,7 @@ __device__ __forceinline__ void mx_tile(const MxArgs& p, u32x4* smem, int g, int
         const int tok = c >> 5, part = c & 31;
         if (part < per_row)
           *reinterpret_cast<u32x4*>(C + (int64_t)(row0 + base + tok) * ncol + n0 + 8 * part) =
-              *reinterpret_cast<const u32x4*>(sC + tok * 256 + 8 * part);
+              *reinterpret_cast<const u32x4*>(sC + tok * kCRow + 8 * part);
       }
     }
   }

@@ -43,9 +43,13 @@ constexpr int NT = 256;
 constexpr int FRAG = 2048;         // 16-byte fragments per packed block (32 KiB)
 // LDS: token tile double buffer + token scales; the epilogue reuses it.
 constexpr size_t kLdsMain = (size_t)2 * BM * 8 * sizeof(u32x4) + 2 * BM * sizeof(float);
-constexpr size_t kLdsEpi1 = (size_t)4 * BM * sizeof(float) + (size_t)BM * 128;   // amax + codes
-constexpr size_t kLdsEpi2 = (size_t)BM * 256 * sizeof(uint16_t);                  // bf16 rows
-constexpr size_t kLds = std::max(kLdsMain, std::max(kLdsEpi1, kLdsEpi2));        // 64 KiB
+// Epilogue LDS rows are padded by 16 bytes (kQRow, kCRow), so that the 32
+// token rows a wave writes with one instruction fall in different banks.
+constexpr int kQRow = 128 + 16;    // bytes per h-code row
+constexpr int kCRow = 256 + 8;     // bf16 values per output row
+constexpr size_t kLdsEpi1 = (size_t)4 * BM * sizeof(float) + (size_t)BM * kQRow;  // amax + codes
+constexpr size_t kLdsEpi2 = (size_t)BM * kCRow * sizeof(uint16_t);                // bf16 rows
+constexpr size_t kLds = std::max(kLdsMain, std::max(kLdsEpi1, kLdsEpi2));        // 66 KiB
 
 // fp32 -> e4m3fn bits: round to nearest even, saturate at 448.
 __device__ __forceinline__ uint32_t to_e4m3(float v) {
@@ -301,7 +305,7 @@ __device__ __forceinline__ void fp8_tile(const Packed8Args& p, u32x4* smem, int 
     // quantisation tile (32 per wave): amax over lanes lh = 0, 1 by a
     // shuffle, over the 4 waves through LDS.
     float* sMax = reinterpret_cast<float*>(smem);                   // [4][BM]
-    uint8_t* sQ = reinterpret_cast<uint8_t*>(smem) + 4 * BM * 4;   // [BM][128]
+    uint8_t* sQ = reinterpret_cast<uint8_t*>(smem) + 4 * BM * 4;   // [BM][kQRow]
     float hv[NRB][16];
 #pragma unroll
     for (int r = 0; r < NRB; ++r) {
@@ -335,7 +339,7 @@ __device__ __forceinline__ void fp8_tile(const Packed8Args& p, u32x4* smem, int 
 #pragma unroll
         for (int b = 0; b < 4; ++b) word |= to_e4m3(hv[r][4 * q + b] * inv) << (8 * b);
         // h columns 32 wave + 8 q + 4 lh .. +4 of this tile
-        *reinterpret_cast<uint32_t*>(sQ + tok * 128 + 32 * wave + 8 * q + 4 * lh) = word;
+        *reinterpret_cast<uint32_t*>(sQ + tok * kQRow + 32 * wave + 8 * q + 4 * lh) = word;
       }
       if (wave == 0 && lh == 0 && tok < nrows) HS[(int64_t)(row0 + tok) * nblk + n0 / 128] = scale;
     }
@@ -344,11 +348,11 @@ __device__ __forceinline__ void fp8_tile(const Packed8Args& p, u32x4* smem, int 
     for (int c = tid; c < nrows * 8; c += NT) {
       const int tok = c >> 3, part = c & 7;
       *reinterpret_cast<u32x4*>(HQ + (int64_t)(row0 + tok) * ncol + n0 + 16 * part) =
-          *reinterpret_cast<const u32x4*>(sQ + tok * 128 + 16 * part);
+          *reinterpret_cast<const u32x4*>(sQ + tok * kQRow + 16 * part);
     }
   } else {
     __syncthreads();   // the token tile is no longer read
-    uint16_t* sC = reinterpret_cast<uint16_t*>(smem);   // [BM][256]
+    uint16_t* sC = reinterpret_cast<uint16_t*>(smem);   // [BM][kCRow]
 #pragma unroll
     for (int r = 0; r < NRB; ++r) {
       const int tok = r * 32 + lr;
@@ -359,7 +363,7 @@ __device__ __forceinline__ void fp8_tile(const Packed8Args& p, u32x4* smem, int 
           const int col = 64 * wave + 32 * c + 8 * q + 4 * lh;
           const uint32_t lo = pack_bf16x2(acc[r][c][4 * q], acc[r][c][4 * q + 1]);
           const uint32_t hi = pack_bf16x2(acc[r][c][4 * q + 2], acc[r][c][4 * q + 3]);
-          *reinterpret_cast<uint2*>(sC + tok * 256 + col) = make_uint2(lo, hi);
+          *reinterpret_cast<uint2*>(sC + tok * kCRow + col) = make_uint2(lo, hi);
         }
     }
     __syncthreads();
@@ -370,7 +374,7 @@ __device__ __forceinline__ void fp8_tile(const Packed8Args& p, u32x4* smem, int 
       const int tok = c >> 5, part = c & 31;
       if (part < per_row)
         *reinterpret_cast<u32x4*>(C + (int64_t)(row0 + tok) * ncol + n0 + 8 * part) =
-            *reinterpret_cast<const u32x4*>(sC + tok * 256 + 8 * part);
+            *reinterpret_cast<const u32x4*>(sC + tok * kCRow + 8 * part);
     }
   }
 }
