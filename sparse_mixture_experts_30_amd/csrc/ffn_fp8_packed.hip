@@ -454,7 +454,8 @@ hipError_t launch_ffn_fp8_packed(const FfnDims& d, const uint8_t* xq, const floa
                                  uint16_t* y, uint16_t* ys, hipStream_t s) {
   hipError_t e = set_attrs_fp8_packed();
   if (e != hipSuccess) return e;
-  e = ffn_build_tiles(d, offsets, BM, tiles, s);
+  // balanced M-tiles: a weight tile's M-tiles stream it at the same pace
+  e = ffn_build_tiles(d, offsets, BM, tiles, s, true);
   if (e != hipSuccess) return e;
   const int64_t mt = ffn_grid_mtiles(d, BM);
 
