@@ -52,6 +52,7 @@ KERNEL_SOURCES = {
     "grouped_gemm_bf16": ("ffn_bf16.hip", "moe_internal.hpp"),
     "grouped_gemm_fp8": ("ffn_fp8.hip", "moe_internal.hpp"),
     "gate_logits_bf16_kernel": ("gate.hip", "gate_split.hpp", "moe_internal.hpp"),
+    "gate_select_fused_kernel": ("gate.hip", "gate_split.hpp", "moe_internal.hpp"),
 }
 
 
@@ -113,6 +114,9 @@ def kernel_work(kernel, cfg, active):
         return w + a_in + out, flop
     if base == "gate_logits_bf16_kernel":
         return T * H * ab + E * H * 4 + T * E * 4, 2.0 * T * E * H
+    if base == "gate_select_fused_kernel":
+        # x and the gate weight (fp32) in; the logits, ids and weights out
+        return T * H * ab + E * H * 4 + E * 4 + T * E * 4 + T * K * 8, 2.0 * T * E * H
     if base == "decode_layer_kernel":
         # the whole layer in one launch: the layer's own algorithmic work
         # (x and the output once, the gate weight and bias, the active
@@ -322,6 +326,33 @@ def main():
                           "step_entry_point_ms_same_rounds": round(med[entry], 4)})
             log(f"[bench] {e}: {med[e]:.3f} ms/step (step entry point {entry} "
                 f"{med[entry]:.3f} ms in the same rounds)")
+    if gate_only and not args.profile_only:
+        # The gate and selection in one kernel (MOE_GATE_FUSED) against the
+        # default split kernels: alternating rounds, cold caches, medians.
+        times = {moe.MOE_GATE_SPLIT: [], moe.MOE_GATE_FUSED: []}
+        flush_o = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        try:
+            for r in range(3):
+                for mode in times:
+                    moe.moe_set_gate_mode(mode)
+                    step()
+                    for i in range(args.steps):
+                        flush_o.fill_((r + i) & 0xFF)
+                        ev0.record(stream)
+                        step()
+                        ev1.record(stream)
+                        torch.cuda.synchronize()
+                        times[mode].append(ev0.elapsed_time(ev1))
+        finally:
+            moe.moe_set_gate_mode(moe.MOE_GATE_SPLIT)
+        del flush_o
+        ms_s = statistics.median(times[moe.MOE_GATE_SPLIT])
+        ms_f = statistics.median(times[moe.MOE_GATE_FUSED])
+        other.append({"entry_point": "moe_gate (MOE_GATE_FUSED) + moe_permute", "ms": round(ms_f, 4),
+                      "tokens_per_s": round(T / (ms_f * 1e-3), 1),
+                      "step_entry_point_ms_same_rounds": round(ms_s, 4)})
+        log(f"[bench] fused gate: {ms_f:.3f} ms/step (split gate {ms_s:.3f} ms in the same "
+            f"rounds)")
 
     # Per-phase timing with the separate entry points (same kernels, same
     # stream), HIP events between phases.

@@ -141,6 +141,27 @@ moe_status moe_gate(const moe_config* cfg, int64_t T, const void* x, const float
                     const float* bias, float* logits, int32_t* topk_idx, float* topk_w,
                     void* ws, size_t ws_bytes, void* stream);
 
+/* How moe_gate and moe_forward run the gate and the selection of bf16 tokens
+ * (the same layer step as moe_gate above; the routing is the same function
+ * of the fp32 logits either way, the logits may differ in the last bits
+ * because the k sums are ordered differently):
+ *   MOE_GATE_SPLIT (default): the gate GEMM writes k-split partial logits
+ *     to the workspace and a second kernel sums them and selects;
+ *   MOE_GATE_FUSED: one kernel per 64 tokens computes all E logits over
+ *     the whole hidden size, keeps them in LDS and selects in its epilogue
+ *     (nothing but the outputs goes to memory); taken only for shapes it
+ *     supports (E a multiple of 32 up to 256, n_group dividing E with either
+ *     whole groups per eighth of E or a group spanning 2, 4 or 8 eighths,
+ *     n_group <= 32, top_k <= 16, hidden_size a multiple of 64), else SPLIT.
+ *     On an MI355X it is slower than SPLIT at every batch size measured
+ *     (T = 16384: about 0.28 against 0.26 ms): a workgroup holding every
+ *     expert of its tokens holds only 64 tokens, so each weight byte read
+ *     from L2 feeds half as many MFMAs.
+ * Process-wide; decode batches (T <= 32) of moe_forward keep their own
+ * routing schedule.  Returns MOE_ERR_INVALID_ARG for other values. */
+typedef enum { MOE_GATE_SPLIT = 0, MOE_GATE_FUSED = 1 } moe_gate_mode;
+moe_status moe_set_gate_mode(int mode);
+
 /* Dispatch order (first page, section 2.3).
  *   topk_idx [T, K] int32 in (values in [0, E); others set the device error
  *           flag in ws, see moe_get_device_error, and are skipped)

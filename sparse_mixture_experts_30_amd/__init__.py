@@ -16,6 +16,7 @@ from ._lib import (EXPORTS, MOE_BF16, MOE_ERR_DEVICE_CHECK, MOE_ERR_HIP, MOE_ERR
                    moe_forward_overlap, moe_forward_decode_fused, MOE_NOALLOC_SCRATCH_BYTES,
                    moe_gate, moe_get_device_error,
                    moe_kernel_timer_enable, moe_kernel_timer_read, moe_last_error,
-                   moe_permute, moe_quantize_act, moe_strerror, moe_workspace_bytes, weights)
+                   moe_permute, moe_quantize_act, moe_strerror, moe_workspace_bytes, weights,
+                   moe_set_gate_mode, MOE_GATE_SPLIT, MOE_GATE_FUSED)
 
 __all__ = [n for n in dir() if not n.startswith("_")]

@@ -21,7 +21,7 @@ EXPORTS = ("moe_workspace_bytes", "moe_gate", "moe_permute", "moe_expert_ffn", "
            "moe_get_device_error", "moe_strerror", "moe_last_error", "moe_kernel_timer_enable",
            "moe_kernel_timer_read", "moe_bias_update", "moe_expert_ffn_backward",
            "moe_expert_ffn_backward_workspace_bytes", "moe_backward",
-           "moe_backward_workspace_bytes")
+           "moe_backward_workspace_bytes", "moe_set_gate_mode")
 MOE_W13, MOE_W2, MOE_WS13, MOE_WS2 = 0, 1, 2, 3
 
 
@@ -86,6 +86,7 @@ def lib():
             "moe_strerror": (ctypes.c_char_p, [ctypes.c_int]),
             "moe_last_error": (ctypes.c_char_p, []),
             "moe_kernel_timer_enable": (ctypes.c_int, [ctypes.c_int, ctypes.c_char_p]),
+            "moe_set_gate_mode": (ctypes.c_int, [ctypes.c_int]),
             "moe_kernel_timer_read": (ctypes.c_int, [ctypes.c_int,
                                                      ctypes.POINTER(ctypes.c_char_p),
                                                      ctypes.POINTER(ctypes.c_double),
@@ -254,6 +255,13 @@ def moe_get_device_error(ws, stream=None) -> int:
 
 def moe_kernel_timer_enable(on: bool, only: Optional[str] = None) -> None:
     _check(lib().moe_kernel_timer_enable(1 if on else 0, only.encode() if only else None))
+
+
+MOE_GATE_SPLIT, MOE_GATE_FUSED = 0, 1
+
+
+def moe_set_gate_mode(mode: int) -> None:
+    _check(lib().moe_set_gate_mode(int(mode)))
 
 
 def moe_kernel_timer_read() -> dict:

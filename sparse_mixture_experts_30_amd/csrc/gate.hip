@@ -20,6 +20,8 @@
 
 #include <float.h>
 
+#include <atomic>
+
 namespace moe {
 
 namespace {
@@ -253,6 +255,262 @@ select_kernel(const float* __restrict__ part, int ksplit, const float* __restric
                nullptr);
 }
 
+// ---------------------------------------------------------------- gate + selection in one kernel
+//
+// For batches that fill the GPU with 64-token tiles: one workgroup computes
+// the logits of 64 tokens for every expert over the whole hidden size
+// (eight waves, wave w the 32 experts of block w, three bf16 weight parts
+// per k slice as above), keeps them in LDS and selects in the same launch,
+// so no partial sums go to memory.  The selection is spread over teams of
+// FG_TEAM threads per token: thread q of a team holds experts
+// [q E/8, (q+1) E/8) in registers, the group scores are merged with lane
+// shuffles inside the team and exchanged through LDS, and each of the K
+// picks is the team's butterfly maximum (larger choice wins, equal choices
+// go to the lower id).  The arithmetic of every score, group score and
+// weight is the one select_token uses, so the routing is the same function
+// of the fp32 logits.
+constexpr int FG_T = 64;                 // tokens per workgroup
+constexpr int FG_WAVES = 8;              // wave w: expert block w
+constexpr int FG_THREADS = FG_WAVES * 64;
+constexpr int FG_TEAM = FG_THREADS / FG_T;   // selection threads per token (8)
+constexpr int FG_MAXQ = 32;              // experts per selection thread (E <= 256)
+constexpr int FG_MAXG = 32;              // groups
+constexpr int FG_MAXK = 2 * FG_TEAM;     // picks (each team thread keeps two)
+#ifndef FG_DEPTH
+#define FG_DEPTH 2                       // k steps of weights in flight per wave
+#endif
+static_assert(FG_TEAM == 8, "teams of eight lanes inside one wave");
+
+__host__ __device__ constexpr int fg_lde(int E) { return E + 4; }   // logit row stride (floats)
+
+size_t fg_lds_bytes(int E) {
+  const size_t tiles = (size_t)2 * FG_T * 8 * sizeof(u32x4);
+  const size_t sel = (size_t)FG_T * fg_lde(E) * 4 + (size_t)FG_T * FG_MAXG * 4;
+  return tiles > sel ? tiles : sel;
+}
+
+__global__ void __launch_bounds__(FG_THREADS, 1)
+gate_select_fused_kernel(const uint16_t* __restrict__ x, const u32x4* __restrict__ wp,
+                         const float* __restrict__ bias, float* __restrict__ logits_out,
+                         int32_t* __restrict__ idx_out, float* __restrict__ w_out, int64_t T,
+                         int H, int E, int G, int TG, int K, float rho) {
+  extern __shared__ u32x4 fsm[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 31, lh = lane >> 5;
+  const int64_t t0 = (int64_t)blockIdx.x * FG_T;
+  const bool active = wave < E / 32;             // uniform per wave
+  const int nsteps = H / GBK, last = nsteps - 1;
+
+  // Activation chunk of this thread: token row tid / 8 (rows past T re-read
+  // row T - 1; their results are dropped), 16-byte chunk tid % 8.
+  const int ch = tid & 7;
+  const uint16_t* arow = x + min(t0 + (tid >> 3), T - 1) * H + ch * 8;
+  const u32x4* bsrc = wp + (int64_t)(active ? wave : 0) * nsteps * GFRAG + lane;
+  u32x4 ra, rb[FG_DEPTH][12];
+  auto aload = [&](int step) {
+    ra = *reinterpret_cast<const u32x4*>(arow + min(step, last) * GBK);
+  };
+  auto astore = [&](int buf) { fsm[buf * FG_T * 8 + gswz(tid >> 3, ch)] = ra; };
+  auto bload = [&](u32x4 (&dst)[12], int step) {
+    if (!active) return;
+    const u32x4* src = bsrc + (int64_t)min(step, last) * GFRAG;
+#pragma unroll
+    for (int i = 0; i < 12; ++i) dst[i] = src[i * 64];   // [part][kk]
+  };
+
+  f32x16 acc[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[r][i] = 0.0f;
+
+  // Step t reads LDS buffer t % 2 and weight slot t % FG_DEPTH; the weights
+  // of a step are requested FG_DEPTH steps ahead, its activation rows two.
+  aload(0);
+  astore(0);
+  aload(1);
+#pragma unroll
+  for (int j = 0; j < FG_DEPTH; ++j) bload(rb[j], j);
+  __syncthreads();
+
+  auto step_body = [&](int buf, u32x4 (&b)[12], int step) {
+    const u32x4* as = fsm + buf * FG_T * 8;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const bf16x8 a0 = as_bf16x8(as[gswz(lr, 4 * lh + kk)]);
+      const bf16x8 a1 = as_bf16x8(as[gswz(32 + lr, 4 * lh + kk)]);
+      if (active) {
+#pragma unroll
+        for (int pt = 0; pt < 3; ++pt) {
+          const bf16x8 bv = as_bf16x8(b[pt * 4 + kk]);
+          acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bv, acc[0], 0, 0, 0);
+          acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bv, acc[1], 0, 0, 0);
+        }
+      }
+    }
+    astore(buf ^ 1);
+    aload(step + 2);
+    bload(b, step + FG_DEPTH);
+    __syncthreads();
+  };
+  constexpr int U = (FG_DEPTH % 2) ? 2 * FG_DEPTH : FG_DEPTH;   // every index static
+  int s = 0;
+  for (; s + U <= nsteps; s += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) step_body(u & 1, rb[u % FG_DEPTH], s + u);
+  }
+#pragma unroll
+  for (int u = 0; u < U - 1; ++u)
+    if (s + u < nsteps) step_body(u & 1, rb[u % FG_DEPTH], s + u);
+
+  // Logits of the 64 tokens into LDS (over the activation buffers, which
+  // every wave has finished reading at the last barrier).  C layout of a
+  // 32x32 block: lane holds column lane%32, rows 8*(i/4) + 4*(lane/32) + i%4.
+  const int lde = fg_lde(E);
+  float* s_lg = reinterpret_cast<float*>(fsm);
+  float* s_g = s_lg + FG_T * lde;
+  if (active) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        s_lg[(r * 32 + 8 * (i >> 2) + 4 * lh + (i & 3)) * lde + wave * 32 + lr] = acc[r][i];
+  }
+  __syncthreads();
+
+  // Selection: team of token tk, thread q holds experts e0 + j, j < EQ.
+  const int tk = tid / FG_TEAM, q = tid % FG_TEAM;
+  const int64_t t = t0 + tk;
+  const bool valid = t < T;
+  const int EQ = E / FG_TEAM, e0 = q * EQ, Eg = E / G;
+  float sc[FG_MAXQ], c[FG_MAXQ];
+#pragma unroll
+  for (int j = 0; j < FG_MAXQ; j += 4) {
+    if (j < EQ) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(s_lg + tk * lde + e0 + j);
+      if (logits_out && valid) *reinterpret_cast<f32x4*>(logits_out + t * E + e0 + j) = v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const double sd = 1.0 / (1.0 + exp(-(double)v[i]));
+        sc[j + i] = (float)sd;
+        float ci = sc[j + i] + bias[e0 + j + i];
+        if (ci != ci) ci = -INFINITY;    // a NaN choice competes as -inf
+        c[j + i] = ci;
+      }
+    }
+  }
+
+  // Group scores: the sum of a group's two largest choices.  G >= 8: the
+  // thread holds G / 8 whole groups; G < 8: a group spans 8 / G threads,
+  // whose two largest values are merged through the team.
+  {
+    float m1 = -INFINITY, m2 = -INFINITY;
+    int cnt = 0, gi = e0 / Eg;
+#pragma unroll
+    for (int j = 0; j < FG_MAXQ; ++j) {
+      if (j < EQ) {
+        const float v = c[j];
+        if (v > m1) {
+          m2 = m1;
+          m1 = v;
+        } else if (v > m2) {
+          m2 = v;
+        }
+        if (++cnt == Eg) {
+          float g = m1 + m2;
+          if (g != g) g = -INFINITY;
+          s_g[tk * FG_MAXG + gi] = g;
+          ++gi;
+          cnt = 0;
+          m1 = m2 = -INFINITY;
+        }
+      }
+    }
+    if (Eg > EQ) {
+      const int span = Eg / EQ;   // threads per group: 2, 4 or 8
+      for (int off = 1; off < span; off <<= 1) {
+        const float o1 = __shfl_xor(m1, off, 64), o2 = __shfl_xor(m2, off, 64);
+        const float hi = fmaxf(m1, o1), lo = fminf(m1, o1);
+        m2 = fmaxf(lo, fmaxf(m2, o2));
+        m1 = hi;
+      }
+      if (q % span == 0) {
+        float g = m1 + m2;
+        if (g != g) g = -INFINITY;
+        s_g[tk * FG_MAXG + gi] = g;
+      }
+    }
+  }
+  __syncthreads();
+
+  // The TG best groups (ties to the lower group index); every thread of the
+  // team computes the same mask.
+  float gs[FG_MAXG];
+#pragma unroll
+  for (int j = 0; j < FG_MAXG; ++j) gs[j] = j < G ? s_g[tk * FG_MAXG + j] : -INFINITY;
+  uint32_t keep = 0;
+  for (int r = 0; r < TG; ++r) {
+    float bv = -INFINITY;
+    int bi = -1;
+#pragma unroll
+    for (int j = 0; j < FG_MAXG; ++j)
+      if (j < G && !((keep >> j) & 1u) && (bi < 0 || gs[j] > bv)) {
+        bv = gs[j];
+        bi = j;
+      }
+    keep |= 1u << bi;
+  }
+#pragma unroll
+  for (int j = 0; j < FG_MAXQ; ++j)
+    if (j < EQ && !((keep >> ((e0 + j) / Eg)) & 1u)) c[j] = 0.0f;
+
+  // Top K by team maxima; thread q keeps picks q and q + 8.
+  uint32_t taken = 0;
+  float sum = 0.0f, ps0 = 0.0f, ps1 = 0.0f;
+  int pe0 = 0, pe1 = 0;
+  for (int k = 0; k < K; ++k) {
+    float bv = -INFINITY, bs = 0.0f;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < FG_MAXQ; ++j)
+      if (j < EQ && !((taken >> j) & 1u) && (bi == 0x7fffffff || c[j] > bv)) {
+        bv = c[j];
+        bi = e0 + j;
+        bs = sc[j];
+      }
+#pragma unroll
+    for (int off = 1; off < FG_TEAM; off <<= 1) {
+      const float ov = __shfl_xor(bv, off, 64), os = __shfl_xor(bs, off, 64);
+      const int oi = __shfl_xor(bi, off, 64);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+        bs = os;
+      }
+    }
+    if (bi >= e0 && bi < e0 + EQ) taken |= 1u << (bi - e0);
+    sum += bs;
+    if (k == q) {
+      pe0 = bi;
+      ps0 = bs;
+    } else if (k == q + FG_TEAM) {
+      pe1 = bi;
+      ps1 = bs;
+    }
+  }
+  if (valid) {
+    if (q < K) {
+      idx_out[t * K + q] = pe0;
+      w_out[t * K + q] = ((K > 1) ? ps0 / (sum + 1e-20f) : ps0) * rho;
+    }
+    if (q + FG_TEAM < K) {
+      idx_out[t * K + q + FG_TEAM] = pe1;
+      w_out[t * K + q + FG_TEAM] = (ps1 / (sum + 1e-20f)) * rho;
+    }
+  }
+}
+
 }  // namespace
 
 int gate_ksplit(int64_t T, int H, int E) {
@@ -300,6 +558,51 @@ hipError_t launch_gate_logits(const void* x, bool x_bf16, const float* gate_w, v
       hipLaunchKernelGGL(gate_logits_f32_kernel, grid, dim3(256), 0, s, (const float*)x, gate_w,
                          partials, T, H, E));
   }
+  return hipGetLastError();
+}
+
+namespace {
+std::atomic<int> g_gate_mode{0};   // 0 split kernels, 1 fused whenever the shape allows
+}  // namespace
+
+void set_gate_mode(int mode) { g_gate_mode.store(mode); }
+int gate_mode() { return g_gate_mode.load(); }
+
+bool gate_fused_shape_ok(int H, int E, int G, int TG, int K) {
+  if (H % GBK || H < GBK || E % 32 || E > 32 * FG_WAVES || G < 1 || G > FG_MAXG || E % G)
+    return false;
+  const int EQ = E / FG_TEAM, Eg = E / G;
+  const bool whole = Eg <= EQ && EQ % Eg == 0;    // a thread holds whole groups
+  const bool span = Eg > EQ && Eg % EQ == 0;      // a group spans 2, 4 or 8 threads
+  return (whole || span) && TG >= 1 && TG <= G && K >= 1 && K <= FG_MAXK;
+}
+
+// The split kernels are the default at every batch size: at T = 16384 on
+// an MI355X (one 64-token tile per compute unit) the fused kernel takes
+// about 0.28 ms against 0.26 ms for the k-split gate plus the selection,
+// because a workgroup that holds all experts of its tokens can hold only 64
+// of them, which doubles the weight bytes each MFMA is fed from L2.
+bool gate_use_fused(int64_t T, int H, int E, int G, int TG, int K) {
+  return g_gate_mode.load() == 1 && T >= 1 && gate_fused_shape_ok(H, E, G, TG, K);
+}
+
+hipError_t launch_gate_select_fused(const uint16_t* x, const float* gate_w, void* wsplit,
+                                    const float* bias, float* logits_out, int32_t* idx,
+                                    float* w, int64_t T, int H, int E, int G, int TG, int K,
+                                    float rho, hipStream_t s) {
+  static hipError_t attr = hipFuncSetAttribute((const void*)gate_select_fused_kernel,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               (int)fg_lds_bytes(32 * FG_WAVES));
+  if (attr != hipSuccess) return attr;
+  const int neb = gate_expert_blocks(E);
+  const int64_t nslot = (int64_t)neb * (H / GBK) * 256;
+  MOE_TIMED_LAUNCH(s, "gate_split_kernel",
+    hipLaunchKernelGGL(gate_split_kernel, dim3((unsigned)((nslot + 255) / 256)), dim3(256), 0, s,
+                       gate_w, (u32x4*)wsplit, E, H, nslot));
+  MOE_TIMED_LAUNCH(s, "gate_select_fused_kernel",
+    hipLaunchKernelGGL(gate_select_fused_kernel, dim3((unsigned)((T + FG_T - 1) / FG_T)),
+                       dim3(FG_THREADS), fg_lds_bytes(E), s, (const uint16_t*)x,
+                       (const u32x4*)wsplit, bias, logits_out, idx, w, T, H, E, G, TG, K, rho));
   return hipGetLastError();
 }
 

@@ -171,6 +171,15 @@ moe_status run_gate(const moe_config* c, int64_t T, const void* x, const float* 
                     const Layout& L, hipStream_t s) {
   float* part = at<float>(ws, L.part);
   const bool bf16 = c->act_dtype == MOE_BF16;
+  if (bf16 && moe::gate_use_fused(T, c->hidden_size, c->n_routed_experts, c->n_group,
+                                  c->topk_group, c->num_experts_per_tok)) {
+    HIPCALL(moe::launch_gate_select_fused((const uint16_t*)x, gate_w, at<void>(ws, L.gsplit), bias,
+                                          logits, idx, w, T, c->hidden_size,
+                                          c->n_routed_experts, c->n_group, c->topk_group,
+                                          c->num_experts_per_tok, c->routed_scaling_factor, s),
+            "gate and selection");
+    return MOE_OK;
+  }
   HIPCALL(moe::launch_gate_logits(x, bf16, gate_w, at<void>(ws, L.gsplit), part, T,
                                   c->hidden_size, c->n_routed_experts, L.ksplit, s),
           "gate logits");
@@ -441,6 +450,13 @@ extern "C" {
 size_t moe_workspace_bytes(const moe_config* cfg, int64_t T) {
   if (check_cfg(cfg) != MOE_OK || T < 0 || check_T(T, cfg) != MOE_OK) return 0;
   return layout(cfg, T).total;
+}
+
+moe_status moe_set_gate_mode(int mode) {
+  if (mode != MOE_GATE_SPLIT && mode != MOE_GATE_FUSED)
+    return fail(MOE_ERR_INVALID_ARG, "gate mode %d is neither 0 (split) nor 1 (fused)", mode);
+  moe::set_gate_mode(mode);
+  return MOE_OK;
 }
 
 moe_status moe_gate(const moe_config* cfg, int64_t T, const void* x, const float* gate_w,

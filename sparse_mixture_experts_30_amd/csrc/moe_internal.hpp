@@ -107,6 +107,17 @@ int gate_ksplit(int64_t T, int H, int E);
 hipError_t launch_select(const float* partials, int ksplit, const float* bias, float* logits_out,
                          int32_t* idx, float* w, int64_t T, int E, int G, int TG, int K,
                          float rho, hipStream_t s);
+// Gate and selection in one launch (bf16 tokens): no partial sums in memory.
+// gate_use_fused: the gate mode asks for it (set_gate_mode: 0 split, 1
+// fused) and the shape allows it.
+bool gate_fused_shape_ok(int H, int E, int G, int TG, int K);
+bool gate_use_fused(int64_t T, int H, int E, int G, int TG, int K);
+void set_gate_mode(int mode);
+int gate_mode();
+hipError_t launch_gate_select_fused(const uint16_t* x, const float* gate_w, void* wsplit,
+                                    const float* bias, float* logits_out, int32_t* idx,
+                                    float* w, int64_t T, int H, int E, int G, int TG, int K,
+                                    float rho, hipStream_t s);
 
 // Decode routing (decode.hip): gate, selection, permutation and the tile
 // list of the expert GEMMs in three launches, for 1 <= T <= kDecodeMaxT.

@@ -227,3 +227,13 @@ def test_noalloc_forward_limit_and_constant():
     st = moe.lib().moe_forward_noalloc(ctypes.byref(_cfg(K=0)), 4, FAKE, ctypes.byref(W), FAKE,
                                        None, None, None, None, None, None)
     assert st == moe.MOE_ERR_INVALID_ARG
+
+
+def test_gate_mode_values():
+    """moe_set_gate_mode takes 0 (split) and 1 (fused) and rejects anything
+    else on the host."""
+    L = moe.lib()
+    for bad in (-1, 2, 100):
+        assert L.moe_set_gate_mode(bad) == moe.MOE_ERR_INVALID_ARG
+    for mode in (moe.MOE_GATE_FUSED, moe.MOE_GATE_SPLIT):
+        assert L.moe_set_gate_mode(mode) == moe.MOE_OK

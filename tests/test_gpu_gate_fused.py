@@ -1,0 +1,154 @@
+"""The gate and the selection in one kernel (MOE_GATE_FUSED), against the
+oracle's contract: logits within 1e-5 relative L2 of the fp64 logits, the
+expert ids bit-exact and the weights within 1e-6 * rho of the oracle's
+fp32 selection from the GPU's own logits.  The shapes cover every way the
+kernel splits a token's experts over its eight selection threads: one or
+several whole groups per thread, a group over 2, 4 or 8 threads, idle waves
+(E < 256), top_k above 8 (two picks per thread), K = 1, a ragged last tile,
+negative choice scores (masked experts win) and a NaN token."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import sparse_mixture_experts_30_amd as moe
+from synth import device as sd
+
+from gpu_util import DEV, check_routing, host, log, run_gate, sync
+
+pytestmark = pytest.mark.gpu
+
+_B = synth.C3
+
+
+def _cfg(name, **kw):
+    return _B.replace(name=name, I=128, Is=128, rho=2.5, **kw)
+
+
+FUSED = [
+    _cfg("fg-T200-H512-E256-G8-TG4-K8", T=200, H=512, E=256, G=8, TG=4, K=8),
+    _cfg("fg-T130-H768-E64-G8-TG4-K8", T=130, H=768, E=64, G=8, TG=4, K=8),
+    _cfg("fg-T65-H256-E128-G16-TG4-K6", T=65, H=256, E=128, G=16, TG=4, K=6),
+    _cfg("fg-T100-H256-E256-G32-TG8-K9", T=100, H=256, E=256, G=32, TG=8, K=9),
+    _cfg("fg-T64-H384-E64-G4-TG2-K4", T=64, H=384, E=64, G=4, TG=2, K=4),
+    _cfg("fg-T70-H256-E128-G2-TG1-K5", T=70, H=256, E=128, G=2, TG=1, K=5),
+    _cfg("fg-T70-H256-E32-G1-TG1-K16", T=70, H=256, E=32, G=1, TG=1, K=16),
+    _cfg("fg-T90-H320-E160-G8-TG3-K8", T=90, H=320, E=160, G=8, TG=3, K=8),
+    _cfg("fg-T33-H256-E256-G8-TG4-K1", T=33, H=256, E=256, G=8, TG=4, K=1),
+    _cfg("fg-T1-H256-E256-G8-TG4-K8", T=1, H=256, E=256, G=8, TG=4, K=8),
+]
+
+
+@pytest.fixture
+def fused_mode():
+    moe.moe_set_gate_mode(moe.MOE_GATE_FUSED)
+    yield
+    moe.moe_set_gate_mode(moe.MOE_GATE_SPLIT)
+
+
+def _gate_inputs(cfg):
+    inp = {"x": synth.gen_x(cfg)}
+    inp["gate_w"], inp["bias"] = synth.gen_gate(cfg)
+    dev = {k: sd.tensor(v) for k, v in inp.items()}
+    return inp, dev
+
+
+def _timed_gate(cfg, dev, T):
+    moe.moe_kernel_timer_read()
+    moe.moe_kernel_timer_enable(True)
+    try:
+        out = run_gate(cfg, dev, T)
+    finally:
+        moe.moe_kernel_timer_enable(False)
+    return out, moe.moe_kernel_timer_read()
+
+
+@pytest.mark.parametrize("cfg", FUSED, ids=lambda c: c.name)
+def test_gate_fused(cfg, fused_mode):
+    log(f"fused gate {cfg.name}")
+    inp, dev = _gate_inputs(cfg)
+    (lg, idx, w), kernels = _timed_gate(cfg, dev, cfg.T)
+    assert "gate_select_fused_kernel" in kernels and "select_kernel" not in kernels, kernels
+    check_routing(cfg, inp["x"], inp["gate_w"], inp["bias"], lg, idx, w, cfg.name)
+    # without the logits output the routing is the same
+    E, K, T = cfg.E, cfg.K, cfg.T
+    idx2 = torch.empty((T, K), dtype=torch.int32, device=DEV)
+    w2 = torch.empty((T, K), dtype=torch.float32, device=DEV)
+    moe.moe_gate(sd.moe_config(cfg), T, dev["x"], dev["gate_w"], dev["bias"], None, idx2, w2,
+                 sd.workspace(cfg, T))
+    sync()
+    np.testing.assert_array_equal(host(idx2), idx)
+    np.testing.assert_array_equal(host(w2), w)
+
+
+def test_gate_fused_negative_choice_scores(fused_mode):
+    """Kept groups with fewer than K positive choices: masked experts
+    (choice 0.0) must win, as in the split path."""
+    cfg = _cfg("fg-neg-bias-T96-H256-E256", T=96, H=256, E=256, G=8, TG=2, K=8,
+               bias_lo=-1.5, bias_hi=-0.9)
+    inp, dev = _gate_inputs(cfg)
+    lg, idx, w = run_gate(cfg, dev, cfg.T)
+    check_routing(cfg, inp["x"], inp["gate_w"], inp["bias"], lg, idx, w, cfg.name)
+    Eg = cfg.E // cfg.G
+    c = 1 / (1 + np.exp(-lg.astype(np.float64))) + inp["bias"].astype(np.float64)
+    g = np.sort(c.reshape(cfg.T, cfg.G, Eg), axis=2)[:, :, -2:].sum(2)
+    kept = np.argsort(-g, axis=1, kind="stable")[:, :cfg.TG]
+    outside = [not set((idx[t] // Eg).tolist()) <= set(kept[t].tolist()) for t in range(cfg.T)]
+    assert np.mean(outside) > 0.5
+
+
+@pytest.mark.parametrize("TG", [8, 3])
+def test_gate_fused_nan_token(TG, fused_mode):
+    """A NaN in a token: its choices compete as -inf and it still gets K
+    distinct valid ids (with every group kept there is no 0.0 to fall back
+    on); the other tokens route as the contract says."""
+    cfg = _cfg(f"fg-nan-T80-H256-E64-G8-TG{TG}-K8", T=80, H=256, E=64, G=8, TG=TG, K=8)
+    inp, dev = _gate_inputs(cfg)
+    bad = 41
+    x = inp["x"].copy()
+    x[bad, 7] = 0x7FC0                    # bf16 quiet NaN
+    dev["x"] = sd.tensor(x)
+    lg, idx, w = run_gate(cfg, dev, cfg.T)
+    assert np.all(np.isnan(lg[bad]))
+    assert idx.min() >= 0 and idx.max() < cfg.E
+    assert all(len(set(row.tolist())) == cfg.K for row in idx)
+    good = np.array([t for t in range(cfg.T) if t != bad])
+    idx_c, w_c = oracle.route_f32(cfg, lg[good], inp["bias"])
+    np.testing.assert_array_equal(idx[good], idx_c)
+    assert float(np.abs(w[good] - w_c).max()) <= 1e-6 * cfg.rho
+
+
+def test_gate_fused_matches_split_routing(fused_mode):
+    """Both gate paths are the same function of their logits: each one's ids
+    and weights are the oracle's fp32 selection from its own logits, and the
+    logits agree to fp32 rounding of the k sums."""
+    cfg = _cfg("fg-vs-split-T257-H1024-E256", T=257, H=1024, E=256, G=8, TG=4, K=8)
+    inp, dev = _gate_inputs(cfg)
+    lf, idf, wf = run_gate(cfg, dev, cfg.T)
+    moe.moe_set_gate_mode(moe.MOE_GATE_SPLIT)
+    (ls, ids, wsp), kernels = _timed_gate(cfg, dev, cfg.T)
+    assert "gate_select_fused_kernel" not in kernels
+    for lg, idx, w in ((lf, idf, wf), (ls, ids, wsp)):
+        idx_c, w_c = oracle.route_f32(cfg, lg, inp["bias"])
+        np.testing.assert_array_equal(idx, idx_c)
+        assert float(np.abs(w - w_c).max()) <= 1e-6 * cfg.rho
+    rel = float(np.linalg.norm(lf - ls) / np.linalg.norm(ls))
+    log(f"  fused vs split logits relL2={rel:.2e}, ids equal on "
+        f"{int(np.all(idf == ids, axis=1).sum())}/{cfg.T} tokens")
+    assert rel <= 2e-6
+
+
+def test_gate_fused_v3_T16384(fused_mode):
+    """The V3 gate at T = 16384 through the fused kernel: routing on every
+    token under the oracle's contract, counts of the permutation exact; the
+    default (split) path is restored afterwards."""
+    cfg = synth.C2
+    inp, dev = _gate_inputs(cfg)
+    (lg, idx, w), kernels = _timed_gate(cfg, dev, cfg.T)
+    log(f"  kernels: { {k: round(v[0] / v[1], 4) for k, v in kernels.items()} } ms")
+    assert "gate_select_fused_kernel" in kernels and "select_kernel" not in kernels
+    check_routing(cfg, inp["x"], inp["gate_w"], inp["bias"], lg, idx, w, cfg.name)
+    moe.moe_set_gate_mode(moe.MOE_GATE_SPLIT)
+    _, kernels = _timed_gate(cfg, dev, cfg.T)
+    assert "gate_select_fused_kernel" not in kernels and "select_kernel" in kernels
