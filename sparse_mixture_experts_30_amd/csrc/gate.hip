@@ -272,20 +272,16 @@ select_kernel(const float* __restrict__ part, int ksplit, const float* __restric
 constexpr int FG_T = 64;                 // tokens per workgroup
 constexpr int FG_WAVES = 8;              // wave w: expert block w
 constexpr int FG_THREADS = FG_WAVES * 64;
-constexpr int FG_TEAM = FG_THREADS / FG_T;   // selection threads per token (8)
-constexpr int FG_MAXQ = 32;              // experts per selection thread (E <= 256)
-constexpr int FG_MAXG = 32;              // groups
-constexpr int FG_MAXK = 2 * FG_TEAM;     // picks (each team thread keeps two)
+static_assert(FG_THREADS == FG_T * SEL_TEAM, "one selection team per token");
 #ifndef FG_DEPTH
 #define FG_DEPTH 2                       // k steps of weights in flight per wave
 #endif
-static_assert(FG_TEAM == 8, "teams of eight lanes inside one wave");
 
 __host__ __device__ constexpr int fg_lde(int E) { return E + 4; }   // logit row stride (floats)
 
 size_t fg_lds_bytes(int E) {
   const size_t tiles = (size_t)2 * FG_T * 8 * sizeof(u32x4);
-  const size_t sel = (size_t)FG_T * fg_lde(E) * 4 + (size_t)FG_T * FG_MAXG * 4;
+  const size_t sel = (size_t)FG_T * fg_lde(E) * 4 + (size_t)FG_T * SEL_TG * 4;
   return tiles > sel ? tiles : sel;
 }
 
@@ -379,136 +375,23 @@ gate_select_fused_kernel(const uint16_t* __restrict__ x, const u32x4* __restrict
   }
   __syncthreads();
 
-  // Selection: team of token tk, thread q holds experts e0 + j, j < EQ.
-  const int tk = tid / FG_TEAM, q = tid % FG_TEAM;
+  // Selection: thread q of token tk's team reads its experts' logits.
+  const int tk = tid / SEL_TEAM, q = tid % SEL_TEAM;
   const int64_t t = t0 + tk;
   const bool valid = t < T;
-  const int EQ = E / FG_TEAM, e0 = q * EQ, Eg = E / G;
-  float sc[FG_MAXQ], c[FG_MAXQ];
+  const int64_t tc = valid ? t : T - 1;   // rows past T: nothing is written
+  const int EQ = E / SEL_TEAM, e0 = q * EQ;
+  float lg[SEL_TQ];
 #pragma unroll
-  for (int j = 0; j < FG_MAXQ; j += 4) {
+  for (int j = 0; j < SEL_TQ; j += 4) {
     if (j < EQ) {
       const f32x4 v = *reinterpret_cast<const f32x4*>(s_lg + tk * lde + e0 + j);
-      if (logits_out && valid) *reinterpret_cast<f32x4*>(logits_out + t * E + e0 + j) = v;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const double sd = 1.0 / (1.0 + exp(-(double)v[i]));
-        sc[j + i] = (float)sd;
-        float ci = sc[j + i] + bias[e0 + j + i];
-        if (ci != ci) ci = -INFINITY;    // a NaN choice competes as -inf
-        c[j + i] = ci;
-      }
+      for (int i = 0; i < 4; ++i) lg[j + i] = v[i];
     }
   }
-
-  // Group scores: the sum of a group's two largest choices.  G >= 8: the
-  // thread holds G / 8 whole groups; G < 8: a group spans 8 / G threads,
-  // whose two largest values are merged through the team.
-  {
-    float m1 = -INFINITY, m2 = -INFINITY;
-    int cnt = 0, gi = e0 / Eg;
-#pragma unroll
-    for (int j = 0; j < FG_MAXQ; ++j) {
-      if (j < EQ) {
-        const float v = c[j];
-        if (v > m1) {
-          m2 = m1;
-          m1 = v;
-        } else if (v > m2) {
-          m2 = v;
-        }
-        if (++cnt == Eg) {
-          float g = m1 + m2;
-          if (g != g) g = -INFINITY;
-          s_g[tk * FG_MAXG + gi] = g;
-          ++gi;
-          cnt = 0;
-          m1 = m2 = -INFINITY;
-        }
-      }
-    }
-    if (Eg > EQ) {
-      const int span = Eg / EQ;   // threads per group: 2, 4 or 8
-      for (int off = 1; off < span; off <<= 1) {
-        const float o1 = __shfl_xor(m1, off, 64), o2 = __shfl_xor(m2, off, 64);
-        const float hi = fmaxf(m1, o1), lo = fminf(m1, o1);
-        m2 = fmaxf(lo, fmaxf(m2, o2));
-        m1 = hi;
-      }
-      if (q % span == 0) {
-        float g = m1 + m2;
-        if (g != g) g = -INFINITY;
-        s_g[tk * FG_MAXG + gi] = g;
-      }
-    }
-  }
-  __syncthreads();
-
-  // The TG best groups (ties to the lower group index); every thread of the
-  // team computes the same mask.
-  float gs[FG_MAXG];
-#pragma unroll
-  for (int j = 0; j < FG_MAXG; ++j) gs[j] = j < G ? s_g[tk * FG_MAXG + j] : -INFINITY;
-  uint32_t keep = 0;
-  for (int r = 0; r < TG; ++r) {
-    float bv = -INFINITY;
-    int bi = -1;
-#pragma unroll
-    for (int j = 0; j < FG_MAXG; ++j)
-      if (j < G && !((keep >> j) & 1u) && (bi < 0 || gs[j] > bv)) {
-        bv = gs[j];
-        bi = j;
-      }
-    keep |= 1u << bi;
-  }
-#pragma unroll
-  for (int j = 0; j < FG_MAXQ; ++j)
-    if (j < EQ && !((keep >> ((e0 + j) / Eg)) & 1u)) c[j] = 0.0f;
-
-  // Top K by team maxima; thread q keeps picks q and q + 8.
-  uint32_t taken = 0;
-  float sum = 0.0f, ps0 = 0.0f, ps1 = 0.0f;
-  int pe0 = 0, pe1 = 0;
-  for (int k = 0; k < K; ++k) {
-    float bv = -INFINITY, bs = 0.0f;
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int j = 0; j < FG_MAXQ; ++j)
-      if (j < EQ && !((taken >> j) & 1u) && (bi == 0x7fffffff || c[j] > bv)) {
-        bv = c[j];
-        bi = e0 + j;
-        bs = sc[j];
-      }
-#pragma unroll
-    for (int off = 1; off < FG_TEAM; off <<= 1) {
-      const float ov = __shfl_xor(bv, off, 64), os = __shfl_xor(bs, off, 64);
-      const int oi = __shfl_xor(bi, off, 64);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-        bs = os;
-      }
-    }
-    if (bi >= e0 && bi < e0 + EQ) taken |= 1u << (bi - e0);
-    sum += bs;
-    if (k == q) {
-      pe0 = bi;
-      ps0 = bs;
-    } else if (k == q + FG_TEAM) {
-      pe1 = bi;
-      ps1 = bs;
-    }
-  }
-  if (valid) {
-    if (q < K) {
-      idx_out[t * K + q] = pe0;
-      w_out[t * K + q] = ((K > 1) ? ps0 / (sum + 1e-20f) : ps0) * rho;
-    }
-    if (q + FG_TEAM < K) {
-      idx_out[t * K + q + FG_TEAM] = pe1;
-      w_out[t * K + q + FG_TEAM] = (ps1 / (sum + 1e-20f)) * rho;
-    }
-  }
+  select_team(lg, q, valid, bias, s_g + tk * SEL_TG, E, G, TG, K, rho,
+              logits_out ? logits_out + tc * E : nullptr, idx_out + tc * K, w_out + tc * K);
 }
 
 }  // namespace
@@ -569,12 +452,7 @@ void set_gate_mode(int mode) { g_gate_mode.store(mode); }
 int gate_mode() { return g_gate_mode.load(); }
 
 bool gate_fused_shape_ok(int H, int E, int G, int TG, int K) {
-  if (H % GBK || H < GBK || E % 32 || E > 32 * FG_WAVES || G < 1 || G > FG_MAXG || E % G)
-    return false;
-  const int EQ = E / FG_TEAM, Eg = E / G;
-  const bool whole = Eg <= EQ && EQ % Eg == 0;    // a thread holds whole groups
-  const bool span = Eg > EQ && Eg % EQ == 0;      // a group spans 2, 4 or 8 threads
-  return (whole || span) && TG >= 1 && TG <= G && K >= 1 && K <= FG_MAXK;
+  return H % GBK == 0 && H >= GBK && E <= 32 * FG_WAVES && select_team_ok(E, G, TG, K);
 }
 
 // The split kernels are the default at every batch size: at T = 16384 on

@@ -164,4 +164,165 @@ __device__ __forceinline__ void select_token(const float (&lgs)[SEL_MAXV], int l
   }
 }
 
+// ---------------------------------------------------------------- selection by teams of lanes
+//
+// The same selection as select_token, spread over a team of SEL_TEAM
+// consecutive lanes of one wave per token: thread q of the team holds
+// experts [q E/8, (q+1) E/8) in registers.  The group scores (sum of a
+// group's two largest choices) are formed per thread (G >= 8: G / 8 whole
+// groups per thread) or merged with lane shuffles (G < 8: a group over
+// 8 / G threads) and exchanged through LDS; every pick of the top K is the
+// team's butterfly maximum (larger choice wins, equal choices go to the
+// lower id).  Every score, group score and weight is computed with
+// select_token's arithmetic, so both give the same routing from the same
+// fp32 logits.
+constexpr int SEL_TEAM = 8;          // lanes per token
+constexpr int SEL_TQ = 32;           // experts per lane (E <= 256)
+constexpr int SEL_TG = 32;           // groups (LDS row of a token's group scores)
+constexpr int SEL_TK = 2 * SEL_TEAM; // picks (each lane keeps two)
+
+inline bool select_team_ok(int E, int G, int TG, int K) {
+  if (E % 32 || E > SEL_TEAM * SEL_TQ || G < 1 || G > SEL_TG || E % G) return false;
+  const int EQ = E / SEL_TEAM, Eg = E / G;
+  const bool whole = Eg <= EQ && EQ % Eg == 0;    // a thread holds whole groups
+  const bool span = Eg > EQ && Eg % EQ == 0;      // a group spans 2, 4 or 8 threads
+  return (whole || span) && TG >= 1 && TG <= G && K >= 1 && K <= SEL_TK;
+}
+
+// lg: this lane's logits (experts q E/8 + j, j < E/8); s_grow: the token's
+// LDS row of SEL_TG floats (shared by the team).  Contains a workgroup
+// barrier: every thread of the workgroup calls it.  Writes the logits row
+// (if not null), ids and weights only when `valid`.
+__device__ __forceinline__ void select_team(const float (&lg)[SEL_TQ], int q, bool valid,
+                                            const float* __restrict__ bias, float* s_grow, int E,
+                                            int G, int TG, int K, float rho,
+                                            float* logits_row, int32_t* idx_row, float* w_row) {
+  const int EQ = E / SEL_TEAM, e0 = q * EQ, Eg = E / G;
+  float sc[SEL_TQ], c[SEL_TQ];
+#pragma unroll
+  for (int j = 0; j < SEL_TQ; j += 4) {
+    if (j < EQ) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (logits_row && valid) logits_row[e0 + j + i] = lg[j + i];   // any 4-byte alignment
+        const double sd = 1.0 / (1.0 + exp(-(double)lg[j + i]));
+        sc[j + i] = (float)sd;
+        float ci = sc[j + i] + bias[e0 + j + i];
+        if (ci != ci) ci = -INFINITY;    // a NaN choice competes as -inf
+        c[j + i] = ci;
+      }
+    }
+  }
+
+  // Group scores into the token's LDS row.
+  {
+    float m1 = -INFINITY, m2 = -INFINITY;
+    int cnt = 0, gi = e0 / Eg;
+#pragma unroll
+    for (int j = 0; j < SEL_TQ; ++j) {
+      if (j < EQ) {
+        const float v = c[j];
+        if (v > m1) {
+          m2 = m1;
+          m1 = v;
+        } else if (v > m2) {
+          m2 = v;
+        }
+        if (++cnt == Eg) {
+          float g = m1 + m2;
+          if (g != g) g = -INFINITY;   // -inf + inf
+          s_grow[gi] = g;
+          ++gi;
+          cnt = 0;
+          m1 = m2 = -INFINITY;
+        }
+      }
+    }
+    if (Eg > EQ) {
+      const int span = Eg / EQ;   // threads per group: 2, 4 or 8
+      for (int off = 1; off < span; off <<= 1) {
+        const float o1 = __shfl_xor(m1, off, 64), o2 = __shfl_xor(m2, off, 64);
+        const float hi = fmaxf(m1, o1), lo = fminf(m1, o1);
+        m2 = fmaxf(lo, fmaxf(m2, o2));
+        m1 = hi;
+      }
+      if (q % span == 0) {
+        float g = m1 + m2;
+        if (g != g) g = -INFINITY;
+        s_grow[gi] = g;
+      }
+    }
+  }
+  __syncthreads();
+
+  // The TG best groups (ties to the lower index); the same mask in every
+  // thread of the team.
+  float gs[SEL_TG];
+#pragma unroll
+  for (int j = 0; j < SEL_TG; ++j) gs[j] = j < G ? s_grow[j] : -INFINITY;
+  uint32_t keep = 0;
+  for (int r = 0; r < TG; ++r) {
+    float bv = -INFINITY;
+    int bi = -1;
+#pragma unroll
+    for (int j = 0; j < SEL_TG; ++j)
+      if (j < G && !((keep >> j) & 1u) && (bi < 0 || gs[j] > bv)) {
+        bv = gs[j];
+        bi = j;
+      }
+    keep |= 1u << bi;
+  }
+  // Experts outside the kept groups compete with choice 0.0.
+#pragma unroll
+  for (int j = 0; j < SEL_TQ; ++j)
+    if (j < EQ && !((keep >> ((e0 + j) / Eg)) & 1u)) c[j] = 0.0f;
+
+  // Top K by team maxima; lane q keeps picks q and q + SEL_TEAM.  A lane
+  // offers its best untaken expert even at -inf, so K <= E valid ids exist.
+  uint32_t taken = 0;
+  float sum = 0.0f, ps0 = 0.0f, ps1 = 0.0f;
+  int pe0 = 0, pe1 = 0;
+  for (int k = 0; k < K; ++k) {
+    float bv = -INFINITY, bs = 0.0f;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < SEL_TQ; ++j)
+      if (j < EQ && !((taken >> j) & 1u) && (bi == 0x7fffffff || c[j] > bv)) {
+        bv = c[j];
+        bi = e0 + j;
+        bs = sc[j];
+      }
+#pragma unroll
+    for (int off = 1; off < SEL_TEAM; off <<= 1) {
+      const float ov = __shfl_xor(bv, off, 64), os = __shfl_xor(bs, off, 64);
+      const int oi = __shfl_xor(bi, off, 64);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+        bs = os;
+      }
+    }
+    if (bi >= e0 && bi < e0 + EQ) taken |= 1u << (bi - e0);
+    sum += bs;   // the unbiased scores of the picks, in pick order
+    if (k == q) {
+      pe0 = bi;
+      ps0 = bs;
+    } else if (k == q + SEL_TEAM) {
+      pe1 = bi;
+      ps1 = bs;
+    }
+  }
+  // Weights: normalised over the K picks (K > 1), times rho.
+  if (valid) {
+    if (q < K) {
+      idx_row[q] = pe0;
+      w_row[q] = ((K > 1) ? ps0 / (sum + 1e-20f) : ps0) * rho;
+    }
+    if (q + SEL_TEAM < K) {
+      idx_row[q + SEL_TEAM] = pe1;
+      w_row[q + SEL_TEAM] = (ps1 / (sum + 1e-20f)) * rho;
+    }
+  }
+}
+
 }  // namespace moe

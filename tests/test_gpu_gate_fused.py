@@ -69,7 +69,8 @@ def test_gate_fused(cfg, fused_mode):
     log(f"fused gate {cfg.name}")
     inp, dev = _gate_inputs(cfg)
     (lg, idx, w), kernels = _timed_gate(cfg, dev, cfg.T)
-    assert "gate_select_fused_kernel" in kernels and "select_kernel" not in kernels, kernels
+    assert "gate_select_fused_kernel" in kernels, kernels
+    assert "select_kernel" not in kernels, kernels
     check_routing(cfg, inp["x"], inp["gate_w"], inp["bias"], lg, idx, w, cfg.name)
     # without the logits output the routing is the same
     E, K, T = cfg.E, cfg.K, cfg.T
@@ -80,6 +81,19 @@ def test_gate_fused(cfg, fused_mode):
     sync()
     np.testing.assert_array_equal(host(idx2), idx)
     np.testing.assert_array_equal(host(w2), w)
+
+
+@pytest.mark.parametrize("cfg", FUSED, ids=lambda c: c.name)
+def test_gate_split_same_shapes(cfg):
+    """The default split path on the same shapes (the k-split gate, then
+    one wave per token in the selection): routing under the oracle's
+    contract."""
+    log(f"split gate {cfg.name}")
+    inp, dev = _gate_inputs(cfg)
+    (lg, idx, w), kernels = _timed_gate(cfg, dev, cfg.T)
+    assert "gate_select_fused_kernel" not in kernels
+    assert "select_kernel" in kernels, kernels
+    check_routing(cfg, inp["x"], inp["gate_w"], inp["bias"], lg, idx, w, cfg.name)
 
 
 def test_gate_fused_negative_choice_scores(fused_mode):
@@ -147,8 +161,10 @@ def test_gate_fused_v3_T16384(fused_mode):
     inp, dev = _gate_inputs(cfg)
     (lg, idx, w), kernels = _timed_gate(cfg, dev, cfg.T)
     log(f"  kernels: { {k: round(v[0] / v[1], 4) for k, v in kernels.items()} } ms")
-    assert "gate_select_fused_kernel" in kernels and "select_kernel" not in kernels
+    assert "gate_select_fused_kernel" in kernels
+    assert "select_kernel" not in kernels, kernels
     check_routing(cfg, inp["x"], inp["gate_w"], inp["bias"], lg, idx, w, cfg.name)
     moe.moe_set_gate_mode(moe.MOE_GATE_SPLIT)
     _, kernels = _timed_gate(cfg, dev, cfg.T)
-    assert "gate_select_fused_kernel" not in kernels and "select_kernel" in kernels
+    assert "gate_select_fused_kernel" not in kernels
+    assert "select_kernel" in kernels, kernels
