@@ -463,7 +463,7 @@ def main():
         backward["dtype"] = "e4m3 operands, fp32 accumulation" if bwd_fp8 else "bf16"
         del wsb
 
-    if drow is not None and not bwd_fp8:
+    if drow is not None:
         # the layer: y (the routed expert outputs) from the phase timing above
         dout = torch.randn((T, H), generator=gen, device=dev).to(torch.bfloat16)
         dxl = torch.empty((T, H), **bf)
@@ -476,6 +476,7 @@ def main():
         # + y and dout read, the gate weight read and its gradient written
         layer_backward = figures(lms, bflop + 6.0 * T * K * H,
                                  bbytes + (T * K + T) * H * 2 + 2 * E * H * 4, lk)
+        layer_backward["dtype"] = backward["dtype"]
         del dyb, dysb, dxb, dxsb, dw13, dw2, dws13, dws2, wsl, dout, dxl, dgw
 
     # Algorithmic work (routed rows only; active experts' weights only).

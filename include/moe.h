@@ -354,9 +354,13 @@ moe_status moe_expert_ffn_backward(const moe_config* cfg, int64_t T, const void*
  *   (rho dw_k for top-1),  dlogit_tk = ds_k s_k (1 - s_k),
  *   dgate_w[e] = sum over the rows routed to e of dlogit x_t (fp32),
  *   dx_t = sum_k dlogit_tk Wg[idx_tk] + the experts' input gradients
- *   (moe_expert_ffn_backward, with the shared expert's output gradient dout).
- *   x [T, H] bf16; w: gate_w [E, H] fp32 and row-major bf16 expert weights
- *      (packed = 0) as in moe_expert_ffn_backward;
+ *   (moe_expert_ffn_backward, with the shared expert's output gradient dout;
+ *   with e4m3 weights that is the FP8 expert backward, its operands
+ *   quantised per 128 along each GEMM's contraction, "深入理解 DeepSeek-V3…",
+ *   section 3.2).
+ *   x [T, H] bf16; w: gate_w [E, H] fp32 and row-major bf16 or e4m3 expert
+ *      weights with their block scales (packed = 0) as in
+ *      moe_expert_ffn_backward;
  *   logits [T, E] fp32, topk_idx / topk_w [T, K], perm [T*K], offsets [E+1],
  *      pos [T*K]: the forward's (moe_gate, moe_permute);
  *   y [T*K, H] bf16: the routed expert outputs of the forward in sorted row
@@ -367,8 +371,9 @@ moe_status moe_expert_ffn_backward(const moe_config* cfg, int64_t T, const void*
  *   moe_expert_ffn_backward.
  * Workspace: moe_backward_workspace_bytes(cfg, T) bytes (0 for a config the
  * backward does not take), 256-byte aligned.
- * Errors: MOE_ERR_UNSUPPORTED for non-bf16 configs or packed weights;
- * MOE_ERR_INVALID_ARG for a missing array; MOE_ERR_WORKSPACE. */
+ * Errors: MOE_ERR_UNSUPPORTED for fp32 activations or weights, or packed
+ * weights; MOE_ERR_INVALID_ARG for a missing array (the block scales too,
+ * with e4m3 weights); MOE_ERR_WORKSPACE. */
 size_t moe_backward_workspace_bytes(const moe_config* cfg, int64_t T);
 moe_status moe_backward(const moe_config* cfg, int64_t T, const void* x, const moe_weights* w,
                         const float* logits, const int32_t* topk_idx, const float* topk_w,

@@ -353,8 +353,15 @@ def routing_weights(cfg, lg: np.ndarray, idx: np.ndarray) -> np.ndarray:
     return s * cfg.rho
 
 
+def round_bf16(v: np.ndarray) -> np.ndarray:
+    """Values rounded to fp32, then to bf16 (nearest, ties to even), as fp64."""
+    u = np.ascontiguousarray(v, np.float32).view(np.uint32).astype(np.uint64)
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
 def layer_backward(cfg, inp: dict, idx: np.ndarray, dout: np.ndarray, tokens=None,
-                   want=("dx", "dgate_w", "dw")) -> dict:
+                   want=("dx", "dgate_w", "dw"), quant_act=False) -> dict:
     """Exact fp64 gradients of L = sum_t <dout_t, out_t> for the layer with
     its routing held at idx (the top-k choice is piecewise constant in the
     inputs: the gradient reaches the gate only through the chosen experts'
@@ -364,7 +371,14 @@ def layer_backward(cfg, inp: dict, idx: np.ndarray, dout: np.ndarray, tokens=Non
     dw2 [E, H, I] and, with a shared expert, dws13 [2Is, H], dws2 [H, Is].
     With tokens (indices into x, idx and dout), L sums over those tokens only:
     dx holds their rows, and dgate_w[e] is exact for an expert e all of whose
-    tokens are listed."""
+    tokens are listed.
+    e4m3 weights with quant_act: the FP8 layer -- the expert outputs y of the
+    activation-quantised forward (F2) enter the routing-weight gradient, and
+    each expert's backward is the FP8 backward (R15) of its rows, in sorted
+    order, with dy = w dout ("深入理解 DeepSeek-V3…", section 3.2); the
+    combine, routing-weight and gate terms are the formulas above.  The
+    routed rows' dy reach the expert backward as bf16 values (its operands'
+    interface type), so their e4m3 codes are decided from bf16-rounded dy."""
     if tokens is not None:
         tokens = np.asarray(tokens, np.int64)
         inp = dict(inp, x=np.asarray(inp["x"])[tokens])
@@ -380,7 +394,8 @@ def layer_backward(cfg, inp: dict, idx: np.ndarray, dout: np.ndarray, tokens=Non
     s = 1.0 / (1.0 + np.exp(-np.take_along_axis(lg, idx, axis=1)))          # [T, K]
     w = routing_weights(cfg, lg, idx)
     tok = np.repeat(np.arange(T), K)
-    y = ffn(cfg, inp, tok, idx.ravel().astype(np.int32)).reshape(T, K, H)  # expert outputs
+    y = ffn(cfg, inp, tok, idx.ravel().astype(np.int32),
+            quant_act=quant_act).reshape(T, K, H)                            # expert outputs
     dw = np.einsum("th,tkh->tk", dout, y)
     if K > 1:   # w_k = rho s_k / D, D = sum_j s_j + 1e-20
         D = s.sum(axis=1, keepdims=True) + 1e-20
@@ -399,13 +414,14 @@ def layer_backward(cfg, inp: dict, idx: np.ndarray, dout: np.ndarray, tokens=Non
         return out
     for e in np.unique(idx):
         rows = np.flatnonzero(idx.ravel() == e)
-        b = ffn_backward(cfg, inp, int(e), tok[rows], w.ravel()[rows, None] * dout[tok[rows]],
-                         want=parts)
+        dy = w.ravel()[rows, None] * dout[tok[rows]]
+        b = ffn_backward(cfg, inp, int(e), tok[rows], round_bf16(dy) if quant_act else dy,
+                         want=parts, quant_act=quant_act)
         if wdw:
             out["dw13"][e], out["dw2"][e] = b["dw13"], b["dw2"]
         np.add.at(dx, tok[rows], b["dx"])
     if cfg.Is:
-        b = ffn_backward(cfg, inp, -1, np.arange(T), dout, want=parts)
+        b = ffn_backward(cfg, inp, -1, np.arange(T), dout, want=parts, quant_act=quant_act)
         if wdw:
             out["dws13"], out["dws2"] = b["dw13"], b["dw2"]
         dx += b["dx"]

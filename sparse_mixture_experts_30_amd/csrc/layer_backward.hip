@@ -1,5 +1,5 @@
-// Backward of the whole layer (training), bf16, with the routing held at the
-// forward's choice: the gradient reaches the gate only through the chosen
+// Backward of the whole layer (training), bf16 activations with bf16 or e4m3
+// expert weights, with the routing held at the forward's choice: the gradient reaches the gate only through the chosen
 // experts' weights, and the selection-only bias gets none.
 //
 // The forward (page "从 1024 块 GPU 到 558 万美元：拆解 DeepSeek-V3 的算法-系统协同设计",
@@ -173,17 +173,16 @@ size_t al256(size_t b) { return (b + 255) / 256 * 256; }
 
 }  // namespace
 
-size_t layer_backward_ws_bytes(const FfnDims& d) {
+size_t layer_backward_ws_bytes(const FfnDims& d, bool fp8) {
   const size_t rows = (size_t)d.N * d.H * 2;
   return al256(rows) + al256(rows) + al256((size_t)d.T * d.H * 2) + al256((size_t)d.N * 4) +
-         ffn_backward_ws_bytes(d);
+         (fp8 ? ffn_backward_fp8_ws_bytes(d) : ffn_backward_ws_bytes(d));
 }
 
 hipError_t launch_layer_backward(const FfnDims& d, const uint16_t* x, const float* gate_w,
                                  const float* logits, const int32_t* idx, const float* topk_w,
                                  const int32_t* perm, const int32_t* offsets, const int32_t* pos,
-                                 const uint16_t* y, const uint16_t* dout, const uint16_t* w13,
-                                 const uint16_t* w2, const uint16_t* ws13, const uint16_t* ws2,
+                                 const uint16_t* y, const uint16_t* dout, const ExpertWeights& wt,
                                  float rho, uint16_t* dx, float* dgate_w, uint16_t* dw13,
                                  uint16_t* dw2, uint16_t* dws13, uint16_t* dws2, void* ws,
                                  hipStream_t s) {
@@ -204,9 +203,19 @@ hipError_t launch_layer_backward(const FfnDims& d, const uint16_t* x, const floa
                        dout, y, pos, topk_w, logits, idx, d.H, d.K, d.E, rho, dyr, dlogit));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // The shared expert's output gradient is dout itself.
-  e = launch_ffn_backward(d, x, perm, offsets, w13, w2, ws13, ws2, dyr, sh ? dout : nullptr, dxr,
-                          sh ? dxs : nullptr, dw13, dw2, dws13, dws2, wsf, s);
+  // The shared expert's output gradient is dout itself.  e4m3 weights take
+  // the FP8 expert backward (operands quantised per 128 along each GEMM's
+  // contraction), bf16 weights the bf16 one.
+  if (wt.fp8)
+    e = launch_ffn_backward_fp8(d, wt.pow2, x, perm, offsets, (const uint8_t*)wt.w13, wt.w13s,
+                                (const uint8_t*)wt.w2, wt.w2s, (const uint8_t*)wt.ws13, wt.ws13s,
+                                (const uint8_t*)wt.ws2, wt.ws2s, dyr, sh ? dout : nullptr, dxr,
+                                sh ? dxs : nullptr, dw13, dw2, dws13, dws2, wsf, s);
+  else
+    e = launch_ffn_backward(d, x, perm, offsets, (const uint16_t*)wt.w13,
+                            (const uint16_t*)wt.w2, (const uint16_t*)wt.ws13,
+                            (const uint16_t*)wt.ws2, dyr, sh ? dout : nullptr, dxr,
+                            sh ? dxs : nullptr, dw13, dw2, dws13, dws2, wsf, s);
   if (e != hipSuccess) return e;
   MOE_TIMED_LAUNCH(s, "gate_dw_kernel",
     hipLaunchKernelGGL(gate_dw_kernel, dim3(d.E, (d.H + LB_THREADS - 1) / LB_THREADS),

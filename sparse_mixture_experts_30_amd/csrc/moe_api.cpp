@@ -655,11 +655,11 @@ moe_status moe_expert_ffn_backward(const moe_config* cfg, int64_t T, const void*
 
 size_t moe_backward_workspace_bytes(const moe_config* cfg, int64_t T) {
   if (check_cfg(cfg) != MOE_OK || check_T(T, cfg) != MOE_OK) return 0;
-  if (cfg->weight_dtype != MOE_BF16 || cfg->act_dtype != MOE_BF16) return 0;
+  if (cfg->weight_dtype == MOE_F32 || cfg->act_dtype != MOE_BF16) return 0;
   moe::FfnDims d{T, T * cfg->num_experts_per_tok, cfg->hidden_size, cfg->moe_intermediate_size,
                  cfg->shared_intermediate_size, cfg->n_routed_experts,
                  cfg->num_experts_per_tok};
-  return moe::layer_backward_ws_bytes(d);
+  return moe::layer_backward_ws_bytes(d, is_fp8(cfg->weight_dtype));
 }
 
 moe_status moe_backward(const moe_config* cfg, int64_t T, const void* x, const moe_weights* w,
@@ -670,8 +670,10 @@ moe_status moe_backward(const moe_config* cfg, int64_t T, const void* x, const m
                         void* stream) {
   CHECK(check_cfg(cfg));
   CHECK(check_T(T, cfg));
-  if (cfg->weight_dtype != MOE_BF16 || cfg->act_dtype != MOE_BF16)
-    return fail(MOE_ERR_UNSUPPORTED, "the layer backward takes bf16 activations and weights");
+  const bool fp8 = is_fp8(cfg->weight_dtype);
+  if (cfg->act_dtype != MOE_BF16 || cfg->weight_dtype == MOE_F32)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "the layer backward takes bf16 activations with bf16 or e4m3 weights");
   if (T == 0) return MOE_OK;
   NONNULL(w);
   if (w->packed)
@@ -699,17 +701,32 @@ moe_status moe_backward(const moe_config* cfg, int64_t T, const void* x, const m
     NONNULL(dws13);
     NONNULL(dws2);
   }
+  if (fp8) {
+    NONNULL(w->w13_scale);
+    NONNULL(w->w2_scale);
+    if (sh) {
+      NONNULL(w->ws13_scale);
+      NONNULL(w->ws2_scale);
+    }
+  }
   moe::FfnDims d{T, T * cfg->num_experts_per_tok, cfg->hidden_size, cfg->moe_intermediate_size,
                  cfg->shared_intermediate_size, cfg->n_routed_experts,
                  cfg->num_experts_per_tok};
-  const size_t need = moe::layer_backward_ws_bytes(d);
+  const size_t need = moe::layer_backward_ws_bytes(d, fp8);
   if (!ws || ws_bytes < need || ((uintptr_t)ws & 255))
     return fail(MOE_ERR_WORKSPACE, "workspace must be 256-byte aligned and >= %zu bytes", need);
+  moe::ExpertWeights ew{w->w13, w->w2, sh ? w->ws13 : nullptr, sh ? w->ws2 : nullptr};
+  if (fp8) {
+    ew.w13s = w->w13_scale;
+    ew.w2s = w->w2_scale;
+    ew.ws13s = sh ? w->ws13_scale : nullptr;
+    ew.ws2s = sh ? w->ws2_scale : nullptr;
+    ew.fp8 = true;
+    ew.pow2 = cfg->weight_dtype == MOE_FP8_E4M3_E8M0;
+  }
   HIPCALL(moe::launch_layer_backward(
               d, (const uint16_t*)x, w->gate_w, logits, topk_idx, topk_w, perm, offsets, pos,
-              (const uint16_t*)y, (const uint16_t*)dout, (const uint16_t*)w->w13,
-              (const uint16_t*)w->w2, (const uint16_t*)(sh ? w->ws13 : nullptr),
-              (const uint16_t*)(sh ? w->ws2 : nullptr), cfg->routed_scaling_factor,
+              (const uint16_t*)y, (const uint16_t*)dout, ew, cfg->routed_scaling_factor,
               (uint16_t*)dx, dgate_w, (uint16_t*)dw13, (uint16_t*)dw2,
               (uint16_t*)(sh ? dws13 : nullptr), (uint16_t*)(sh ? dws2 : nullptr), ws,
               (hipStream_t)stream),

@@ -163,14 +163,24 @@ def test_argument_validation():
                               FAKE, FAKE, FAKE, FAKE, FAKE, dgw, FAKE, FAKE, FAKE, FAKE, ws,
                               ws_bytes, None)
     wg = moe.weights(gate_w=FAKE, w13=FAKE, w2=FAKE, ws13=FAKE, ws2=FAKE)
-    assert lbwd(_cfg(wdtype="fp8"), wg) == moe.MOE_ERR_UNSUPPORTED
+    # e4m3 weights: the FP8 expert backward inside, which needs the block scales
+    assert lbwd(_cfg(wdtype="fp8"), wg) == moe.MOE_ERR_INVALID_ARG
+    wg8 = moe.weights(gate_w=FAKE, w13=FAKE, w13_scale=FAKE, w2=FAKE, w2_scale=FAKE, ws13=FAKE,
+                      ws13_scale=FAKE, ws2=FAKE, ws2_scale=FAKE)
+    assert lbwd(_cfg(wdtype="fp8e8m0"), wg8, ws_bytes=100) == moe.MOE_ERR_WORKSPACE
+    wg8.packed = 1
+    assert lbwd(_cfg(wdtype="fp8"), wg8) == moe.MOE_ERR_UNSUPPORTED
+    assert lbwd(_cfg(act="f32", wdtype="f32"), wg) == moe.MOE_ERR_UNSUPPORTED
     assert lbwd(cfg, moe.weights(gate_w=FAKE, w13=FAKE, w2=FAKE, ws13=FAKE, ws2=FAKE,
                                  packed=1)) == moe.MOE_ERR_UNSUPPORTED
     assert lbwd(cfg, wrow) == moe.MOE_ERR_INVALID_ARG                    # no gate weight
     assert lbwd(cfg, wg, logits=None) == moe.MOE_ERR_INVALID_ARG
     assert lbwd(cfg, wg, dgw=None) == moe.MOE_ERR_INVALID_ARG
     assert lbwd(cfg, wg, ws_bytes=100) == moe.MOE_ERR_WORKSPACE
-    assert moe.moe_backward_workspace_bytes(_cfg(wdtype="fp8"), 16) == 0
+    assert moe.moe_backward_workspace_bytes(_cfg(act="f32", wdtype="f32"), 16) == 0
+    for wd in ("fp8", "fp8e8m0"):
+        assert moe.moe_backward_workspace_bytes(_cfg(wdtype=wd), 16) > \
+            moe.moe_expert_ffn_backward_workspace_bytes(_cfg(wdtype=wd), 16)
     assert moe.moe_backward_workspace_bytes(cfg, 16) > moe.moe_expert_ffn_backward_workspace_bytes(
         cfg, 16)
     assert moe.moe_expert_ffn_backward_workspace_bytes(cfg, 16) > 0

@@ -11,7 +11,7 @@ import synth
 import sparse_mixture_experts_30_amd as moe
 from synth import device as sd
 
-from gpu_util import DEV, host, log, rel_l2, sync
+from gpu_util import DEV, FP8_QUANT_TOL, host, log, rel_l2, sync
 
 pytestmark = pytest.mark.gpu
 
@@ -29,11 +29,28 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("cfg", CASES, ids=lambda c: c.name)
+# e4m3 expert weights (fp32 or power-of-two block scales): the FP8 expert
+# backward inside.  Against the oracle's FP8 layer backward (the forward's
+# expert outputs of the activation-quantised forward, each expert's FP8
+# backward): the GPU's dy rows are rounded to bf16 before they are quantised,
+# and y is the GPU forward's; against the exact backward of the dequantised
+# weights, the e4m3 rounding of every GEMM's operands.
+FP8_CASES = [
+    synth.C5.replace(name="lbwd8-T300-H1024-E16-K4", T=300, H=1024, E=16, G=4, TG=2, K=4, I=256,
+                     Is=256, rho=2.5),
+    synth.C5.replace(name="lbwd8p2-T300-H1024-E16-K4", T=300, H=1024, E=16, G=4, TG=2, K=4,
+                     I=256, Is=256, rho=2.5, wdtype="fp8e8m0"),
+    synth.C5.replace(name="lbwd8-T60-H256-E64-K1-noshared", T=60, H=256, E=64, G=8, TG=2, K=1,
+                     I=128, Is=0, rho=1.0),
+]
+
+
+@pytest.mark.parametrize("cfg", CASES + FP8_CASES, ids=lambda c: c.name)
 def test_layer_backward(cfg):
     log(f"layer backward {cfg.name}")
+    fp8 = cfg.wdtype in ("fp8", "fp8e8m0")
     inp = synth.gen_inputs(cfg)
-    dev = sd.to_device(inp)            # row-major bf16 weights
+    dev = sd.to_device(inp)            # row-major weights (the backward's layout)
     T, H, E, K, I, Is = cfg.T, cfg.H, cfg.E, cfg.K, cfg.I, cfg.Is
     N = T * K
     C = sd.moe_config(cfg)
@@ -47,7 +64,11 @@ def test_layer_backward(cfg):
     y, ys = torch.empty((N, H), **bf), torch.empty((T, H), **bf)
     moe.moe_gate(C, T, dev["x"], dev["gate_w"], dev["bias"], lg, idx, w, ws)
     moe.moe_permute(C, T, idx, counts, offsets, perm, pos, ws)
-    moe.moe_expert_ffn(C, T, dev["x"], perm, offsets, W, y, ys if Is else None, ws)
+    # the forward's expert outputs (e4m3: from the packed layout, which takes
+    # both scale forms)
+    devp = sd.packed_copy(dev) if fp8 else None   # kept alive until the end
+    Wf = sd.weights_struct(devp) if fp8 else W
+    moe.moe_expert_ffn(C, T, dev["x"], perm, offsets, Wf, y, ys if Is else None, ws)
     rng = np.random.default_rng(31)
     dout_b = torch.from_numpy(rng.standard_normal((T, H), dtype=np.float32)).to(torch.bfloat16)
     dout = dout_b.to(DEV)
@@ -62,7 +83,8 @@ def test_layer_backward(cfg):
                      dw2, dws13, dws2, wsb)
     sync()
 
-    ref = oracle.layer_backward(cfg, inp, host(idx), dout_b.float().numpy().astype(np.float64))
+    dout64 = dout_b.float().numpy().astype(np.float64)
+    ref = oracle.layer_backward(cfg, inp, host(idx), dout64, quant_act=fp8)
     cnt = host(counts)
     g13, g2, ggw = host(dw13), host(dw2), host(dgw)
     errs = {"dx": rel_l2(host(dx), ref["dx"]), "dgate_w": rel_l2(ggw, ref["dgate_w"])}
@@ -78,4 +100,17 @@ def test_layer_backward(cfg):
     log("  " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()) +
         f"; experts with rows {int(busy.sum())}/{E}")
     for k, v in errs.items():
-        assert v <= TOL, (k, v)
+        assert v <= (FP8_QUANT_TOL if fp8 else TOL), (k, v)
+    if fp8:
+        ex = oracle.layer_backward(cfg, inp, host(idx), dout64)
+        got = {"dx": host(dx), "dgate_w": ggw, "dw13": g13[busy], "dw2": g2[busy]}
+        exact = {"dx": ex["dx"], "dgate_w": ex["dgate_w"], "dw13": ex["dw13"][busy],
+                 "dw2": ex["dw2"][busy]}
+        if Is:
+            got.update(dws13=host(dws13), dws2=host(dws2))
+            exact.update(dws13=ex["dws13"], dws2=ex["dws2"])
+        e2 = {k: rel_l2(got[k], exact[k]) for k in got}
+        log("  vs the exact backward of the dequantised weights: " +
+            ", ".join(f"{k} {v:.2e}" for k, v in e2.items()))
+        for k, v in e2.items():
+            assert v <= 1e-1, (k, v)

@@ -997,3 +997,97 @@ def test_layer_backward_token_subsets_agree_with_the_whole():
     toks = np.flatnonzero((idx == e).any(axis=1))
     sub = oracle.layer_backward(cfg, inp, idx, dout, tokens=toks, want=("dgate_w",))
     np.testing.assert_allclose(sub["dgate_w"][e], full["dgate_w"][e], rtol=1e-12, atol=1e-14)
+
+
+# FP8 layer backward (e4m3 expert weights, quant_act): the gate's gradient is
+# that of the activation-quantised forward (F2) with the routing held -- the
+# F2 expert outputs do not depend on the gate weight, so central differences
+# of L = sum_t <dout_t, out_F2_t> in gate_w pin the combine and routing-weight
+# terms; the experts' terms are the FP8 expert backward, pinned above, and
+# differ from the exact backward of the dequantised weights by the e4m3
+# rounding of their operands.
+LB8_CFG = synth.C5.replace(name="lbwd8-T6-H128-E4-K2", T=6, H=128, E=4, G=2, TG=1, K=2, I=128,
+                           Is=128, rho=2.5)
+
+
+def test_fp8_layer_backward_gate_gradient_matches_f2_differences():
+    cfg = LB8_CFG
+    inp = synth.gen_inputs(cfg)
+    lg = oracle.logits(inp["x"], cfg.act, inp["gate_w"])
+    idx, _, margin = oracle.route_f64(cfg, lg, inp["bias"])
+    assert margin.min() > 1e-4
+    dout = np.random.default_rng(24).standard_normal((cfg.T, cfg.H))
+    b = oracle.layer_backward(cfg, inp, idx, dout, want=("dgate_w",), quant_act=True)
+    eps = 2.0 ** -12
+
+    def loss(gw):
+        lg2 = oracle.logits(inp["x"], cfg.act, gw)
+        idx2, _, _ = oracle.route_f64(cfg, lg2, inp["bias"])
+        assert np.array_equal(idx2, idx), "perturbation changed the routing"
+        out = oracle.layer(cfg, inp, idx, oracle.routing_weights(cfg, lg2, idx), quant_act=True)
+        return float((out * dout).sum())
+
+    gw = inp["gate_w"].astype(np.float64)
+    num = np.zeros_like(gw)
+    for e in np.unique(idx):
+        for h in range(cfg.H):
+            p, m = gw.copy(), gw.copy()
+            p[e, h] += eps
+            m[e, h] -= eps
+            num[e, h] = (loss(p) - loss(m)) / (2 * eps)
+    np.testing.assert_allclose(b["dgate_w"], num, rtol=1e-5, atol=1e-5 * np.abs(num).max())
+    # the unquantised mode gives a different (dequantised-forward) gate gradient
+    b1 = oracle.layer_backward(cfg, inp, idx, dout, want=("dgate_w",))
+    d = np.linalg.norm(b1["dgate_w"] - b["dgate_w"]) / np.linalg.norm(b["dgate_w"])
+    assert 1e-4 < d < 0.2, d
+
+
+def test_fp8_layer_backward_experts_are_the_fp8_expert_backward():
+    # quant_act moves every expert term by about the e4m3 rounding of its
+    # operands; without it the layer backward of e4m3 weights is the exact
+    # backward of the dequantised weights (central differences in x)
+    cfg = LB8_CFG
+    inp = synth.gen_inputs(cfg)
+    lg = oracle.logits(inp["x"], cfg.act, inp["gate_w"])
+    idx, _, _ = oracle.route_f64(cfg, lg, inp["bias"])
+    dout = np.random.default_rng(25).standard_normal((cfg.T, cfg.H))
+    bq = oracle.layer_backward(cfg, inp, idx, dout, quant_act=True)
+    be = oracle.layer_backward(cfg, inp, idx, dout)
+    for k in ("dx", "dw13", "dw2", "dws13", "dws2"):
+        busy = np.unique(idx) if k in ("dw13", "dw2") else slice(None)
+        d = np.linalg.norm(bq[k][busy] - be[k][busy]) / np.linalg.norm(be[k][busy])
+        assert 1e-3 < d < 0.15, (k, d)
+    # the exact mode's dx: central differences of the dequantised-weight
+    # forward in x would need bf16 x perturbations; the routing weights and
+    # experts are differentiated in fp64 through the float x the oracle reads
+    xf = (inp["x"].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    w = oracle.routing_weights(cfg, lg, idx)
+    t, h = 3, 17
+    eps = 2.0 ** -10
+
+    def loss(xv):
+        x2 = dict(inp, x=xv.astype(np.float32))
+        cf = cfg.replace(act="f32")
+        lg2 = oracle.logits(x2["x"], "f32", inp["gate_w"])
+        out = oracle.layer(cf, x2, idx, oracle.routing_weights(cf, lg2, idx))
+        return float((out * dout).sum())
+
+    p, m = xf.copy(), xf.copy()
+    p[t, h] += eps
+    m[t, h] -= eps
+    num = (loss(p) - loss(m)) / (2 * eps)
+    assert abs(be["dx"][t, h] - num) <= 1e-5 * max(1.0, abs(num)), (be["dx"][t, h], num)
+    assert np.array_equal(w, oracle.routing_weights(cfg, lg, idx))
+
+
+def test_round_bf16_is_torch_bf16_cast():
+    # the bf16 rounding of the FP8 layer backward's dy rows: fp32 first, then
+    # nearest-even to bf16, as torch's cast does it (ties, subnormals, signs)
+    import torch
+    rng = np.random.default_rng(26)
+    v = rng.standard_normal(200000) * np.exp(rng.uniform(-90, 90, 200000))
+    v[:4] = [0.0, -0.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8]   # exact ties
+    got = oracle.round_bf16(v)
+    ref = torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16).float().double().numpy()
+    np.testing.assert_array_equal(got, ref)
+    assert got[2] == 1.0 and got[3] == 1.0 + 2.0 ** -6
