@@ -401,3 +401,74 @@ def test_layer_backward_v3_bf16_T4096_sampled():
         log(f"  expert {ex} ({len(tok)} rows): dW13 relL2 {e13:.3e}, dW2 relL2 {e2:.3e}")
         assert e13 <= 2e-2 and e2 <= 2e-2, ex
     log(f"  oracle {time.time() - t0:.1f}s")
+
+
+def test_layer_backward_v3_fp8e8m0_T8192_sampled():
+    """Backward of the whole FP8 layer at the benchmark's e4m3 workload
+    (T = 8192, V3 shape, power-of-two block scales; the forward on the packed
+    weights, the backward on the row-major ones) against the oracle's FP8
+    layer backward: sampled dx rows (a row's dx depends on its own rows
+    alone), the gate weight's gradient row of the expert with the fewest
+    rows, and that expert's whole dW13 and dW2 (its column tiles need all its
+    rows), each within 1e-2."""
+    cfg = synth.C5P
+    inp, dev = _inputs(cfg)
+    row = dict(dev, **_Weights.row["fp8e8m0"])
+    row.pop("packed", None)
+    T, H, E, K, I, Is = cfg.T, cfg.H, cfg.E, cfg.K, cfg.I, cfg.Is
+    N = T * K
+    C = sd.moe_config(cfg)
+    log(f"{cfg.name}: FP8 backward of the layer")
+    ws = sd.workspace(cfg, T)
+    f32, i32 = dict(dtype=torch.float32, device=DEV), dict(dtype=torch.int32, device=DEV)
+    bf = dict(dtype=torch.bfloat16, device=DEV)
+    lg, idx, w = torch.empty((T, E), **f32), torch.empty((T, K), **i32), torch.empty((T, K), **f32)
+    counts, offsets = torch.empty(E, **i32), torch.empty(E + 1, **i32)
+    perm, pos = torch.empty(N, **i32), torch.empty(N, **i32)
+    y, ys = torch.empty((N, H), **bf), torch.empty((T, H), **bf)
+    moe.moe_gate(C, T, dev["x"], dev["gate_w"], dev["bias"], lg, idx, w, ws)
+    moe.moe_permute(C, T, idx, counts, offsets, perm, pos, ws)
+    moe.moe_expert_ffn(C, T, dev["x"], perm, offsets, sd.weights_struct(dev), y, ys, ws)
+    rng = np.random.default_rng(41)
+    dout_b = torch.from_numpy(rng.standard_normal((T, H), dtype=np.float32)).to(torch.bfloat16)
+    dout_np = dout_b.float().numpy().astype(np.float64)
+    dx, dgw = torch.empty((T, H), **bf), torch.empty((E, H), **f32)
+    dw13, dw2 = torch.empty((E, 2 * I, H), **bf), torch.empty((E, H, I), **bf)
+    dws13, dws2 = torch.empty((2 * Is, H), **bf), torch.empty((H, Is), **bf)
+    wsb = torch.empty(moe.moe_backward_workspace_bytes(C, T), dtype=torch.uint8, device=DEV)
+    moe.moe_backward(C, T, row["x"], sd.weights_struct(row), lg, idx, w, perm, offsets, pos, y,
+                     dout_b.to(DEV), dx, dgw, dw13, dw2, dws13, dws2, wsb)
+    sync()
+    for name, a in (("dx", dx), ("dgate_w", dgw), ("dW13", dw13), ("dW2", dw2),
+                    ("dW13_shared", dws13), ("dW2_shared", dws2)):
+        assert bool(torch.isfinite(a).all()), name
+    idx_h, w_h, cnt, offs_h, perm_h = host(idx), host(w), host(counts), host(offsets), host(perm)
+    for e in np.flatnonzero(cnt == 0):
+        assert not bool(dw13[e].any()) and not bool(dw2[e].any()), f"expert {e} without rows"
+
+    t0 = time.time()
+    toks = _samples(T, 8, 71)
+    ref = oracle.layer_backward(cfg, inp, idx_h, dout_np, tokens=toks, want=("dx",),
+                                quant_act=True)["dx"]
+    g = host(dx[torch.from_numpy(toks).to(DEV)])
+    worst = max(rel_l2(g[j], ref[j]) for j in range(len(toks)))
+    log(f"  dx: {len(toks)} tokens, worst row relL2 {worst:.3e}")
+    assert worst <= FP8_QUANT_TOL
+
+    busy = np.flatnonzero(cnt > 0)
+    e = int(busy[np.argmin(cnt[busy])])
+    etoks = np.flatnonzero((idx_h == e).any(axis=1))
+    ref = oracle.layer_backward(cfg, inp, idx_h, dout_np, tokens=etoks, want=("dgate_w",),
+                                quant_act=True)
+    r = rel_l2(host(dgw[e]), ref["dgate_w"][e])
+    log(f"  dgate_w row of expert {e} ({len(etoks)} tokens): relL2 {r:.3e}")
+    assert r <= FP8_QUANT_TOL
+
+    # the expert's rows in sorted order, dy = w dout as the GPU rounds it
+    f = perm_h[offs_h[e]:offs_h[e + 1]]
+    dyr = oracle.round_bf16(w_h.ravel()[f].astype(np.float64)[:, None] * dout_np[f // K])
+    ref = oracle.ffn_backward(cfg, inp, e, f // K, dyr, want=("dw13", "dw2"), quant_act=True)
+    e13, e2 = rel_l2(host(dw13[e]), ref["dw13"]), rel_l2(host(dw2[e]), ref["dw2"])
+    log(f"  expert {e} ({len(f)} rows): dW13 relL2 {e13:.3e}, dW2 relL2 {e2:.3e}")
+    assert e13 <= FP8_QUANT_TOL and e2 <= FP8_QUANT_TOL
+    log(f"  oracle {time.time() - t0:.1f}s")
