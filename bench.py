@@ -147,6 +147,9 @@ def main():
     ap.add_argument("--fused", action="store_true",
                     help="time moe_forward_decode_fused (the decode layer in one launch) as the "
                          "step")
+    ap.add_argument("--gate-fused", action="store_true",
+                    help="gate + permute workload: run the gate and the selection as one kernel "
+                         "(MOE_GATE_FUSED) in the timed step")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the expert-FFN backward measurement of the bf16 layer workloads")
     ap.add_argument("--row-major", action="store_true",
@@ -225,8 +228,12 @@ def main():
                                     (["moe_forward_decode_fused"] if fused_ok else []))
     if args.fused and not fused_ok:
         sys.exit("--fused: the one-launch decode layer takes T <= 32, bf16, packed weights")
-    entry = None if gate_only else ("moe_forward_decode_fused" if args.fused else
-                                    "moe_forward_overlap" if args.overlap else "moe_forward")
+    if gate_only:
+        entry = ("moe_gate (MOE_GATE_FUSED) + moe_permute" if args.gate_fused
+                 else "moe_gate + moe_permute")
+    else:
+        entry = ("moe_forward_decode_fused" if args.fused else
+                 "moe_forward_overlap" if args.overlap else "moe_forward")
 
     def forward(name):
         if name == "moe_forward_overlap":
@@ -235,6 +242,11 @@ def main():
             moe.moe_forward_decode_fused(C, T, d["x"], W, out, ws, stream=stream)
         else:
             moe.moe_forward(C, T, d["x"], W, out, ws, stream=stream)
+
+    if args.gate_fused:
+        if not gate_only:
+            sys.exit("--gate-fused: for the gate + permute workload")
+        moe.moe_set_gate_mode(moe.MOE_GATE_FUSED)
 
     def step():
         if gate_only:
@@ -326,7 +338,7 @@ def main():
                           "step_entry_point_ms_same_rounds": round(med[entry], 4)})
             log(f"[bench] {e}: {med[e]:.3f} ms/step (step entry point {entry} "
                 f"{med[entry]:.3f} ms in the same rounds)")
-    if gate_only and not args.profile_only:
+    if gate_only and not args.profile_only and not args.gate_fused:
         # The gate and selection in one kernel (MOE_GATE_FUSED) against the
         # default split kernels: alternating rounds, cold caches, medians.
         times = {moe.MOE_GATE_SPLIT: [], moe.MOE_GATE_FUSED: []}

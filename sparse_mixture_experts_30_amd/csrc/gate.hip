@@ -375,6 +375,15 @@ gate_select_fused_kernel(const uint16_t* __restrict__ x, const u32x4* __restrict
   }
   __syncthreads();
 
+  // The logits rows out of LDS, consecutive threads on consecutive experts.
+  if (logits_out) {
+    const int rows = (int)min((int64_t)FG_T, T - t0);
+    for (int i = tid; i < rows * E; i += FG_THREADS) {
+      const int r = i / E, e = i - r * E;
+      logits_out[(t0 + r) * E + e] = s_lg[r * lde + e];
+    }
+  }
+
   // Selection: thread q of token tk's team reads its experts' logits.
   const int tk = tid / SEL_TEAM, q = tid % SEL_TEAM;
   const int64_t t = t0 + tk;
@@ -390,8 +399,8 @@ gate_select_fused_kernel(const uint16_t* __restrict__ x, const u32x4* __restrict
       for (int i = 0; i < 4; ++i) lg[j + i] = v[i];
     }
   }
-  select_team(lg, q, valid, bias, s_g + tk * SEL_TG, E, G, TG, K, rho,
-              logits_out ? logits_out + tc * E : nullptr, idx_out + tc * K, w_out + tc * K);
+  select_team(lg, q, valid, bias, s_g + tk * SEL_TG, E, G, TG, K, rho, idx_out + tc * K,
+              w_out + tc * K);
 }
 
 }  // namespace

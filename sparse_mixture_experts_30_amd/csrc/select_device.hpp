@@ -191,12 +191,12 @@ inline bool select_team_ok(int E, int G, int TG, int K) {
 
 // lg: this lane's logits (experts q E/8 + j, j < E/8); s_grow: the token's
 // LDS row of SEL_TG floats (shared by the team).  Contains a workgroup
-// barrier: every thread of the workgroup calls it.  Writes the logits row
-// (if not null), ids and weights only when `valid`.
+// barrier: every thread of the workgroup calls it.  Writes the ids and
+// weights only when `valid`.
 __device__ __forceinline__ void select_team(const float (&lg)[SEL_TQ], int q, bool valid,
                                             const float* __restrict__ bias, float* s_grow, int E,
-                                            int G, int TG, int K, float rho,
-                                            float* logits_row, int32_t* idx_row, float* w_row) {
+                                            int G, int TG, int K, float rho, int32_t* idx_row,
+                                            float* w_row) {
   const int EQ = E / SEL_TEAM, e0 = q * EQ, Eg = E / G;
   float sc[SEL_TQ], c[SEL_TQ];
 #pragma unroll
@@ -204,7 +204,6 @@ __device__ __forceinline__ void select_team(const float (&lg)[SEL_TQ], int q, bo
     if (j < EQ) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (logits_row && valid) logits_row[e0 + j + i] = lg[j + i];   // any 4-byte alignment
         const double sd = 1.0 / (1.0 + exp(-(double)lg[j + i]));
         sc[j + i] = (float)sd;
         float ci = sc[j + i] + bias[e0 + j + i];
