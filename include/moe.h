@@ -35,10 +35,11 @@
  *   - Layouts are row-major.  Weight matrices are stored "output rows x
  *     input columns" with the input dimension contiguous.
  *   - T == 0 is a no-op returning MOE_OK.
- *   - Global state: the kernel timer below (off by default), kernel
- *     attributes set once per process on first use, the two fork/join
- *     events of moe_forward_overlap (per device and host thread), and the
- *     static workspace of moe_forward_noalloc (one per device).  Calls on
+ *   - Global state: the kernel timer below (off by default), the gate mode
+ *     (moe_set_gate_mode, split by default), kernel attributes set once per
+ *     process on first use, the two fork/join events of moe_forward_overlap (per device and host
+ *     thread), and the static workspace of moe_forward_noalloc (one per
+ *     device).  Calls on
  *     different streams with different workspaces may run concurrently.
  *   - Results are deterministic: no floating-point atomics anywhere, so two
  *     runs on the same inputs give bitwise-identical outputs.
