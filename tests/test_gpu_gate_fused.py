@@ -168,3 +168,35 @@ def test_gate_fused_v3_T16384(fused_mode):
     _, kernels = _timed_gate(cfg, dev, cfg.T)
     assert "gate_select_fused_kernel" not in kernels
     assert "select_kernel" in kernels, kernels
+
+
+@pytest.mark.parametrize("wdtype", ["bf16", "fp8e8m0"])
+def test_forward_with_fused_gate(wdtype, fused_mode):
+    """moe_forward with the fused gate (packed weights): routing under the
+    oracle's contract, counts and permutation exact, the layer output
+    within the dtype's tolerance (bf16 2e-2; e4m3 1e-2 against the
+    activation-quantised oracle)."""
+    from gpu_util import layer_reference, rel_l2, run_forward
+    cfg = _cfg(f"fg-layer-{wdtype}-T150-H512-E64-G8-K8", T=150, H=512, E=64, G=8, TG=4, K=8,
+               wdtype=wdtype)
+    inp = synth.gen_inputs(cfg)
+    dev = sd.packed_copy(sd.to_device(inp))
+    moe.moe_kernel_timer_read()
+    moe.moe_kernel_timer_enable(True)
+    try:
+        r = run_forward(cfg, dev, cfg.T)
+    finally:
+        moe.moe_kernel_timer_enable(False)
+    kernels = moe.moe_kernel_timer_read()
+    assert "gate_select_fused_kernel" in kernels and "select_kernel" not in kernels, kernels
+    idx_c, _ = oracle.route_f32(cfg, r["logits"], inp["bias"])
+    np.testing.assert_array_equal(r["idx"], idx_c)
+    rc, _, rp, _ = oracle.permute(r["idx"], cfg.E)
+    np.testing.assert_array_equal(r["counts"], rc)
+    np.testing.assert_array_equal(r["perm"], rp)
+    tokens = np.arange(cfg.T)
+    fp8 = wdtype != "bf16"
+    ref, _ = layer_reference(cfg, inp, r["idx"], tokens, quant_act=fp8)
+    rel = rel_l2(r["out"], ref)
+    log(f"  layer with the fused gate ({wdtype}): relL2 {rel:.3e}")
+    assert rel <= (1e-2 if fp8 else 2e-2)
