@@ -200,3 +200,17 @@ def test_forward_with_fused_gate(wdtype, fused_mode):
     rel = rel_l2(r["out"], ref)
     log(f"  layer with the fused gate ({wdtype}): relL2 {rel:.3e}")
     assert rel <= (1e-2 if fp8 else 2e-2)
+
+
+@pytest.mark.parametrize("cfg", [
+    _cfg("fg-fallback-T70-H256-E48-G4-TG2-K4", T=70, H=256, E=48, G=4, TG=2, K=4),      # E % 32
+    _cfg("fg-fallback-T70-H256-E96-G3-TG2-K4", T=70, H=256, E=96, G=3, TG=2, K=4),      # groups
+    _cfg("fg-fallback-T70-H256-E64-G8-TG4-K17", T=70, H=256, E=64, G=8, TG=4, K=17),    # top_k
+], ids=lambda c: c.name)
+def test_gate_fused_mode_falls_back_for_other_shapes(cfg, fused_mode):
+    """Shapes the fused kernel does not take run the split kernels in fused
+    mode, with the same routing contract."""
+    inp, dev = _gate_inputs(cfg)
+    (lg, idx, w), kernels = _timed_gate(cfg, dev, cfg.T)
+    assert "gate_select_fused_kernel" not in kernels and "select_kernel" in kernels, kernels
+    check_routing(cfg, inp["x"], inp["gate_w"], inp["bias"], lg, idx, w, cfg.name)
