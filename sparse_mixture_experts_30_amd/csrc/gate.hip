@@ -257,25 +257,24 @@ select_kernel(const float* __restrict__ part, int ksplit, const float* __restric
 
 // ---------------------------------------------------------------- gate + selection in one kernel
 //
-// For batches that fill the GPU with 64-token tiles: one workgroup computes
-// the logits of 64 tokens for every expert over the whole hidden size
-// (eight waves, wave w the 32 experts of block w, three bf16 weight parts
-// per k slice as above), keeps them in LDS and selects in the same launch,
-// so no partial sums go to memory.  The selection is spread over teams of
-// FG_TEAM threads per token: thread q of a team holds experts
-// [q E/8, (q+1) E/8) in registers, the group scores are merged with lane
-// shuffles inside the team and exchanged through LDS, and each of the K
-// picks is the team's butterfly maximum (larger choice wins, equal choices
-// go to the lower id).  The arithmetic of every score, group score and
-// weight is the one select_token uses, so the routing is the same function
-// of the fp32 logits.
+// The gate mode MOE_GATE_FUSED: one workgroup computes the logits of 64
+// tokens for every expert over the whole hidden size (eight waves, wave w
+// the 32 experts of block w, three bf16 weight parts per k slice as above),
+// keeps them in LDS and selects in the same launch, so no partial sums go to
+// memory.  The selection is spread over teams of SEL_TEAM threads per token
+// (select_team: thread q of a team holds experts [q E/8, (q+1) E/8) in
+// registers, the group scores are merged with lane shuffles inside the team
+// and exchanged through LDS, and each of the K picks is the team's butterfly
+// maximum); its arithmetic is select_token's, so the routing is the same
+// function of the fp32 logits.  Holding all experts of its tokens, a
+// workgroup can hold only 64 tokens if a 16384-token batch is to fill 256
+// compute units, half the split kernel's 128: each weight byte from L2 then
+// feeds half as many MFMAs, and the split kernels stay the default.
 constexpr int FG_T = 64;                 // tokens per workgroup
 constexpr int FG_WAVES = 8;              // wave w: expert block w
 constexpr int FG_THREADS = FG_WAVES * 64;
 static_assert(FG_THREADS == FG_T * SEL_TEAM, "one selection team per token");
-#ifndef FG_DEPTH
-#define FG_DEPTH 2                       // k steps of weights in flight per wave
-#endif
+constexpr int FG_DEPTH = 2;              // k steps of weights in flight per wave
 
 __host__ __device__ constexpr int fg_lde(int E) { return E + 4; }   // logit row stride (floats)
 
